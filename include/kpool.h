@@ -1,0 +1,180 @@
+/*
+ * kpool.h -- C ABI of the KPool-DSA sparse-attention layer (GLM-5.3-Flash) for AMD Instinct MI355X (gfx950).
+ *
+ * The layer runs in four calls, each a hand-written HIP kernel enqueued on the caller's stream:
+ *
+ *   kpool_compress     pools of P consecutive tokens -> one pooled index key per complete pool
+ *   dsa_indexer_score  head-weighted ReLU scores of the complete pools each query may see
+ *   dsa_topk_select    causal top-k pools per query, the incomplete tail pool always kept
+ *   sparse_mla_attn    nope-only absorbed MLA of each query over the tokens of its selected pools
+ *
+ * Sources (page title, section):
+ *   [MAX "max.pipelines.architectures.glm5_next" API page]: fields index_kpool (tokens per scoring pool),
+ *     index_kpool_always_select_tail, index_kpool_compress (gate logits plus a learned intra-pool position
+ *     embedding weight each pool's tokens), mla_use_nope (no rotary embedding), build_layers() (576-wide latent
+ *     carrying 64 rotary columns that are all zero), mla_head_dim.
+ *   [llama.cpp pull request "add GLM-5.3-Flash (GLM5-Next) support", "What I implemented new"]: pools of 4
+ *     consecutive tokens are scored and the incomplete tail is always kept; the indexer cache holds key and gate
+ *     per token; attention layers are nope-only MLA.  Same page, soft_max crash report: the pooling softmax is
+ *     over each pool's 4 tokens per channel, and a launch that put the pool axis on grid y failed beyond 65,535
+ *     pools -- here no grid axis other than x ever scales with pools, tokens or queries.
+ *   [GLM-5.3-Flash model card, "Raw config fields"]: index_head_dim 128, index_n_heads 32, index_kpool 4,
+ *     index_topk 2048, kv_lora_rank 512, num_attention_heads 64, qk_head_dim 256.
+ *   The layer's specification fixes what the pages leave open: pooling = softmax over (gate + position term)
+ *   within the pool, then a weighted sum of the keys; score = sum_h w_h * ReLU(q_h . k_pool); ties toward the
+ *   lower pool index.
+ *
+ * Conventions shared by every call
+ *   - Ownership: the caller owns every buffer.  The library allocates no device memory and keeps no state
+ *     between calls; scratch comes in through the workspace arguments, sized by the *_workspace_size queries.
+ *   - Pointers: "device" pointers are HIP device memory; "host" pointers are read during the call only.
+ *     Device buffers must be 16-byte aligned.
+ *   - Streams: all work is enqueued on `stream` (a hipStream_t; NULL = the null stream) with no host or device
+ *     synchronisation.  Calls on different streams are safe when their outputs do not overlap.
+ *   - Errors: each call returns a kp_status.  On a validation failure nothing is launched and kp_last_error()
+ *     (thread-local) says why.  KP_ERR_LAUNCH reports the HIP launch error.  Faults inside a kernel surface at
+ *     the caller's next synchronisation.  The library never aborts the process.
+ *   - Data contract (not checked): positions lie within the caches' filled extent, block-table entries that a
+ *     query can reach are valid pages, the rotary columns v_dim..latent_dim-1 of q and of the latent cache are
+ *     zero, values are finite, every queries->pos[i] <= queries->max_pos.
+ *   - Positions: a query at absolute position i (0-based) sees the complete pools p < n_c = (i+1) / P; its
+ *     trailing pool tau = i / P is incomplete when r = (i+1) mod P != 0 and then holds tokens P*tau .. i.
+ *   - Paging: both caches share one block table of physical page ids.  A page holds `page_tokens` latent rows
+ *     and `page_tokens / pool` pooled-key rows; page_tokens is a power of two and a multiple of `pool`, so no
+ *     pool straddles a page.  A contiguous cache is a block table 0, 1, 2, ...
+ *   - Widths: pool ids, positions and counts are int32; all byte offsets are computed in 64 bits.
+ */
+#ifndef KPOOL_H
+#define KPOOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KP_OK = 0,
+  KP_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misaligned buffer, inconsistent dims           */
+  KP_ERR_UNSUPPORTED = -2,   /* valid but not built: dtype / head dim / value width combination       */
+  KP_ERR_WORKSPACE = -3,     /* workspace missing or smaller than the matching *_workspace_size query */
+  KP_ERR_LAUNCH = -4         /* the HIP launch failed; kp_last_error() holds hipGetErrorString         */
+} kp_status;
+
+typedef enum { KP_DTYPE_F32 = 0, KP_DTYPE_BF16 = 1 } kp_dtype;
+
+/* Layer dimensions (host struct, read during the call only). */
+typedef struct {
+  int32_t pool;        /* P: tokens per pool (index_kpool = 4); power of two, 1..32                         */
+  int32_t idx_dim;     /* D: index head dim (128); built: 32, 128                                            */
+  int32_t idx_heads;   /* Hi: index heads (32); 1..32                                                        */
+  int32_t topk;        /* k: pools kept per query, the forced tail included (2048); >= 1                     */
+  int32_t heads;       /* H: MLA heads (64); 1..64                                                           */
+  int32_t latent_dim;  /* L: latent row width (576 = 512 + 64 zero rotary columns); >= v_dim                */
+  int32_t v_dim;       /* V: value / nope width (512); built: 512, 64 (64 also for f32)                      */
+  int32_t page_tokens; /* tokens per cache page; power of two, multiple of pool                              */
+  int32_t dtype;       /* kp_dtype: storage type of keys, gates, ape, q_idx, q, both caches and out          */
+  float scale;         /* attention softmax scale (1/sqrt(qk_head_dim) = 1/16 for the model)                 */
+} kp_dims;
+
+/* The two paged caches of one layer (host struct; the pointers are device memory). */
+typedef struct {
+  void* latent;                /* [n_pages, page_tokens, latent_dim] storage dtype                           */
+  void* pooled;                /* [n_pages, page_tokens / pool, idx_dim] storage dtype                       */
+  const int32_t* block_table;  /* [n_seq, bt_stride] physical page ids                                       */
+  int32_t bt_stride;           /* entries per block-table row                                                */
+} kp_cache;
+
+/* A batch of queries (host struct; seq and pos are device arrays). */
+typedef struct {
+  int32_t n_q;                 /* number of queries; 0 is a valid empty call                                 */
+  const int32_t* seq;          /* [n_q] block-table row of each query's sequence                             */
+  const int32_t* pos;          /* [n_q] absolute 0-based position of each query                              */
+  int32_t max_pos;             /* host: an upper bound of pos[]; sizes the grids without a device sync       */
+  int32_t group;               /* host hint: runs of `group` consecutive queries that share a sequence (a
+                                  prefill chunk); 1 = no promise.  Results never depend on it: a run that
+                                  breaks the promise is processed one query at a time.                       */
+} kp_queries;
+
+/*
+ * kpool_compress -- pooled index keys of complete pools.
+ *   [MAX glm5_next API page, index_kpool_compress]; [llama.cpp PR, "What I implemented new"; soft_max crash
+ *   report: softmax over a pool's tokens per channel]; formula per the layer's specification.
+ *   For pool i (0 <= i < n_pools), channel c < D and token j < P of the pool:
+ *     z_j = gate[j, c] + ape[j, c];  a = softmax_j(z);  pooled[c] = sum_j a_j * key[j, c]
+ *   computed in fp32 as key[0,c] + sum_j a_j * (key[j,c] - key[0,c]) (equal in exact arithmetic; it makes a
+ *   constant key pool to exactly that key), rounded once (nearest-even) to the storage dtype and written to
+ *   row pool_id[i] of sequence pool_seq[i] of the pooled cache.
+ *   keys, gates: device [n_src, P, D]; pool i reads source row src[i] (src NULL: row i).  A decode step passes
+ *     its per-sequence ring of pending key/gate rows directly, with src = the sequences whose pool completes.
+ *   ape: device [P, D].  pool_seq, pool_id: device [n_pools].
+ *   Errors: KP_ERR_INVALID_ARG on null pointers (n_pools > 0) or bad dims.
+ */
+kp_status kpool_compress(const kp_dims* dims, const kp_cache* cache, int32_t n_pools, const void* keys,
+                         const void* gates, const int32_t* src, const void* ape, const int32_t* pool_seq,
+                         const int32_t* pool_id, void* stream);
+
+/*
+ * dsa_indexer_score -- scores of every complete pool each query can see.
+ *   [llama.cpp PR, "What I implemented new": the indexer scores pools]; [GLM-5.3-Flash model card, "Raw
+ *   config fields": 32 index heads of dim 128]; formula per the layer's specification:
+ *     scores[q, p] = sum_{h < Hi} w[q, h] * max(0, sum_{c < D} q_idx[q, h, c] * pooled[seq(q), p, c])
+ *   for p < n_c(pos(q)), accumulated in fp32 (products of storage values are exact in fp32).  One pooled key
+ *   per pool serves every index head.  Columns p >= n_c(pos(q)) of a row are not written.
+ *   q_idx: device [n_q, Hi, D] storage dtype; w: device [n_q, Hi] fp32 (any sign).
+ *   scores: device fp32 [n_q, ld_scores], ld_scores >= (max_pos + 1) / P.
+ *   MFMA: 32 index heads form the M side of a 32x32x16 bf16 (32x32x2 f32) tile; pools are N; D is K.
+ *   Errors: KP_ERR_INVALID_ARG (null pointers, ld_scores too small), KP_ERR_UNSUPPORTED (D, dtype).
+ */
+kp_status dsa_indexer_score(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries,
+                            const void* q_idx, const float* w, float* scores, int64_t ld_scores, void* stream);
+
+/*
+ * dsa_topk_select -- causal top-k pools of each query, the incomplete tail forced.
+ *   [MAX glm5_next API page, index_kpool_always_select_tail: the incomplete trailing pool is always visible];
+ *   [llama.cpp PR, "What I implemented new": always keeps the incomplete tail]; [GLM-5.3-Flash model card,
+ *   "Raw config fields": index_topk 2048, counted in pools]; ties toward the lower pool index per the layer's
+ *   specification.  For a query at position i:
+ *     budget = min(k - [r != 0], n_c); keep the `budget` complete pools first in the order (score desc,
+ *     pool index asc), with -0.0 equal to +0.0; add tau when r != 0.
+ *   sel: device int32 [n_q, k], the kept pool ids ascending, padded with -1; n_sel: device int32 [n_q].
+ *   scores: as written by dsa_indexer_score (only columns < n_c are read).
+ *   workspace: device, at least dsa_topk_workspace_size bytes (NULL when that is 0).
+ *   Errors: KP_ERR_INVALID_ARG, KP_ERR_WORKSPACE.
+ */
+size_t dsa_topk_workspace_size(const kp_dims* dims, const kp_queries* queries);
+kp_status dsa_topk_select(const kp_dims* dims, const kp_queries* queries, const float* scores,
+                          int64_t ld_scores, int32_t* sel, int32_t* n_sel, void* workspace, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * sparse_mla_attn -- nope-only absorbed MLA over the selected tokens.
+ *   [llama.cpp PR, "What I implemented new": attention layers are nope-only MLA]; [MAX glm5_next API page,
+ *   mla_use_nope (no rotary embedding), build_layers() (576-wide latent, 64 rotary columns all zero)];
+ *   [GLM-5.3-Flash model card, "Raw config fields": kv_lora_rank 512, 64 heads].  For query q and head h:
+ *     S = tokens of the selected complete pools, plus tokens P*tau .. i of the tail pool when it is selected;
+ *     l_t = scale * q[h] . latent[t]  (the key is the latent row; columns >= V are zero by contract and are
+ *     not read);  a = softmax_t(l);  out[q, h, :] = sum_t a_t * latent[t, :V];  lse[q, h] = ln sum_t e^{l_t}.
+ *   q: device [n_q, H, L] storage dtype; sel / n_sel: as written by dsa_topk_select.
+ *   out: device [n_q, H, V] storage dtype (rounded once, nearest-even); lse: device fp32 [n_q, H] or NULL.
+ *   Accumulation in fp32; softmax weights enter the value product in the storage dtype.
+ *   workspace: device, at least sparse_mla_workspace_size bytes (split-KV partials; NULL when that is 0).
+ *   Errors: KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED (V, H, dtype), KP_ERR_WORKSPACE.
+ */
+size_t sparse_mla_workspace_size(const kp_dims* dims, const kp_queries* queries);
+kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
+                          const int32_t* sel, const int32_t* n_sel, void* out, float* lse, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/* Message of the last failed call on this thread ("" if none).  Owned by the library. */
+const char* kp_last_error(void);
+
+/* ABI version of this header (bumped on any signature or struct change). */
+int32_t kp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KPOOL_H */

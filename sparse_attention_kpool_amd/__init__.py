@@ -1,0 +1,193 @@
+"""Python binding of the KPool-DSA sparse-attention library (libkpool.so, C ABI in include/kpool.h).
+
+Argument marshalling only: every stage runs in the library's HIP kernels for gfx950.  torch supplies device
+memory and the current stream; nothing else.  There is no fallback: if libkpool.so is missing or fails to load,
+every call raises.
+
+The four calls keep the C names:
+    kpool_compress, dsa_indexer_score, dsa_topk_select, sparse_mla_attn
+plus the workspace queries dsa_topk_workspace_size and sparse_mla_workspace_size.  Outputs and workspaces are
+caller-allocated tensors, as in the C ABI.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkpool.so")
+
+KP_OK, KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED, KP_ERR_WORKSPACE, KP_ERR_LAUNCH = 0, -1, -2, -3, -4
+KP_DTYPE_F32, KP_DTYPE_BF16 = 0, 1
+ABI_VERSION = 1
+
+EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk_select",
+            "sparse_mla_workspace_size", "sparse_mla_attn", "kp_last_error", "kp_abi_version")
+
+
+class KpError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed ({status}): {msg}")
+        self.status = status
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("pool", ctypes.c_int32), ("idx_dim", ctypes.c_int32), ("idx_heads", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("heads", ctypes.c_int32), ("latent_dim", ctypes.c_int32),
+                ("v_dim", ctypes.c_int32), ("page_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("latent", ctypes.c_void_p), ("pooled", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("bt_stride", ctypes.c_int32)]
+
+
+class _Queries(ctypes.Structure):
+    _fields_ = [("n_q", ctypes.c_int32), ("seq", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("max_pos", ctypes.c_int32), ("group", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libkpool.so (once).  Raises if it is missing: there is no other implementation."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m sparse_attention_kpool_amd.build` "
+                           "(the KPool-DSA layer has no CPU or PyTorch fallback)")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D, C, Q = ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.POINTER(_Queries)
+    lib.kpool_compress.argtypes = [D, C, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.dsa_indexer_score.argtypes = [D, C, Q, vp, vp, vp, i64, vp]
+    lib.dsa_topk_workspace_size.argtypes = [D, Q]
+    lib.dsa_topk_workspace_size.restype = sz
+    lib.dsa_topk_select.argtypes = [D, Q, vp, i64, vp, vp, vp, sz, vp]
+    lib.sparse_mla_workspace_size.argtypes = [D, Q]
+    lib.sparse_mla_workspace_size.restype = sz
+    lib.sparse_mla_attn.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.kp_last_error.restype = ctypes.c_char_p
+    lib.kp_abi_version.restype = i32
+    if lib.kp_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libkpool.so ABI {lib.kp_abi_version()} != binding ABI {ABI_VERSION}; rebuild")
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().kp_last_error().decode()
+
+
+# ----------------------------------------------------------------------------------------------------------
+# Python-side descriptions of the C structs
+# ----------------------------------------------------------------------------------------------------------
+@dataclass
+class Dims:
+    pool: int = 4
+    idx_dim: int = 128
+    idx_heads: int = 32
+    topk: int = 2048
+    heads: int = 64
+    latent_dim: int = 576
+    v_dim: int = 512
+    page_tokens: int = 64
+    dtype: str = "bf16"          # 'bf16' or 'f32'
+    scale: float = 1.0 / 16.0
+
+    def c(self) -> _Dims:
+        return _Dims(self.pool, self.idx_dim, self.idx_heads, self.topk, self.heads, self.latent_dim, self.v_dim,
+                     self.page_tokens, KP_DTYPE_BF16 if self.dtype == "bf16" else KP_DTYPE_F32, self.scale)
+
+
+@dataclass
+class Cache:
+    latent: object = None        # torch tensor [n_pages, page_tokens, L]
+    pooled: object = None        # torch tensor [n_pages, page_tokens / P, D]
+    block_table: object = None   # torch int32 tensor [n_seq, stride]
+
+    def c(self) -> _Cache:
+        return _Cache(_ptr(self.latent), _ptr(self.pooled), _ptr(self.block_table),
+                      int(self.block_table.shape[1]) if self.block_table is not None else 0)
+
+
+@dataclass
+class Queries:
+    seq: object                  # torch int32 [n_q]
+    pos: object                  # torch int32 [n_q]
+    max_pos: int                 # host upper bound of pos
+    group: int = 1               # runs of `group` consecutive queries share a sequence (a hint)
+
+    def c(self) -> _Queries:
+        return _Queries(int(self.seq.numel()), _ptr(self.seq), _ptr(self.pos), int(self.max_pos), int(self.group))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    h = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return h or None
+
+
+def _check(fn: str, status: int) -> None:
+    if status != KP_OK:
+        raise KpError(fn, status, last_error())
+
+
+# ----------------------------------------------------------------------------------------------------------
+# the four calls
+# ----------------------------------------------------------------------------------------------------------
+def kpool_compress(dims: Dims, cache: Cache, keys, gates, ape, pool_seq, pool_id, src=None, stream=None) -> None:
+    """Pooled keys of complete pools -> rows (pool_seq[i], pool_id[i]) of cache.pooled (see include/kpool.h)."""
+    n = int(pool_seq.numel())
+    _check("kpool_compress", load().kpool_compress(ctypes.byref(dims.c()), ctypes.byref(cache.c()), n,
+                                                   _ptr(keys), _ptr(gates), _ptr(src), _ptr(ape), _ptr(pool_seq),
+                                                   _ptr(pool_id), _stream(stream)))
+
+
+def dsa_indexer_score(dims: Dims, cache: Cache, queries: Queries, q_idx, w, scores, stream=None) -> None:
+    """scores[q, p] for p < (pos[q] + 1) / P; scores is fp32 [n_q, ld]."""
+    _check("dsa_indexer_score", load().dsa_indexer_score(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+                                                         ctypes.byref(queries.c()), _ptr(q_idx), _ptr(w),
+                                                         _ptr(scores), int(scores.stride(0)), _stream(stream)))
+
+
+def dsa_topk_workspace_size(dims: Dims, queries: Queries) -> int:
+    return int(load().dsa_topk_workspace_size(ctypes.byref(dims.c()), ctypes.byref(queries.c())))
+
+
+def dsa_topk_select(dims: Dims, queries: Queries, scores, sel, n_sel, workspace=None, stream=None) -> None:
+    """sel [n_q, k] int32 ascending pool ids padded with -1; n_sel [n_q] int32."""
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    _check("dsa_topk_select", load().dsa_topk_select(ctypes.byref(dims.c()), ctypes.byref(queries.c()),
+                                                     _ptr(scores), int(scores.stride(0)), _ptr(sel), _ptr(n_sel),
+                                                     _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def sparse_mla_workspace_size(dims: Dims, queries: Queries) -> int:
+    return int(load().sparse_mla_workspace_size(ctypes.byref(dims.c()), ctypes.byref(queries.c())))
+
+
+def sparse_mla_attn(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, out, lse=None, workspace=None,
+                    stream=None) -> None:
+    """out [n_q, H, V] (storage dtype), lse [n_q, H] fp32 (optional)."""
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    _check("sparse_mla_attn", load().sparse_mla_attn(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+                                                     ctypes.byref(queries.c()), _ptr(q), _ptr(sel), _ptr(n_sel),
+                                                     _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                                     _stream(stream)))

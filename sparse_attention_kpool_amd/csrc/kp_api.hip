@@ -1,0 +1,254 @@
+// The extern "C" entry points declared in include/kpool.h: argument validation, then one launcher per call.
+// Nothing here touches device memory or synchronises; a validation failure launches nothing.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "kp_internal.hpp"
+
+namespace kp {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+kp_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: launch failed: %s", what, hipGetErrorString(e));
+    return KP_ERR_LAUNCH;
+  }
+  return KP_OK;
+}
+
+static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+static bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define KP_REQUIRE(cond, code, ...) \
+  do {                              \
+    if (!(cond)) {                  \
+      set_error(__VA_ARGS__);       \
+      return code;                  \
+    }                               \
+  } while (0)
+
+static kp_status check_dims(const kp_dims* d, const char* fn) {
+  KP_REQUIRE(d, KP_ERR_INVALID_ARG, "%s: dims is NULL", fn);
+  KP_REQUIRE(d->dtype == KP_DTYPE_F32 || d->dtype == KP_DTYPE_BF16, KP_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn,
+             d->dtype);
+  KP_REQUIRE(pow2(d->pool) && d->pool <= 32, KP_ERR_INVALID_ARG, "%s: pool must be a power of two in 1..32 (got %d)",
+             fn, d->pool);
+  KP_REQUIRE(d->idx_dim >= 1 && d->idx_heads >= 1 && d->heads >= 1, KP_ERR_INVALID_ARG,
+             "%s: idx_dim, idx_heads and heads must be >= 1", fn);
+  KP_REQUIRE(d->topk >= 1, KP_ERR_INVALID_ARG, "%s: topk must be >= 1 (got %d)", fn, d->topk);
+  KP_REQUIRE(d->v_dim >= 1 && d->v_dim <= d->latent_dim, KP_ERR_INVALID_ARG,
+             "%s: need 1 <= v_dim <= latent_dim (got %d, %d)", fn, d->v_dim, d->latent_dim);
+  KP_REQUIRE(pow2(d->page_tokens) && d->page_tokens % d->pool == 0, KP_ERR_INVALID_ARG,
+             "%s: page_tokens must be a power of two and a multiple of pool (got %d, pool %d)", fn, d->page_tokens,
+             d->pool);
+  return KP_OK;
+}
+
+static kp_status check_cache(const kp_cache* c, bool need_latent, bool need_pooled, const char* fn) {
+  KP_REQUIRE(c, KP_ERR_INVALID_ARG, "%s: cache is NULL", fn);
+  KP_REQUIRE(c->block_table, KP_ERR_INVALID_ARG, "%s: block_table is NULL", fn);
+  KP_REQUIRE(c->bt_stride >= 1, KP_ERR_INVALID_ARG, "%s: bt_stride must be >= 1", fn);
+  if (need_latent) KP_REQUIRE(c->latent && aligned(c->latent), KP_ERR_INVALID_ARG, "%s: latent NULL or misaligned", fn);
+  if (need_pooled) KP_REQUIRE(c->pooled && aligned(c->pooled), KP_ERR_INVALID_ARG, "%s: pooled NULL or misaligned", fn);
+  return KP_OK;
+}
+
+static kp_status check_queries(const kp_queries* q, const char* fn) {
+  KP_REQUIRE(q, KP_ERR_INVALID_ARG, "%s: queries is NULL", fn);
+  KP_REQUIRE(q->n_q >= 0, KP_ERR_INVALID_ARG, "%s: n_q < 0", fn);
+  if (q->n_q == 0) return KP_OK;
+  KP_REQUIRE(q->seq && q->pos, KP_ERR_INVALID_ARG, "%s: queries seq/pos NULL", fn);
+  KP_REQUIRE(q->max_pos >= 0, KP_ERR_INVALID_ARG, "%s: max_pos < 0", fn);
+  return KP_OK;
+}
+
+static bool score_built(const kp_dims* d) {
+  return (d->dtype == KP_DTYPE_BF16 && (d->idx_dim == 128 || d->idx_dim == 32)) ||
+         (d->dtype == KP_DTYPE_F32 && d->idx_dim == 32);
+}
+
+static bool attn_built(const kp_dims* d) {
+  return (d->dtype == KP_DTYPE_BF16 && (d->v_dim == 512 || d->v_dim == 64)) ||
+         (d->dtype == KP_DTYPE_F32 && d->v_dim == 64);
+}
+
+static size_t elem_size(const kp_dims* d) { return d->dtype == KP_DTYPE_BF16 ? 2 : 4; }
+
+}  // namespace kp
+
+using namespace kp;
+
+extern "C" {
+
+int32_t kp_abi_version(void) { return 1; }
+
+const char* kp_last_error(void) { return g_err; }
+
+kp_status kpool_compress(const kp_dims* dims, const kp_cache* cache, int32_t n_pools, const void* keys,
+                         const void* gates, const int32_t* src, const void* ape, const int32_t* pool_seq,
+                         const int32_t* pool_id, void* stream) {
+  const char* fn = "kpool_compress";
+  kp_status st = check_dims(dims, fn);
+  if (st != KP_OK) return st;
+  st = check_cache(cache, false, true, fn);
+  if (st != KP_OK) return st;
+  KP_REQUIRE(n_pools >= 0, KP_ERR_INVALID_ARG, "%s: n_pools < 0", fn);
+  if (n_pools == 0) return KP_OK;
+  KP_REQUIRE(keys && gates && ape && pool_seq && pool_id, KP_ERR_INVALID_ARG, "%s: NULL input", fn);
+  KP_REQUIRE(aligned(keys) && aligned(gates) && aligned(ape), KP_ERR_INVALID_ARG, "%s: misaligned input", fn);
+  CompressLaunch a{};
+  a.dtype = dims->dtype;
+  a.P = dims->pool;
+  a.D = dims->idx_dim;
+  a.n_pools = n_pools;
+  a.log2_ppp = ilog2(dims->page_tokens / dims->pool);
+  a.bt_stride = cache->bt_stride;
+  a.keys = keys;
+  a.gates = gates;
+  a.src = src;
+  a.ape = ape;
+  a.pool_seq = pool_seq;
+  a.pool_id = pool_id;
+  a.pooled = cache->pooled;
+  a.bt = cache->block_table;
+  return launch_compress(a, (hipStream_t)stream);
+}
+
+kp_status dsa_indexer_score(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries,
+                            const void* q_idx, const float* w, float* scores, int64_t ld_scores, void* stream) {
+  const char* fn = "dsa_indexer_score";
+  kp_status st = check_dims(dims, fn);
+  if (st != KP_OK) return st;
+  st = check_queries(queries, fn);
+  if (st != KP_OK) return st;
+  if (queries->n_q == 0) return KP_OK;
+  st = check_cache(cache, false, true, fn);
+  if (st != KP_OK) return st;
+  KP_REQUIRE(score_built(dims), KP_ERR_UNSUPPORTED, "%s: idx_dim %d with dtype %d is not built (bf16: 32, 128; f32: 32)",
+             fn, dims->idx_dim, dims->dtype);
+  KP_REQUIRE(dims->idx_heads <= 32, KP_ERR_UNSUPPORTED, "%s: idx_heads %d > 32", fn, dims->idx_heads);
+  KP_REQUIRE(q_idx && w && scores, KP_ERR_INVALID_ARG, "%s: NULL q_idx, w or scores", fn);
+  KP_REQUIRE(aligned(q_idx) && aligned(w) && aligned(scores), KP_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  const int64_t need = (int64_t(queries->max_pos) + 1) / dims->pool;
+  KP_REQUIRE(ld_scores >= need && ld_scores >= 1, KP_ERR_INVALID_ARG, "%s: ld_scores %lld < %lld visible pools", fn,
+             (long long)ld_scores, (long long)need);
+  ScoreLaunch a{};
+  a.dtype = dims->dtype;
+  a.P = dims->pool;
+  a.D = dims->idx_dim;
+  a.Hi = dims->idx_heads;
+  a.n_q = queries->n_q;
+  a.max_pos = queries->max_pos;
+  a.group = queries->group;
+  a.log2_ppp = ilog2(dims->page_tokens / dims->pool);
+  a.bt_stride = cache->bt_stride;
+  a.pooled = cache->pooled;
+  a.bt = cache->block_table;
+  a.q_idx = q_idx;
+  a.w = w;
+  a.q_seq = queries->seq;
+  a.q_pos = queries->pos;
+  a.scores = scores;
+  a.ld = ld_scores;
+  return launch_score(a, (hipStream_t)stream);
+}
+
+size_t dsa_topk_workspace_size(const kp_dims* dims, const kp_queries* queries) {
+  if (!dims || !queries) return 0;
+  return topk_workspace(dims->pool, dims->topk, queries->n_q, queries->max_pos);
+}
+
+kp_status dsa_topk_select(const kp_dims* dims, const kp_queries* queries, const float* scores, int64_t ld_scores,
+                          int32_t* sel, int32_t* n_sel, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "dsa_topk_select";
+  kp_status st = check_dims(dims, fn);
+  if (st != KP_OK) return st;
+  st = check_queries(queries, fn);
+  if (st != KP_OK) return st;
+  if (queries->n_q == 0) return KP_OK;
+  KP_REQUIRE(scores && sel && n_sel, KP_ERR_INVALID_ARG, "%s: NULL scores, sel or n_sel", fn);
+  KP_REQUIRE(aligned(scores) && aligned(sel) && aligned(n_sel), KP_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  const int64_t need = (int64_t(queries->max_pos) + 1) / dims->pool;
+  KP_REQUIRE(ld_scores >= need && ld_scores >= 1, KP_ERR_INVALID_ARG, "%s: ld_scores %lld < %lld visible pools", fn,
+             (long long)ld_scores, (long long)need);
+  const size_t ws_need = topk_workspace(dims->pool, dims->topk, queries->n_q, queries->max_pos);
+  KP_REQUIRE(ws_bytes >= ws_need && (ws_need == 0 || workspace), KP_ERR_WORKSPACE,
+             "%s: workspace of %zu bytes < %zu required", fn, ws_bytes, ws_need);
+  TopkLaunch a{};
+  a.P = dims->pool;
+  a.k = dims->topk;
+  a.n_q = queries->n_q;
+  a.max_pos = queries->max_pos;
+  a.scores = scores;
+  a.ld = ld_scores;
+  a.q_pos = queries->pos;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.ws = workspace;
+  a.ws_bytes = ws_bytes;
+  return launch_topk(a, (hipStream_t)stream);
+}
+
+size_t sparse_mla_workspace_size(const kp_dims* dims, const kp_queries* queries) {
+  if (!dims || !queries || queries->n_q <= 0 || dims->pool < 1 || dims->topk < 1) return 0;
+  return attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q);
+}
+
+kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
+                          const int32_t* sel, const int32_t* n_sel, void* out, float* lse, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  const char* fn = "sparse_mla_attn";
+  kp_status st = check_dims(dims, fn);
+  if (st != KP_OK) return st;
+  st = check_queries(queries, fn);
+  if (st != KP_OK) return st;
+  if (queries->n_q == 0) return KP_OK;
+  st = check_cache(cache, true, false, fn);
+  if (st != KP_OK) return st;
+  KP_REQUIRE(attn_built(dims), KP_ERR_UNSUPPORTED, "%s: v_dim %d with dtype %d is not built (bf16: 512, 64; f32: 64)",
+             fn, dims->v_dim, dims->dtype);
+  KP_REQUIRE(dims->heads <= 64, KP_ERR_UNSUPPORTED, "%s: heads %d > 64", fn, dims->heads);
+  KP_REQUIRE((int64_t(dims->latent_dim) * int64_t(elem_size(dims))) % 16 == 0, KP_ERR_INVALID_ARG,
+             "%s: latent rows must be a multiple of 16 bytes (latent_dim %d)", fn, dims->latent_dim);
+  KP_REQUIRE(q && sel && n_sel && out, KP_ERR_INVALID_ARG, "%s: NULL q, sel, n_sel or out", fn);
+  KP_REQUIRE(aligned(q) && aligned(sel) && aligned(n_sel) && aligned(out) && (!lse || aligned(lse)),
+             KP_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  const size_t ws_need = attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q);
+  KP_REQUIRE(ws_bytes >= ws_need && (ws_need == 0 || (workspace && aligned(workspace))), KP_ERR_WORKSPACE,
+             "%s: workspace of %zu bytes < %zu required", fn, ws_bytes, ws_need);
+  AttnLaunch a{};
+  a.dtype = dims->dtype;
+  a.P = dims->pool;
+  a.H = dims->heads;
+  a.L = dims->latent_dim;
+  a.V = dims->v_dim;
+  a.k = dims->topk;
+  a.n_q = queries->n_q;
+  a.max_pos = queries->max_pos;
+  a.log2_pt = ilog2(dims->page_tokens);
+  a.bt_stride = cache->bt_stride;
+  a.scale = dims->scale;
+  a.latent = cache->latent;
+  a.bt = cache->block_table;
+  a.q = q;
+  a.q_seq = queries->seq;
+  a.q_pos = queries->pos;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.out = out;
+  a.lse = lse;
+  a.ws = workspace;
+  a.ws_bytes = ws_bytes;
+  return launch_attn(a, (hipStream_t)stream);
+}
+
+}  // extern "C"

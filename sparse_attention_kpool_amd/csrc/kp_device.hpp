@@ -1,0 +1,94 @@
+// Device helpers shared by the KPool-DSA kernels: storage types, bf16 rounding, MFMA wrappers, paging.
+//
+// gfx950 matrix-core operand layouts used throughout (wave64; "g" = lane group):
+//   16x16 family (v_mfma_f32_16x16x32_bf16: 8 bf16 per lane; v_mfma_f32_16x16x4_f32: 1 float per lane)
+//     A[m][k]: lane l holds row m = l % 16, k-group g = l / 16 (4 groups)
+//     B[k][n]: lane l holds col n = l % 16, k-group g = l / 16
+//     D[m][n]: lane l, element i (0..3) holds row m = 4 * (l / 16) + i, col n = l % 16
+//   32x32 family (v_mfma_f32_32x32x16_bf16: 8 bf16 per lane; v_mfma_f32_32x32x2_f32: 1 float per lane)
+//     A[m][k]: lane l holds row m = l % 32, k-group g = l / 32 (2 groups)
+//     B[k][n]: lane l holds col n = l % 32, k-group g = l / 32
+//     D[m][n]: lane l, element i (0..15) holds row m = 8 * (i / 4) + 4 * (l / 32) + (i % 4), col n = l % 32
+// Within a k-group the hardware pairs A's element e with B's element e, so which logical k index each
+// (group, element) slot carries is ours to choose, as long as A and B agree.  The kernels pick it so every
+// lane reads contiguous memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// bf16 storage is raw 16-bit patterns.
+struct bf16 {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <class T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  static constexpr int kpl = 1;  // k elements per lane per MFMA
+  typedef float frag;
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static float to_f32(float v) { return v; }
+  __device__ __forceinline__ static float from_f32(float v) { return v; }
+  __device__ __forceinline__ static frag frag_load(const float* p) { return *p; }
+  __device__ __forceinline__ static frag frag_zero() { return 0.f; }
+};
+
+template <>
+struct Elem<bf16> {
+  static constexpr int kpl = 8;
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static float to_f32(bf16 v) { return bf16_to_f32(v.bits); }
+  __device__ __forceinline__ static bf16 from_f32(float v) { return bf16{f32_to_bf16(v)}; }
+  __device__ __forceinline__ static frag frag_load(const bf16* p) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    return __builtin_bit_cast(frag, v);
+  }
+  __device__ __forceinline__ static frag frag_zero() { return __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0)); }
+};
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Row index (in units of rows of `rows_per_page` per page) of logical row `r` of sequence row `seq`.
+__device__ __forceinline__ int64_t paged_row(const int32_t* __restrict__ bt, int bt_stride, int seq, int r,
+                                             int log2_rows_per_page) {
+  const int page = bt[int64_t(seq) * bt_stride + (r >> log2_rows_per_page)];
+  return (int64_t(page) << log2_rows_per_page) + (r & ((1 << log2_rows_per_page) - 1));
+}
+
+// Order-preserving uint32 image of an fp32 score; -0.0 is mapped to +0.0 first.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace kp

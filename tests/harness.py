@@ -1,0 +1,137 @@
+"""Test-only glue: builds a workload's inputs on the device through the seeded generator, runs the layer through
+the C ABI, and recomputes sampled queries with the CPU oracle from host-regenerated inputs.
+
+Nothing here is imported by the product path."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import kpool_synth as ks
+import oracle as O
+import sparse_attention_kpool_amd as K
+from sparse_attention_kpool_amd.layer import CompressInput, KPoolDSALayer
+
+
+def dims_of(wl: ks.Workload) -> K.Dims:
+    return K.Dims(pool=wl.P, idx_dim=wl.D, idx_heads=wl.Hi, topk=wl.k, heads=wl.H, latent_dim=wl.L, v_dim=wl.V,
+                  page_tokens=wl.page_tokens, dtype=wl.dtype, scale=wl.scale)
+
+
+def compress_pools(wl: ks.Workload):
+    """(seq, pool) of every pool that completes during the step: pools [new_from // P, ctx // P)."""
+    out = []
+    for s in range(wl.B):
+        for p in range(wl.new_from[s] // wl.P, wl.ctx[s] // wl.P):
+            out.append((s, p))
+    return out
+
+
+class DeviceRun:
+    """Device-side inputs of one workload plus the layer's outputs after `run()`."""
+
+    def __init__(self, wl: ks.Workload, device="cuda", group=None):
+        self.wl = wl
+        self.dev = torch.device(device)
+        self.dims = dims_of(wl)
+        self.bt_np = wl.block_table()
+        self.latent, self.pooled = ks.device_caches(wl, self.dev)
+        bt = torch.from_numpy(self.bt_np).to(self.dev)
+        self.cache = K.Cache(latent=self.latent, pooled=self.pooled, block_table=bt)
+        self.q_seq = torch.from_numpy(wl.q_seq.astype(np.int32)).to(self.dev)
+        self.q_pos = torch.from_numpy(wl.q_pos.astype(np.int32)).to(self.dev)
+        if group is None:
+            group = wl.n_q if len(set(wl.q_seq.tolist())) == 1 else 1
+        self.queries = K.Queries(seq=self.q_seq, pos=self.q_pos, max_pos=wl.max_pos(), group=group)
+        self.q_idx, self.w, self.q = ks.device_queries(wl, self.dev)
+        # pools completing in-step
+        cp = compress_pools(wl)
+        self.cpools = cp
+        if cp:
+            ks_, gs_ = [], []
+            for s in sorted(set(s for s, _ in cp)):
+                ps = [p for ss, p in cp if ss == s]
+                toks = np.concatenate([np.arange(p * wl.P, p * wl.P + wl.P) for p in ps])
+                kk, gg = ks.device_tokens(wl, s, toks, self.dev)
+                ks_.append(kk.view(len(ps), wl.P, wl.D))
+                gs_.append(gg.view(len(ps), wl.P, wl.D))
+            order = sorted(cp)
+            self.compress = CompressInput(
+                keys=torch.cat(ks_).contiguous(), gates=torch.cat(gs_).contiguous(), ape=ks.device_ape(wl, self.dev),
+                pool_seq=torch.tensor([s for s, _ in order], dtype=torch.int32, device=self.dev),
+                pool_id=torch.tensor([p for _, p in order], dtype=torch.int32, device=self.dev))
+        else:
+            self.compress = None
+        self.layer = KPoolDSALayer(self.dims, self.dev, max_q=wl.n_q, max_pos=max(wl.max_pos(), 0))
+        tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        self.out = torch.empty((wl.n_q, wl.H, wl.V), dtype=tdt, device=self.dev)
+        self.lse = torch.empty((wl.n_q, wl.H), dtype=torch.float32, device=self.dev)
+
+    def run(self):
+        self.layer.step(self.cache, self.queries, self.q_idx, self.w, self.q, self.out, lse=self.lse,
+                        compress=self.compress)
+        torch.cuda.synchronize()
+        return self
+
+    # ---- host copies of what the device produced -----------------------------------------------------
+    def pooled_rows(self, s: int, pools) -> np.ndarray:
+        wl = self.wl
+        ppp = wl.page_tokens // wl.P
+        pools = np.asarray(pools, dtype=np.int64)
+        pages = torch.from_numpy(self.bt_np[s, pools // ppp].astype(np.int64)).to(self.dev)
+        slots = torch.from_numpy(pools % ppp).to(self.dev)
+        return self.pooled[pages, slots].float().cpu().numpy().astype(np.float64)
+
+    def scores_row(self, j: int, n_c: int) -> np.ndarray:
+        return self.layer.scores[j, :n_c].cpu().numpy().astype(np.float64)
+
+    def sel_row(self, j: int):
+        ns = int(self.layer.n_sel[j].item())
+        return self.layer.sel[j].cpu().numpy(), ns
+
+
+# ----------------------------------------------------------------------------------------------------------
+# oracle side (host regeneration)
+# ----------------------------------------------------------------------------------------------------------
+def oracle_pooled(wl: ks.Workload, s: int, n_c: int) -> np.ndarray:
+    """Pooled keys of sequence s, pools < n_c, as the cache holds them after the step (storage precision)."""
+    P, D = wl.P, wl.D
+    out = np.zeros((n_c, D), dtype=np.float64)
+    first_new = wl.new_from[s] // P
+    old = min(first_new, n_c)
+    if old:
+        out[:old] = ks.host_pool_keys(wl, s, np.arange(old))        # pre-filled constant-key pools
+    if n_c > old:
+        toks = np.arange(old * P, n_c * P)
+        keys = ks.host_token_keys(wl, s, toks).reshape(-1, P, D)
+        gates = ks.host_gates(wl, s, toks).reshape(-1, P, D)
+        out[old:] = O.store_round(O.pool_compress(keys, gates, ks.host_ape(wl)), wl.dtype)
+    return out
+
+
+def oracle_query(wl: ks.Workload, j: int, pooled=None, sel=None):
+    """Oracle result for query j.  `pooled` / `sel` override the oracle's own stage outputs (stage parity)."""
+    s, i = int(wl.q_seq[j]), int(wl.q_pos[j])
+    n_c, r, tau = O.pool_geometry(i, wl.P)
+    if pooled is None:
+        pooled = oracle_pooled(wl, s, n_c)
+    qidx = ks.host_qidx(wl, s, i)[0]
+    w = ks.host_w(wl, s, i)[0]
+    scores = O.indexer_scores(qidx, w, pooled, n_c)
+    own_sel = O.select_pools(scores, i, wl.P, wl.k)
+    use_sel = own_sel if sel is None else sel
+    toks = O.attended_tokens(use_sel, i, wl.P)
+    q = ks.host_q(wl, s, i)[0]
+    out, lse = O.sparse_mla(q, ks.host_latent(wl, s, toks), wl.scale, wl.V)
+    return dict(scores=scores, sel=own_sel, tokens=toks, out=out, lse=lse, n_c=n_c, r=r, tau=tau)
+
+
+def attn_tolerance(dtype: str):
+    """(max-abs, rel-RMS) bounds for the attention output."""
+    return (3e-2, 1e-2) if dtype == "bf16" else (1e-4, 1e-5)
+
+
+def rel_rms(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.sqrt(((a - b) ** 2).sum()) / max(np.sqrt((b ** 2).sum()), 1e-30))

@@ -1,0 +1,130 @@
+"""The C-ABI library: it loads, exports every function include/kpool.h declares, and its host-side validation
+returns the documented status codes.  Every call here fails validation before any HIP call, so no GPU is
+needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_kpool_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kpool.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;]*\)\s*;", src, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn",
+              "dsa_topk_workspace_size", "sparse_mla_workspace_size", "kp_last_error", "kp_abi_version"):
+        assert f in names
+    assert set(names) == set(K.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = K.load()
+    for f in _declared():
+        assert hasattr(lib, f), f
+    assert lib.kp_abi_version() == K.ABI_VERSION
+
+
+def _dims(**kw):
+    d = dict(pool=4, idx_dim=128, idx_heads=32, topk=2048, heads=64, latent_dim=576, v_dim=512, page_tokens=64,
+             dtype=K.KP_DTYPE_BF16, scale=1 / 16)
+    d.update(kw)
+    return K._Dims(**d)
+
+
+FAKE = 1 << 20          # an aligned, non-null address; validation must fail before anything dereferences it
+
+
+def _cache():
+    return K._Cache(FAKE, FAKE, FAKE, 16)
+
+
+def _queries(n_q=4, max_pos=100, group=1):
+    return K._Queries(n_q, FAKE, FAKE, max_pos, group)
+
+
+def _score(d, c=None, q=None, ld=64, qidx=FAKE):
+    lib = K.load()
+    return lib.dsa_indexer_score(ctypes.byref(d), None if c is False else ctypes.byref(c or _cache()),
+                                 ctypes.byref(q or _queries()), qidx, FAKE, FAKE, ld, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pool=3), K.KP_ERR_INVALID_ARG),               # not a power of two
+    (dict(pool=64), K.KP_ERR_INVALID_ARG),
+    (dict(topk=0), K.KP_ERR_INVALID_ARG),
+    (dict(v_dim=600), K.KP_ERR_INVALID_ARG),            # V > L
+    (dict(page_tokens=2), K.KP_ERR_INVALID_ARG),        # not a multiple of the pool
+    (dict(page_tokens=96), K.KP_ERR_INVALID_ARG),       # not a power of two
+    (dict(dtype=7), K.KP_ERR_UNSUPPORTED),
+    (dict(idx_dim=64), K.KP_ERR_UNSUPPORTED),           # D not built
+    (dict(idx_heads=33), K.KP_ERR_UNSUPPORTED),
+    (dict(dtype=K.KP_DTYPE_F32), K.KP_ERR_UNSUPPORTED), # f32 is built for D = 32 only
+])
+def test_score_rejects_bad_dims(kw, code):
+    assert _score(_dims(**kw)) == code
+    assert K.last_error().startswith("dsa_indexer_score")
+
+
+def test_score_rejects_small_ld_and_nulls_and_misalignment():
+    assert _score(_dims(), ld=10) == K.KP_ERR_INVALID_ARG            # 25 visible pools
+    assert "ld_scores" in K.last_error()
+    assert _score(_dims(), c=False) == K.KP_ERR_INVALID_ARG
+    assert _score(_dims(), qidx=None) == K.KP_ERR_INVALID_ARG
+    assert _score(_dims(), qidx=FAKE + 8) == K.KP_ERR_INVALID_ARG
+    assert "misaligned" in K.last_error()
+    assert _score(_dims(), q=K._Queries(4, None, FAKE, 100, 1)) == K.KP_ERR_INVALID_ARG
+
+
+def test_empty_query_batches_are_valid_noops():
+    assert _score(_dims(), q=K._Queries(0, None, None, 0, 1), ld=0) == K.KP_OK
+    lib = K.load()
+    assert lib.kpool_compress(ctypes.byref(_dims()), ctypes.byref(_cache()), 0, None, None, None, None, None,
+                              None, None) == K.KP_OK
+
+
+def test_topk_and_attn_validation():
+    lib = K.load()
+    d, q = _dims(), _queries()
+    assert lib.dsa_topk_select(ctypes.byref(d), ctypes.byref(q), FAKE, 10, FAKE, FAKE, None, 0, None) \
+        == K.KP_ERR_INVALID_ARG
+    assert lib.dsa_topk_select(ctypes.byref(d), ctypes.byref(q), None, 64, FAKE, FAKE, None, 0, None) \
+        == K.KP_ERR_INVALID_ARG
+    need = lib.sparse_mla_workspace_size(ctypes.byref(d), ctypes.byref(q))
+    assert need > 0      # 4 queries split their selections across blocks
+    st = lib.sparse_mla_attn(ctypes.byref(d), ctypes.byref(_cache()), ctypes.byref(q), FAKE, FAKE, FAKE, FAKE,
+                             None, FAKE, need - 16, None)
+    assert st == K.KP_ERR_WORKSPACE and "workspace" in K.last_error()
+    st = lib.sparse_mla_attn(ctypes.byref(_dims(v_dim=128)), ctypes.byref(_cache()), ctypes.byref(q), FAKE, FAKE,
+                             FAKE, FAKE, None, FAKE, need, None)
+    assert st == K.KP_ERR_UNSUPPORTED
+    st = lib.sparse_mla_attn(ctypes.byref(_dims(heads=65)), ctypes.byref(_cache()), ctypes.byref(q), FAKE, FAKE,
+                             FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert st == K.KP_ERR_UNSUPPORTED
+    st = lib.sparse_mla_attn(ctypes.byref(_dims(latent_dim=577)), ctypes.byref(_cache()), ctypes.byref(q), FAKE,
+                             FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert st == K.KP_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_follow_the_split_rule():
+    lib = K.load()
+    d = _dims()
+    big = lib.sparse_mla_workspace_size(ctypes.byref(d), ctypes.byref(_queries(n_q=4096)))
+    assert big == 0                      # enough queries to fill the chip: no split, no workspace
+    assert lib.dsa_topk_workspace_size(ctypes.byref(d), ctypes.byref(_queries())) >= 0
+
+
+def test_binding_raises_without_library(tmp_path, monkeypatch):
+    import importlib
+    monkeypatch.setattr(K, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU or PyTorch fallback"):
+        K.load(str(tmp_path / "missing.so"))
+    importlib.reload(K)

@@ -1,0 +1,234 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle, stage by stage and end to end.
+
+Each stage is compared on the inputs the previous GPU stage produced, so a mismatch names its stage:
+  compress  pooled-cache rows written in-step  vs  oracle pooling of the same key/gate rows (bit-exact on the
+            constant-key parity instance; <= 1 bf16 ulp / 1e-6 relative in fp32 otherwise)
+  score     GPU score row  vs  oracle scores from the GPU's pooled cache (bit-exact on integer data)
+  select    GPU selection  vs  oracle top-k of the GPU's own score row (always bit-exact)
+  attend    GPU output     vs  oracle attention over the GPU's selection (bf16: max-abs 3e-2, rel-RMS 1e-2;
+            fp32: max-abs 1e-4, rel-RMS 1e-5)
+On the parity instance the oracle's own end-to-end selection must equal the GPU's as well.
+Full-size workloads check sampled queries (every score of a sampled row, its selection and output).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kpool_synth as ks
+import oracle as O
+from harness import DeviceRun, attn_tolerance, oracle_pooled, oracle_query, rel_rms
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def check_run(run: DeviceRun, samples, n_compress_check=64, parity=True):
+    wl = run.wl
+    P = wl.P
+    errs, refs, max_abs = [], [], 0.0
+    # -------- compress: rows written this step
+    if run.cpools:
+        rng = np.random.default_rng(0)
+        pick = run.cpools if len(run.cpools) <= n_compress_check else [
+            run.cpools[t] for t in sorted(rng.choice(len(run.cpools), n_compress_check, replace=False))]
+        for s, p in pick:
+            got = run.pooled_rows(s, [p])[0]
+            toks = np.arange(p * P, p * P + P)
+            ref = O.store_round(O.pool_compress(ks.host_token_keys(wl, s, toks)[None],
+                                                ks.host_gates(wl, s, toks)[None], ks.host_ape(wl)), wl.dtype)[0]
+            if parity:
+                np.testing.assert_array_equal(got, ref, err_msg=f"compress seq {s} pool {p}")
+            elif wl.dtype == "bf16":
+                ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(ref), 1e-30))[1] - 8)
+                assert (np.abs(got - ref) <= ulp).all(), f"compress seq {s} pool {p}"
+            else:
+                np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-6, err_msg=f"compress seq {s} pool {p}")
+    # -------- per sampled query
+    for j in samples:
+        s, i = int(wl.q_seq[j]), int(wl.q_pos[j])
+        n_c, r, tau = O.pool_geometry(i, P)
+        gpu_pooled = run.pooled_rows(s, np.arange(n_c)) if n_c else np.zeros((0, wl.D))
+        if parity:
+            np.testing.assert_array_equal(gpu_pooled, oracle_pooled(wl, s, n_c), err_msg=f"pooled cache q{j}")
+        qidx, w = ks.host_qidx(wl, s, i)[0], ks.host_w(wl, s, i)[0]
+        ref_scores = O.indexer_scores(qidx, w, gpu_pooled, n_c)
+        got_scores = run.scores_row(j, n_c)
+        if parity:
+            np.testing.assert_array_equal(got_scores, ref_scores, err_msg=f"scores q{j} (seq {s}, pos {i})")
+        else:
+            bound = 1e-5 * (np.abs(w)[None, :] * np.abs(gpu_pooled @ np.abs(qidx).T)).sum(1) + 1e-30
+            assert (np.abs(got_scores - ref_scores) <= bound).all(), f"scores q{j}"
+        sel_row, ns = run.sel_row(j)
+        ref_sel = O.select_pools(got_scores, i, P, wl.k)
+        assert ns == len(ref_sel), f"n_sel q{j}: {ns} != {len(ref_sel)}"
+        np.testing.assert_array_equal(sel_row[:ns], ref_sel, err_msg=f"selection q{j} (seq {s}, pos {i})")
+        assert (sel_row[ns:] == -1).all(), f"padding q{j}"
+        if parity:
+            own = oracle_query(wl, j)
+            np.testing.assert_array_equal(own["sel"], ref_sel, err_msg=f"end-to-end selection q{j}")
+        ref = oracle_query(wl, j, pooled=gpu_pooled, sel=ref_sel)
+        got = run.out[j].float().cpu().numpy().astype(np.float64)
+        got_lse = run.lse[j].cpu().numpy().astype(np.float64)
+        errs.append(got - ref["out"])
+        refs.append(ref["out"])
+        max_abs = max(max_abs, float(np.abs(got - ref["out"]).max()))
+        np.testing.assert_allclose(got_lse, ref["lse"], rtol=1e-4, atol=1e-3, err_msg=f"lse q{j}")
+    tol_abs, tol_rel = attn_tolerance(wl.dtype)
+    rr = rel_rms(np.concatenate([e.ravel() for e in errs]) + np.concatenate([x.ravel() for x in refs]),
+                 np.concatenate([x.ravel() for x in refs]))
+    _say(f"  {wl.name}: {len(samples)} queries, attention max-abs {max_abs:.3g} (<= {tol_abs}), rel-RMS {rr:.3g} "
+         f"(<= {tol_rel})")
+    assert max_abs <= tol_abs, f"attention max-abs {max_abs}"
+    assert rr <= tol_rel, f"attention rel-RMS {rr}"
+
+
+# ----------------------------------------------------------------------------------------------------------
+# small cases: every query checked
+# ----------------------------------------------------------------------------------------------------------
+def _small_decode(name="small_decode", ctx=(37, 1000, 4099, 8192, 20001), **kw):
+    wl = ks.workloads()["batch64"]
+    ctx = list(ctx)
+    base = dict(name=name, ctx=ctx, new_from=[t - 1 for t in ctx], q_seq=np.arange(len(ctx), dtype=np.int32),
+                q_pos=np.array([t - 1 for t in ctx], np.int32), page_perm_seed=7)
+    base.update(kw)
+    return ks.scaled(wl, **base)
+
+
+SMALL = {
+    "tiny": lambda: ks.workloads()["tiny"],
+    "tiny_general": lambda: ks.scaled(ks.workloads()["tiny"], name="tiny_general", key_per_token=True),
+    "tiny_dense_k": lambda: ks.scaled(ks.workloads()["tiny"], name="tiny_dense_k", k=64),
+    "tiny_k1": lambda: ks.scaled(ks.workloads()["tiny"], name="tiny_k1", k=1),
+    "small_decode": lambda: _small_decode(),
+    "small_decode_pool16": lambda: _small_decode("small_decode_pool16", P=16, k=128),
+    "small_decode_pool1": lambda: _small_decode("small_decode_pool1", ctx=(5, 300, 2500), P=1, k=512),
+    "small_decode_contig": lambda: _small_decode("small_decode_contig", page_perm_seed=None, page_tokens=1 << 15),
+    "small_bf16_narrow": lambda: ks.scaled(_small_decode("small_bf16_narrow", ctx=(3, 64, 777, 5000)), D=32, Hi=1,
+                                           H=4, L=80, V=64, k=16),
+    "small_prefill": lambda: ks.scaled(ks.workloads()["prefill64k"], name="small_prefill", ctx=[3000],
+                                       new_from=[2500], q_seq=np.zeros(500, np.int32),
+                                       q_pos=np.arange(2500, 3000, dtype=np.int32), k=256),
+}
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_small_all_queries(case):
+    wl = SMALL[case]()
+    _say(f"[case {case}] B={wl.B} n_q={wl.n_q} dtype={wl.dtype} P={wl.P} k={wl.k}")
+    run = DeviceRun(wl).run()
+    check_run(run, range(wl.n_q), parity=not wl.key_per_token)
+    del run
+    _free()
+
+
+def test_group_hint_violated_is_still_exact():
+    """Queries of different sequences under a group hint that promises otherwise: results unchanged."""
+    wl = _small_decode("mixed_groups", ctx=(100, 2000, 2001, 333, 4096, 70, 9000, 12))
+    _say(f"[case mixed_groups] n_q={wl.n_q}")
+    a = DeviceRun(wl, group=1).run()
+    b = DeviceRun(wl, group=4).run()
+    for j in range(wl.n_q):
+        n_c = (int(wl.q_pos[j]) + 1) // wl.P
+        np.testing.assert_array_equal(a.scores_row(j, n_c), b.scores_row(j, n_c))
+    assert torch.equal(a.layer.sel, b.layer.sel) and torch.equal(a.out, b.out)
+    check_run(b, range(wl.n_q))
+    del a, b
+    _free()
+
+
+def test_paged_equals_contiguous_and_deterministic():
+    wl1 = _small_decode("paged", ctx=(5000, 17, 9999))
+    wl2 = ks.scaled(wl1, name="contig", page_perm_seed=None, page_tokens=1 << 14)
+    _say("[case paged_vs_contig]")
+    a = DeviceRun(wl1).run()
+    out1, sel1 = a.out.clone(), a.layer.sel.clone()
+    a.run()
+    assert torch.equal(out1, a.out) and torch.equal(sel1, a.layer.sel), "two runs differ"
+    b = DeviceRun(wl2).run()
+    assert torch.equal(sel1, b.layer.sel)
+    assert torch.equal(out1, b.out)
+    del a, b
+    _free()
+
+
+def test_empty_calls():
+    """n_q = 0 and n_pools = 0 are valid and write nothing."""
+    import sparse_attention_kpool_amd as K
+    wl = _small_decode("empty", ctx=(64,))
+    run = DeviceRun(wl)
+    before = run.pooled.clone()
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    qe = K.Queries(seq=e, pos=e, max_pos=0)
+    K.dsa_indexer_score(run.dims, run.cache, qe, run.q_idx, run.w, run.layer.scores[:0])
+    K.dsa_topk_select(run.dims, qe, run.layer.scores[:0], run.layer.sel[:0], run.layer.n_sel[:0])
+    K.sparse_mla_attn(run.dims, run.cache, qe, run.q, run.layer.sel[:0], run.layer.n_sel[:0], run.out[:0])
+    K.kpool_compress(run.dims, run.cache, run.q_idx, run.q_idx, run.q_idx, e, e)
+    torch.cuda.synchronize()
+    assert torch.equal(before, run.pooled)
+    del run
+    _free()
+
+
+# ----------------------------------------------------------------------------------------------------------
+# published workload shapes at full size: sampled queries
+# ----------------------------------------------------------------------------------------------------------
+def test_full_decode32k():
+    wl = ks.workloads()["decode32k"]
+    _say("[case decode32k] B=1 T=32768")
+    run = DeviceRun(wl).run()
+    check_run(run, [0])
+    del run
+    _free()
+
+
+def test_full_decode128k():
+    wl = ks.workloads()["decode128k"]
+    _say("[case decode128k] B=1 T=131072")
+    run = DeviceRun(wl).run()
+    check_run(run, [0])
+    del run
+    _free()
+
+
+@pytest.mark.slow
+def test_full_batch64():
+    wl = ks.workloads()["batch64"]
+    _say(f"[case batch64] B=64 sumT={sum(wl.ctx)}")
+    run = DeviceRun(wl).run()
+    ctx = np.array(wl.ctx)
+    picks = sorted({int(ctx.argmax()), int(ctx.argmin()), 0, 31, 63,
+                    int(np.flatnonzero(ctx % 4 == 0)[0]), int(np.flatnonzero(ctx % 4 == 1)[0])})
+    check_run(run, picks)
+    del run
+    _free()
+
+
+@pytest.mark.slow
+def test_full_prefill64k():
+    wl = ks.workloads()["prefill64k"]
+    _say("[case prefill64k] 4096 queries on 65536 tokens")
+    run = DeviceRun(wl).run()
+    check_run(run, [0, 1, 2, 3, 1234, 2047, 4094, 4095], n_compress_check=1024)
+    del run
+    _free()
+
+
+@pytest.mark.slow
+def test_full_long1m():
+    wl = ks.workloads()["long1m"]
+    _say("[case long1m] B=8 T=1048576")
+    run = DeviceRun(wl).run()
+    check_run(run, [0, 5])
+    del run
+    _free()
