@@ -390,3 +390,45 @@ def device_queries(wl: Workload, device):
 def device_ape(wl: Workload, device):
     import torch
     return torch.from_numpy(host_ape(wl)).to(device).to(_torch_dtype(wl))
+
+
+def compress_pools(wl: Workload):
+    """(seq, pool) of every pool that completes during the step: pools [new_from // P, ctx // P)."""
+    out = []
+    for s in range(wl.B):
+        for p in range(wl.new_from[s] // wl.P, wl.ctx[s] // wl.P):
+            out.append((s, p))
+    return out
+
+
+class DeviceInputs:
+    """Every device-side input of one workload step: the two paged caches and their block table, the queries,
+    and the key/gate rows of the pools that complete in-step (as [n, P, D] blocks with their destinations)."""
+
+    def __init__(self, wl: Workload, device):
+        import torch
+        self.wl = wl
+        self.device = torch.device(device)
+        self.block_table_np = wl.block_table()
+        self.latent, self.pooled = device_caches(wl, self.device)
+        self.block_table = torch.from_numpy(self.block_table_np).to(self.device)
+        self.q_seq = torch.from_numpy(wl.q_seq.astype(np.int32)).to(self.device)
+        self.q_pos = torch.from_numpy(wl.q_pos.astype(np.int32)).to(self.device)
+        self.q_idx, self.w, self.q = device_queries(wl, self.device)
+        self.cpools = compress_pools(wl)
+        self.ape = device_ape(wl, self.device)
+        if self.cpools:
+            ks_, gs_ = [], []
+            for s in sorted(set(s for s, _ in self.cpools)):
+                ps = [p for ss, p in self.cpools if ss == s]
+                toks = np.concatenate([np.arange(p * wl.P, p * wl.P + wl.P) for p in ps])
+                kk, gg = device_tokens(wl, s, toks, self.device)
+                ks_.append(kk.view(len(ps), wl.P, wl.D))
+                gs_.append(gg.view(len(ps), wl.P, wl.D))
+            order = sorted(self.cpools)
+            self.c_keys = torch.cat(ks_).contiguous()
+            self.c_gates = torch.cat(gs_).contiguous()
+            self.c_seq = torch.tensor([s for s, _ in order], dtype=torch.int32, device=self.device)
+            self.c_pool = torch.tensor([p for _, p in order], dtype=torch.int32, device=self.device)
+        else:
+            self.c_keys = self.c_gates = self.c_seq = self.c_pool = None

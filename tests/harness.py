@@ -18,50 +18,25 @@ def dims_of(wl: ks.Workload) -> K.Dims:
                   page_tokens=wl.page_tokens, dtype=wl.dtype, scale=wl.scale)
 
 
-def compress_pools(wl: ks.Workload):
-    """(seq, pool) of every pool that completes during the step: pools [new_from // P, ctx // P)."""
-    out = []
-    for s in range(wl.B):
-        for p in range(wl.new_from[s] // wl.P, wl.ctx[s] // wl.P):
-            out.append((s, p))
-    return out
-
-
 class DeviceRun:
-    """Device-side inputs of one workload plus the layer's outputs after `run()`."""
+    """Device-side inputs of one workload (from the seeded generator) plus the layer's outputs after `run()`."""
 
     def __init__(self, wl: ks.Workload, device="cuda", group=None):
         self.wl = wl
         self.dev = torch.device(device)
         self.dims = dims_of(wl)
-        self.bt_np = wl.block_table()
-        self.latent, self.pooled = ks.device_caches(wl, self.dev)
-        bt = torch.from_numpy(self.bt_np).to(self.dev)
-        self.cache = K.Cache(latent=self.latent, pooled=self.pooled, block_table=bt)
-        self.q_seq = torch.from_numpy(wl.q_seq.astype(np.int32)).to(self.dev)
-        self.q_pos = torch.from_numpy(wl.q_pos.astype(np.int32)).to(self.dev)
+        d = ks.DeviceInputs(wl, self.dev)
+        self.inputs = d
+        self.bt_np = d.block_table_np
+        self.latent, self.pooled = d.latent, d.pooled
+        self.cache = K.Cache(latent=d.latent, pooled=d.pooled, block_table=d.block_table)
         if group is None:
             group = wl.n_q if len(set(wl.q_seq.tolist())) == 1 else 1
-        self.queries = K.Queries(seq=self.q_seq, pos=self.q_pos, max_pos=wl.max_pos(), group=group)
-        self.q_idx, self.w, self.q = ks.device_queries(wl, self.dev)
-        # pools completing in-step
-        cp = compress_pools(wl)
-        self.cpools = cp
-        if cp:
-            ks_, gs_ = [], []
-            for s in sorted(set(s for s, _ in cp)):
-                ps = [p for ss, p in cp if ss == s]
-                toks = np.concatenate([np.arange(p * wl.P, p * wl.P + wl.P) for p in ps])
-                kk, gg = ks.device_tokens(wl, s, toks, self.dev)
-                ks_.append(kk.view(len(ps), wl.P, wl.D))
-                gs_.append(gg.view(len(ps), wl.P, wl.D))
-            order = sorted(cp)
-            self.compress = CompressInput(
-                keys=torch.cat(ks_).contiguous(), gates=torch.cat(gs_).contiguous(), ape=ks.device_ape(wl, self.dev),
-                pool_seq=torch.tensor([s for s, _ in order], dtype=torch.int32, device=self.dev),
-                pool_id=torch.tensor([p for _, p in order], dtype=torch.int32, device=self.dev))
-        else:
-            self.compress = None
+        self.queries = K.Queries(seq=d.q_seq, pos=d.q_pos, max_pos=wl.max_pos(), group=group)
+        self.q_idx, self.w, self.q = d.q_idx, d.w, d.q
+        self.cpools = d.cpools
+        self.compress = None if d.c_keys is None else CompressInput(
+            keys=d.c_keys, gates=d.c_gates, ape=d.ape, pool_seq=d.c_seq, pool_id=d.c_pool)
         self.layer = KPoolDSALayer(self.dims, self.dev, max_q=wl.n_q, max_pos=max(wl.max_pos(), 0))
         tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
         self.out = torch.empty((wl.n_q, wl.H, wl.V), dtype=tdt, device=self.dev)
