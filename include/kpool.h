@@ -123,7 +123,7 @@ kp_status kpool_compress(const kp_dims* dims, const kp_cache* cache, int32_t n_p
  *   for p < n_c(pos(q)), accumulated in fp32 (products of storage values are exact in fp32).  One pooled key
  *   per pool serves every index head.  Columns p >= n_c(pos(q)) of a row are not written.
  *   q_idx: device [n_q, Hi, D] storage dtype; w: device [n_q, Hi] fp32 (any sign).
- *   scores: device fp32 [n_q, ld_scores], ld_scores >= (max_pos + 1) / P.
+ *   scores: device fp32 [n_q, ld_scores], ld_scores >= (max_pos + 1) / P and a multiple of 4 (16-byte rows).
  *   MFMA: 32 index heads form the M side of a 32x32x16 bf16 (32x32x2 f32) tile; pools are N; D is K.
  *   Errors: KP_ERR_INVALID_ARG (null pointers, ld_scores too small), KP_ERR_UNSUPPORTED (D, dtype).
  */
@@ -139,9 +139,12 @@ kp_status dsa_indexer_score(const kp_dims* dims, const kp_cache* cache, const kp
  *     budget = min(k - [r != 0], n_c); keep the `budget` complete pools first in the order (score desc,
  *     pool index asc), with -0.0 equal to +0.0; add tau when r != 0.
  *   sel: device int32 [n_q, k], the kept pool ids ascending, padded with -1; n_sel: device int32 [n_q].
- *   scores: as written by dsa_indexer_score (only columns < n_c are read).
- *   workspace: device, at least dsa_topk_workspace_size bytes (NULL when that is 0).
- *   Errors: KP_ERR_INVALID_ARG, KP_ERR_WORKSPACE.
+ *   scores: as written by dsa_indexer_score (only columns < n_c are read); ld_scores as there.
+ *   workspace: device, at least dsa_topk_workspace_size bytes (NULL when that is 0).  Rows of more than 32768
+ *     pools are selected in two steps (per-32768-pool-chunk candidates, then a final pass) through it.
+ *   Limit: (max_pos + 1) / P <= 16 * 32768 pools and 16 * topk <= 32768 when two steps are needed, else
+ *     KP_ERR_UNSUPPORTED (covers 1M-token contexts at P = 4, topk = 2048).
+ *   Errors: KP_ERR_INVALID_ARG, KP_ERR_WORKSPACE, KP_ERR_UNSUPPORTED.
  */
 size_t dsa_topk_workspace_size(const kp_dims* dims, const kp_queries* queries);
 kp_status dsa_topk_select(const kp_dims* dims, const kp_queries* queries, const float* scores,

@@ -133,6 +133,7 @@ class Workload:
     latent_int: bool = False         # q and latents U{-4..4} instead of N(0,1)
     key_per_token: bool = False      # general instance: keys drawn per token (else constant per pool)
     page_perm_seed: Optional[int] = None   # None: pages placed in order; else a seeded random permutation
+    w_scale: float = 1.0             # multiplies the head weights (0 makes every score 0: a pure tie-break case)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -255,8 +256,10 @@ def host_w(wl: Workload, seq, pos) -> np.ndarray:
     st = _seqtok(seq, pos).reshape(-1)
     idx = st[:, None] * wl.Hi + np.arange(wl.Hi)[None, :]
     if wl.w_int:
-        return uniform_int(wl.key("w"), idx, -4, 4).astype(np.float32)
-    return (uniform_int(wl.key("w"), idx, 0, 255).astype(np.float32) / 256.0).astype(np.float32)
+        w = uniform_int(wl.key("w"), idx, -4, 4).astype(np.float32)
+    else:
+        w = (uniform_int(wl.key("w"), idx, 0, 255).astype(np.float32) / 256.0).astype(np.float32)
+    return (w * np.float32(wl.w_scale)).astype(np.float32)
 
 
 def host_q(wl: Workload, seq, pos) -> np.ndarray:
@@ -375,6 +378,7 @@ def device_queries(wl: Workload, device):
         w = uniform_int(wl.key("w"), widx, -4, 4).to(torch.float32)
     else:
         w = uniform_int(wl.key("w"), widx, 0, 255).to(torch.float32) / 256.0
+    w = w * float(wl.w_scale)
     h = torch.arange(wl.H, dtype=torch.int64, device=device)
     lc = torch.arange(wl.L, dtype=torch.int64, device=device)
     qi = (st[:, None, None] * wl.H + h[None, :, None]) * wl.L + lc[None, None, :]

@@ -141,6 +141,8 @@ kp_status dsa_indexer_score(const kp_dims* dims, const kp_cache* cache, const kp
   const int64_t need = (int64_t(queries->max_pos) + 1) / dims->pool;
   KP_REQUIRE(ld_scores >= need && ld_scores >= 1, KP_ERR_INVALID_ARG, "%s: ld_scores %lld < %lld visible pools", fn,
              (long long)ld_scores, (long long)need);
+  KP_REQUIRE(ld_scores % 4 == 0, KP_ERR_INVALID_ARG, "%s: ld_scores %lld is not a multiple of 4", fn,
+             (long long)ld_scores);
   ScoreLaunch a{};
   a.dtype = dims->dtype;
   a.P = dims->pool;
@@ -180,6 +182,8 @@ kp_status dsa_topk_select(const kp_dims* dims, const kp_queries* queries, const 
   const int64_t need = (int64_t(queries->max_pos) + 1) / dims->pool;
   KP_REQUIRE(ld_scores >= need && ld_scores >= 1, KP_ERR_INVALID_ARG, "%s: ld_scores %lld < %lld visible pools", fn,
              (long long)ld_scores, (long long)need);
+  KP_REQUIRE(ld_scores % 4 == 0, KP_ERR_INVALID_ARG, "%s: ld_scores %lld is not a multiple of 4", fn,
+             (long long)ld_scores);
   const size_t ws_need = topk_workspace(dims->pool, dims->topk, queries->n_q, queries->max_pos);
   KP_REQUIRE(ws_bytes >= ws_need && (ws_need == 0 || workspace), KP_ERR_WORKSPACE,
              "%s: workspace of %zu bytes < %zu required", fn, ws_bytes, ws_need);

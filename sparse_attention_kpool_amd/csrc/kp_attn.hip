@@ -6,19 +6,26 @@
 // kv_lora_rank 512, 64 heads.  Absorbed MLA: the key of token t is its latent row, the value its first V
 // columns; the zero rotary columns add nothing to q . latent and are not read.
 //
-// One block (4 waves) per (query, split of its selected tokens).  Token slots are taken 32 at a time: slot j
+// One block of 8 waves per (query, split of its selected tokens).  Token slots are taken 32 at a time: slot j
 // is token P * sel[j / P] + j % P, valid while j < P * n_sel and the token is <= the query position (the tail
-// pool is cut at the query itself).  Per 32-slot block:
-//   load   every thread gathers 16-byte chunks of the V-wide value rows (8 threads cover 128 contiguous bytes
-//          of a row) into registers one block ahead, then writes them to LDS twice: row-major (token x
-//          channel) and transposed (channel x token).
-//   S      wave w owns heads 16w..16w+15 and computes S^T = C . Q^T on 16x16x32 bf16 MFMA (tokens = M,
-//          heads = N, channels = K).  Its Q fragments stay in registers for the whole call; C comes from the
-//          row-major copy with one 16-byte read per lane per k-step.  Online softmax per head: each lane holds
-//          one head, so the row max / sum take two cross-lane steps (xor 16, xor 32).
-//   O      wave w owns value channels w*V/4 .. (w+1)*V/4 for all heads: O^T += C^T . P^T, with C^T from the
-//          transposed copy and P (stored by the S waves in LDS) as B.  Its accumulators (V/4 x 64 heads fp32)
-//          stay in registers; each head's rescale factor is one scalar per lane.
+// pool is cut at the query itself).  At start the block turns its split's pool ids into cache-row bases (one
+// block-table lookup per pool) in LDS, so no gathered load waits on another global load.
+//
+// The 8 waves form a two-stage pipeline over 32-slot blocks, one barrier per block:
+//   load   every thread keeps 16-byte chunks of the V-wide value rows in registers two blocks ahead (a wave
+//          covers one whole 1 KiB row per instruction) and writes them to a 3-deep ring of row-major LDS
+//          buffers.
+//   S      waves 0..3 (S waves), block j: wave w owns heads 16w..16w+15 and computes S^T = C . Q^T on
+//          16x16x32 bf16 MFMA (tokens = M, heads = N, channels = K); its Q fragments stay in registers.  Online
+//          softmax per head with a lazy running max (raised only when a block's max exceeds it by more than
+//          2^64, far inside the fp32 / bf16 exponent range), so blocks practically never rescale.  P and the
+//          rescale factor go to LDS.
+//   O      waves 4..7 (O waves), block j-1 at the same time: wave w owns value channels (w-4)*V/4 .. +V/4 for
+//          all heads: O^T += C^T . P^T.  The C^T operand is read from the same row-major buffer with the LDS
+//          transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane s points at 4 channels of token
+//          8g + s/4 and lane i receives channel i of those 4 tokens.
+// Each SIMD runs one S wave and one O wave, so the two products overlap on the matrix core.  S waves keep Q in
+// the same register bank in which O waves keep their accumulators.
 // Splits write unnormalised partials (O, running max, running sum) that a second kernel merges in split
 // order, so results are deterministic.
 //
@@ -29,57 +36,74 @@
 
 namespace kp {
 
-constexpr int AT_NT = 32;  // token slots per block
+constexpr int AT_NT = 32;         // token slots per block
+constexpr int AT_THREADS = 512;   // 4 S waves + 4 O waves
+constexpr int AT_MAXPOOL = 2048;  // pools of one split held in LDS
 constexpr float LN2 = 0.69314718055994530942f;
+// log2 headroom before the running max is raised: weights up to 2^64 stay far inside the fp32 / bf16 exponent
+// range, so the accumulators are rescaled only when a later block's max beats the running one by 2^64.
+constexpr float LAZY_MAX = 64.f;
 
-template <class T, int V>
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <class T, int V, int HT>
 struct AttnShape {
   static constexpr int KPL = Elem<T>::kpl;
-  static constexpr int EPC = 16 / int(sizeof(T));   // elements per 16-byte chunk
-  static constexpr int CPR = V / EPC;               // chunks per value row
-  static constexpr int UNITS = 8 * CPR;             // (4-token group, chunk) load units per block
-  static constexpr int UPT = (UNITS + 255) / 256;   // units per thread
-  static constexpr int RS = V + EPC;                // row-major LDS stride (elements), +16 B against conflicts
-  static constexpr int TS = AT_NT + EPC;            // transposed LDS stride
-  static constexpr int PS = AT_NT + EPC;            // P stride
-  static constexpr int VW = V / 4;                  // value channels per wave in the O product
-  static constexpr int MT = VW / 16;                // 16-channel tiles per wave
-  static constexpr int SK = V / (4 * KPL);          // k-steps of the S product (K = V channels)
-  static constexpr int OK = AT_NT / (4 * KPL);      // k-steps of the O product (K = 32 tokens)
-  static_assert(CPR % 8 == 0, "value row must be a multiple of 128 bytes");
-  static_assert(VW % 16 == 0, "value width must split into 16-channel tiles per wave");
+  static constexpr int EPC = 16 / int(sizeof(T));                     // elements per 16-byte chunk
+  static constexpr int CPR = V / EPC;                                 // chunks per value row
+  static constexpr int CHUNKS = AT_NT * CPR;                          // chunks per block
+  static constexpr int CHT = (CHUNKS + AT_THREADS - 1) / AT_THREADS;  // chunks per thread per block
+  static constexpr int RS = V + EPC;                                  // LDS row stride (+16 B against conflicts)
+  static constexpr int PS = AT_NT + EPC;                              // P row stride
+  static constexpr int VW = V / 4;                                    // value channels per O wave
+  static constexpr int MT = VW / 16;                                  // 16-channel tiles per O wave
+  static constexpr int SK = V / (4 * KPL);                            // k-steps of the S product (K = V)
+  static constexpr int OK = AT_NT / (4 * KPL);                        // k-steps of the O product (K = 32 tokens)
+  static constexpr int QB = (SK * KPL * int(sizeof(T))) / 16;         // 16-byte units of one wave's Q fragments
+  static constexpr int NB = (MT * HT > QB) ? MT * HT : QB;            // shared register bank (f32x4 units)
+  static_assert(VW % 16 == 0, "value width must split into 16-channel tiles per O wave");
+  static_assert((SK * KPL * int(sizeof(T))) % 16 == 0, "Q fragments fill whole 16-byte units");
 };
 
-template <class T>
-__device__ __forceinline__ uint32_t chunk_elem_bits(const uint4& v, int e) {
+// A-operand fragment of C^T (channels c0 .. c0+15 x tokens 8g .. 8g+7 of k-step s) from the row-major block.
+template <class T, int RS>
+__device__ __forceinline__ typename Elem<T>::frag ct_frag(const T* blk, int c0, int g, int l16, int s) {
   if constexpr (sizeof(T) == 2) {
-    const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
-    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+    const int e = l16 >> 2, a = l16 & 3;
+    const T* p1 = blk + (8 * g + e) * RS + c0 + 4 * a;   // tokens 8g .. 8g+3
+    const T* p2 = p1 + 4 * RS;                           // tokens 8g+4 .. 8g+7
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p1));
+    const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p2));
+    const uint2 u1 = __builtin_bit_cast(uint2, v1), u2 = __builtin_bit_cast(uint2, v2);
+    return __builtin_bit_cast(bf16x8, make_uint4(u1.x, u1.y, u2.x, u2.y));
   } else {
-    return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+    return blk[(8 * g + s) * RS + c0 + l16];
   }
 }
 
-template <class T, int V>
-__global__ __launch_bounds__(256) void attn_kernel(
+template <class T, int V, int HT>
+__global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     const T* __restrict__ latent, int L, const int32_t* __restrict__ bt, int bt_stride, int log2_pt,
     const T* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int log2P, int k, int H, float scale_log2,
     int n_split, int blocks_per_split, T* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
-  using S = AttnShape<T, V>;
+  using S = AttnShape<T, V, HT>;
   using E = Elem<T>;
   using F = typename E::frag;
-  __shared__ __align__(16) T crm[AT_NT * S::RS];
-  __shared__ __align__(16) T ct[V * S::TS];
-  __shared__ __align__(16) T ps[64 * S::PS];
-  __shared__ float alpha_s[64];
+  __shared__ __align__(16) T crm[3][AT_NT * S::RS];
+  __shared__ __align__(16) T ps[2][16 * HT * S::PS];
+  __shared__ int32_t pool_row[AT_MAXPOOL];
+  __shared__ uint8_t pool_ntok[AT_MAXPOOL];
+  __shared__ float alpha_s[2][64];
   __shared__ float m_s[64];
   __shared__ float l_s[64];
-  __shared__ uint32_t vmask_s;
+  __shared__ uint32_t vmask_s[3];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
+  const bool o_wave = wave >= 4;
+  const int wl = wave & 3;  // index within the wave's role
   const int qi = blockIdx.x / n_split;
   const int sp = blockIdx.x - qi * n_split;
   const int seq = q_seq[qi];
@@ -88,228 +112,237 @@ __global__ __launch_bounds__(256) void attn_kernel(
   const int n_slots = n_sel[qi] * P;
   const int s_begin = sp * blocks_per_split * AT_NT;
   const int s_end = min(s_begin + blocks_per_split * AT_NT, n_slots);
-  const int32_t* qsel = sel + int64_t(qi) * k;
 
   if (s_begin >= s_end) {  // an empty split (this query selected fewer tokens)
     if (n_split > 1) {
-      for (int h = tid; h < H; h += 256) {
+      for (int h = tid; h < H; h += AT_THREADS) {
         part_ml[(int64_t(qi * n_split + sp) * H + h) * 2 + 0] = -INFINITY;
         part_ml[(int64_t(qi * n_split + sp) * H + h) * 2 + 1] = 0.f;
       }
     } else {
-      for (int64_t e = tid; e < int64_t(H) * V; e += 256) out[int64_t(qi) * H * V + e] = E::from_f32(0.f);
+      for (int64_t e = tid; e < int64_t(H) * V; e += AT_THREADS) out[int64_t(qi) * H * V + e] = E::from_f32(0.f);
       if (lse)
-        for (int h = tid; h < H; h += 256) lse[int64_t(qi) * H + h] = -INFINITY;
+        for (int h = tid; h < H; h += AT_THREADS) lse[int64_t(qi) * H + h] = -INFINITY;
     }
     return;
   }
   const int nblk = (s_end - s_begin + AT_NT - 1) / AT_NT;
+  const int pool0 = s_begin >> log2P;
+  const int npool = (s_end - s_begin) >> log2P;
 
-  // Q^T fragments of this wave's 16 heads (B operand of S^T = C . Q^T): lane holds head 16*wave + l16,
-  // channels g*(V/4) + s*KPL .. +KPL for k-step s
-  const bool s_wave = 16 * wave < H;
-  F qf[S::SK];
+  // cache-row base and visible token count of every pool of this split
   {
-    const int h = 16 * wave + l16;
+    const int32_t* qsel = sel + int64_t(qi) * k + pool0;
+    const int pt_mask = (1 << log2_pt) - 1;
+    for (int j = tid; j < npool; j += AT_THREADS) {
+      const int p = qsel[j];
+      int nt = 0, row = 0;
+      if (p >= 0) {
+        const int first = p << log2P;
+        nt = min(P, pos - first + 1);
+        if (nt > 0) row = bt[int64_t(seq) * bt_stride + (first >> log2_pt)] * (pt_mask + 1) + (first & pt_mask);
+      }
+      pool_row[j] = row;
+      pool_ntok[j] = uint8_t(max(nt, 0));
+    }
+  }
+
+  // Register bank: an S wave keeps the Q^T fragments of its 16 heads there (B operand of S^T = C . Q^T; lane
+  // holds head 16*wl + l16, channels g*(V/4) + s*KPL .. +KPL for k-step s); an O wave keeps its accumulators
+  // O^T[16 channels x 16 heads] tiles at bank[mt * HT + nt].
+  f32x4 bank[S::NB];
+#pragma unroll
+  for (int b = 0; b < S::NB; ++b) bank[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool s_active = !o_wave && wl < HT;
+  if (s_active) {
+    const int h = 16 * wl + l16;
     const bool hv = h < H;
     const T* qp = q + (int64_t(qi) * H + (hv ? h : 0)) * L + g * (V / 4);
+    if (hv) {
 #pragma unroll
-    for (int s = 0; s < S::SK; ++s) qf[s] = hv ? E::frag_load(qp + s * S::KPL) : E::frag_zero();
+      for (int s = 0; s < S::SK; ++s) {
+        if constexpr (sizeof(T) == 2) bank[s] = __builtin_bit_cast(f32x4, E::frag_load(qp + s * S::KPL));
+        else bank[s >> 2][s & 3] = qp[s];
+      }
+    }
   }
+  auto qfrag = [&](int s) __attribute__((always_inline)) -> F {
+    if constexpr (sizeof(T) == 2) return __builtin_bit_cast(bf16x8, bank[s]);
+    else return bank[s >> 2][s & 3];
+  };
+  float m_run = -INFINITY, l_run = 0.f;  // S waves: running max / sum of the lane's head
 
-  f32x4 oacc[S::MT][4];
-#pragma unroll
-  for (int mt = 0; mt < S::MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  __syncthreads();  // pool tables ready
 
-  uint4 buf[S::UPT][4];
-  uint32_t vmask = 0;
-
-  // token of slot `slot`, or -1 when the slot is past this split or past the query (causal tail)
-  auto slot_token = [&](int slot) -> int {
-    if (slot >= s_end) return -1;
-    const int p = qsel[slot >> log2P];
-    if (p < 0) return -1;
-    const int t = (p << log2P) + (slot & (P - 1));
-    return t <= pos ? t : -1;
+  // cache row of slot t (0..31) of block b, or -1 when past the split or past the query
+  auto slot_row = [&](int b, int t) __attribute__((always_inline)) -> int {
+    const int rel = b * AT_NT + t;
+    if (s_begin + rel >= s_end) return -1;
+    const int pi = rel >> log2P, within = rel & (P - 1);
+    return within < int(pool_ntok[pi]) ? pool_row[pi] + within : -1;
   };
 
-  auto load_block = [&](int b) {
-    const int slot0 = s_begin + b * AT_NT;
+  // Loads are unconditional (an invalid slot reads row 0 of the cache and is zeroed when stored): branch-free
+  // loads let the compiler wait for exactly the block it needs instead of draining every load in flight.
+  auto load_block = [&](int b, u32x4(&R)[S::CHT], bool(&vrow)[S::CHT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < S::UPT; ++j) {
-      const int u = tid + 256 * j;
-      const int c = ((u >> 6) << 3) | (u & 7);
-      const int pg = (u >> 3) & 7;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int tok = (u < S::UNITS) ? slot_token(slot0 + 4 * pg + t) : -1;
-        if (tok >= 0) {
-          const int64_t row = paged_row(bt, bt_stride, seq, tok, log2_pt);
-          buf[j][t] = *reinterpret_cast<const uint4*>(latent + row * L + c * S::EPC);
-        } else {
-          buf[j][t] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-    if (wave == 0) {
-      const bool v = lane < AT_NT && slot_token(slot0 + lane) >= 0;
-      vmask = uint32_t(__ballot(v));
+    for (int i = 0; i < S::CHT; ++i) {
+      const int c = min(tid + AT_THREADS * i, S::CHUNKS - 1);
+      const int row = slot_row(b, c / S::CPR);
+      R[i] = *reinterpret_cast<const u32x4*>(latent + int64_t(max(row, 0)) * L + (c % S::CPR) * S::EPC);
+      vrow[i] = row >= 0;
     }
   };
 
-  auto store_block = [&]() {
+  auto s_phase = [&](int j) __attribute__((always_inline)) {
+    const T* blk = crm[j % 3];
+    f32x4 sa[2][2];
 #pragma unroll
-    for (int j = 0; j < S::UPT; ++j) {
-      const int u = tid + 256 * j;
-      if (u >= S::UNITS) continue;
-      const int c = ((u >> 6) << 3) | (u & 7);
-      const int pg = (u >> 3) & 7;
+    for (int t = 0; t < 2; ++t) {
+      sa[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sa[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const T* ap = blk + (16 * t + l16) * S::RS + g * (V / 4);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) *reinterpret_cast<uint4*>(&crm[(4 * pg + t) * S::RS + c * S::EPC]) = buf[j][t];
+      for (int s = 0; s < S::SK; ++s) sa[t][s & 1] = mfma16(E::frag_load(ap + s * S::KPL), qfrag(s), sa[t][s & 1]);
+    }
+    // lane holds head 16*wl + l16, slots 16t + 4g + i
+    const uint32_t vm = vmask_s[j % 3];
+    float x[2][4];
+    float bmax = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < S::EPC; ++e) {
-        T* dst = &ct[(c * S::EPC + e) * S::TS + 4 * pg];
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t lo = chunk_elem_bits<T>(buf[j][0], e) | (chunk_elem_bits<T>(buf[j][1], e) << 16);
-          const uint32_t hi = chunk_elem_bits<T>(buf[j][2], e) | (chunk_elem_bits<T>(buf[j][3], e) << 16);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<uint4*>(dst) =
-              make_uint4(chunk_elem_bits<T>(buf[j][0], e), chunk_elem_bits<T>(buf[j][1], e),
-                         chunk_elem_bits<T>(buf[j][2], e), chunk_elem_bits<T>(buf[j][3], e));
-        }
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = 16 * t + 4 * g + i;
+        x[t][i] = ((vm >> slot) & 1u) ? (sa[t][0][i] + sa[t][1][i]) * scale_log2 : -INFINITY;
+        bmax = fmaxf(bmax, x[t][i]);
+      }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float m_new = (bmax > m_run + LAZY_MAX) ? bmax : m_run;
+    const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
+    float rsum = 0.f;
+    float pv[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[t][i] = (x[t][i] == -INFINITY) ? 0.f : fast_exp2(x[t][i] - m_new);
+        rsum += pv[t][i];
+      }
+    rsum += __shfl_xor(rsum, 16);
+    rsum += __shfl_xor(rsum, 32);
+    l_run = l_run * alpha + rsum;
+    m_run = m_new;
+    T* prow = ps[j & 1] + (16 * wl + l16) * S::PS;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint2*>(prow + 16 * t + 4 * g) =
+            make_uint2(pack_bf16x2(pv[t][0], pv[t][1]), pack_bf16x2(pv[t][2], pv[t][3]));
+      } else {
+        *reinterpret_cast<float4*>(prow + 16 * t + 4 * g) = make_float4(pv[t][0], pv[t][1], pv[t][2], pv[t][3]);
       }
     }
-    if (tid == 0) vmask_s = vmask;
+    if (g == 0) alpha_s[j & 1][16 * wl + l16] = alpha;
   };
 
-  load_block(0);
-  for (int b = 0; b < nblk; ++b) {
-    __syncthreads();  // every wave is done reading the previous block from LDS
-    store_block();
-    __syncthreads();
-    if (b + 1 < nblk) load_block(b + 1);  // in flight while this block is computed
-    const uint32_t vm = vmask_s;
-
-    if (s_wave) {
-      // S^T tiles for tokens 0..15 and 16..31 of the block
-      f32x4 sacc[2];
+  auto o_phase = [&](int j) __attribute__((always_inline)) {
+    const T* blk = crm[j % 3];
+    const T* pb = ps[j & 1];
+    // rescale only the head tiles whose running max moved
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const T* ap = &crm[(16 * t + l16) * S::RS + g * (V / 4)];
+    for (int nt = 0; nt < HT; ++nt) {
+      const float a = alpha_s[j & 1][16 * nt + l16];
+      if (__ballot(a != 1.f)) {
 #pragma unroll
-        for (int s = 0; s < S::SK; ++s) sacc[t] = mfma16(E::frag_load(ap + s * S::KPL), qf[s], sacc[t]);
+        for (int mt = 0; mt < S::MT; ++mt) bank[mt * HT + nt] *= a;
       }
-      // lane holds head 16*wave + l16, tokens 16t + 4g + i
-      float x[2][4];
-      float bmax = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int slot = 16 * t + 4 * g + i;
-          x[t][i] = ((vm >> slot) & 1u) ? sacc[t][i] * scale_log2 : -INFINITY;
-          bmax = fmaxf(bmax, x[t][i]);
-        }
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      const float m_new = fmaxf(m_run, bmax);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-      float rsum = 0.f;
-      float pv[2][4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[t][i] = (x[t][i] == -INFINITY) ? 0.f : exp2f(x[t][i] - m_new);
-          rsum += pv[t][i];
-        }
-      rsum += __shfl_xor(rsum, 16);
-      rsum += __shfl_xor(rsum, 32);
-      l_run = l_run * alpha + rsum;
-      m_run = m_new;
-      T* prow = &ps[(16 * wave + l16) * S::PS];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t lo = uint32_t(f32_to_bf16(pv[t][0])) | (uint32_t(f32_to_bf16(pv[t][1])) << 16);
-          const uint32_t hi = uint32_t(f32_to_bf16(pv[t][2])) | (uint32_t(f32_to_bf16(pv[t][3])) << 16);
-          *reinterpret_cast<uint2*>(prow + 16 * t + 4 * g) = make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<float4*>(prow + 16 * t + 4 * g) = make_float4(pv[t][0], pv[t][1], pv[t][2], pv[t][3]);
-        }
-      }
-      if (g == 0) alpha_s[16 * wave + l16] = alpha;
     }
-    __syncthreads();
-
-    // O^T[channels of this wave][heads] += C^T . P^T; slot for (group g, step s, element e) = 8g + s*KPL + e
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      if (16 * nt >= H) break;
-      const float a = alpha_s[16 * nt + l16];
-#pragma unroll
-      for (int mt = 0; mt < S::MT; ++mt) oacc[mt][nt] *= a;
-    }
+    // O^T[channels of this wave][heads] += C^T . P^T; k-slot (group g, step s, element e) = token 8g + s*KPL + e
 #pragma unroll
     for (int s = 0; s < S::OK; ++s) {
-      F bq[4];
+      F bq[HT];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        bq[nt] = (16 * nt < H) ? E::frag_load(&ps[(16 * nt + l16) * S::PS + 8 * g + s * S::KPL]) : E::frag_zero();
+      for (int nt = 0; nt < HT; ++nt) bq[nt] = E::frag_load(pb + (16 * nt + l16) * S::PS + 8 * g + s * S::KPL);
 #pragma unroll
       for (int mt = 0; mt < S::MT; ++mt) {
-        const F av = E::frag_load(&ct[(wave * S::VW + 16 * mt + l16) * S::TS + 8 * g + s * S::KPL]);
+        const F av = ct_frag<T, S::RS>(blk, wl * S::VW + 16 * mt, g, l16, s);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          if (16 * nt < H) oacc[mt][nt] = mfma16(av, bq[nt], oacc[mt][nt]);
+        for (int nt = 0; nt < HT; ++nt) bank[mt * HT + nt] = mfma16(av, bq[nt], bank[mt * HT + nt]);
       }
     }
+  };
+
+  // iteration j: store block j into the ring, start loading block j+2, then S(j) on S waves and O(j-1) on
+  // O waves.  Buffer j % 3 was last read by O(j-3) in iteration j-2, two barriers ago.
+  auto iter = [&](int j, u32x4(&R)[S::CHT], bool(&vrow)[S::CHT]) __attribute__((always_inline)) {
+    if (j < nblk) {
+      T* blk = crm[j % 3];
+#pragma unroll
+      for (int i = 0; i < S::CHT; ++i) {
+        const int c = tid + AT_THREADS * i;
+        if (c < S::CHUNKS)
+          *reinterpret_cast<u32x4*>(blk + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) =
+              vrow[i] ? R[i] : u32x4{0, 0, 0, 0};
+      }
+      if (wave == 0) {
+        const uint32_t vm = uint32_t(__ballot(lane < AT_NT && slot_row(j, lane) >= 0));
+        if (lane == 0) vmask_s[j % 3] = vm;
+      }
+      if (j + 2 < nblk) load_block(j + 2, R, vrow);
+    }
+    __syncthreads();
+    if (o_wave) {
+      if (j >= 1) o_phase(j - 1);
+    } else if (s_active && j < nblk) {
+      s_phase(j);
+    }
+  };
+
+  u32x4 R0[S::CHT], R1[S::CHT];
+  bool V0[S::CHT], V1[S::CHT];
+  load_block(0, R0, V0);
+  if (nblk > 1) load_block(1, R1, V1);
+  for (int j = 0; j <= nblk; j += 2) {
+    iter(j, R0, V0);
+    if (j + 1 <= nblk) iter(j + 1, R1, V1);
   }
 
-  if (s_wave && g == 0) {
-    m_s[16 * wave + l16] = m_run;
-    l_s[16 * wave + l16] = l_run;
+  if (s_active && g == 0) {
+    m_s[16 * wl + l16] = m_run;
+    l_s[16 * wl + l16] = l_run;
   }
   __syncthreads();
+  if (!o_wave) return;
 
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < HT; ++nt) {
     const int h = 16 * nt + l16;
-    if (16 * nt >= H) break;
     if (h >= H) continue;
     const float mh = m_s[h], lh = l_s[h];
     if (n_split == 1) {
       const float inv = 1.f / lh;
 #pragma unroll
       for (int mt = 0; mt < S::MT; ++mt) {
-        const int ch0 = wave * S::VW + 16 * mt + 4 * g;
-        T* op = out + (int64_t(qi) * H + h) * V + ch0;
+        const f32x4 o = bank[mt * HT + nt] * inv;
+        T* op = out + (int64_t(qi) * H + h) * V + wl * S::VW + 16 * mt + 4 * g;
         if constexpr (sizeof(T) == 2) {
-          const uint32_t lo = uint32_t(f32_to_bf16(oacc[mt][nt][0] * inv)) |
-                              (uint32_t(f32_to_bf16(oacc[mt][nt][1] * inv)) << 16);
-          const uint32_t hi = uint32_t(f32_to_bf16(oacc[mt][nt][2] * inv)) |
-                              (uint32_t(f32_to_bf16(oacc[mt][nt][3] * inv)) << 16);
-          *reinterpret_cast<uint2*>(op) = make_uint2(lo, hi);
+          *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         } else {
-          *reinterpret_cast<float4*>(op) = make_float4(oacc[mt][nt][0] * inv, oacc[mt][nt][1] * inv,
-                                                       oacc[mt][nt][2] * inv, oacc[mt][nt][3] * inv);
+          *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
         }
       }
-      if (lse && wave == 0 && g == 0) lse[int64_t(qi) * H + h] = (mh + log2f(lh)) * LN2;
+      if (lse && wl == 0 && g == 0) lse[int64_t(qi) * H + h] = (mh + log2f(lh)) * LN2;
     } else {
       const int64_t base = int64_t(qi * n_split + sp) * H + h;
 #pragma unroll
       for (int mt = 0; mt < S::MT; ++mt) {
-        const int ch0 = wave * S::VW + 16 * mt + 4 * g;
-        *reinterpret_cast<float4*>(part_o + base * V + ch0) =
-            make_float4(oacc[mt][nt][0], oacc[mt][nt][1], oacc[mt][nt][2], oacc[mt][nt][3]);
+        const f32x4 o = bank[mt * HT + nt];
+        *reinterpret_cast<float4*>(part_o + base * V + wl * S::VW + 16 * mt + 4 * g) =
+            make_float4(o[0], o[1], o[2], o[3]);
       }
-      if (wave == 0 && g == 0) {
+      if (wl == 0 && g == 0) {
         part_ml[base * 2 + 0] = mh;
         part_ml[base * 2 + 1] = lh;
       }
@@ -349,10 +382,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 }
 
 int attn_splits(int P, int k, int n_q) {
+  // about one block per CU (256), at most 32 splits, and few enough pools per split for the LDS pool table
   const int64_t blocks = (int64_t(k) * P + AT_NT - 1) / AT_NT;
-  int64_t want = (512 + int64_t(n_q) - 1) / (n_q > 0 ? n_q : 1);
+  int64_t want = (256 + int64_t(n_q) - 1) / (n_q > 0 ? n_q : 1);
   if (want > blocks) want = blocks;
   if (want > 32) want = 32;
+  const int64_t min_splits = (blocks + 64 * int64_t(P) - 1) / (64 * int64_t(P));
+  if (want < min_splits) want = min_splits;
   return want < 1 ? 1 : int(want);
 }
 
@@ -362,7 +398,7 @@ size_t attn_workspace(int P, int k, int H, int V, int n_q) {
   return size_t(n_q) * ns * H * (size_t(V) + 2) * sizeof(float);
 }
 
-template <class T, int V>
+template <class T, int V, int HT>
 static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
   const int ns = attn_splits(a.P, a.k, a.n_q);
   const int64_t blocks = (int64_t(a.k) * a.P + AT_NT - 1) / AT_NT;
@@ -374,7 +410,7 @@ static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
     part_ml = part_o + size_t(a.n_q) * ns * a.H * a.V;
   }
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  attn_kernel<T, V><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(256), 0, s>>>(
+  attn_kernel<T, V, HT><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
       (const T*)a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
       ilog2(a.P), a.k, a.H, scale_log2, ns, bps, (T*)a.out, a.lse, part_o, part_ml);
   kp_status st = check_launch("sparse_mla_attn");
@@ -390,11 +426,21 @@ kp_status launch_attn(const AttnLaunch& a, hipStream_t s) {
     set_error("sparse_mla_attn: too many queries for one launch");
     return KP_ERR_INVALID_ARG;
   }
+  // 16-head tiles: 1 (H <= 16), 2 (H <= 32) or 4 (H <= 64)
+  const int ht = a.H <= 16 ? 1 : a.H <= 32 ? 2 : 4;
   if (a.dtype == KP_DTYPE_BF16) {
-    if (a.V == 512) return launch_attn_t<bf16, 512>(a, s);
-    return launch_attn_t<bf16, 64>(a, s);
+    if (a.V == 512) {
+      if (ht == 4) return launch_attn_t<bf16, 512, 4>(a, s);
+      if (ht == 2) return launch_attn_t<bf16, 512, 2>(a, s);
+      return launch_attn_t<bf16, 512, 1>(a, s);
+    }
+    if (ht == 4) return launch_attn_t<bf16, 64, 4>(a, s);
+    if (ht == 2) return launch_attn_t<bf16, 64, 2>(a, s);
+    return launch_attn_t<bf16, 64, 1>(a, s);
   }
-  return launch_attn_t<float, 64>(a, s);
+  if (ht == 4) return launch_attn_t<float, 64, 4>(a, s);
+  if (ht == 2) return launch_attn_t<float, 64, 2>(a, s);
+  return launch_attn_t<float, 64, 1>(a, s);
 }
 
 }  // namespace kp

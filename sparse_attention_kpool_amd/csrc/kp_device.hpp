@@ -20,6 +20,9 @@
 namespace kp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// 16-byte staging registers.  A native vector type, not HIP's uint4 struct: copies of that struct-with-union
+// can keep whole staging arrays out of registers (in scratch).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -30,12 +33,20 @@ struct bf16 {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// Round-to-nearest-even fp32 -> bf16 (finite inputs).
+// Round-to-nearest-even fp32 -> bf16 (gfx950 v_cvt_pk_bf16_f32 under the default rounding mode).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
+
+// Two fp32 values -> two RNE bf16 in one dword (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 2^x on the hardware exp unit (v_exp_f32, about 1 ulp; results below the normal range flush to zero).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <class T>
 struct Elem;
@@ -57,11 +68,8 @@ struct Elem<bf16> {
   typedef bf16x8 frag;
   __device__ __forceinline__ static float to_f32(bf16 v) { return bf16_to_f32(v.bits); }
   __device__ __forceinline__ static bf16 from_f32(float v) { return bf16{f32_to_bf16(v)}; }
-  __device__ __forceinline__ static frag frag_load(const bf16* p) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
-    return __builtin_bit_cast(frag, v);
-  }
-  __device__ __forceinline__ static frag frag_zero() { return __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0)); }
+  __device__ __forceinline__ static frag frag_load(const bf16* p) { return *reinterpret_cast<const frag*>(p); }
+  __device__ __forceinline__ static frag frag_zero() { return __builtin_bit_cast(frag, u32x4{0, 0, 0, 0}); }
 };
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {

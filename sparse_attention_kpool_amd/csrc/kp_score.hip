@@ -6,150 +6,298 @@
 //
 // Mapping onto the matrix cores: for one query, [32 heads x D] . [D x 32 pools] is one 32x32 MFMA tile
 // (32x32x16 bf16, or 32x32x2 f32), the index heads forming M.  Lane group g of the 32x32 layout carries the
-// channels [g*D/2, (g+1)*D/2), so each lane streams one contiguous half-row (128 B for bf16 D = 128) of a
-// pooled key.  The epilogue is in registers: each lane holds 16 heads of one pool, weights them with ReLU,
-// sums in-lane, then adds its partner lane (l ^ 32) -- one cross-lane step per pool tile.
+// channels [g*D/2, (g+1)*D/2).  The epilogue stays in registers: each lane holds 16 heads of one pool, weights
+// them with ReLU, sums in-lane, then adds its partner lane (l ^ 32).
 //
-// Work split: grid x = (query group) x (pool chunk).  A query group is QW consecutive queries that the caller
-// says share a sequence (a prefill chunk); each pooled-key tile loaded is then reused by QW queries.  If a
-// group's queries turn out to belong to different sequences, the group is processed one sequence at a time,
-// so the result never depends on that promise.  Within a block, the 4 waves take interleaved 32-pool tiles.
+// Data path: pooled keys stream in 32-pool tiles.  A tile is loaded with fully coalesced 16-byte loads (a wave
+// instruction covers 1 KiB of consecutive pooled rows; the pools of one page are contiguous), kept two tiles
+// ahead in registers, written to LDS and read back in the MFMA operand layout.  Page ids are looked up once
+// per block (never in the tile loop), so no key load waits on another global load.
+//
+// Two kernels:
+//   decode   one query per block; each wave streams its own quarter of the block's pool range through a
+//            private LDS tile, with no block-wide barrier in the loop.
+//   prefill  8 consecutive queries per block that the caller says share a sequence (a prefill chunk); each
+//            32-pool tile is loaded once into LDS and computed by all 4 waves for 2 queries each.  If the
+//            queries turn out to belong to different sequences, the block handles one sequence at a time, so
+//            results never depend on that promise.
 //
 // Bound: decode is HBM-bound (the pooled-key stream, 256 B per pool at D = 128 bf16 for 32 x 128 MACs, i.e.
-// 32 flop/B: above the VALU ridge, so the contraction runs on MFMA); prefill (many queries per sequence) is
-// MFMA-bound.
+// 32 flop/B: above the VALU ridge, so the contraction runs on MFMA); prefill is MFMA-bound.
 #include "kp_device.hpp"
 #include "kp_internal.hpp"
 
 namespace kp {
 
-template <class T, int D, int QW>
-__global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ pooled, const int32_t* __restrict__ bt,
-                                                    int bt_stride, int log2_ppp, const T* __restrict__ q_idx,
-                                                    const float* __restrict__ w, const int32_t* __restrict__ q_seq,
-                                                    const int32_t* __restrict__ q_pos, int n_q, int Hi, int P,
-                                                    float* __restrict__ scores, int64_t ld, int chunk_pools,
-                                                    int n_chunks) {
+template <class T, int D>
+struct ScoreShape {
+  static constexpr int KPL = Elem<T>::kpl;
+  static constexpr int STEPS = D / (2 * KPL);          // 32x32 k-steps over D
+  static constexpr int EPC = 16 / int(sizeof(T));      // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;                  // chunks per pooled row
+  static constexpr int RS = D + EPC;                   // LDS row stride (elements): +16 B against conflicts
+  static constexpr int TCH = 32 * CPR;                 // 16-byte chunks per 32-pool tile
+};
+
+// Index-query fragments (A operand) and head weights of one query, in the 32x32 layout.
+template <class T, int D>
+__device__ __forceinline__ void score_query_frags(const T* __restrict__ q_idx, const float* __restrict__ w, int row,
+                                                  bool rv, int Hi, int n, int g,
+                                                  typename Elem<T>::frag (&qa)[ScoreShape<T, D>::STEPS],
+                                                  float (&wv)[16]) {
+  using S = ScoreShape<T, D>;
+  using E = Elem<T>;
+  const bool hv = (n < Hi) && rv;
+  const T* qp = q_idx + (int64_t(rv ? row : 0) * Hi + (hv ? n : 0)) * D + g * (D / 2);
+#pragma unroll
+  for (int s = 0; s < S::STEPS; ++s) qa[s] = hv ? E::frag_load(qp + s * S::KPL) : E::frag_zero();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int h = 8 * (i / 4) + 4 * g + (i % 4);
+    wv[i] = (h < Hi && rv) ? w[int64_t(row) * Hi + h] : 0.f;
+  }
+}
+
+// ReLU-weighted head sum of one 32x32 tile; lanes 0..31 return the scores of pools 0..31.
+template <class T, int D>
+__device__ __forceinline__ float score_tile(const typename Elem<T>::frag (&qa)[ScoreShape<T, D>::STEPS],
+                                            const typename Elem<T>::frag (&kb)[ScoreShape<T, D>::STEPS],
+                                            const float (&wv)[16]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < ScoreShape<T, D>::STEPS; ++s) acc = mfma32(qa[s], kb[s], acc);
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) part += wv[i] * fmaxf(acc[i], 0.f);
+  return part + __shfl_xor(part, 32);
+}
+
+// ---------------------------------------------------------------------------------------------------------------
+// decode: grid = n_q x n_chunks; a block covers `chunk_pools` pools of one query, a wave `chunk_pools / 4`
+// (at most 64 pages, so the wave's page ids fit one register per lane)
+// ---------------------------------------------------------------------------------------------------------------
+template <class T, int D>
+__global__ __launch_bounds__(256) void score_decode_kernel(
+    const T* __restrict__ pooled, const int32_t* __restrict__ bt, int bt_stride, int log2_ppp,
+    const T* __restrict__ q_idx, const float* __restrict__ w, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int Hi, int P, float* __restrict__ scores, int64_t ld, int chunk_pools,
+    int n_chunks) {
+  using S = ScoreShape<T, D>;
   using E = Elem<T>;
   using F = typename E::frag;
-  constexpr int KPL = E::kpl;
-  constexpr int STEPS = D / (2 * KPL);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int n = lane & 31;  // A row (head) and B column (pool) of this lane
-  const int g = lane >> 5;  // k-group: channels [g*D/2, (g+1)*D/2)
+  constexpr int CHT = S::TCH / 64;  // chunks per lane per tile
+  __shared__ __align__(16) T tiles[4][32 * S::RS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, g = lane >> 5;
+  const int qi = blockIdx.x / n_chunks;
+  const int chunk = blockIdx.x - qi * n_chunks;
+  const int seq = q_seq[qi];
+  const int n_c = int(min(int64_t((q_pos[qi] + 1) / P), ld));  // ld bounds a row
+  const int sub = chunk_pools / 4;
+  const int w_begin = chunk * chunk_pools + wave * sub;
+  const int w_end = min(w_begin + sub, n_c);
+  if (w_begin >= w_end) return;  // no block-wide barrier below: waves finish independently
+
+  F qa[S::STEPS];
+  float wv[16];
+  score_query_frags<T, D>(q_idx, w, qi, true, Hi, n, g, qa, wv);
+
+  // page id of each page the wave touches: lane l holds page (w_begin >> log2_ppp) + l
+  const int pg0 = w_begin >> log2_ppp;
+  const int npg = ((w_end - 1) >> log2_ppp) - pg0 + 1;
+  const int page_reg = lane < npg ? bt[int64_t(seq) * bt_stride + pg0 + lane] : 0;
+  const int ppp_mask = (1 << log2_ppp) - 1;
+
+  T* tile = tiles[wave];
+  const int ntile = (w_end - w_begin + 31) / 32;
+  auto load_tile = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CHT; ++i) {
+      const int c = i * 64 + lane;
+      int pool = w_begin + t * 32 + c / S::CPR;
+      pool = pool < w_end ? pool : w_begin;  // past the range: re-read a valid pool, never scored
+      const int page = __shfl(page_reg, (pool >> log2_ppp) - pg0);
+      const int64_t row = (int64_t(page) << log2_ppp) + (pool & ppp_mask);
+      R[i] = *reinterpret_cast<const u32x4*>(pooled + row * D + (c % S::CPR) * S::EPC);
+    }
+  };
+  auto step = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CHT; ++i) {
+      const int c = i * 64 + lane;
+      *reinterpret_cast<u32x4*>(tile + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
+    }
+    if (t + 2 < ntile) load_tile(t + 2, R);
+    F kb[S::STEPS];
+    const T* kp = tile + n * S::RS + g * (D / 2);
+#pragma unroll
+    for (int s = 0; s < S::STEPS; ++s) kb[s] = E::frag_load(kp + s * S::KPL);
+    const float sc = score_tile<T, D>(qa, kb, wv);
+    const int pool = w_begin + t * 32 + n;
+    if (g == 0 && pool < w_end) scores[int64_t(qi) * ld + pool] = sc;
+  };
+
+  u32x4 R0[CHT], R1[CHT];
+  load_tile(0, R0);
+  if (ntile > 1) load_tile(1, R1);
+  for (int t = 0; t < ntile; t += 2) {
+    step(t, R0);
+    if (t + 1 < ntile) step(t + 1, R1);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------------
+// prefill: grid = (n_q / 8) x n_chunks; a block covers `chunk_pools` pools for 8 queries
+// ---------------------------------------------------------------------------------------------------------------
+constexpr int SC_QW = 2;              // queries per wave
+constexpr int SC_QG = 4 * SC_QW;      // queries per block
+constexpr int SC_MAXPG = 1024;        // page ids of one block's pool range held in LDS
+
+template <class T, int D>
+__global__ __launch_bounds__(256) void score_prefill_kernel(
+    const T* __restrict__ pooled, const int32_t* __restrict__ bt, int bt_stride, int log2_ppp,
+    const T* __restrict__ q_idx, const float* __restrict__ w, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int n_q, int Hi, int P, float* __restrict__ scores, int64_t ld,
+    int chunk_pools, int n_chunks) {
+  using S = ScoreShape<T, D>;
+  using E = Elem<T>;
+  using F = typename E::frag;
+  constexpr int CHT = (S::TCH + 255) / 256;  // chunks per thread per tile
+  __shared__ __align__(16) T tile[32 * S::RS];
+  __shared__ int page_s[SC_MAXPG];
+  __shared__ int seq_s[SC_QG];
+  __shared__ int nc_s[SC_QG];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, g = lane >> 5;
   const int grp = blockIdx.x / n_chunks;
   const int chunk = blockIdx.x - grp * n_chunks;
-  const int r0 = grp * QW;
+  const int r0 = grp * SC_QG;
+  if (tid < SC_QG) {
+    const int row = r0 + tid;
+    seq_s[tid] = row < n_q ? q_seq[row] : -1;
+    nc_s[tid] = row < n_q ? int(min(int64_t((q_pos[row] + 1) / P), ld)) : 0;
+  }
+  F qa[SC_QW][S::STEPS];
+  float wv[SC_QW][16];
+#pragma unroll
+  for (int r = 0; r < SC_QW; ++r) {
+    const int row = r0 + wave * SC_QW + r;
+    score_query_frags<T, D>(q_idx, w, row, row < n_q, Hi, n, g, qa[r], wv[r]);
+  }
+  __syncthreads();
 
-  int seqs[QW], ncs[QW];
   unsigned pending = 0;
-#pragma unroll
-  for (int r = 0; r < QW; ++r) {
-    const int row = r0 + r;
-    if (row < n_q) {
-      seqs[r] = q_seq[row];
-      ncs[r] = int(min(int64_t((q_pos[row] + 1) / P), ld));  // ld bounds the row even if pos > max_pos
-      pending |= 1u << r;
-    } else {
-      seqs[r] = -1;
-      ncs[r] = 0;
-    }
-  }
-
-  // index-query fragments (A operand) and the head weights of the 16 D-rows this lane holds
-  F qa[QW][STEPS];
-  float wv[QW][16];
-#pragma unroll
-  for (int r = 0; r < QW; ++r) {
-    const int row = (r0 + r < n_q) ? r0 + r : 0;
-    const bool hv = (n < Hi) && (r0 + r < n_q);
-    const T* qp = q_idx + (int64_t(row) * Hi + (hv ? n : 0)) * D + g * (D / 2);
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) qa[r][s] = hv ? E::frag_load(qp + s * KPL) : E::frag_zero();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int h = 8 * (i / 4) + 4 * g + (i % 4);
-      wv[r][i] = (h < Hi && r0 + r < n_q) ? w[int64_t(row) * Hi + h] : 0.f;
-    }
-  }
-
+  for (int r = 0; r < SC_QG; ++r)
+    if (seq_s[r] >= 0) pending |= 1u << r;
   const int p_begin = chunk * chunk_pools;
+  const int ppp_mask = (1 << log2_ppp) - 1;
+
   while (pending) {
-    const int lead = __builtin_ctz(pending);
-    const int seq = seqs[lead];
+    const int seq = seq_s[__builtin_ctz(pending)];
     unsigned active = 0;
     int ncmax = 0;
-#pragma unroll
-    for (int r = 0; r < QW; ++r)
-      if (((pending >> r) & 1u) && seqs[r] == seq) {
+    for (int r = 0; r < SC_QG; ++r)
+      if (((pending >> r) & 1u) && seq_s[r] == seq) {
         active |= 1u << r;
-        ncmax = max(ncmax, ncs[r]);
+        ncmax = max(ncmax, nc_s[r]);
       }
     pending &= ~active;
     const int p_end = min(p_begin + chunk_pools, ncmax);
+    if (p_end <= p_begin) continue;
+    const int ntile = (p_end - p_begin + 31) / 32;
+    const int pg0 = p_begin >> log2_ppp;
+    const int npg = ((p_end - 1) >> log2_ppp) - pg0 + 1;
+    __syncthreads();  // the previous sequence's tiles and page ids are no longer read
+    for (int j = tid; j < npg; j += 256) page_s[j] = bt[int64_t(seq) * bt_stride + pg0 + j];
+    __syncthreads();
 
-    for (int t0 = p_begin + wave * 32; t0 < p_end; t0 += 4 * 32) {
-      const int pool = t0 + n;
-      F kb[STEPS];
-      if (pool < p_end) {
-        const int64_t row = paged_row(bt, bt_stride, seq, pool, log2_ppp);
-        const T* kp = pooled + row * D + g * (D / 2);
+    auto load_tile = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) kb[s] = E::frag_load(kp + s * KPL);
-      } else {
-#pragma unroll
-        for (int s = 0; s < STEPS; ++s) kb[s] = E::frag_zero();
+      for (int i = 0; i < CHT; ++i) {
+        const int c = min(tid + 256 * i, S::TCH - 1);
+        int pool = p_begin + t * 32 + c / S::CPR;
+        pool = pool < p_end ? pool : p_begin;
+        const int64_t row = (int64_t(page_s[(pool >> log2_ppp) - pg0]) << log2_ppp) + (pool & ppp_mask);
+        R[i] = *reinterpret_cast<const u32x4*>(pooled + row * D + (c % S::CPR) * S::EPC);
       }
+    };
+    auto step = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
+      __syncthreads();  // the previous tile is fully read
 #pragma unroll
-      for (int r = 0; r < QW; ++r) {
-        if (!((active >> r) & 1u)) continue;
-        f32x16 acc = {};
-#pragma unroll
-        for (int s = 0; s < STEPS; ++s) acc = mfma32(qa[r][s], kb[s], acc);
-        float part = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) part += wv[r][i] * fmaxf(acc[i], 0.f);
-        part += __shfl_xor(part, 32);
-        if (g == 0 && pool < ncs[r]) scores[int64_t(r0 + r) * ld + pool] = part;
+      for (int i = 0; i < CHT; ++i) {
+        const int c = tid + 256 * i;
+        if (c < S::TCH) *reinterpret_cast<u32x4*>(tile + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
       }
+      if (t + 2 < ntile) load_tile(t + 2, R);
+      __syncthreads();
+      F kb[S::STEPS];
+      const T* kp = tile + n * S::RS + g * (D / 2);
+#pragma unroll
+      for (int s = 0; s < S::STEPS; ++s) kb[s] = E::frag_load(kp + s * S::KPL);
+      const int pool = p_begin + t * 32 + n;
+#pragma unroll
+      for (int r = 0; r < SC_QW; ++r) {
+        const int qr = wave * SC_QW + r;
+        if (!((active >> qr) & 1u)) continue;
+        const float sc = score_tile<T, D>(qa[r], kb, wv[r]);
+        if (g == 0 && pool < nc_s[qr]) scores[int64_t(r0 + qr) * ld + pool] = sc;
+      }
+    };
+    u32x4 R0[CHT], R1[CHT];
+    load_tile(0, R0);
+    if (ntile > 1) load_tile(1, R1);
+    for (int t = 0; t < ntile; t += 2) {
+      step(t, R0);
+      if (t + 1 < ntile) step(t + 1, R1);
     }
   }
 }
 
 template <class T, int D>
-static void launch_score_t(const ScoreLaunch& a, int qw, int chunk, int n_chunks, int n_groups, hipStream_t s) {
+static void launch_score_t(const ScoreLaunch& a, bool prefill, int chunk, int n_chunks, int n_groups,
+                           hipStream_t s) {
   const dim3 grid(unsigned(int64_t(n_groups) * n_chunks)), block(256);
-  if (qw == 4)
-    score_kernel<T, D, 4><<<grid, block, 0, s>>>((const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp,
-                                                 (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.n_q, a.Hi, a.P,
-                                                 a.scores, a.ld, chunk, n_chunks);
+  if (prefill)
+    score_prefill_kernel<T, D><<<grid, block, 0, s>>>((const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp,
+                                                      (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.n_q, a.Hi, a.P,
+                                                      a.scores, a.ld, chunk, n_chunks);
   else
-    score_kernel<T, D, 1><<<grid, block, 0, s>>>((const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp,
-                                                 (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.n_q, a.Hi, a.P,
-                                                 a.scores, a.ld, chunk, n_chunks);
+    score_decode_kernel<T, D><<<grid, block, 0, s>>>((const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp,
+                                                     (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.Hi, a.P,
+                                                     a.scores, a.ld, chunk, n_chunks);
 }
 
 kp_status launch_score(const ScoreLaunch& a, hipStream_t s) {
   const int64_t ncmax = (int64_t(a.max_pos) + 1) / a.P;
   if (a.n_q == 0 || ncmax == 0) return KP_OK;
-  const int qw = (a.group >= 4) ? 4 : 1;
-  const int64_t n_groups = (a.n_q + qw - 1) / qw;
-  // pools per block: a multiple of 4 waves x 32 pools, sized for about 2048 blocks in flight
+  const int64_t ppp = int64_t(1) << a.log2_ppp;
+  // prefill shape when the caller promises runs of >= 8 queries of one sequence
+  const bool prefill = a.group >= SC_QG;
+  const int64_t n_groups = prefill ? (a.n_q + SC_QG - 1) / SC_QG : a.n_q;
+  // pools per block: a multiple of 128 sized for about 2048 blocks, at most 4096, and (decode) at most 64
+  // pages per wave or (prefill) SC_MAXPG pages per block
   int64_t chunk = (ncmax * n_groups + 2047) / 2048;
   chunk = ((chunk + 127) / 128) * 128;
   if (chunk < 128) chunk = 128;
   if (chunk > 4096) chunk = 4096;
+  const int64_t cap = prefill ? int64_t(SC_MAXPG - 1) * ppp : 4 * 63 * ppp;
+  while (chunk > 128 && chunk > cap) chunk -= 128;
+  if (chunk > cap) {
+    set_error("dsa_indexer_score: pages of %lld pooled rows are too small", (long long)ppp);
+    return KP_ERR_UNSUPPORTED;
+  }
   const int64_t n_chunks = (ncmax + chunk - 1) / chunk;
   if (n_groups * n_chunks > 0x7fffffff) {
     set_error("dsa_indexer_score: grid of %lld blocks is too large", (long long)(n_groups * n_chunks));
     return KP_ERR_INVALID_ARG;
   }
   if (a.dtype == KP_DTYPE_BF16) {
-    if (a.D == 128) launch_score_t<bf16, 128>(a, qw, int(chunk), int(n_chunks), int(n_groups), s);
-    else launch_score_t<bf16, 32>(a, qw, int(chunk), int(n_chunks), int(n_groups), s);
+    if (a.D == 128) launch_score_t<bf16, 128>(a, prefill, int(chunk), int(n_chunks), int(n_groups), s);
+    else launch_score_t<bf16, 32>(a, prefill, int(chunk), int(n_chunks), int(n_groups), s);
   } else {
-    launch_score_t<float, 32>(a, qw, int(chunk), int(n_chunks), int(n_groups), s);
+    launch_score_t<float, 32>(a, prefill, int(chunk), int(n_chunks), int(n_groups), s);
   }
   return check_launch("dsa_indexer_score");
 }

@@ -5,138 +5,328 @@
 // the incomplete tail.  [GLM-5.3-Flash model card, "Raw config fields"]: index_topk 2048 (pools).  Ties go to
 // the lower pool index (the layer's specification).
 //
-// Algorithm (exact, deterministic, no sort):
-//   1. Radix select on order-preserving uint32 keys of the fp32 scores (-0 folded into +0): four 8-bit
-//      passes from the top digit find the key T of the budget-th largest score and how many copies of T the
-//      budget still needs (need_eq).  Histograms are integer LDS atomics, so the result does not depend on
-//      their order.
-//   2. One pass in index order keeps every pool with key > T and the first need_eq pools with key == T.  A
-//      pass in index order emits the kept pool ids already ascending, which is the output format, and taking
-//      the first equal keys is exactly the lower-index tie-break.
-//   3. The tail pool tau (when (i+1) mod P != 0) is appended; it is larger than every complete pool id.
-// One 1024-thread block per query row.
+// Exact and deterministic, with no sort.  For one row of n scores and a budget b < n:
+//   1. The row is copied once into LDS as order-preserving uint32 keys (-0 folded into +0), padded one word
+//      in 32 so that each thread's contiguous segment is read without bank conflicts.
+//   2. Radix select: the block's min and max key fix the common high bits; the varying bits below are resolved
+//      11 at a time (at most three passes), finding the key T of the b-th largest score and how many copies of
+//      T the budget still takes (need_eq).  Histograms are integer LDS atomics, so their order does not
+//      matter.
+//   3. Compaction in index order: every thread counts its segment's keys > T and == T; two block scans give
+//      each thread its output offset and its share of the equal keys (the lowest indices first -- exactly the
+//      lower-index tie-break); the kept ids come out already ascending, which is the output format.
+//   4. The tail pool tau (when (i+1) mod P != 0) is appended; it is larger than every complete pool id.
+// Rows of at most 32768 pools take one block.  Longer rows (up to 16 x 32768) take two steps: every 32768-pool
+// chunk keeps its own top-b candidates (ascending), then one block selects the final b among the candidates.
+// Exact because an element in the row's top b (under score desc, index asc) is in the top b of its chunk.
 #include "kp_device.hpp"
 #include "kp_internal.hpp"
 
 namespace kp {
 
-constexpr int TK_THREADS = 1024;
+constexpr int TK_THREADS = 512;
 constexpr int TK_WAVES = TK_THREADS / 64;
+constexpr int TK_MAXN = 32768;          // keys held in LDS by one block
+constexpr int TK_MAXCHUNKS = 16;        // chunks of a two-step row
 
-// Exclusive count of `flag` over the block in thread order; `total` receives the block-wide count.
-__device__ __forceinline__ int block_excl_count(bool flag, int* wsum, int& total) {
+__device__ __forceinline__ int tk_slot(int i) { return i + (i >> 5); }
+
+struct TkShared {
+  uint32_t keys[TK_MAXN + TK_MAXN / 32];
+  uint32_t hist[2048];
+  int wsum[TK_WAVES];
+  uint32_t wmin[TK_WAVES], wmax[TK_WAVES];
+  uint32_t digit, remaining;
+};
+
+// Exclusive prefix sum of `v` over the block (thread order); `total` receives the block sum.
+__device__ __forceinline__ int tk_block_scan(int v, int* wsum, int& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint64_t b = __ballot(flag);
-  const int rank = __popcll(b & ((uint64_t(1) << lane) - 1));
-  if (lane == 0) wsum[wv] = __popcll(b);
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(inc, off);
+    if (lane >= off) inc += u;
+  }
+  if (lane == 63) wsum[wv] = inc;
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int k = 0; k < TK_WAVES; ++k) {
-    const int c = wsum[k];
-    before += (k < wv) ? c : 0;
+  for (int w = 0; w < TK_WAVES; ++w) {
+    const int c = wsum[w];
+    before += (w < wv) ? c : 0;
     tot += c;
   }
   __syncthreads();
   total = tot;
-  return before + rank;
+  return before + inc - v;
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restrict__ scores, int64_t ld,
-                                                          const int32_t* __restrict__ q_pos, int P, int k,
-                                                          int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
-  __shared__ uint32_t hist[256];
-  __shared__ int wsum[TK_WAVES];
-  __shared__ uint32_t sh_digit, sh_remaining;
-  const int q = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int i = q_pos[q];
-  const int n_c = int(min(int64_t((i + 1) / P), ld));  // ld bounds the row even if pos > max_pos
-  const int r = (i + 1) % P;
-  const int tau = i / P;
-  const int budget = min(k - (r ? 1 : 0), n_c);
-  const float* row = scores + int64_t(q) * ld;
-  int32_t* out = sel + int64_t(q) * k;
+// Selects the `budget` largest of keys[0..n) (0 < budget < n) and calls emit(out_pos, i) for each kept i,
+// out_pos ascending with i.
+//
+// The radix passes only cover the bits in which the row's keys differ: a first pass takes the block min and
+// max, their common high bits are fixed, and the varying bits below are resolved 11 at a time (at most three
+// passes).  Digits of varying bits are spread, so plain LDS atomics seldom collide.  A row whose keys are all
+// equal needs no pass at all.
+template <class Emit>
+__device__ void tk_select(TkShared& sh, int n, int budget, Emit emit) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int E = (n + TK_THREADS - 1) / TK_THREADS;
+  const int i0 = min(tid * E, n), i1 = min(i0 + E, n);
 
-  if (budget >= n_c) {
-    for (int p = tid; p < n_c; p += TK_THREADS) out[p] = p;
-  } else if (budget > 0) {
-    uint32_t prefix = 0, mask = 0, remaining = uint32_t(budget);
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      for (int p = tid; p < n_c; p += TK_THREADS) {
-        const uint32_t key = score_key(row[p]);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid < 64) {
-        // wave 0: lane l owns digits 4l..4l+3; find the digit where the count from the top reaches `remaining`
-        uint32_t c[4], mine = 0;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = sh.keys[tk_slot(i)];
+    mn = min(mn, key);
+    mx = max(mx, key);
+  }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          c[j] = hist[4 * tid + j];
-          mine += c[j];
-        }
-        // inclusive suffix sum over lanes (lanes above hold higher digits)
-        uint32_t suf = mine;
+  for (int off = 32; off >= 1; off >>= 1) {
+    mn = min(mn, uint32_t(__shfl_xor(int(mn), off)));
+    mx = max(mx, uint32_t(__shfl_xor(int(mx), off)));
+  }
+  if (lane == 0) {
+    sh.wmin[wv] = mn;
+    sh.wmax[wv] = mx;
+  }
+  __syncthreads();
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t v = __shfl_down(suf, off);
-          if (tid + off < 64) suf += v;
-        }
-        const uint32_t above = suf - mine;  // count of keys with a higher digit than this lane's range
-        if (above < remaining && remaining <= suf) {
-          uint32_t acc = above;
-          for (int j = 3; j >= 0; --j) {
-            if (acc + c[j] >= remaining) {
-              sh_digit = uint32_t(4 * tid + j);
-              sh_remaining = remaining - acc;
-              break;
-            }
-            acc += c[j];
-          }
-        }
-      }
-      __syncthreads();
-      prefix |= sh_digit << shift;
-      mask |= 255u << shift;
-      remaining = sh_remaining;
-      __syncthreads();
+  for (int w = 0; w < TK_WAVES; ++w) {
+    mn = min(mn, sh.wmin[w]);
+    mx = max(mx, sh.wmax[w]);
+  }
+  // bits [0, lo) vary; bits at and above lo are common to every key and fixed in `prefix`
+  int lo = (mn == mx) ? 0 : 32 - __clz(int(mn ^ mx));
+  uint32_t mask = lo == 32 ? 0u : ~((1u << lo) - 1u);
+  uint32_t prefix = mn & mask;
+  uint32_t remaining = uint32_t(budget);
+  while (lo > 0) {
+    const int width = min(11, lo);
+    const int shift = lo - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int j = tid; j < 2048; j += TK_THREADS) sh.hist[j] = 0;
+    __syncthreads();
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t key = sh.keys[tk_slot(i)];
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
     }
-    const uint32_t T = prefix;
-    const int need_eq = int(remaining);
-    int base = 0, eq_base = 0;
-    for (int p0 = 0; p0 < n_c; p0 += TK_THREADS) {
-      const int p = p0 + tid;
-      const uint32_t key = (p < n_c) ? score_key(row[p]) : 0u;
-      const bool gt = (p < n_c) && key > T;
-      const bool eq = (p < n_c) && key == T;
-      int eq_tot, take_tot;
-      const int eq_rank = eq_base + block_excl_count(eq, wsum, eq_tot);
-      const bool take = gt || (eq && eq_rank < need_eq);
-      const int at = base + block_excl_count(take, wsum, take_tot);
-      if (take) out[at] = p;
-      base += take_tot;
-      eq_base += eq_tot;
+    __syncthreads();
+    // thread t owns digits 4t .. 4t+3; `above` counts keys with a higher digit than its range
+    uint32_t c[4], mine = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = 4 * tid + j;
+      c[j] = d <= int(dmask) ? sh.hist[d] : 0u;
+      mine += c[j];
+    }
+    int total;
+    const int before = tk_block_scan(int(mine), sh.wsum, total);
+    const uint32_t above = uint32_t(total - before) - mine;
+    if (above < remaining && remaining <= above + mine) {
+      uint32_t acc = above;
+      for (int j = 3; j >= 0; --j) {
+        if (acc + c[j] >= remaining) {
+          sh.digit = uint32_t(4 * tid + j);
+          sh.remaining = remaining - acc;
+          break;
+        }
+        acc += c[j];
+      }
+    }
+    __syncthreads();
+    prefix |= sh.digit << shift;
+    mask |= dmask << shift;
+    remaining = sh.remaining;
+    lo = shift;
+  }
+  const uint32_t T = prefix;
+  const int need_eq = int(remaining);
+  int gt = 0, eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = sh.keys[tk_slot(i)];
+    gt += key > T;
+    eq += key == T;
+  }
+  int tot;
+  const int eq_before = tk_block_scan(eq, sh.wsum, tot);
+  const int take_eq = min(max(need_eq - eq_before, 0), eq);
+  int at = tk_block_scan(gt + take_eq, sh.wsum, tot);
+  int eq_left = take_eq;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = sh.keys[tk_slot(i)];
+    if (key > T || (key == T && eq_left > 0)) {
+      if (key == T) --eq_left;
+      emit(at++, i);
     }
   }
-  const int cnt = max(budget, 0);
-  if (tid == 0) {
+}
+
+// Copies n fp32 scores (16-byte aligned source) into LDS as keys.  Every thread issues all of its loads before
+// its first LDS store (up to 16 float4 per thread per round), so the copy costs about one memory latency per
+// round instead of one per element.
+__device__ __forceinline__ void tk_load_keys(TkShared& sh, const float* __restrict__ src, int n) {
+  constexpr int U = 16;
+  const int n4 = n >> 2;
+  const float4* s4 = reinterpret_cast<const float4*>(src);
+  for (int base = 0; base < n4; base += U * TK_THREADS) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i4 = base + u * TK_THREADS + int(threadIdx.x);
+      v[u] = s4[min(i4, max(n4 - 1, 0))];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i4 = base + u * TK_THREADS + int(threadIdx.x);
+      if (i4 < n4) {
+        sh.keys[tk_slot(4 * i4 + 0)] = score_key(v[u].x);
+        sh.keys[tk_slot(4 * i4 + 1)] = score_key(v[u].y);
+        sh.keys[tk_slot(4 * i4 + 2)] = score_key(v[u].z);
+        sh.keys[tk_slot(4 * i4 + 3)] = score_key(v[u].w);
+      }
+    }
+  }
+  for (int i = 4 * n4 + int(threadIdx.x); i < n; i += TK_THREADS) sh.keys[tk_slot(i)] = score_key(src[i]);
+}
+
+__device__ __forceinline__ void tk_geometry(int pos, int P, int k, int64_t ld, int& n_c, int& r, int& tau, int& b) {
+  n_c = int(min(int64_t((pos + 1) / P), ld));  // ld bounds a row even if pos exceeds the promised max
+  r = (pos + 1) % P;
+  tau = pos / P;
+  b = min(k - (r ? 1 : 0), n_c);
+}
+
+// Tail, -1 padding and the count, after `cnt` complete pools were written.
+__device__ __forceinline__ void tk_finish(int32_t* out, int32_t* n_sel, int q, int k, int cnt, int r, int tau) {
+  if (threadIdx.x == 0) {
     if (r) out[cnt] = tau;
     n_sel[q] = cnt + (r ? 1 : 0);
   }
-  for (int j = cnt + (r ? 1 : 0) + tid; j < k; j += TK_THREADS) out[j] = -1;
+  for (int j = cnt + (r ? 1 : 0) + threadIdx.x; j < k; j += TK_THREADS) out[j] = -1;
 }
 
-size_t topk_workspace(int, int, int, int) { return 0; }
+// One block per query row (rows of at most TK_MAXN pools).
+__global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
+                                                              const int32_t* __restrict__ q_pos, int P, int k,
+                                                              int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
+  __shared__ TkShared sh;
+  const int q = blockIdx.x;
+  int n_c, r, tau, b;
+  tk_geometry(q_pos[q], P, k, ld, n_c, r, tau, b);
+  const float* row = scores + int64_t(q) * ld;
+  int32_t* out = sel + int64_t(q) * k;
+  if (b >= n_c) {
+    for (int p = threadIdx.x; p < n_c; p += TK_THREADS) out[p] = p;
+  } else if (b > 0) {
+    tk_load_keys(sh, row, n_c);
+    __syncthreads();
+    tk_select(sh, n_c, b, [&](int at, int i) __attribute__((always_inline)) { out[at] = i; });
+  }
+  tk_finish(out, n_sel, q, k, max(b, 0), r, tau);
+}
+
+// Step 1 of a long row: chunk c of row q keeps min(b, chunk length) candidates (key, pool id), ascending.
+__global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                const int32_t* __restrict__ q_pos, int P, int k,
+                                                                int n_chunks, uint32_t* __restrict__ cand_key,
+                                                                int32_t* __restrict__ cand_idx) {
+  __shared__ TkShared sh;
+  const int q = blockIdx.x / n_chunks;
+  const int c = blockIdx.x - q * n_chunks;
+  int n_c, r, tau, b;
+  tk_geometry(q_pos[q], P, k, ld, n_c, r, tau, b);
+  const int base = c * TK_MAXN;
+  const int len = min(TK_MAXN, n_c - base);
+  if (len <= 0 || b <= 0) return;
+  const float* row = scores + int64_t(q) * ld + base;
+  const int64_t cb = (int64_t(q) * n_chunks + c) * k;
+  tk_load_keys(sh, row, len);
+  __syncthreads();
+  if (b >= len) {
+    for (int i = threadIdx.x; i < len; i += TK_THREADS) {
+      cand_key[cb + i] = sh.keys[tk_slot(i)];
+      cand_idx[cb + i] = base + i;
+    }
+  } else {
+    tk_select(sh, len, b, [&](int at, int i) __attribute__((always_inline)) {
+      cand_key[cb + at] = sh.keys[tk_slot(i)];
+      cand_idx[cb + at] = base + i;
+    });
+  }
+}
+
+// Step 2 of a long row: the final b among the chunks' candidates, taken in chunk order (ascending ids).
+__global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(const uint32_t* __restrict__ cand_key,
+                                                                const int32_t* __restrict__ cand_idx, int64_t ld,
+                                                                const int32_t* __restrict__ q_pos, int P, int k,
+                                                                int n_chunks, int32_t* __restrict__ sel,
+                                                                int32_t* __restrict__ n_sel) {
+  __shared__ TkShared sh;
+  __shared__ int cstart[TK_MAXCHUNKS + 1];
+  const int q = blockIdx.x;
+  int n_c, r, tau, b;
+  tk_geometry(q_pos[q], P, k, ld, n_c, r, tau, b);
+  int32_t* out = sel + int64_t(q) * k;
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      cstart[c] = acc;
+      const int len = max(0, min(TK_MAXN, n_c - c * TK_MAXN));
+      acc += min(max(b, 0), len);
+    }
+    cstart[n_chunks] = acc;
+  }
+  __syncthreads();
+  const int n2 = cstart[n_chunks];
+  auto cand = [&](int i) __attribute__((always_inline)) -> int64_t {  // workspace offset of candidate i
+    int c = 0;
+    while (c + 1 < n_chunks && cstart[c + 1] <= i) ++c;
+    return (int64_t(q) * n_chunks + c) * k + (i - cstart[c]);
+  };
+  if (b >= n2) {
+    for (int i = threadIdx.x; i < n2; i += TK_THREADS) out[i] = cand_idx[cand(i)];
+  } else if (b > 0) {
+    for (int i = threadIdx.x; i < n2; i += TK_THREADS) sh.keys[tk_slot(i)] = cand_key[cand(i)];
+    __syncthreads();
+    tk_select(sh, n2, b, [&](int at, int i) __attribute__((always_inline)) { out[at] = cand_idx[cand(i)]; });
+  }
+  tk_finish(out, n_sel, q, k, max(b, 0), r, tau);
+}
+
+static int tk_chunks(int P, int max_pos) {
+  const int64_t ncmax = (int64_t(max_pos) + 1) / P;
+  return int((ncmax + TK_MAXN - 1) / TK_MAXN);
+}
+
+size_t topk_workspace(int P, int k, int n_q, int max_pos) {
+  const int nch = tk_chunks(P, max_pos);
+  if (nch <= 1) return 0;
+  return size_t(n_q) * nch * k * (sizeof(uint32_t) + sizeof(int32_t));
+}
 
 kp_status launch_topk(const TopkLaunch& a, hipStream_t s) {
   if (a.n_q == 0) return KP_OK;
-  topk_kernel<<<dim3(unsigned(a.n_q)), dim3(TK_THREADS), 0, s>>>(a.scores, a.ld, a.q_pos, a.P, a.k, a.sel,
-                                                                 a.n_sel);
-  return check_launch("dsa_topk_select");
+  const int nch = tk_chunks(a.P, a.max_pos);
+  if (nch <= 1) {
+    topk_row_kernel<<<dim3(unsigned(a.n_q)), dim3(TK_THREADS), 0, s>>>(a.scores, a.ld, a.q_pos, a.P, a.k, a.sel,
+                                                                       a.n_sel);
+    return check_launch("dsa_topk_select");
+  }
+  if (nch > TK_MAXCHUNKS || int64_t(nch) * a.k > TK_MAXN) {
+    set_error("dsa_topk_select: %d pools per row with top-%d exceeds the two-step limit", (a.max_pos + 1) / a.P,
+              a.k);
+    return KP_ERR_UNSUPPORTED;
+  }
+  uint32_t* cand_key = reinterpret_cast<uint32_t*>(a.ws);
+  int32_t* cand_idx = reinterpret_cast<int32_t*>(cand_key + size_t(a.n_q) * nch * a.k);
+  topk_chunk_kernel<<<dim3(unsigned(int64_t(a.n_q) * nch)), dim3(TK_THREADS), 0, s>>>(
+      a.scores, a.ld, a.q_pos, a.P, a.k, nch, cand_key, cand_idx);
+  kp_status st = check_launch("dsa_topk_select (chunks)");
+  if (st != KP_OK) return st;
+  topk_merge_kernel<<<dim3(unsigned(a.n_q)), dim3(TK_THREADS), 0, s>>>(cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k,
+                                                                       nch, a.sel, a.n_sel);
+  return check_launch("dsa_topk_select (merge)");
 }
 
 }  // namespace kp

@@ -119,6 +119,10 @@ SMALL = {
     "small_prefill": lambda: ks.scaled(ks.workloads()["prefill64k"], name="small_prefill", ctx=[3000],
                                        new_from=[2500], q_seq=np.zeros(500, np.int32),
                                        q_pos=np.arange(2500, 3000, dtype=np.int32), k=256),
+    # rows longer than one LDS-resident top-k block (32768 pools) next to a short row: the two-step selection
+    "two_step_mixed": lambda: _small_decode("two_step_mixed", ctx=(140001, 3001, 131076)),
+    # every score 0: selection is decided by the lower-index tie-break alone, at full top-k
+    "all_ties": lambda: ks.scaled(_small_decode("all_ties", ctx=(20000, 9001, 70003)), w_scale=0.0),
 }
 
 
@@ -137,7 +141,7 @@ def test_group_hint_violated_is_still_exact():
     wl = _small_decode("mixed_groups", ctx=(100, 2000, 2001, 333, 4096, 70, 9000, 12))
     _say(f"[case mixed_groups] n_q={wl.n_q}")
     a = DeviceRun(wl, group=1).run()
-    b = DeviceRun(wl, group=4).run()
+    b = DeviceRun(wl, group=8).run()   # promises one sequence per 8 queries: the prefill shape
     for j in range(wl.n_q):
         n_c = (int(wl.q_pos[j]) + 1) // wl.P
         np.testing.assert_array_equal(a.scores_row(j, n_c), b.scores_row(j, n_c))
