@@ -14,6 +14,8 @@ Legs (inputs are seeded synthetic data already resident in HBM when timing start
   128k     one sequence at context 131,072 (the exact 128K point), rotating 40 cache copies.
   prefill  4096 new queries on 65,536 tokens: the indexer's TFLOP/s against the bf16 MFMA peak, and the
            whole prefill step.
+  copy     a plain 1 GiB device-to-device copy: the achievable-bandwidth reference, and the kernel of known
+           traffic against which the FETCH_SIZE / WRITE_SIZE counters are scaled.
 Rank 0 prints one JSON line.  Algorithmic bytes/flops count what the method must move or compute; the
 derivation is in the docstrings of `decode_bytes` and `prefill_flops`.
 """
@@ -149,14 +151,36 @@ class Leg:
         self.torch.cuda.empty_cache()
 
 
+STAGE_KERNELS = {"score": ["kp::score_decode_kernel<kp::bf16, 128>"],
+                 "attend": ["kp::attn_kernel<kp::bf16, 512, 4>", "kp::attn_combine_kernel<kp::bf16>"]}
+
+
+def measured_traffic(stage: str):
+    """HBM bytes per launch of a stage's kernels from the committed counter record (profiles/), scaled by the
+    copy-kernel calibration; None when any of those kernels' sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_batch64_decode.json")
+    try:
+        rec = json.load(open(path))
+        total = 0.0
+        for k in STAGE_KERNELS[stage]:
+            e = rec["kernels"][k]
+            cur = hashlib.sha256(open(os.path.join(ROOT, e["source"]), "rb").read()).hexdigest()[:16]
+            if cur != e["sha256_16"]:
+                return None
+            total += e["read_bytes"] + e["write_bytes"]
+        return int(total)
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def roofline(stage_ms: dict, stage_bytes: dict) -> dict:
     dom = max(("score", "attend"), key=lambda s: stage_ms[s])
-    kernels = {"score": "kp::score_kernel<bf16,128,1>",
-               "attend": "kp::attn_kernel<bf16,512> + kp::attn_combine_kernel<bf16>"}
     achieved = stage_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
-    return {"bound": "hbm", "stage": dom, "kernel": kernels[dom], "achieved": round(achieved, 1),
+    return {"bound": "hbm", "stage": dom, "kernel": " + ".join(STAGE_KERNELS[dom]), "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "bytes_per_launch": int(stage_bytes[dom]), "ms_per_launch": round(stage_ms[dom], 5), "traffic": None}
+            "bytes_per_launch": int(stage_bytes[dom]), "ms_per_launch": round(stage_ms[dom], 5),
+            "traffic": measured_traffic(dom)}
 
 
 # ----------------------------------------------------------------------------------------------------------
@@ -222,7 +246,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,128k,prefill")
+    ap.add_argument("--legs", default="decode,128k,prefill,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=16)
     args = ap.parse_args()
@@ -286,6 +310,26 @@ def main():
                                   "ms": round(st["score"], 4), "flops": fl, "step_ms": round(ms, 4),
                                   "stages_ms": {k: round(v, 4) for k, v in st.items()}}
         leg.free()
+    if "copy" in legs:
+        print("[bench] copy leg: 1 GiB device copy", file=sys.stderr, flush=True)
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res["copy"] = {"bytes_moved": 2 * 4 * n, "ms": round(ms, 4),
+                       "gbs": round(2 * 4 * n / (ms * 1e-3) / 1e9, 1)}
+        del src, dst
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)

@@ -6,15 +6,16 @@
 // the lower pool index (the layer's specification).
 //
 // Exact and deterministic, with no sort.  For one row of n scores and a budget b < n:
-//   1. The row is copied once into LDS as order-preserving uint32 keys (-0 folded into +0), padded one word
-//      in 32 so that each thread's contiguous segment is read without bank conflicts.
+//   1. The row is copied once into LDS as order-preserving uint32 keys (-0 folded into +0).  Each wave owns a
+//      contiguous range of it.
 //   2. Radix select: the block's min and max key fix the common high bits; the varying bits below are resolved
 //      11 at a time (at most three passes), finding the key T of the b-th largest score and how many copies of
 //      T the budget still takes (need_eq).  Histograms are integer LDS atomics, so their order does not
 //      matter.
-//   3. Compaction in index order: every thread counts its segment's keys > T and == T; two block scans give
-//      each thread its output offset and its share of the equal keys (the lowest indices first -- exactly the
-//      lower-index tie-break); the kept ids come out already ascending, which is the output format.
+//   3. Compaction in index order: every wave counts its range's keys > T and == T with ballots; one exchange of
+//      the per-wave totals gives each wave its output offset and its share of the equal keys (the lowest
+//      indices first -- exactly the lower-index tie-break); the kept ids come out already ascending, which is
+//      the output format.
 //   4. The tail pool tau (when (i+1) mod P != 0) is appended; it is larger than every complete pool id.
 // Rows of at most 32768 pools take one block.  Longer rows (up to 16 x 32768) take two steps: every 32768-pool
 // chunk keeps its own top-b candidates (ascending), then one block selects the final b among the candidates.
@@ -29,37 +30,19 @@ constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int TK_MAXN = 32768;          // keys held in LDS by one block
 constexpr int TK_MAXCHUNKS = 16;        // chunks of a two-step row
 
-__device__ __forceinline__ int tk_slot(int i) { return i + (i >> 5); }
-
 struct TkShared {
-  uint32_t keys[TK_MAXN + TK_MAXN / 32];
+  alignas(16) uint32_t keys[TK_MAXN];
   uint32_t hist[2048];
-  int wsum[TK_WAVES];
-  uint32_t wmin[TK_WAVES], wmax[TK_WAVES];
+  uint32_t wa[TK_WAVES], wb[TK_WAVES];
   uint32_t digit, remaining;
 };
 
-// Exclusive prefix sum of `v` over the block (thread order); `total` receives the block sum.
-__device__ __forceinline__ int tk_block_scan(int v, int* wsum, int& total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int u = __shfl_up(inc, off);
-    if (lane >= off) inc += u;
-  }
-  if (lane == 63) wsum[wv] = inc;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < TK_WAVES; ++w) {
-    const int c = wsum[w];
-    before += (w < wv) ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  total = tot;
-  return before + inc - v;
+// Each wave owns a contiguous range of the row: [wave_lo, wave_hi), a multiple of 256 keys long.
+__device__ __forceinline__ void tk_wave_range(int n, int& lo, int& hi) {
+  const int per = ((n + TK_WAVES * 256 - 1) / (TK_WAVES * 256)) * 256;
+  const int w = threadIdx.x >> 6;
+  lo = min(w * per, n);
+  hi = min(lo + per, n);
 }
 
 // Selects the `budget` largest of keys[0..n) (0 < budget < n) and calls emit(out_pos, i) for each kept i,
@@ -68,18 +51,29 @@ __device__ __forceinline__ int tk_block_scan(int v, int* wsum, int& total) {
 // The radix passes only cover the bits in which the row's keys differ: a first pass takes the block min and
 // max, their common high bits are fixed, and the varying bits below are resolved 11 at a time (at most three
 // passes).  Digits of varying bits are spread, so plain LDS atomics seldom collide.  A row whose keys are all
-// equal needs no pass at all.
+// equal needs no pass at all.  Order-free passes read 16 bytes per lane from the wave's contiguous range; the
+// compaction walks that range 64 keys per step with ballots, so only the per-wave totals cross waves.
 template <class Emit>
 __device__ void tk_select(TkShared& sh, int n, int budget, Emit emit) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int E = (n + TK_THREADS - 1) / TK_THREADS;
-  const int i0 = min(tid * E, n), i1 = min(i0 + E, n);
+  int lo_i, hi_i;
+  tk_wave_range(n, lo_i, hi_i);
+  const uint4* k4 = reinterpret_cast<const uint4*>(sh.keys);
 
+  // min / max (keys past n are skipped by index)
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = sh.keys[tk_slot(i)];
-    mn = min(mn, key);
-    mx = max(mx, key);
+  for (int base = lo_i; base < hi_i; base += 256) {
+    const int i = base + 4 * lane;
+    if (i < hi_i) {
+      const uint4 v = k4[i >> 2];
+      const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i + j < hi_i) {
+          mn = min(mn, e[j]);
+          mx = max(mx, e[j]);
+        }
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -87,15 +81,16 @@ __device__ void tk_select(TkShared& sh, int n, int budget, Emit emit) {
     mx = max(mx, uint32_t(__shfl_xor(int(mx), off)));
   }
   if (lane == 0) {
-    sh.wmin[wv] = mn;
-    sh.wmax[wv] = mx;
+    sh.wa[wv] = mn;
+    sh.wb[wv] = mx;
   }
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < TK_WAVES; ++w) {
-    mn = min(mn, sh.wmin[w]);
-    mx = max(mx, sh.wmax[w]);
+    mn = min(mn, sh.wa[w]);
+    mx = max(mx, sh.wb[w]);
   }
+  __syncthreads();
   // bits [0, lo) vary; bits at and above lo are common to every key and fixed in `prefix`
   int lo = (mn == mx) ? 0 : 32 - __clz(int(mn ^ mx));
   uint32_t mask = lo == 32 ? 0u : ~((1u << lo) - 1u);
@@ -107,9 +102,15 @@ __device__ void tk_select(TkShared& sh, int n, int budget, Emit emit) {
     const uint32_t dmask = (1u << width) - 1u;
     for (int j = tid; j < 2048; j += TK_THREADS) sh.hist[j] = 0;
     __syncthreads();
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t key = sh.keys[tk_slot(i)];
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+    for (int base = lo_i; base < hi_i; base += 256) {
+      const int i = base + 4 * lane;
+      if (i < hi_i) {
+        const uint4 v = k4[i >> 2];
+        const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (i + j < hi_i && (e[j] & mask) == prefix) atomicAdd(&sh.hist[(e[j] >> shift) & dmask], 1u);
+      }
     }
     __syncthreads();
     // thread t owns digits 4t .. 4t+3; `above` counts keys with a higher digit than its range
@@ -120,9 +121,22 @@ __device__ void tk_select(TkShared& sh, int n, int budget, Emit emit) {
       c[j] = d <= int(dmask) ? sh.hist[d] : 0u;
       mine += c[j];
     }
-    int total;
-    const int before = tk_block_scan(int(mine), sh.wsum, total);
-    const uint32_t above = uint32_t(total - before) - mine;
+    // inclusive prefix over threads (thread order = digit order), then count from the top
+    uint32_t inc = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t u = uint32_t(__shfl_up(int(inc), off));
+      if (lane >= off) inc += u;
+    }
+    if (lane == 63) sh.wa[wv] = inc;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < TK_WAVES; ++w) {
+      before += (w < wv) ? sh.wa[w] : 0u;
+      total += sh.wa[w];
+    }
+    const uint32_t above = total - (before + inc);
     if (above < remaining && remaining <= above + mine) {
       uint32_t acc = above;
       for (int j = 3; j >= 0; --j) {
@@ -139,27 +153,48 @@ __device__ void tk_select(TkShared& sh, int n, int budget, Emit emit) {
     mask |= dmask << shift;
     remaining = sh.remaining;
     lo = shift;
+    __syncthreads();
   }
   const uint32_t T = prefix;
-  const int need_eq = int(remaining);
-  int gt = 0, eq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = sh.keys[tk_slot(i)];
-    gt += key > T;
-    eq += key == T;
+  const uint32_t need_eq = remaining;
+
+  // compaction: per-wave counts, one exchange, then each wave emits its range in index order
+  uint32_t gt = 0, eq = 0;
+  for (int base = lo_i; base < hi_i; base += 64) {
+    const int i = base + lane;
+    const uint32_t key = i < hi_i ? sh.keys[i] : 0u;
+    gt += uint32_t(__popcll(__ballot(i < hi_i && key > T)));
+    eq += uint32_t(__popcll(__ballot(i < hi_i && key == T)));
   }
-  int tot;
-  const int eq_before = tk_block_scan(eq, sh.wsum, tot);
-  const int take_eq = min(max(need_eq - eq_before, 0), eq);
-  int at = tk_block_scan(gt + take_eq, sh.wsum, tot);
-  int eq_left = take_eq;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = sh.keys[tk_slot(i)];
-    if (key > T || (key == T && eq_left > 0)) {
-      if (key == T) --eq_left;
-      emit(at++, i);
+  if (lane == 0) {
+    sh.wa[wv] = gt;
+    sh.wb[wv] = eq;
+  }
+  __syncthreads();
+  uint32_t gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int w = 0; w < TK_WAVES; ++w)
+    if (w < wv) {
+      gt_before += sh.wa[w];
+      eq_before += sh.wb[w];
     }
+  // kept before this wave: all greater keys plus the first need_eq equal keys in index order
+  uint32_t at = gt_before + min(eq_before, need_eq);
+  uint32_t eq_seen = eq_before;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  for (int base = lo_i; base < hi_i; base += 64) {
+    const int i = base + lane;
+    const uint32_t key = i < hi_i ? sh.keys[i] : 0u;
+    const bool is_eq = i < hi_i && key == T;
+    const uint64_t eqm = __ballot(is_eq);
+    const uint32_t eq_rank = eq_seen + uint32_t(__popcll(eqm & below));
+    const bool take = (i < hi_i && key > T) || (is_eq && eq_rank < need_eq);
+    const uint64_t tm = __ballot(take);
+    if (take) emit(int(at + uint32_t(__popcll(tm & below))), i);
+    at += uint32_t(__popcll(tm));
+    eq_seen += uint32_t(__popcll(eqm));
   }
+  __syncthreads();
 }
 
 // Copies n fp32 scores (16-byte aligned source) into LDS as keys.  Every thread issues all of its loads before
@@ -169,6 +204,7 @@ __device__ __forceinline__ void tk_load_keys(TkShared& sh, const float* __restri
   constexpr int U = 16;
   const int n4 = n >> 2;
   const float4* s4 = reinterpret_cast<const float4*>(src);
+  uint4* k4 = reinterpret_cast<uint4*>(sh.keys);
   for (int base = 0; base < n4; base += U * TK_THREADS) {
     float4 v[U];
 #pragma unroll
@@ -179,15 +215,11 @@ __device__ __forceinline__ void tk_load_keys(TkShared& sh, const float* __restri
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i4 = base + u * TK_THREADS + int(threadIdx.x);
-      if (i4 < n4) {
-        sh.keys[tk_slot(4 * i4 + 0)] = score_key(v[u].x);
-        sh.keys[tk_slot(4 * i4 + 1)] = score_key(v[u].y);
-        sh.keys[tk_slot(4 * i4 + 2)] = score_key(v[u].z);
-        sh.keys[tk_slot(4 * i4 + 3)] = score_key(v[u].w);
-      }
+      if (i4 < n4)
+        k4[i4] = make_uint4(score_key(v[u].x), score_key(v[u].y), score_key(v[u].z), score_key(v[u].w));
     }
   }
-  for (int i = 4 * n4 + int(threadIdx.x); i < n; i += TK_THREADS) sh.keys[tk_slot(i)] = score_key(src[i]);
+  for (int i = 4 * n4 + int(threadIdx.x); i < n; i += TK_THREADS) sh.keys[i] = score_key(src[i]);
 }
 
 __device__ __forceinline__ void tk_geometry(int pos, int P, int k, int64_t ld, int& n_c, int& r, int& tau, int& b) {
@@ -245,12 +277,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(const float* __r
   __syncthreads();
   if (b >= len) {
     for (int i = threadIdx.x; i < len; i += TK_THREADS) {
-      cand_key[cb + i] = sh.keys[tk_slot(i)];
+      cand_key[cb + i] = sh.keys[i];
       cand_idx[cb + i] = base + i;
     }
   } else {
     tk_select(sh, len, b, [&](int at, int i) __attribute__((always_inline)) {
-      cand_key[cb + at] = sh.keys[tk_slot(i)];
+      cand_key[cb + at] = sh.keys[i];
       cand_idx[cb + at] = base + i;
     });
   }
@@ -287,7 +319,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(const uint32_t* 
   if (b >= n2) {
     for (int i = threadIdx.x; i < n2; i += TK_THREADS) out[i] = cand_idx[cand(i)];
   } else if (b > 0) {
-    for (int i = threadIdx.x; i < n2; i += TK_THREADS) sh.keys[tk_slot(i)] = cand_key[cand(i)];
+    for (int i = threadIdx.x; i < n2; i += TK_THREADS) sh.keys[i] = cand_key[cand(i)];
     __syncthreads();
     tk_select(sh, n2, b, [&](int at, int i) __attribute__((always_inline)) { out[at] = cand_idx[cand(i)]; });
   }
