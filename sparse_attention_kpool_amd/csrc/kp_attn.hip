@@ -38,7 +38,7 @@ namespace kp {
 
 constexpr int AT_NT = 32;         // token slots per block
 constexpr int AT_THREADS = 512;   // 4 S waves + 4 O waves
-constexpr int AT_MAXPOOL = 2048;  // pools of one split held in LDS
+constexpr int AT_MAXSLOT = 8192;  // token slots of one split held in the LDS slot table
 constexpr float LN2 = 0.69314718055994530942f;
 // log2 headroom before the running max is raised: weights up to 2^64 stay far inside the fp32 / bf16 exponent
 // range, so the accumulators are rescaled only when a later block's max beats the running one by 2^64.
@@ -93,9 +93,9 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
   using F = typename E::frag;
   __shared__ __align__(16) T crm[3][AT_NT * S::RS];
   __shared__ __align__(16) T ps[2][16 * HT * S::PS];
-  __shared__ int32_t pool_row[AT_MAXPOOL];
-  __shared__ uint8_t pool_ntok[AT_MAXPOOL];
+  __shared__ int32_t slot_tab[AT_MAXSLOT];
   __shared__ float alpha_s[2][64];
+  __shared__ uint32_t resc_s[2];
   __shared__ float m_s[64];
   __shared__ float l_s[64];
   __shared__ uint32_t vmask_s[3];
@@ -126,15 +126,15 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     }
     return;
   }
-  const int nblk = (s_end - s_begin + AT_NT - 1) / AT_NT;
-  const int pool0 = s_begin >> log2P;
-  const int npool = (s_end - s_begin) >> log2P;
+  const int nsl = s_end - s_begin;  // slots of this split (a whole number of pools)
+  const int nblk = (nsl + AT_NT - 1) / AT_NT;
 
-  // cache-row base and visible token count of every pool of this split
+  // Slot table: cache row of every slot of the split, -1 for a slot past the query (the cut tail pool).  One
+  // block-table lookup per pool, done once; in the loop a slot's row is then a single LDS read.
   {
-    const int32_t* qsel = sel + int64_t(qi) * k + pool0;
+    const int32_t* qsel = sel + int64_t(qi) * k + (s_begin >> log2P);
     const int pt_mask = (1 << log2_pt) - 1;
-    for (int j = tid; j < npool; j += AT_THREADS) {
+    for (int j = tid; j < (nsl >> log2P); j += AT_THREADS) {
       const int p = qsel[j];
       int nt = 0, row = 0;
       if (p >= 0) {
@@ -142,8 +142,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
         nt = min(P, pos - first + 1);
         if (nt > 0) row = bt[int64_t(seq) * bt_stride + (first >> log2_pt)] * (pt_mask + 1) + (first & pt_mask);
       }
-      pool_row[j] = row;
-      pool_ntok[j] = uint8_t(max(nt, 0));
+      for (int w = 0; w < P; ++w) slot_tab[(j << log2P) + w] = w < nt ? row + w : -1;
     }
   }
 
@@ -170,27 +169,38 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     if constexpr (sizeof(T) == 2) return __builtin_bit_cast(bf16x8, bank[s]);
     else return bank[s >> 2][s & 3];
   };
-  float m_run = -INFINITY, l_run = 0.f;  // S waves: running max / sum of the lane's head
+  // S waves: running max of the lane's head (the same in all four lanes of a head) and the lane's own part of
+  // the running sum (its 8 slots of each block; the four parts are added once at the end)
+  float m_run = -INFINITY, l_run = 0.f;
 
-  __syncthreads();  // pool tables ready
+  __syncthreads();  // slot table ready
 
-  // cache row of slot t (0..31) of block b, or -1 when past the split or past the query
-  auto slot_row = [&](int b, int t) __attribute__((always_inline)) -> int {
+  // table entry of slot t (0..31) of block b: its cache row, or -1 (past the split or past the query)
+  auto slot_entry = [&](int b, int t) __attribute__((always_inline)) -> int {
     const int rel = b * AT_NT + t;
-    if (s_begin + rel >= s_end) return -1;
-    const int pi = rel >> log2P, within = rel & (P - 1);
-    return within < int(pool_ntok[pi]) ? pool_row[pi] + within : -1;
+    const int e = slot_tab[min(rel, AT_MAXSLOT - 1)];
+    return rel < nsl ? e : -1;
   };
 
   // Loads are unconditional (an invalid slot reads row 0 of the cache and is zeroed when stored): branch-free
-  // loads let the compiler wait for exactly the block it needs instead of draining every load in flight.
+  // loads let the compiler wait for exactly the block it needs instead of draining every load in flight.  With
+  // one whole value row per wave instruction the row is wave-uniform and its address is computed on the
+  // scalar unit.
   auto load_block = [&](int b, u32x4(&R)[S::CHT], bool(&vrow)[S::CHT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < S::CHT; ++i) {
-      const int c = min(tid + AT_THREADS * i, S::CHUNKS - 1);
-      const int row = slot_row(b, c / S::CPR);
-      R[i] = *reinterpret_cast<const u32x4*>(latent + int64_t(max(row, 0)) * L + (c % S::CPR) * S::EPC);
-      vrow[i] = row >= 0;
+      if constexpr (S::CPR == 64 && S::CHUNKS % AT_THREADS == 0) {
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        const int e = __builtin_amdgcn_readfirstlane(slot_entry(b, wv + (AT_THREADS / 64) * i));
+        const T* rp = latent + int64_t(max(e, 0)) * L;
+        R[i] = *reinterpret_cast<const u32x4*>(rp + lane * S::EPC);
+        vrow[i] = e >= 0;
+      } else {
+        const int c = min(tid + AT_THREADS * i, S::CHUNKS - 1);
+        const int e = slot_entry(b, c / S::CPR);
+        R[i] = *reinterpret_cast<const u32x4*>(latent + int64_t(max(e, 0)) * L + (c % S::CPR) * S::EPC);
+        vrow[i] = e >= 0;
+      }
     }
   };
 
@@ -208,32 +218,37 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     // lane holds head 16*wl + l16, slots 16t + 4g + i
     const uint32_t vm = vmask_s[j % 3];
     float x[2][4];
-    float bmax = -INFINITY;
+    float lmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int slot = 16 * t + 4 * g + i;
         x[t][i] = ((vm >> slot) & 1u) ? (sa[t][0][i] + sa[t][1][i]) * scale_log2 : -INFINITY;
-        bmax = fmaxf(bmax, x[t][i]);
+        lmax = fmaxf(lmax, x[t][i]);
       }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float m_new = (bmax > m_run + LAZY_MAX) ? bmax : m_run;
-    const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
+    // The running max is raised only for a head whose block max beats it by more than LAZY_MAX; no lane over
+    // that bound means no head is raised, so the cross-lane max is needed only on the (rare) raising blocks.
+    float alpha = 1.f;
+    const bool raise = __ballot(lmax > m_run + LAZY_MAX) != 0;
+    if (raise) {
+      float bmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      const float m_new = (bmax > m_run + LAZY_MAX) ? bmax : m_run;
+      alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      if (g == 0) alpha_s[j & 1][16 * wl + l16] = alpha;
+    }
     float rsum = 0.f;
     float pv[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pv[t][i] = (x[t][i] == -INFINITY) ? 0.f : fast_exp2(x[t][i] - m_new);
+        pv[t][i] = (x[t][i] == -INFINITY) ? 0.f : fast_exp2(x[t][i] - m_run);
         rsum += pv[t][i];
       }
-    rsum += __shfl_xor(rsum, 16);
-    rsum += __shfl_xor(rsum, 32);
     l_run = l_run * alpha + rsum;
-    m_run = m_new;
     T* prow = ps[j & 1] + (16 * wl + l16) * S::PS;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -244,19 +259,22 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
         *reinterpret_cast<float4*>(prow + 16 * t + 4 * g) = make_float4(pv[t][0], pv[t][1], pv[t][2], pv[t][3]);
       }
     }
-    if (g == 0) alpha_s[j & 1][16 * wl + l16] = alpha;
+    if (lane == 0) reinterpret_cast<uint8_t*>(&resc_s[j & 1])[wl] = raise ? 1 : 0;
   };
 
   auto o_phase = [&](int j) __attribute__((always_inline)) {
     const T* blk = crm[j % 3];
     const T* pb = ps[j & 1];
     // rescale only the head tiles whose running max moved
+    const uint32_t rf = resc_s[j & 1];
+    if (rf) {
 #pragma unroll
-    for (int nt = 0; nt < HT; ++nt) {
-      const float a = alpha_s[j & 1][16 * nt + l16];
-      if (__ballot(a != 1.f)) {
+      for (int nt = 0; nt < HT; ++nt) {
+        if ((rf >> (8 * nt)) & 0xffu) {
+          const float a = alpha_s[j & 1][16 * nt + l16];
 #pragma unroll
-        for (int mt = 0; mt < S::MT; ++mt) bank[mt * HT + nt] *= a;
+          for (int mt = 0; mt < S::MT; ++mt) bank[mt * HT + nt] *= a;
+        }
       }
     }
     // O^T[channels of this wave][heads] += C^T . P^T; k-slot (group g, step s, element e) = token 8g + s*KPL + e
@@ -276,25 +294,26 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
 
   // iteration j: store block j into the ring, start loading block j+2, then S(j) on S waves and O(j-1) on
   // O waves.  Buffer j % 3 was last read by O(j-3) in iteration j-2, two barriers ago.
+  // Stores and loads are unconditional, also for blocks past the end (all slots invalid: zeros are stored,
+  // row 0 is read): with no load or store under a branch the compiler's wait counts stay exact, and a wave
+  // waits only for the block it stores, never for the one loaded after it.
   auto iter = [&](int j, u32x4(&R)[S::CHT], bool(&vrow)[S::CHT]) __attribute__((always_inline)) {
-    if (j < nblk) {
-      T* blk = crm[j % 3];
+    T* blk = crm[j % 3];
 #pragma unroll
-      for (int i = 0; i < S::CHT; ++i) {
-        const int c = tid + AT_THREADS * i;
-        if (c < S::CHUNKS)
-          *reinterpret_cast<u32x4*>(blk + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) =
-              vrow[i] ? R[i] : u32x4{0, 0, 0, 0};
-      }
-      if (wave == 0) {
-        const uint32_t vm = uint32_t(__ballot(lane < AT_NT && slot_row(j, lane) >= 0));
-        if (lane == 0) vmask_s[j % 3] = vm;
-      }
-      if (j + 2 < nblk) load_block(j + 2, R, vrow);
+    for (int i = 0; i < S::CHT; ++i) {
+      const int c = tid + AT_THREADS * i;
+      if (S::CHUNKS % AT_THREADS == 0 || c < S::CHUNKS)
+        *reinterpret_cast<u32x4*>(blk + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) =
+            vrow[i] ? R[i] : u32x4{0, 0, 0, 0};
     }
+    if (wave == 0) {
+      const uint32_t vm = uint32_t(__ballot(lane < AT_NT && slot_entry(j, lane & (AT_NT - 1)) >= 0));
+      if (lane == 0) vmask_s[j % 3] = vm;
+    }
+    load_block(j + 2, R, vrow);
     __syncthreads();
     if (o_wave) {
-      if (j >= 1) o_phase(j - 1);
+      if (j >= 1 && j - 1 < nblk) o_phase(j - 1);
     } else if (s_active && j < nblk) {
       s_phase(j);
     }
@@ -303,15 +322,19 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
   u32x4 R0[S::CHT], R1[S::CHT];
   bool V0[S::CHT], V1[S::CHT];
   load_block(0, R0, V0);
-  if (nblk > 1) load_block(1, R1, V1);
+  load_block(1, R1, V1);
   for (int j = 0; j <= nblk; j += 2) {
     iter(j, R0, V0);
-    if (j + 1 <= nblk) iter(j + 1, R1, V1);
+    iter(j + 1, R1, V1);
   }
 
-  if (s_active && g == 0) {
-    m_s[16 * wl + l16] = m_run;
-    l_s[16 * wl + l16] = l_run;
+  if (s_active) {
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (g == 0) {
+      m_s[16 * wl + l16] = m_run;
+      l_s[16 * wl + l16] = l_run;
+    }
   }
   __syncthreads();
   if (!o_wave) return;
@@ -382,12 +405,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 }
 
 int attn_splits(int P, int k, int n_q) {
-  // about one block per CU (256), at most 32 splits, and few enough pools per split for the LDS pool table
+  // about one block per CU (256), at most 32 splits, and few enough slots per split for the LDS slot table
   const int64_t blocks = (int64_t(k) * P + AT_NT - 1) / AT_NT;
   int64_t want = (256 + int64_t(n_q) - 1) / (n_q > 0 ? n_q : 1);
   if (want > blocks) want = blocks;
   if (want > 32) want = 32;
-  const int64_t min_splits = (blocks + 64 * int64_t(P) - 1) / (64 * int64_t(P));
+  const int64_t min_splits = (blocks * AT_NT + AT_MAXSLOT - 1) / AT_MAXSLOT;
   if (want < min_splits) want = min_splits;
   return want < 1 ? 1 : int(want);
 }
