@@ -373,35 +373,55 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
   }
 }
 
-// Merge of the split partials of one (query, head): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s per (query, head), with
+// M the max of m_s over non-empty splits, summed in split order.  128 threads per block, 4 channels (one float4)
+// per thread, V / 4 threads per head; the partials of four splits are loaded at once, unconditionally (an empty
+// split's O was never written: its weight is 0 and a select drops it).
+constexpr int CB_THREADS = 128;
+
 template <class T>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml, int n_split, int H,
-                                                           int V, T* __restrict__ out, float* __restrict__ lse) {
-  const int qh = blockIdx.x;
-  const int qi = qh / H, h = qh - qi * H;
+__global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                                  const float* __restrict__ part_ml, int n_split,
+                                                                  int H, int V, T* __restrict__ out,
+                                                                  float* __restrict__ lse) {
+  const int tph = V / 4;                    // threads per head
+  const int hpb = CB_THREADS / tph;         // heads per block
+  const int bpq = (H + hpb - 1) / hpb;      // blocks per query
+  const int qi = blockIdx.x / bpq;
+  const int h = (blockIdx.x - qi * bpq) * hpb + int(threadIdx.x) / tph;
+  if (h >= H) return;
+  const int c = (int(threadIdx.x) % tph) * 4;
+  const float* ml = part_ml + (int64_t(qi) * n_split * H + h) * 2;   // split s at ml + s * 2H
+  const float* po = part_o + (int64_t(qi) * n_split * H + h) * V + c; // split s at po + s * H * V
+  const int64_t mls = int64_t(H) * 2, pos_ = int64_t(H) * V;
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) {
-    const int64_t b = (int64_t(qi * n_split + s) * H + h) * 2;
-    if (part_ml[b + 1] > 0.f) M = fmaxf(M, part_ml[b]);
-  }
+  for (int s = 0; s < n_split; ++s)
+    if (ml[s * mls + 1] > 0.f) M = fmaxf(M, ml[s * mls]);
   float wsum = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const int64_t b = (int64_t(qi * n_split + s) * H + h) * 2;
-    const float l = part_ml[b + 1];
-    if (l > 0.f) wsum += l * exp2f(part_ml[b] - M);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto add = [&](float m, float l, f32x4 o) __attribute__((always_inline)) {
+    const float w = l > 0.f ? exp2f(m - M) : 0.f;
+    wsum += l > 0.f ? l * w : 0.f;
+    acc += l > 0.f ? w * o : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  int s = 0;
+  for (; s + 4 <= n_split; s += 4) {
+    f32x4 o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = *reinterpret_cast<const f32x4*>(po + (s + u) * pos_);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) add(ml[(s + u) * mls], ml[(s + u) * mls + 1], o[u]);
   }
+  for (; s < n_split; ++s) add(ml[s * mls], ml[s * mls + 1], *reinterpret_cast<const f32x4*>(po + s * pos_));
   const float inv = 1.f / wsum;
-  for (int c = threadIdx.x; c < V; c += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const int64_t b = int64_t(qi * n_split + s) * H + h;
-      const float l = part_ml[b * 2 + 1];
-      if (l > 0.f) acc += part_o[b * V + c] * exp2f(part_ml[b * 2] - M);
-    }
-    out[int64_t(qh) * V + c] = Elem<T>::from_f32(acc * inv);
+  T* op = out + (int64_t(qi) * H + h) * V + c;
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                               pack_bf16x2(acc[2] * inv, acc[3] * inv));
+  } else {
+    *reinterpret_cast<float4*>(op) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   }
-  if (lse && threadIdx.x == 0) lse[qh] = (M + log2f(wsum)) * LN2;
+  if (lse && c == 0) lse[int64_t(qi) * H + h] = (M + log2f(wsum)) * LN2;
 }
 
 int attn_splits(int P, int k, int n_q) {
@@ -438,8 +458,10 @@ static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
       ilog2(a.P), a.k, a.H, scale_log2, ns, bps, (T*)a.out, a.lse, part_o, part_ml);
   kp_status st = check_launch("sparse_mla_attn");
   if (st != KP_OK || ns == 1) return st;
-  attn_combine_kernel<T><<<dim3(unsigned(int64_t(a.n_q) * a.H)), dim3(256), 0, s>>>(part_o, part_ml, ns, a.H, a.V,
-                                                                                     (T*)a.out, a.lse);
+  const int hpb = CB_THREADS / (a.V / 4);
+  const int64_t cblocks = int64_t(a.n_q) * ((a.H + hpb - 1) / hpb);
+  attn_combine_kernel<T><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H, a.V,
+                                                                                (T*)a.out, a.lse);
   return check_launch("sparse_mla_attn (split merge)");
 }
 

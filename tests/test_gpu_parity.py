@@ -166,6 +166,44 @@ def test_paged_equals_contiguous_and_deterministic():
     _free()
 
 
+def test_workspace_reuse_across_query_counts():
+    """One attention workspace serves calls with different query counts (so different split counts) in any
+    order: results repeat bit for bit, and match a repeated batch within the attention tolerance."""
+    import sparse_attention_kpool_amd as K
+    wl = _small_decode("ws_reuse")
+    _say("[case ws_reuse]")
+    run = DeviceRun(wl).run()
+    n5 = wl.n_q
+    rep = 20
+    idx = torch.arange(n5, device="cuda").repeat(rep)
+    seq, pos = run.queries.seq[idx].contiguous(), run.queries.pos[idx].contiguous()
+    q100 = K.Queries(seq=seq, pos=pos, max_pos=run.queries.max_pos, group=1)
+    q5 = K.Queries(seq=run.queries.seq, pos=run.queries.pos, max_pos=run.queries.max_pos, group=1)
+    sel5, nsel5 = run.layer.sel[:n5], run.layer.n_sel[:n5]
+    sel100, nsel100 = sel5[idx].contiguous(), nsel5[idx].contiguous()
+    qq100 = run.q[idx].contiguous()
+    need = max(K.sparse_mla_workspace_size(run.dims, q5), K.sparse_mla_workspace_size(run.dims, q100))
+    ws = torch.empty((need + 15) // 16 * 4, dtype=torch.float32, device="cuda")
+    out100 = torch.empty((n5 * rep, wl.H, wl.V), dtype=run.out.dtype, device="cuda")
+    out5 = torch.empty_like(run.out)
+
+    def call(queries, q, sel, nsel, out):
+        K.sparse_mla_attn(run.dims, run.cache, queries, q, sel, nsel, out, workspace=ws)
+        torch.cuda.synchronize()
+        return out.clone()
+
+    a1 = call(q100, qq100, sel100, nsel100, out100)
+    b1 = call(q5, run.q, sel5, nsel5, out5)
+    a2 = call(q100, qq100, sel100, nsel100, out100)
+    b2 = call(q5, run.q, sel5, nsel5, out5)
+    assert torch.equal(a1, a2) and torch.equal(b1, b2), "repeated calls differ"
+    assert torch.equal(b1, run.out), "the layer step with the same queries gave another result"
+    ref = b1.float().repeat(rep, 1, 1)
+    assert (a1.float() - ref).abs().max().item() <= attn_tolerance(wl.dtype)[0]
+    del run
+    _free()
+
+
 def test_empty_calls():
     """n_q = 0 and n_pools = 0 are valid and write nothing."""
     import sparse_attention_kpool_amd as K
