@@ -141,7 +141,8 @@ kp_status dsa_indexer_score(const kp_dims* dims, const kp_cache* cache, const kp
  *   sel: device int32 [n_q, k], the kept pool ids ascending, padded with -1; n_sel: device int32 [n_q].
  *   scores: as written by dsa_indexer_score (only columns < n_c are read); ld_scores as there.
  *   workspace: device, at least dsa_topk_workspace_size bytes (NULL when that is 0).  Rows of more than 32768
- *     pools are selected in two steps (per-32768-pool-chunk candidates, then a final pass) through it.
+ *     pools, and the rows of a batch too small to fill the GPU, are selected in two steps through it
+ *     (per-chunk candidates, then a final pass); its size depends on n_q and max_pos.
  *   Limit: (max_pos + 1) / P <= 16 * 32768 pools and 16 * topk <= 32768 when two steps are needed, else
  *     KP_ERR_UNSUPPORTED (covers 1M-token contexts at P = 4, topk = 2048).
  *   Errors: KP_ERR_INVALID_ARG, KP_ERR_WORKSPACE, KP_ERR_UNSUPPORTED.

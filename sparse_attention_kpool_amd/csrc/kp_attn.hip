@@ -12,7 +12,7 @@
 // block-table lookup per pool) in LDS, so no gathered load waits on another global load.
 //
 // The 8 waves form a two-stage pipeline over 32-slot blocks, one barrier per block:
-//   load   every thread keeps 16-byte chunks of the V-wide value rows in registers two blocks ahead (a wave
+//   load   every thread keeps 16-byte chunks of the V-wide value rows in registers four blocks ahead (a wave
 //          covers one whole 1 KiB row per instruction) and writes them to a 3-deep ring of row-major LDS
 //          buffers.
 //   S      waves 0..3 (S waves), block j: wave w owns heads 16w..16w+15 and computes S^T = C . Q^T on
@@ -38,6 +38,7 @@ namespace kp {
 
 constexpr int AT_NT = 32;         // token slots per block
 constexpr int AT_THREADS = 512;   // 4 S waves + 4 O waves
+constexpr int AT_DEPTH = 4;       // blocks in flight from HBM (register-staged)
 constexpr int AT_MAXSLOT = 8192;  // token slots of one split held in the LDS slot table
 constexpr float LN2 = 0.69314718055994530942f;
 // log2 headroom before the running max is raised: weights up to 2^64 stay far inside the fp32 / bf16 exponent
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     }
   };
 
-  // iteration j: store block j into the ring, start loading block j+2, then S(j) on S waves and O(j-1) on
+  // iteration j: store block j into the ring, start loading block j+AT_DEPTH, then S(j) on S waves and O(j-1) on
   // O waves.  Buffer j % 3 was last read by O(j-3) in iteration j-2, two barriers ago.
   // Stores and loads are unconditional, also for blocks past the end (all slots invalid: zeros are stored,
   // row 0 is read): with no load or store under a branch the compiler's wait counts stay exact, and a wave
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
       const uint32_t vm = uint32_t(__ballot(lane < AT_NT && slot_entry(j, lane & (AT_NT - 1)) >= 0));
       if (lane == 0) vmask_s[j % 3] = vm;
     }
-    load_block(j + 2, R, vrow);
+    load_block(j + AT_DEPTH, R, vrow);
     __syncthreads();
     if (o_wave) {
       if (j >= 1 && j - 1 < nblk) o_phase(j - 1);
@@ -319,13 +320,13 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     }
   };
 
-  u32x4 R0[S::CHT], R1[S::CHT];
-  bool V0[S::CHT], V1[S::CHT];
-  load_block(0, R0, V0);
-  load_block(1, R1, V1);
-  for (int j = 0; j <= nblk; j += 2) {
-    iter(j, R0, V0);
-    iter(j + 1, R1, V1);
+  u32x4 R[AT_DEPTH][S::CHT];
+  bool vr[AT_DEPTH][S::CHT];
+#pragma unroll
+  for (int d = 0; d < AT_DEPTH; ++d) load_block(d, R[d], vr[d]);
+  for (int j = 0; j <= nblk; j += AT_DEPTH) {
+#pragma unroll
+    for (int d = 0; d < AT_DEPTH; ++d) iter(j + d, R[d], vr[d]);
   }
 
   if (s_active) {

@@ -72,6 +72,8 @@ __device__ __forceinline__ float score_tile(const typename Elem<T>::frag (&qa)[S
   return part + __shfl_xor(part, 32);
 }
 
+constexpr int SC_MAXCHUNK = 4096;    // pools per block
+
 // ---------------------------------------------------------------------------------------------------------------
 // decode: grid = n_q x n_chunks; a block covers `chunk_pools` pools of one query, a wave `chunk_pools / 4`
 // (at most 64 pages, so the wave's page ids fit one register per lane)
@@ -87,6 +89,7 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   using F = typename E::frag;
   constexpr int CHT = S::TCH / 64;  // chunks per lane per tile
   __shared__ __align__(16) T tiles[4][32 * S::RS];
+  __shared__ float sbuf[4][SC_MAXCHUNK / 4];  // each wave's scores, written out after its loop
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
@@ -108,9 +111,16 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   const int npg = ((w_end - 1) >> log2_ppp) - pg0 + 1;
   const int page_reg = lane < npg ? bt[int64_t(seq) * bt_stride + pg0 + lane] : 0;
   const int ppp_mask = (1 << log2_ppp) - 1;
+  // The first tile needs the page ids anyway: wait for every prologue load here, so that only tile loads are
+  // in flight in the loop and the compiler's wait counts there stay exact.
+  __builtin_amdgcn_s_waitcnt(0);
 
   T* tile = tiles[wave];
   const int ntile = (w_end - w_begin + 31) / 32;
+  // Loads and steps are unconditional (a tile past the range re-reads a valid pool) and no global store sits in
+  // the loop (stores share the load counter and would force full drains): the compiler's wait counts stay exact
+  // and a wave waits only for the tile it stores to LDS, never for the one loaded after it.
+  float* sb = sbuf[wave];
   auto load_tile = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CHT; ++i) {
@@ -128,23 +138,25 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
       const int c = i * 64 + lane;
       *reinterpret_cast<u32x4*>(tile + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
     }
-    if (t + 2 < ntile) load_tile(t + 2, R);
+    load_tile(t + 2, R);
     F kb[S::STEPS];
     const T* kp = tile + n * S::RS + g * (D / 2);
 #pragma unroll
     for (int s = 0; s < S::STEPS; ++s) kb[s] = E::frag_load(kp + s * S::KPL);
     const float sc = score_tile<T, D>(qa, kb, wv);
-    const int pool = w_begin + t * 32 + n;
-    if (g == 0 && pool < w_end) scores[int64_t(qi) * ld + pool] = sc;
+    if (g == 0) sb[t * 32 + n] = sc;  // slots past the range are never written out
   };
 
   u32x4 R0[CHT], R1[CHT];
   load_tile(0, R0);
-  if (ntile > 1) load_tile(1, R1);
+  __builtin_amdgcn_sched_barrier(0);  // keep tile 0's loads older than tile 1's, as in the loop
+  load_tile(1, R1);
   for (int t = 0; t < ntile; t += 2) {
     step(t, R0);
-    if (t + 1 < ntile) step(t + 1, R1);
+    step(t + 1, R1);
   }
+  float* srow = scores + int64_t(qi) * ld + w_begin;
+  for (int i = lane; i < w_end - w_begin; i += 64) srow[i] = sb[i];
 }
 
 // ---------------------------------------------------------------------------------------------------------------
@@ -153,6 +165,7 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
 constexpr int SC_QW = 2;              // queries per wave
 constexpr int SC_QG = 4 * SC_QW;      // queries per block
 constexpr int SC_MAXPG = 1024;        // page ids of one block's pool range held in LDS
+constexpr int SC_PMAXCHUNK = 1024;    // pools per block (its scores are buffered in LDS)
 
 template <class T, int D>
 __global__ __launch_bounds__(256) void score_prefill_kernel(
@@ -166,6 +179,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
   constexpr int CHT = (S::TCH + 255) / 256;  // chunks per thread per tile
   __shared__ __align__(16) T tile[32 * S::RS];
   __shared__ int page_s[SC_MAXPG];
+  __shared__ float psb[SC_QG][SC_PMAXCHUNK];  // the block's scores, written out after each sequence pass
   __shared__ int seq_s[SC_QG];
   __shared__ int nc_s[SC_QG];
 
@@ -230,7 +244,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
         const int c = tid + 256 * i;
         if (c < S::TCH) *reinterpret_cast<u32x4*>(tile + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
       }
-      if (t + 2 < ntile) load_tile(t + 2, R);
+      load_tile(t + 2, R);
       __syncthreads();
       F kb[S::STEPS];
       const T* kp = tile + n * S::RS + g * (D / 2);
@@ -239,18 +253,25 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
       const int pool = p_begin + t * 32 + n;
 #pragma unroll
       for (int r = 0; r < SC_QW; ++r) {
-        const int qr = wave * SC_QW + r;
-        if (!((active >> qr) & 1u)) continue;
         const float sc = score_tile<T, D>(qa[r], kb, wv[r]);
-        if (g == 0 && pool < nc_s[qr]) scores[int64_t(r0 + qr) * ld + pool] = sc;
+        if (g == 0) psb[wave * SC_QW + r][pool - p_begin] = sc;  // written out only where visible and active
       }
     };
+    // As in the decode kernel: loads and steps are unconditional, no global store sits in the tile loop, and
+    // tile 0's loads stay older than tile 1's, so the loop's wait counts are exact.
     u32x4 R0[CHT], R1[CHT];
     load_tile(0, R0);
-    if (ntile > 1) load_tile(1, R1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(1, R1);
     for (int t = 0; t < ntile; t += 2) {
       step(t, R0);
-      if (t + 1 < ntile) step(t + 1, R1);
+      step(t + 1, R1);
+    }
+    __syncthreads();
+    for (int e = tid; e < SC_QG * chunk_pools; e += 256) {
+      const int qr = e / chunk_pools, i = e - qr * chunk_pools;
+      if (((active >> qr) & 1u) && p_begin + i < min(nc_s[qr], p_end))
+        scores[int64_t(r0 + qr) * ld + p_begin + i] = psb[qr][i];
     }
   }
 }
@@ -276,12 +297,14 @@ kp_status launch_score(const ScoreLaunch& a, hipStream_t s) {
   // prefill shape when the caller promises runs of >= 8 queries of one sequence
   const bool prefill = a.group >= SC_QG;
   const int64_t n_groups = prefill ? (a.n_q + SC_QG - 1) / SC_QG : a.n_q;
-  // pools per block: a multiple of 128 sized for about 2048 blocks, at most 4096, and (decode) at most 64
-  // pages per wave or (prefill) SC_MAXPG pages per block
-  int64_t chunk = (ncmax * n_groups + 2047) / 2048;
+  // pools per block: a multiple of 128 sized for about 4096 (decode) or 2048 (prefill) blocks, at most
+  // SC_MAXCHUNK (decode) or SC_PMAXCHUNK (prefill), and (decode) at most 64 pages per wave or (prefill)
+  // SC_MAXPG pages per block
+  const int64_t target = prefill ? 2048 : 4096;  // decode: many short blocks even out rows of unequal length
+  int64_t chunk = (ncmax * n_groups + target - 1) / target;
   chunk = ((chunk + 127) / 128) * 128;
   if (chunk < 128) chunk = 128;
-  if (chunk > 4096) chunk = 4096;
+  if (chunk > (prefill ? SC_PMAXCHUNK : SC_MAXCHUNK)) chunk = prefill ? SC_PMAXCHUNK : SC_MAXCHUNK;
   const int64_t cap = prefill ? int64_t(SC_MAXPG - 1) * ppp : 4 * 63 * ppp;
   while (chunk > 128 && chunk > cap) chunk -= 128;
   if (chunk > cap) {

@@ -6,8 +6,9 @@
 // the lower pool index (the layer's specification).
 //
 // Exact and deterministic, with no sort.  For one row of n scores and a budget b < n:
-//   1. The row is copied once into LDS as order-preserving uint32 keys (-0 folded into +0).  Each wave owns a
-//      contiguous range of it.
+//   1. The row is read once into registers as order-preserving uint32 keys (-0 folded into +0): wave w owns a
+//      contiguous range of the row and lane l holds its indices lo_w + 64 j + l.  Every later pass works on
+//      these registers; LDS only holds a histogram and a few per-wave totals.
 //   2. Radix select: the block's min and max key fix the common high bits; the varying bits below are resolved
 //      11 at a time (at most three passes), finding the key T of the b-th largest score and how many copies of
 //      T the budget still takes (need_eq).  Histograms are integer LDS atomics, so their order does not
@@ -17,9 +18,11 @@
 //      indices first -- exactly the lower-index tie-break); the kept ids come out already ascending, which is
 //      the output format.
 //   4. The tail pool tau (when (i+1) mod P != 0) is appended; it is larger than every complete pool id.
-// Rows of at most 32768 pools take one block.  Longer rows (up to 16 x 32768) take two steps: every 32768-pool
-// chunk keeps its own top-b candidates (ascending), then one block selects the final b among the candidates.
-// Exact because an element in the row's top b (under score desc, index asc) is in the top b of its chunk.
+// A row takes one block, or two steps: every chunk of the row keeps its own top-b candidates (ascending), then
+// one block selects the final b among the candidates.  Exact because an element in the row's top b (under score
+// desc, index asc) is in the top b of its chunk.  Rows longer than 32768 pools (up to 16 chunks of at most
+// 32768, 16 b <= 32768) always take two steps; so do rows of a small batch, whose chunks then spread over more
+// blocks.
 #include "kp_device.hpp"
 #include "kp_internal.hpp"
 
@@ -27,53 +30,51 @@ namespace kp {
 
 constexpr int TK_THREADS = 512;
 constexpr int TK_WAVES = TK_THREADS / 64;
-constexpr int TK_MAXN = 32768;          // keys held in LDS by one block
+constexpr int TK_MAXN = 32768;          // keys of one block: 64 per lane
 constexpr int TK_MAXCHUNKS = 16;        // chunks of a two-step row
 
-struct TkShared {
-  alignas(16) uint32_t keys[TK_MAXN];
+// LDS state of one selection.
+struct TkSync {
   uint32_t hist[2048];
   uint32_t wa[TK_WAVES], wb[TK_WAVES];
   uint32_t digit, remaining;
 };
 
-// Each wave owns a contiguous range of the row: [wave_lo, wave_hi), a multiple of 256 keys long.
-__device__ __forceinline__ void tk_wave_range(int n, int& lo, int& hi) {
-  const int per = ((n + TK_WAVES * 256 - 1) / (TK_WAVES * 256)) * 256;
-  const int w = threadIdx.x >> 6;
-  lo = min(w * per, n);
-  hi = min(lo + per, n);
+// Keys held in registers: lane `lane` of wave w holds indices lo + 64 j + lane (j < NJ) of the row, valid below
+// lo + cnt.  Wave ranges are multiples of 64 keys long, so ballot order is index order.
+template <int NJ>
+struct TkKeys {
+  uint32_t k[NJ];
+  int lo, cnt;
+};
+
+template <int NJ, class Load>
+__device__ __forceinline__ void tk_load(TkKeys<NJ>& K, int n, Load load) {
+  const int per = ((n + TK_WAVES * 64 - 1) / (TK_WAVES * 64)) * 64;  // <= 64 NJ by the caller's choice of NJ
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  K.lo = min(w * per, n);
+  K.cnt = min(per, n - K.lo);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int i = 64 * j + lane;
+    // unconditional (clamped) loads: every load is issued before the first is needed
+    const uint32_t v = load(min(K.lo + i, n - 1));
+    K.k[j] = i < K.cnt ? v : 0u;
+  }
 }
 
-// Selects the `budget` largest of keys[0..n) (0 < budget < n) and calls emit(out_pos, i) for each kept i,
-// out_pos ascending with i.
-//
-// The radix passes only cover the bits in which the row's keys differ: a first pass takes the block min and
-// max, their common high bits are fixed, and the varying bits below are resolved 11 at a time (at most three
-// passes).  Digits of varying bits are spread, so plain LDS atomics seldom collide.  A row whose keys are all
-// equal needs no pass at all.  Order-free passes read 16 bytes per lane from the wave's contiguous range; the
-// compaction walks that range 64 keys per step with ballots, so only the per-wave totals cross waves.
-template <class Emit>
-__device__ void tk_select(TkShared& sh, int n, int budget, Emit emit) {
+// Selects the `budget` largest of the block's n keys (0 < budget < n) and calls emit(out_pos, i, key) for each
+// kept index i, out_pos ascending with i.
+template <int NJ, class Emit>
+__device__ void tk_select(TkSync& sy, const TkKeys<NJ>& K, int budget, Emit emit) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int lo_i, hi_i;
-  tk_wave_range(n, lo_i, hi_i);
-  const uint4* k4 = reinterpret_cast<const uint4*>(sh.keys);
+  auto valid = [&](int j) __attribute__((always_inline)) { return 64 * j + lane < K.cnt; };
 
-  // min / max (keys past n are skipped by index)
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int base = lo_i; base < hi_i; base += 256) {
-    const int i = base + 4 * lane;
-    if (i < hi_i) {
-      const uint4 v = k4[i >> 2];
-      const uint32_t e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (i + j < hi_i) {
-          mn = min(mn, e[j]);
-          mx = max(mx, e[j]);
-        }
-    }
+  for (int j = 0; j < NJ; ++j) {
+    mn = min(mn, valid(j) ? K.k[j] : 0xFFFFFFFFu);
+    mx = max(mx, valid(j) ? K.k[j] : 0u);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -81,14 +82,14 @@ __device__ void tk_select(TkShared& sh, int n, int budget, Emit emit) {
     mx = max(mx, uint32_t(__shfl_xor(int(mx), off)));
   }
   if (lane == 0) {
-    sh.wa[wv] = mn;
-    sh.wb[wv] = mx;
+    sy.wa[wv] = mn;
+    sy.wb[wv] = mx;
   }
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < TK_WAVES; ++w) {
-    mn = min(mn, sh.wa[w]);
-    mx = max(mx, sh.wb[w]);
+    mn = min(mn, sy.wa[w]);
+    mx = max(mx, sy.wb[w]);
   }
   __syncthreads();
   // bits [0, lo) vary; bits at and above lo are common to every key and fixed in `prefix`
@@ -100,25 +101,18 @@ __device__ void tk_select(TkShared& sh, int n, int budget, Emit emit) {
     const int width = min(11, lo);
     const int shift = lo - width;
     const uint32_t dmask = (1u << width) - 1u;
-    for (int j = tid; j < 2048; j += TK_THREADS) sh.hist[j] = 0;
+    for (int j = tid; j < 2048; j += TK_THREADS) sy.hist[j] = 0;
     __syncthreads();
-    for (int base = lo_i; base < hi_i; base += 256) {
-      const int i = base + 4 * lane;
-      if (i < hi_i) {
-        const uint4 v = k4[i >> 2];
-        const uint32_t e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (i + j < hi_i && (e[j] & mask) == prefix) atomicAdd(&sh.hist[(e[j] >> shift) & dmask], 1u);
-      }
-    }
+    for (int j = 0; j < NJ; ++j)
+      if (valid(j) && (K.k[j] & mask) == prefix) atomicAdd(&sy.hist[(K.k[j] >> shift) & dmask], 1u);
     __syncthreads();
     // thread t owns digits 4t .. 4t+3; `above` counts keys with a higher digit than its range
     uint32_t c[4], mine = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d = 4 * tid + j;
-      c[j] = d <= int(dmask) ? sh.hist[d] : 0u;
+      c[j] = d <= int(dmask) ? sy.hist[d] : 0u;
       mine += c[j];
     }
     // inclusive prefix over threads (thread order = digit order), then count from the top
@@ -128,30 +122,30 @@ __device__ void tk_select(TkShared& sh, int n, int budget, Emit emit) {
       const uint32_t u = uint32_t(__shfl_up(int(inc), off));
       if (lane >= off) inc += u;
     }
-    if (lane == 63) sh.wa[wv] = inc;
+    if (lane == 63) sy.wa[wv] = inc;
     __syncthreads();
     uint32_t before = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < TK_WAVES; ++w) {
-      before += (w < wv) ? sh.wa[w] : 0u;
-      total += sh.wa[w];
+      before += (w < wv) ? sy.wa[w] : 0u;
+      total += sy.wa[w];
     }
     const uint32_t above = total - (before + inc);
     if (above < remaining && remaining <= above + mine) {
       uint32_t acc = above;
       for (int j = 3; j >= 0; --j) {
         if (acc + c[j] >= remaining) {
-          sh.digit = uint32_t(4 * tid + j);
-          sh.remaining = remaining - acc;
+          sy.digit = uint32_t(4 * tid + j);
+          sy.remaining = remaining - acc;
           break;
         }
         acc += c[j];
       }
     }
     __syncthreads();
-    prefix |= sh.digit << shift;
+    prefix |= sy.digit << shift;
     mask |= dmask << shift;
-    remaining = sh.remaining;
+    remaining = sy.remaining;
     lo = shift;
     __syncthreads();
   }
@@ -160,66 +154,39 @@ __device__ void tk_select(TkShared& sh, int n, int budget, Emit emit) {
 
   // compaction: per-wave counts, one exchange, then each wave emits its range in index order
   uint32_t gt = 0, eq = 0;
-  for (int base = lo_i; base < hi_i; base += 64) {
-    const int i = base + lane;
-    const uint32_t key = i < hi_i ? sh.keys[i] : 0u;
-    gt += uint32_t(__popcll(__ballot(i < hi_i && key > T)));
-    eq += uint32_t(__popcll(__ballot(i < hi_i && key == T)));
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    gt += uint32_t(__popcll(__ballot(valid(j) && K.k[j] > T)));
+    eq += uint32_t(__popcll(__ballot(valid(j) && K.k[j] == T)));
   }
   if (lane == 0) {
-    sh.wa[wv] = gt;
-    sh.wb[wv] = eq;
+    sy.wa[wv] = gt;
+    sy.wb[wv] = eq;
   }
   __syncthreads();
   uint32_t gt_before = 0, eq_before = 0;
 #pragma unroll
   for (int w = 0; w < TK_WAVES; ++w)
     if (w < wv) {
-      gt_before += sh.wa[w];
-      eq_before += sh.wb[w];
+      gt_before += sy.wa[w];
+      eq_before += sy.wb[w];
     }
   // kept before this wave: all greater keys plus the first need_eq equal keys in index order
   uint32_t at = gt_before + min(eq_before, need_eq);
   uint32_t eq_seen = eq_before;
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  for (int base = lo_i; base < hi_i; base += 64) {
-    const int i = base + lane;
-    const uint32_t key = i < hi_i ? sh.keys[i] : 0u;
-    const bool is_eq = i < hi_i && key == T;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const bool is_eq = valid(j) && K.k[j] == T;
     const uint64_t eqm = __ballot(is_eq);
     const uint32_t eq_rank = eq_seen + uint32_t(__popcll(eqm & below));
-    const bool take = (i < hi_i && key > T) || (is_eq && eq_rank < need_eq);
+    const bool take = (valid(j) && K.k[j] > T) || (is_eq && eq_rank < need_eq);
     const uint64_t tm = __ballot(take);
-    if (take) emit(int(at + uint32_t(__popcll(tm & below))), i);
+    if (take) emit(int(at + uint32_t(__popcll(tm & below))), K.lo + 64 * j + lane, K.k[j]);
     at += uint32_t(__popcll(tm));
     eq_seen += uint32_t(__popcll(eqm));
   }
   __syncthreads();
-}
-
-// Copies n fp32 scores (16-byte aligned source) into LDS as keys.  Every thread issues all of its loads before
-// its first LDS store (up to 16 float4 per thread per round), so the copy costs about one memory latency per
-// round instead of one per element.
-__device__ __forceinline__ void tk_load_keys(TkShared& sh, const float* __restrict__ src, int n) {
-  constexpr int U = 16;
-  const int n4 = n >> 2;
-  const float4* s4 = reinterpret_cast<const float4*>(src);
-  uint4* k4 = reinterpret_cast<uint4*>(sh.keys);
-  for (int base = 0; base < n4; base += U * TK_THREADS) {
-    float4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i4 = base + u * TK_THREADS + int(threadIdx.x);
-      v[u] = s4[min(i4, max(n4 - 1, 0))];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i4 = base + u * TK_THREADS + int(threadIdx.x);
-      if (i4 < n4)
-        k4[i4] = make_uint4(score_key(v[u].x), score_key(v[u].y), score_key(v[u].z), score_key(v[u].w));
-    }
-  }
-  for (int i = 4 * n4 + int(threadIdx.x); i < n; i += TK_THREADS) sh.keys[i] = score_key(src[i]);
 }
 
 __device__ __forceinline__ void tk_geometry(int pos, int P, int k, int64_t ld, int& n_c, int& r, int& tau, int& b) {
@@ -238,11 +205,12 @@ __device__ __forceinline__ void tk_finish(int32_t* out, int32_t* n_sel, int q, i
   for (int j = cnt + (r ? 1 : 0) + threadIdx.x; j < k; j += TK_THREADS) out[j] = -1;
 }
 
-// One block per query row (rows of at most TK_MAXN pools).
+// One block per query row (rows of at most 64 NJ TK_WAVES pools).
+template <int NJ>
 __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
                                                               const int32_t* __restrict__ q_pos, int P, int k,
                                                               int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
-  __shared__ TkShared sh;
+  __shared__ TkSync sy;
   const int q = blockIdx.x;
   int n_c, r, tau, b;
   tk_geometry(q_pos[q], P, k, ld, n_c, r, tau, b);
@@ -251,114 +219,151 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const float* __res
   if (b >= n_c) {
     for (int p = threadIdx.x; p < n_c; p += TK_THREADS) out[p] = p;
   } else if (b > 0) {
-    tk_load_keys(sh, row, n_c);
-    __syncthreads();
-    tk_select(sh, n_c, b, [&](int at, int i) __attribute__((always_inline)) { out[at] = i; });
+    TkKeys<NJ> K;
+    tk_load(K, n_c, [&](int i) __attribute__((always_inline)) { return score_key(row[i]); });
+    tk_select(sy, K, b, [&](int at, int i, uint32_t) __attribute__((always_inline)) { out[at] = i; });
   }
   tk_finish(out, n_sel, q, k, max(b, 0), r, tau);
 }
 
-// Step 1 of a long row: chunk c of row q keeps min(b, chunk length) candidates (key, pool id), ascending.
+// Step 1 of a two-step row: chunk c of row q keeps min(b, chunk length) candidates (key, pool id), ascending.
+template <int NJ>
 __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(const float* __restrict__ scores, int64_t ld,
                                                                 const int32_t* __restrict__ q_pos, int P, int k,
-                                                                int n_chunks, uint32_t* __restrict__ cand_key,
+                                                                int n_chunks, int chunk_len,
+                                                                uint32_t* __restrict__ cand_key,
                                                                 int32_t* __restrict__ cand_idx) {
-  __shared__ TkShared sh;
+  __shared__ TkSync sy;
   const int q = blockIdx.x / n_chunks;
   const int c = blockIdx.x - q * n_chunks;
   int n_c, r, tau, b;
   tk_geometry(q_pos[q], P, k, ld, n_c, r, tau, b);
-  const int base = c * TK_MAXN;
-  const int len = min(TK_MAXN, n_c - base);
+  const int base = c * chunk_len;
+  const int len = min(chunk_len, n_c - base);
   if (len <= 0 || b <= 0) return;
   const float* row = scores + int64_t(q) * ld + base;
   const int64_t cb = (int64_t(q) * n_chunks + c) * k;
-  tk_load_keys(sh, row, len);
-  __syncthreads();
   if (b >= len) {
     for (int i = threadIdx.x; i < len; i += TK_THREADS) {
-      cand_key[cb + i] = sh.keys[i];
+      cand_key[cb + i] = score_key(row[i]);
       cand_idx[cb + i] = base + i;
     }
   } else {
-    tk_select(sh, len, b, [&](int at, int i) __attribute__((always_inline)) {
-      cand_key[cb + at] = sh.keys[i];
+    TkKeys<NJ> K;
+    tk_load(K, len, [&](int i) __attribute__((always_inline)) { return score_key(row[i]); });
+    tk_select(sy, K, b, [&](int at, int i, uint32_t key) __attribute__((always_inline)) {
+      cand_key[cb + at] = key;
       cand_idx[cb + at] = base + i;
     });
   }
 }
 
-// Step 2 of a long row: the final b among the chunks' candidates, taken in chunk order (ascending ids).
+// Step 2 of a two-step row: the final b among the chunks' candidates, taken in chunk order (ascending ids).
+template <int NJ>
 __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(const uint32_t* __restrict__ cand_key,
                                                                 const int32_t* __restrict__ cand_idx, int64_t ld,
                                                                 const int32_t* __restrict__ q_pos, int P, int k,
-                                                                int n_chunks, int32_t* __restrict__ sel,
+                                                                int n_chunks, int chunk_len,
+                                                                int32_t* __restrict__ sel,
                                                                 int32_t* __restrict__ n_sel) {
-  __shared__ TkShared sh;
-  __shared__ int cstart[TK_MAXCHUNKS + 1];
+  __shared__ TkSync sy;
   const int q = blockIdx.x;
   int n_c, r, tau, b;
   tk_geometry(q_pos[q], P, k, ld, n_c, r, tau, b);
   int32_t* out = sel + int64_t(q) * k;
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      cstart[c] = acc;
-      const int len = max(0, min(TK_MAXN, n_c - c * TK_MAXN));
-      acc += min(max(b, 0), len);
-    }
-    cstart[n_chunks] = acc;
-  }
-  __syncthreads();
-  const int n2 = cstart[n_chunks];
-  auto cand = [&](int i) __attribute__((always_inline)) -> int64_t {  // workspace offset of candidate i
-    int c = 0;
-    while (c + 1 < n_chunks && cstart[c + 1] <= i) ++c;
-    return (int64_t(q) * n_chunks + c) * k + (i - cstart[c]);
-  };
+  // Every chunk before the row's last non-empty one is longer than b (chunks hold at least 4k pools, or all
+  // 32768) and kept exactly b candidates, so candidate i sits in chunk i / b at i % b.
+  const int bb = max(b, 0);
+  int n2 = 0;
+  for (int c = 0; c < n_chunks; ++c) n2 += min(bb, max(0, min(chunk_len, n_c - c * chunk_len)));
+  const int64_t rowc = int64_t(q) * n_chunks * k;
+  auto cand = [&](int i) __attribute__((always_inline)) -> int64_t { return rowc + int64_t(i / bb) * k + i % bb; };
   if (b >= n2) {
     for (int i = threadIdx.x; i < n2; i += TK_THREADS) out[i] = cand_idx[cand(i)];
   } else if (b > 0) {
-    for (int i = threadIdx.x; i < n2; i += TK_THREADS) sh.keys[i] = cand_key[cand(i)];
-    __syncthreads();
-    tk_select(sh, n2, b, [&](int at, int i) __attribute__((always_inline)) { out[at] = cand_idx[cand(i)]; });
+    TkKeys<NJ> K;  // straight from the candidates: every lane issues all its loads at once
+    tk_load(K, n2, [&](int i) __attribute__((always_inline)) { return cand_key[cand(i)]; });
+    tk_select(sy, K, b, [&](int at, int i, uint32_t) __attribute__((always_inline)) { out[at] = cand_idx[cand(i)]; });
   }
   tk_finish(out, n_sel, q, k, max(b, 0), r, tau);
 }
 
-static int tk_chunks(int P, int max_pos) {
+// Chunk length of the row split (a multiple of 256; n_chunks = 1 means one block per row).  A row longer than
+// one block's registers is always split.  With few rows the split also spreads a row over several blocks
+// (about 256 blocks in all), keeping chunks of at least 4k pools so that each chunk's top-k shrinks the merge's
+// input.
+static int tk_chunk_len(int P, int k, int n_q, int max_pos) {
   const int64_t ncmax = (int64_t(max_pos) + 1) / P;
-  return int((ncmax + TK_MAXN - 1) / TK_MAXN);
+  if (ncmax <= TK_MAXN && (n_q >= 192 || ncmax <= 4 * int64_t(k))) return TK_MAXN;
+  const int64_t want = (256 + int64_t(n_q) - 1) / (n_q > 0 ? n_q : 1);
+  int64_t len = (ncmax + want - 1) / want;
+  if (len < 4 * int64_t(k)) len = 4 * int64_t(k);
+  // never more chunks than the merge holds (TK_MAXCHUNKS, and chunks x k <= TK_MAXN)
+  int64_t max_nch = TK_MAXN / (k > 0 ? k : 1);
+  if (max_nch > TK_MAXCHUNKS) max_nch = TK_MAXCHUNKS;
+  if (max_nch < 1) max_nch = 1;
+  if (len < (ncmax + max_nch - 1) / max_nch) len = (ncmax + max_nch - 1) / max_nch;
+  len = (len + 255) / 256 * 256;
+  if (len > TK_MAXN) len = TK_MAXN;
+  return int(len);
+}
+
+static int tk_chunks(int P, int k, int n_q, int max_pos) {
+  const int64_t ncmax = (int64_t(max_pos) + 1) / P;
+  const int len = tk_chunk_len(P, k, n_q, max_pos);
+  return int((ncmax + len - 1) / len);
 }
 
 size_t topk_workspace(int P, int k, int n_q, int max_pos) {
-  const int nch = tk_chunks(P, max_pos);
+  const int nch = tk_chunks(P, k, n_q, max_pos);
   if (nch <= 1) return 0;
   return size_t(n_q) * nch * k * (sizeof(uint32_t) + sizeof(int32_t));
 }
 
-kp_status launch_topk(const TopkLaunch& a, hipStream_t s) {
-  if (a.n_q == 0) return KP_OK;
-  const int nch = tk_chunks(a.P, a.max_pos);
+// keys per lane for n keys in one block: the smallest of 16, 32, 64 that holds them
+static int tk_nj(int64_t n) { return n <= 16 * 64 * TK_WAVES ? 16 : n <= 32 * 64 * TK_WAVES ? 32 : 64; }
+
+template <int NJ>
+static kp_status launch_topk_nj(const TopkLaunch& a, int nch, int clen, int merge_nj, hipStream_t s) {
   if (nch <= 1) {
-    topk_row_kernel<<<dim3(unsigned(a.n_q)), dim3(TK_THREADS), 0, s>>>(a.scores, a.ld, a.q_pos, a.P, a.k, a.sel,
-                                                                       a.n_sel);
+    topk_row_kernel<NJ><<<dim3(unsigned(a.n_q)), dim3(TK_THREADS), 0, s>>>(a.scores, a.ld, a.q_pos, a.P, a.k, a.sel,
+                                                                           a.n_sel);
     return check_launch("dsa_topk_select");
   }
-  if (nch > TK_MAXCHUNKS || int64_t(nch) * a.k > TK_MAXN) {
+  uint32_t* cand_key = reinterpret_cast<uint32_t*>(a.ws);
+  int32_t* cand_idx = reinterpret_cast<int32_t*>(cand_key + size_t(a.n_q) * nch * a.k);
+  topk_chunk_kernel<NJ><<<dim3(unsigned(int64_t(a.n_q) * nch)), dim3(TK_THREADS), 0, s>>>(
+      a.scores, a.ld, a.q_pos, a.P, a.k, nch, clen, cand_key, cand_idx);
+  kp_status st = check_launch("dsa_topk_select (chunks)");
+  if (st != KP_OK) return st;
+  const dim3 grid(unsigned(a.n_q)), block(TK_THREADS);
+  if (merge_nj == 16)
+    topk_merge_kernel<16><<<grid, block, 0, s>>>(cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k, nch, clen, a.sel,
+                                                 a.n_sel);
+  else if (merge_nj == 32)
+    topk_merge_kernel<32><<<grid, block, 0, s>>>(cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k, nch, clen, a.sel,
+                                                 a.n_sel);
+  else
+    topk_merge_kernel<64><<<grid, block, 0, s>>>(cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k, nch, clen, a.sel,
+                                                 a.n_sel);
+  return check_launch("dsa_topk_select (merge)");
+}
+
+kp_status launch_topk(const TopkLaunch& a, hipStream_t s) {
+  if (a.n_q == 0) return KP_OK;
+  const int nch = tk_chunks(a.P, a.k, a.n_q, a.max_pos);
+  const int clen = tk_chunk_len(a.P, a.k, a.n_q, a.max_pos);
+  if (nch > 1 && (nch > TK_MAXCHUNKS || int64_t(nch) * a.k > TK_MAXN)) {
     set_error("dsa_topk_select: %d pools per row with top-%d exceeds the two-step limit", (a.max_pos + 1) / a.P,
               a.k);
     return KP_ERR_UNSUPPORTED;
   }
-  uint32_t* cand_key = reinterpret_cast<uint32_t*>(a.ws);
-  int32_t* cand_idx = reinterpret_cast<int32_t*>(cand_key + size_t(a.n_q) * nch * a.k);
-  topk_chunk_kernel<<<dim3(unsigned(int64_t(a.n_q) * nch)), dim3(TK_THREADS), 0, s>>>(
-      a.scores, a.ld, a.q_pos, a.P, a.k, nch, cand_key, cand_idx);
-  kp_status st = check_launch("dsa_topk_select (chunks)");
-  if (st != KP_OK) return st;
-  topk_merge_kernel<<<dim3(unsigned(a.n_q)), dim3(TK_THREADS), 0, s>>>(cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k,
-                                                                       nch, a.sel, a.n_sel);
-  return check_launch("dsa_topk_select (merge)");
+  const int64_t ncmax = (int64_t(a.max_pos) + 1) / a.P;
+  const int nj = tk_nj(nch <= 1 ? ncmax : clen);
+  const int merge_nj = tk_nj(int64_t(nch) * a.k);
+  if (nj == 16) return launch_topk_nj<16>(a, nch, clen, merge_nj, s);
+  if (nj == 32) return launch_topk_nj<32>(a, nch, clen, merge_nj, s);
+  return launch_topk_nj<64>(a, nch, clen, merge_nj, s);
 }
 
 }  // namespace kp

@@ -37,13 +37,15 @@ class KPoolDSALayer:
         self.n_sel = torch.empty((max_q,), dtype=torch.int32, device=self.device)
         probe = Queries(seq=torch.empty(max_q, dtype=torch.int32), pos=torch.empty(max_q, dtype=torch.int32),
                         max_pos=max_pos)
-        self.ws_topk = self._ws(dsa_topk_workspace_size(dims, probe))
-        # the split-KV count depends on the number of queries; size for the largest need over 1..max_q
-        need = 0
+        # how rows and selections are split depends on the number of queries: size each workspace for the
+        # largest need over 1..max_q
+        need_topk = need_attn = 0
         for n in range(1, max_q + 1):
             qn = Queries(seq=probe.seq[:n], pos=probe.pos[:n], max_pos=max_pos)
-            need = max(need, sparse_mla_workspace_size(dims, qn))
-        self.ws_attn = self._ws(need)
+            need_topk = max(need_topk, dsa_topk_workspace_size(dims, qn))
+            need_attn = max(need_attn, sparse_mla_workspace_size(dims, qn))
+        self.ws_topk = self._ws(need_topk)
+        self.ws_attn = self._ws(need_attn)
         self.max_q, self.max_pos = max_q, max_pos
 
     def _ws(self, nbytes: int):
