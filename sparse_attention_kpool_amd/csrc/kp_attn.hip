@@ -183,6 +183,13 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     return rel < nsl ? e : -1;
   };
 
+  // Slot (row of the block) of a thread's i-th chunk c: with one value row per wave instruction, wave w takes
+  // the CHT consecutive slots w*CHT .. (w+1)*CHT-1 (one whole pool at P = CHT = 4); otherwise c / CPR.
+  auto slot_of = [&](int c, int i) __attribute__((always_inline)) -> int {
+    if constexpr (S::CPR == 64 && S::CHUNKS % AT_THREADS == 0) return (tid >> 6) * S::CHT + i;
+    else return c / S::CPR;
+  };
+
   // Loads are unconditional (an invalid slot reads row 0 of the cache and is zeroed when stored): branch-free
   // loads let the compiler wait for exactly the block it needs instead of draining every load in flight.  With
   // one whole value row per wave instruction the row is wave-uniform and its address is computed on the
@@ -192,7 +199,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     for (int i = 0; i < S::CHT; ++i) {
       if constexpr (S::CPR == 64 && S::CHUNKS % AT_THREADS == 0) {
         const int wv = __builtin_amdgcn_readfirstlane(wave);
-        const int e = __builtin_amdgcn_readfirstlane(slot_entry(b, wv + (AT_THREADS / 64) * i));
+        const int e = __builtin_amdgcn_readfirstlane(slot_entry(b, wv * S::CHT + i));
         const T* rp = latent + int64_t(max(e, 0)) * L;
         R[i] = *reinterpret_cast<const u32x4*>(rp + lane * S::EPC);
         vrow[i] = e >= 0;
@@ -304,7 +311,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     for (int i = 0; i < S::CHT; ++i) {
       const int c = tid + AT_THREADS * i;
       if (S::CHUNKS % AT_THREADS == 0 || c < S::CHUNKS)
-        *reinterpret_cast<u32x4*>(blk + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) =
+        *reinterpret_cast<u32x4*>(blk + slot_of(c, i) * S::RS + (c % S::CPR) * S::EPC) =
             vrow[i] ? R[i] : u32x4{0, 0, 0, 0};
     }
     if (wave == 0) {
