@@ -38,13 +38,18 @@ COMPILE_FLAGS = [
 ]
 
 
+# per-file extras: the scoring kernels keep their MFMA accumulators in ordinary VGPRs, so their ReLU-weighted
+# epilogue reads the results directly (no accumulator-register copies)
+FILE_FLAGS = {"kp_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources() -> list:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMPILE_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMPILE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

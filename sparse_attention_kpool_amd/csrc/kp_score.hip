@@ -58,21 +58,48 @@ __device__ __forceinline__ void score_query_frags(const T* __restrict__ q_idx, c
   }
 }
 
-// ReLU-weighted head sum of one 32x32 tile; lanes 0..31 return the scores of pools 0..31.
-template <class T, int D>
-__device__ __forceinline__ float score_tile(const typename Elem<T>::frag (&qa)[ScoreShape<T, D>::STEPS],
-                                            const typename Elem<T>::frag (&kb)[ScoreShape<T, D>::STEPS],
-                                            const float (&wv)[16]) {
-  f32x16 acc = {};
+// ReLU-weighted head sums of one 32-pool tile for QW queries; lanes 0..31 get the scores of pools 0..31.  The
+// queries' MFMA chains are interleaved k-step by k-step, so QW independent accumulations are in flight.
+template <class T, int D, int QW>
+__device__ __forceinline__ void score_mma(const typename Elem<T>::frag (&qa)[QW][ScoreShape<T, D>::STEPS],
+                                          const typename Elem<T>::frag (&kb)[ScoreShape<T, D>::STEPS],
+                                          f32x16 (&acc)[QW]) {
 #pragma unroll
-  for (int s = 0; s < ScoreShape<T, D>::STEPS; ++s) acc = mfma32(qa[s], kb[s], acc);
-  float part = 0.f;
+  for (int r = 0; r < QW; ++r) acc[r] = f32x16{};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) part += wv[i] * fmaxf(acc[i], 0.f);
-  return part + __shfl_xor(part, 32);
+  for (int s = 0; s < ScoreShape<T, D>::STEPS; ++s)
+#pragma unroll
+    for (int r = 0; r < QW; ++r) acc[r] = mfma32(qa[r][s], kb[s], acc[r]);
 }
 
-constexpr int SC_MAXCHUNK = 4096;    // pools per block
+template <int QW>
+__device__ __forceinline__ void score_reduce(const f32x16 (&acc)[QW], const float (&wv)[QW][16], float (&sc)[QW]) {
+  // ReLU as an integer max on the bits: a negative float (and -0) has the sign bit set, i.e. is a negative
+  // int32, so max(bits, 0) gives +0 for it and leaves a positive float unchanged -- one instruction, where
+  // fmaxf needs a NaN-quieting step first.  (The element is copied to a scalar before the bit cast: a bit cast
+  // applied to a vector element expression directly reads element 0.)
+#pragma unroll
+  for (int r = 0; r < QW; ++r) {
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float s = acc[r][i];
+      part += wv[r][i] * __builtin_bit_cast(float, max(__builtin_bit_cast(int, s), 0));
+    }
+    sc[r] = part + __shfl_xor(part, 32);
+  }
+}
+
+template <class T, int D, int QW>
+__device__ __forceinline__ void score_tiles(const typename Elem<T>::frag (&qa)[QW][ScoreShape<T, D>::STEPS],
+                                            const typename Elem<T>::frag (&kb)[ScoreShape<T, D>::STEPS],
+                                            const float (&wv)[QW][16], float (&sc)[QW]) {
+  f32x16 acc[QW];
+  score_mma<T, D, QW>(qa, kb, acc);
+  score_reduce<QW>(acc, wv, sc);
+}
+
+constexpr int SC_MAXCHUNK = 4096;    // pools per decode block (each wave's scores are buffered in LDS)
 
 // ---------------------------------------------------------------------------------------------------------------
 // decode: grid = n_q x n_chunks; a block covers `chunk_pools` pools of one query, a wave `chunk_pools / 4`
@@ -102,9 +129,9 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   const int w_end = min(w_begin + sub, n_c);
   if (w_begin >= w_end) return;  // no block-wide barrier below: waves finish independently
 
-  F qa[S::STEPS];
-  float wv[16];
-  score_query_frags<T, D>(q_idx, w, qi, true, Hi, n, g, qa, wv);
+  F qa[1][S::STEPS];
+  float wv[1][16];
+  score_query_frags<T, D>(q_idx, w, qi, true, Hi, n, g, qa[0], wv[0]);
 
   // page id of each page the wave touches: lane l holds page (w_begin >> log2_ppp) + l
   const int pg0 = w_begin >> log2_ppp;
@@ -143,8 +170,9 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
     const T* kp = tile + n * S::RS + g * (D / 2);
 #pragma unroll
     for (int s = 0; s < S::STEPS; ++s) kb[s] = E::frag_load(kp + s * S::KPL);
-    const float sc = score_tile<T, D>(qa, kb, wv);
-    if (g == 0) sb[t * 32 + n] = sc;  // slots past the range are never written out
+    float sc[1];
+    score_tiles<T, D, 1>(qa, kb, wv, sc);
+    if (g == 0) sb[t * 32 + n] = sc[0];  // slots past the range are never written out
   };
 
   u32x4 R0[CHT], R1[CHT];
@@ -177,7 +205,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int CHT = (S::TCH + 255) / 256;  // chunks per thread per tile
-  __shared__ __align__(16) T tile[32 * S::RS];
+  __shared__ __align__(16) T tiles[2][32 * S::RS];
   __shared__ int page_s[SC_MAXPG];
   __shared__ float psb[SC_QG][SC_PMAXCHUNK];  // the block's scores, written out after each sequence pass
   __shared__ int seq_s[SC_QG];
@@ -237,36 +265,56 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
         R[i] = *reinterpret_cast<const u32x4*>(pooled + row * D + (c % S::CPR) * S::EPC);
       }
     };
-    auto step = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
-      __syncthreads();  // the previous tile is fully read
+    auto store_tile = [&](int buf, u32x4(&R)[CHT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < CHT; ++i) {
         const int c = tid + 256 * i;
-        if (c < S::TCH) *reinterpret_cast<u32x4*>(tile + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
-      }
-      load_tile(t + 2, R);
-      __syncthreads();
-      F kb[S::STEPS];
-      const T* kp = tile + n * S::RS + g * (D / 2);
-#pragma unroll
-      for (int s = 0; s < S::STEPS; ++s) kb[s] = E::frag_load(kp + s * S::KPL);
-      const int pool = p_begin + t * 32 + n;
-#pragma unroll
-      for (int r = 0; r < SC_QW; ++r) {
-        const float sc = score_tile<T, D>(qa[r], kb, wv[r]);
-        if (g == 0) psb[wave * SC_QW + r][pool - p_begin] = sc;  // written out only where visible and active
+        if (c < S::TCH)
+          *reinterpret_cast<u32x4*>(tiles[buf] + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
       }
     };
-    // As in the decode kernel: loads and steps are unconditional, no global store sits in the tile loop, and
-    // tile 0's loads stay older than tile 1's, so the loop's wait counts are exact.
+    auto mma = [&](int t, f32x16(&acc)[SC_QW]) __attribute__((always_inline)) {
+      F kb[S::STEPS];
+      const T* kp = tiles[t & 1] + n * S::RS + g * (D / 2);
+#pragma unroll
+      for (int s = 0; s < S::STEPS; ++s) kb[s] = E::frag_load(kp + s * S::KPL);
+      score_mma<T, D, SC_QW>(qa, kb, acc);
+    };
+    auto epi = [&](int t, const f32x16(&acc)[SC_QW]) __attribute__((always_inline)) {
+      float sc[SC_QW];
+      score_reduce<SC_QW>(acc, wv, sc);
+#pragma unroll
+      for (int r = 0; r < SC_QW; ++r)
+        if (g == 0) psb[wave * SC_QW + r][t * 32 + n] = sc[r];  // written out only where visible and active
+    };
+    // Iteration t: the MFMAs of tile t (from LDS buffer t & 1) into one accumulator set while the epilogue of
+    // tile t-1 works on the other, so the matrix cores and the VALU overlap within a wave; then tile t+1 goes
+    // from registers into the other LDS buffer (last read in iteration t-1), tile t+3 starts loading, and one
+    // barrier closes the iteration.
+    auto iter = [&](int t, f32x16(&cur)[SC_QW], const f32x16(&prev)[SC_QW], u32x4(&R)[CHT])
+                    __attribute__((always_inline)) {
+      mma(t, cur);
+      if (t >= 1) epi(t - 1, prev);
+      store_tile((t + 1) & 1, R);
+      load_tile(t + 3, R);
+      __syncthreads();
+    };
+    // As in the decode kernel: loads and iterations are unconditional, no global store sits in the tile loop,
+    // and every tile's loads stay older than the next one's, so the loop's wait counts are exact.
     u32x4 R0[CHT], R1[CHT];
+    f32x16 accA[SC_QW], accB[SC_QW];
     load_tile(0, R0);
     __builtin_amdgcn_sched_barrier(0);
     load_tile(1, R1);
-    for (int t = 0; t < ntile; t += 2) {
-      step(t, R0);
-      step(t + 1, R1);
+    store_tile(0, R0);
+    load_tile(2, R0);
+    __syncthreads();
+    int t = 0;
+    for (; t < ntile; t += 2) {
+      iter(t, accA, accB, R1);
+      iter(t + 1, accB, accA, R0);
     }
+    epi(t - 1, accB);  // the last tile computed (t - 1 is odd: accB)
     __syncthreads();
     for (int e = tid; e < SC_QG * chunk_pools; e += 256) {
       const int qr = e / chunk_pools, i = e - qr * chunk_pools;
