@@ -86,7 +86,16 @@ __device__ __forceinline__ void score_reduce(const f32x16 (&acc)[QW], const floa
       const float s = acc[r][i];
       part += wv[r][i] * __builtin_bit_cast(float, max(__builtin_bit_cast(int, s), 0));
     }
-    sc[r] = part + __shfl_xor(part, 32);
+    // partner lane l ^ 32 holds the other 16 heads of the same pool.  v_permlane32_swap(x, y) swaps the upper
+    // half of x with the lower half of y, returning [x lanes 0..31, y lanes 0..31] and [x lanes 32..63,
+    // y lanes 32..63]; with x = part their sum in lanes 0..31 (the lanes that keep the score) is
+    // part[l] + part[l + 32] -- one VALU op instead of an LDS permute.  y is a separate zero: the instruction
+    // rewrites both of its registers, so x and y must not be the same register.
+    // (The results are copied to scalars before the bit casts, which read element 0 of a vector element
+    // expression.)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, part), 0u, false, false);
+    const uint32_t lo = sw[0], hi = sw[1];
+    sc[r] = __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
   }
 }
 
@@ -193,7 +202,8 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
 constexpr int SC_QW = 2;              // queries per wave
 constexpr int SC_QG = 4 * SC_QW;      // queries per block
 constexpr int SC_MAXPG = 1024;        // page ids of one block's pool range held in LDS
-constexpr int SC_PMAXCHUNK = 1024;    // pools per block (its scores are buffered in LDS)
+constexpr int SC_PMAXCHUNK = 4096;    // pools per block
+constexpr int SC_PSEG = 1024;         // pools whose scores are buffered in LDS between write-outs
 
 template <class T, int D>
 __global__ __launch_bounds__(256) void score_prefill_kernel(
@@ -207,7 +217,9 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
   constexpr int CHT = (S::TCH + 255) / 256;  // chunks per thread per tile
   __shared__ __align__(16) T tiles[2][32 * S::RS];
   __shared__ int page_s[SC_MAXPG];
-  __shared__ float psb[SC_QG][SC_PMAXCHUNK];  // the block's scores, written out after each sequence pass
+  // scores of the current 32-tile segment, written out after it (32 extra slots take the stores of the lanes
+  // that hold no score, so storing needs no branch)
+  __shared__ float psb[SC_QG][SC_PSEG + 32];
   __shared__ int seq_s[SC_QG];
   __shared__ int nc_s[SC_QG];
 
@@ -284,8 +296,8 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
       float sc[SC_QW];
       score_reduce<SC_QW>(acc, wv, sc);
 #pragma unroll
-      for (int r = 0; r < SC_QW; ++r)
-        if (g == 0) psb[wave * SC_QW + r][t * 32 + n] = sc[r];  // written out only where visible and active
+      for (int r = 0; r < SC_QW; ++r)  // written out only where visible and active
+        psb[wave * SC_QW + r][g == 0 ? (t & 31) * 32 + n : SC_PSEG + n] = sc[r];
     };
     // Iteration t: the MFMAs of tile t (from LDS buffer t & 1) into one accumulator set while the epilogue of
     // tile t-1 works on the other, so the matrix cores and the VALU overlap within a wave; then tile t+1 goes
@@ -294,7 +306,9 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
     auto iter = [&](int t, f32x16(&cur)[SC_QW], const f32x16(&prev)[SC_QW], u32x4(&R)[CHT])
                     __attribute__((always_inline)) {
       mma(t, cur);
-      if (t >= 1) epi(t - 1, prev);
+      // At t == t0 this writes slot 31 of psb from stale accumulators: the segment's tile 31 overwrites it
+      // later, or (a short last segment) its pools lie past the range and are never written out.  No branch.
+      epi(t - 1, prev);
       store_tile((t + 1) & 1, R);
       load_tile(t + 3, R);
       __syncthreads();
@@ -303,23 +317,31 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
     // and every tile's loads stay older than the next one's, so the loop's wait counts are exact.
     u32x4 R0[CHT], R1[CHT];
     f32x16 accA[SC_QW], accB[SC_QW];
+#pragma unroll
+    for (int r = 0; r < SC_QW; ++r) accA[r] = accB[r] = f32x16{};
     load_tile(0, R0);
     __builtin_amdgcn_sched_barrier(0);
     load_tile(1, R1);
     store_tile(0, R0);
     load_tile(2, R0);
     __syncthreads();
-    int t = 0;
-    for (; t < ntile; t += 2) {
-      iter(t, accA, accB, R1);
-      iter(t + 1, accB, accA, R0);
-    }
-    epi(t - 1, accB);  // the last tile computed (t - 1 is odd: accB)
-    __syncthreads();
-    for (int e = tid; e < SC_QG * chunk_pools; e += 256) {
-      const int qr = e / chunk_pools, i = e - qr * chunk_pools;
-      if (((active >> qr) & 1u) && p_begin + i < min(nc_s[qr], p_end))
-        scores[int64_t(r0 + qr) * ld + p_begin + i] = psb[qr][i];
+    // segments of 32 tiles: their scores collect in psb and are written out (coalesced) after the segment
+    for (int t0 = 0; t0 < ntile; t0 += 32) {
+      const int t1 = min(t0 + 32, ntile);
+      int t = t0;
+      for (; t < t1; t += 2) {
+        iter(t, accA, accB, R1);
+        iter(t + 1, accB, accA, R0);
+      }
+      epi(t - 1, accB);  // the segment's last tile computed (t - 1 is odd: accB)
+      __syncthreads();
+      const int sp0 = p_begin + t0 * 32;  // first pool of the segment
+      for (int e = tid; e < SC_QG * SC_PSEG; e += 256) {
+        const int qr = e / SC_PSEG, i = e - qr * SC_PSEG;
+        if (((active >> qr) & 1u) && sp0 + i < min(nc_s[qr], p_end))
+          scores[int64_t(r0 + qr) * ld + sp0 + i] = psb[qr][i];
+      }
+      __syncthreads();  // psb is written out before the next segment reuses it
     }
   }
 }
