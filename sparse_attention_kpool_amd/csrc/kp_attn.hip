@@ -26,8 +26,9 @@
 //          8g + s/4 and lane i receives channel i of those 4 tokens.
 // Each SIMD runs one S wave and one O wave, so the two products overlap on the matrix core.  S waves keep Q in
 // the same register bank in which O waves keep their accumulators.
-// Splits write unnormalised partials (O, running max, running sum) that a second kernel merges in split
-// order, so results are deterministic.
+// A query's selection is split over several blocks when the batch is small (split s takes every n_split-th
+// selected pool from the s-th on).  Splits write unnormalised partials (O, running max, running sum) that a
+// second kernel merges in split order, so results are deterministic.
 //
 // Bound: HBM (the gather of 1 KiB of bf16 value columns per token feeds 2 x 64 heads x 512 MACs: 128 flop/B,
 // between the VALU and MFMA ridges, hence MFMA for both products).
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     const T* __restrict__ latent, int L, const int32_t* __restrict__ bt, int bt_stride, int log2_pt,
     const T* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int log2P, int k, int H, float scale_log2,
-    int n_split, int blocks_per_split, T* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    int n_split, T* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
   using S = AttnShape<T, V, HT>;
   using E = Elem<T>;
@@ -110,9 +111,12 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
   const int seq = q_seq[qi];
   const int pos = q_pos[qi];
   const int P = 1 << log2P;
-  const int n_slots = n_sel[qi] * P;
-  const int s_begin = sp * blocks_per_split * AT_NT;
-  const int s_end = min(s_begin + blocks_per_split * AT_NT, n_slots);
+  // Split sp takes the selected pools sp, sp + n_split, sp + 2 n_split, ...: interleaved rather than
+  // contiguous, so the blocks of one query read spread-out parts of its (ascending) selection at a time.
+  const int ns_pools = n_sel[qi];
+  const int my_pools = ns_pools > sp ? (ns_pools - sp + n_split - 1) / n_split : 0;
+  const int s_begin = 0;
+  const int s_end = my_pools * P;
 
   if (s_begin >= s_end) {  // an empty split (this query selected fewer tokens)
     if (n_split > 1) {
@@ -133,10 +137,10 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
   // Slot table: cache row of every slot of the split, -1 for a slot past the query (the cut tail pool).  One
   // block-table lookup per pool, done once; in the loop a slot's row is then a single LDS read.
   {
-    const int32_t* qsel = sel + int64_t(qi) * k + (s_begin >> log2P);
+    const int32_t* qsel = sel + int64_t(qi) * k + sp;
     const int pt_mask = (1 << log2_pt) - 1;
     for (int j = tid; j < (nsl >> log2P); j += AT_THREADS) {
-      const int p = qsel[j];
+      const int p = qsel[int64_t(j) * n_split];
       int nt = 0, row = 0;
       if (p >= 0) {
         const int first = p << log2P;
@@ -331,6 +335,8 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
   bool vr[AT_DEPTH][S::CHT];
 #pragma unroll
   for (int d = 0; d < AT_DEPTH; ++d) load_block(d, R[d], vr[d]);
+  // iterations 0 .. nblk (the last one runs O of block nblk - 1), in whole rounds of AT_DEPTH: the up to
+  // AT_DEPTH - 1 iterations past nblk compute nothing and only re-read row 0
   for (int j = 0; j <= nblk; j += AT_DEPTH) {
 #pragma unroll
     for (int d = 0; d < AT_DEPTH; ++d) iter(j + d, R[d], vr[d]);
@@ -433,12 +439,13 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const float* _
 }
 
 int attn_splits(int P, int k, int n_q) {
-  // about one block per CU (256), at most 32 splits, and few enough slots per split for the LDS slot table
-  const int64_t blocks = (int64_t(k) * P + AT_NT - 1) / AT_NT;
+  // about one block per CU (256), at most 32 splits, at least one pool per split, and few enough pools per
+  // split (ceil(k / splits) <= AT_MAXSLOT / P) for the LDS slot table
   int64_t want = (256 + int64_t(n_q) - 1) / (n_q > 0 ? n_q : 1);
-  if (want > blocks) want = blocks;
+  if (want > k) want = k;
   if (want > 32) want = 32;
-  const int64_t min_splits = (blocks * AT_NT + AT_MAXSLOT - 1) / AT_MAXSLOT;
+  const int64_t per_split = AT_MAXSLOT / P;
+  const int64_t min_splits = (int64_t(k) + per_split - 1) / per_split;
   if (want < min_splits) want = min_splits;
   return want < 1 ? 1 : int(want);
 }
@@ -452,8 +459,6 @@ size_t attn_workspace(int P, int k, int H, int V, int n_q) {
 template <class T, int V, int HT>
 static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
   const int ns = attn_splits(a.P, a.k, a.n_q);
-  const int64_t blocks = (int64_t(a.k) * a.P + AT_NT - 1) / AT_NT;
-  const int bps = int((blocks + ns - 1) / ns);
   float* part_o = nullptr;
   float* part_ml = nullptr;
   if (ns > 1) {
@@ -463,7 +468,7 @@ static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
   attn_kernel<T, V, HT><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
       (const T*)a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
-      ilog2(a.P), a.k, a.H, scale_log2, ns, bps, (T*)a.out, a.lse, part_o, part_ml);
+      ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml);
   kp_status st = check_launch("sparse_mla_attn");
   if (st != KP_OK || ns == 1) return st;
   const int hpb = CB_THREADS / (a.V / 4);
