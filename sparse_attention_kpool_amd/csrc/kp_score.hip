@@ -9,18 +9,20 @@
 // channels [g*D/2, (g+1)*D/2).  The epilogue stays in registers: each lane holds 16 heads of one pool, weights
 // them with ReLU, sums in-lane, then adds its partner lane (l ^ 32).
 //
-// Data path: pooled keys stream in 32-pool tiles.  A tile is loaded with fully coalesced 16-byte loads (a wave
-// instruction covers 1 KiB of consecutive pooled rows; the pools of one page are contiguous), kept two tiles
-// ahead in registers, written to LDS and read back in the MFMA operand layout.  Page ids are looked up once
-// per block (never in the tile loop), so no key load waits on another global load.
+// Data path: pooled keys stream in tiles loaded with fully coalesced 16-byte loads (a wave instruction covers
+// 1 KiB of consecutive pooled rows; the pools of one page are contiguous) and read back from LDS in the MFMA
+// operand layout.  Page ids are looked up once per block (never in the tile loop), so no key load waits on
+// another global load.
 //
 // Two kernels:
 //   decode   one query per block; each wave streams its own quarter of the block's pool range through a
-//            private LDS tile, with no block-wide barrier in the loop.
-//   prefill  8 consecutive queries per block that the caller says share a sequence (a prefill chunk); each
-//            32-pool tile is loaded once into LDS and computed by all 4 waves for 2 queries each.  If the
-//            queries turn out to belong to different sequences, the block handles one sequence at a time, so
-//            results never depend on that promise.
+//            private LDS tile (32-pool tiles, kept two ahead in registers), with no block-wide barrier in the
+//            loop.
+//   prefill  16 consecutive queries per block that the caller says share a sequence (a prefill chunk); each
+//            64-pool tile goes straight from global memory into LDS (no register staging), four tiles in
+//            flight, and is computed by all 8 waves for 2 queries each.  If the queries turn out to belong to
+//            different sequences, the block handles one sequence at a time, so results never depend on that
+//            promise.
 //
 // Bound: decode is HBM-bound (the pooled-key stream, 256 B per pool at D = 128 bf16 for 32 x 128 MACs, i.e.
 // 32 flop/B: above the VALU ridge, so the contraction runs on MFMA); prefill is MFMA-bound.
@@ -197,33 +199,76 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------------------------
-// prefill: grid = (n_q / 8) x n_chunks; a block covers `chunk_pools` pools for 8 queries
+// prefill: grid = (n_q / 16) x n_chunks; a block covers `chunk_pools` pools for 16 queries
 // ---------------------------------------------------------------------------------------------------------------
 constexpr int SC_QW = 2;              // queries per wave
-constexpr int SC_QG = 4 * SC_QW;      // queries per block
+constexpr int SC_PWAVES = 8;          // waves per prefill block
+constexpr int SC_PTHREADS = 64 * SC_PWAVES;
+constexpr int SC_QG = SC_PWAVES * SC_QW;  // queries per block
 constexpr int SC_MAXPG = 1024;        // page ids of one block's pool range held in LDS
 constexpr int SC_PMAXCHUNK = 4096;    // pools per block
-constexpr int SC_PSEG = 1024;         // pools whose scores are buffered in LDS between write-outs
+constexpr int SC_PT = 64;             // pools per tile: two 32-pool MFMA column blocks
+constexpr int SC_NBUF = 4;            // LDS tile buffers: tiles t, t + 1 readable, t + 2, t + 3 landing
+
+// LDS image of one 64-pool tile.  Pooled row r holds its 16-byte chunks at positions r * CPR + (c ^ (r & SWZ)):
+// the XOR puts the rows that one B-operand read touches (one chunk of 32 consecutive rows) on distinct bank
+// groups without padding, so each wave-wide direct global-to-LDS load fills 1 KiB of consecutive positions.
+template <class T, int D>
+struct PrefillTile {
+  static constexpr int EPC = 16 / int(sizeof(T));
+  static constexpr int CPR = D / EPC;                  // 16-byte chunks per pooled row
+  static constexpr int TCH = SC_PT * CPR;              // chunks per tile
+  static constexpr int CHT = (TCH + SC_PTHREADS - 1) / SC_PTHREADS;  // direct loads per thread per tile
+  static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;  // XOR mask of a row's chunk positions
+  static constexpr int BYTES = TCH * 16;
+  static_assert(TCH % SC_PTHREADS == 0 || SC_PTHREADS % TCH == 0,
+                "a tile is a whole number of block-wide loads, or part of one");
+  static_assert((SC_PTHREADS / CPR) % (SWZ + 1) == 0, "a thread's chunk position is the same in all its loads");
+};
+
+// One wave-wide 16-byte direct load from global memory into LDS: lane l's 16 bytes at `src` land at LDS byte
+// address lds + 16 * l.  Written as assembly so that the compiler, which cannot tell the LDS buffers of the tile
+// pipeline apart here, adds no waits of its own for it: callers wait with explicit vector-memory counts.  The
+// instruction writes no VGPR; M0 carries the LDS address (one wait state after it is written).
+// (M0 is a reserved register: the compiler warns that clobbering it may be unsafe, but it keeps no value in M0
+// across these statements -- this file makes no other use of it.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding (lgkm and exp free)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <class T, int D>
-__global__ __launch_bounds__(256) void score_prefill_kernel(
+__global__ __launch_bounds__(SC_PTHREADS, 2) void score_prefill_kernel(
     const T* __restrict__ pooled, const int32_t* __restrict__ bt, int bt_stride, int log2_ppp,
     const T* __restrict__ q_idx, const float* __restrict__ w, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int n_q, int Hi, int P, float* __restrict__ scores, int64_t ld,
     int chunk_pools, int n_chunks) {
   using S = ScoreShape<T, D>;
+  using PT = PrefillTile<T, D>;
   using E = Elem<T>;
   using F = typename E::frag;
-  constexpr int CHT = (S::TCH + 255) / 256;  // chunks per thread per tile
-  __shared__ __align__(16) T tiles[2][32 * S::RS];
+  constexpr int CHT = PT::CHT;
+  // separate arrays rather than one: the compiler tells separate LDS variables apart, so a read of one buffer
+  // never waits for the direct loads still landing in another
+  __shared__ __align__(16) char tiles0[PT::BYTES];
+  __shared__ __align__(16) char tiles1[PT::BYTES];
+  __shared__ __align__(16) char tiles2[PT::BYTES];
+  __shared__ __align__(16) char tiles3[PT::BYTES];
+  static_assert(SC_NBUF == 4, "one LDS array per buffer");
+  auto tile_buf = [&](int buf) __attribute__((always_inline)) {
+    return buf == 0 ? tiles0 : buf == 1 ? tiles1 : buf == 2 ? tiles2 : tiles3;
+  };
   __shared__ int page_s[SC_MAXPG];
-  // scores of the current 32-tile segment, written out after it (32 extra slots take the stores of the lanes
-  // that hold no score, so storing needs no branch)
-  __shared__ float psb[SC_QG][SC_PSEG + 32];
   __shared__ int seq_s[SC_QG];
   __shared__ int nc_s[SC_QG];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // the same value, known to be wave-uniform
   const int n = lane & 31, g = lane >> 5;
   const int grp = blockIdx.x / n_chunks;
   const int chunk = blockIdx.x - grp * n_chunks;
@@ -239,6 +284,14 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
   for (int r = 0; r < SC_QW; ++r) {
     const int row = r0 + wave * SC_QW + r;
     score_query_frags<T, D>(q_idx, w, row, row < n_q, Hi, n, g, qa[r], wv[r]);
+  }
+  // byte offset, within a tile, of lane (n, g)'s B operand at k-step s of the first 32-pool column block (the
+  // second block lies 32 rows further; rows 32 apart share their XOR pattern)
+  int koff[S::STEPS];
+#pragma unroll
+  for (int s = 0; s < S::STEPS; ++s) {
+    const int e = g * (D / 2) + s * S::KPL, c = e / PT::EPC;
+    koff[s] = (n * PT::CPR + (c ^ (n & PT::SWZ))) * 16 + (e % PT::EPC) * int(sizeof(T));
   }
   __syncthreads();
 
@@ -260,96 +313,160 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
     pending &= ~active;
     const int p_end = min(p_begin + chunk_pools, ncmax);
     if (p_end <= p_begin) continue;
-    const int ntile = (p_end - p_begin + 31) / 32;
+    const int ntile = (p_end - p_begin + SC_PT - 1) / SC_PT;
     const int pg0 = p_begin >> log2_ppp;
     const int npg = ((p_end - 1) >> log2_ppp) - pg0 + 1;
-    __syncthreads();  // the previous sequence's tiles and page ids are no longer read
-    for (int j = tid; j < npg; j += 256) page_s[j] = bt[int64_t(seq) * bt_stride + pg0 + j];
+    __syncthreads();  // the previous sequence's page ids are no longer read
+    for (int j = tid; j < npg; j += SC_PTHREADS) page_s[j] = bt[int64_t(seq) * bt_stride + pg0 + j];
     __syncthreads();
 
-    auto load_tile = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
+    // Each query row's scores go through a buffer resource sized to the pools this block may write for it
+    // (below min(n_c, p_end); none for a row of another sequence): stores of masked lanes, of pools past the
+    // range and of the pipeline's warm-up step fall outside it and are dropped by the hardware, without a
+    // branch.
+    __amdgpu_buffer_rsrc_t dst[SC_QW];
+#pragma unroll
+    for (int r = 0; r < SC_QW; ++r) {
+      const int qr = wave_u * SC_QW + r;
+      const int lim = ((active >> qr) & 1u) ? min(nc_s[qr], p_end) : 0;
+      const uint64_t base = reinterpret_cast<uint64_t>(scores + int64_t(r0 + qr) * ld);
+      const uint64_t base_u = (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(base >> 32)))) << 32) |
+                              uint32_t(__builtin_amdgcn_readfirstlane(int(base)));
+      dst[r] = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<float*>(base_u), 0,
+                                                 __builtin_amdgcn_readfirstlane(lim) * 4, 0x00020000);
+    }
+    // page ids of the rows this thread loads for tile t (a pool past the range re-reads the first pool)
+    auto tile_pages = [&](int t, int(&pg)[CHT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < CHT; ++i) {
-        const int c = min(tid + 256 * i, S::TCH - 1);
-        int pool = p_begin + t * 32 + c / S::CPR;
+        int pool = p_begin + t * SC_PT + min(i * SC_PTHREADS + tid, PT::TCH - 1) / PT::CPR;
         pool = pool < p_end ? pool : p_begin;
-        const int64_t row = (int64_t(page_s[(pool >> log2_ppp) - pg0]) << log2_ppp) + (pool & ppp_mask);
-        R[i] = *reinterpret_cast<const u32x4*>(pooled + row * D + (c % S::CPR) * S::EPC);
+        pg[i] = page_s[(pool >> log2_ppp) - pg0];
       }
     };
-    auto store_tile = [&](int buf, u32x4(&R)[CHT]) __attribute__((always_inline)) {
+    // tile t into LDS buffer `buf`: CHT wave-wide 16-byte loads straight into LDS per thread
+    auto load_tile = [&](int t, int buf, const int(&pg)[CHT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < CHT; ++i) {
-        const int c = tid + 256 * i;
-        if (c < S::TCH)
-          *reinterpret_cast<u32x4*>(tiles[buf] + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
+        // a tile smaller than one block-wide load is filled by the first waves (a wave-uniform condition)
+        if (PT::TCH < SC_PTHREADS && wave_u * 64 >= PT::TCH) break;
+        const int q = i * SC_PTHREADS + tid, row = q / PT::CPR, c = (q % PT::CPR) ^ (row & PT::SWZ);
+        int pool = p_begin + t * SC_PT + row;
+        pool = pool < p_end ? pool : p_begin;
+        const int64_t prow = (int64_t(pg[i]) << log2_ppp) + (pool & ppp_mask);
+        const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(tile_buf(buf)));  // the LDS offset
+        dma16(pooled + prow * D + c * PT::EPC, lds + uint32_t((i * SC_PTHREADS + wave_u * 64) * 16));
       }
     };
-    auto mma = [&](int t, f32x16(&acc)[SC_QW]) __attribute__((always_inline)) {
-      F kb[S::STEPS];
-      const T* kp = tiles[t & 1] + n * S::RS + g * (D / 2);
+    F kb[S::STEPS];  // B operands of the column block being computed
+    // B operands of one 32-pool column block, read from LDS
+    auto read_kb = [&](const char* kp, F(&kb)[S::STEPS]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int s = 0; s < S::STEPS; ++s) kb[s] = E::frag_load(kp + s * S::KPL);
-      score_mma<T, D, SC_QW>(qa, kb, acc);
+      for (int s = 0; s < S::STEPS; ++s) kb[s] = *reinterpret_cast<const F*>(kp + koff[s]);
     };
-    auto epi = [&](int t, const f32x16(&acc)[SC_QW]) __attribute__((always_inline)) {
+    // One column block: its MFMAs (B operands in kb) interleaved, k-step by k-step, with the epilogue of the
+    // previous block (accumulators `prev`, pools of tile t_prev, block u_prev), and each k-step's B registers
+    // refilled from `next` (the following column block) right after its MFMAs are issued, so every read has a
+    // whole block of MFMAs to land.  A scheduling barrier closes each k-step, which keeps this order.
+    auto half = [&](f32x16(&acc)[SC_QW], const f32x16(&prev)[SC_QW], const char* next, int t_prev, int u_prev)
+                    __attribute__((always_inline)) {
+      constexpr int EPS = 16 / S::STEPS;  // epilogue elements per k-step
+      float part[SC_QW];
+#pragma unroll
+      for (int s = 0; s < S::STEPS; ++s) {
+#pragma unroll
+        for (int r = 0; r < SC_QW; ++r) {
+          acc[r] = mfma32(qa[r][s], kb[s], s == 0 ? f32x16{} : acc[r]);
+#pragma unroll
+          for (int i = s * EPS; i < (s + 1) * EPS; ++i) {  // ReLU as an integer max, as in score_reduce
+            const float x = prev[r][i];
+            const float y = __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+            part[r] = i == 0 ? wv[r][i] * y : part[r] + wv[r][i] * y;
+          }
+        }
+        kb[s] = *reinterpret_cast<const F*>(next + koff[s]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the partner lane l ^ 32 holds the other 16 heads of the pool (as in score_reduce)
+      float sc[SC_QW];
+#pragma unroll
+      for (int r = 0; r < SC_QW; ++r) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, part[r]), 0u, false, false);
+        const uint32_t lo = sw[0], hi = sw[1];
+        sc[r] = __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+      }
+      const int off =
+          (g == 0 && t_prev >= 0) ? (p_begin + t_prev * SC_PT + u_prev * 32 + n) * 4 : int(0x80000000);
+#pragma unroll
+      for (int r = 0; r < SC_QW; ++r)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc[r]), dst[r], off, 0, 0);
+    };
+    auto epi = [&](int t, int u, const f32x16(&acc)[SC_QW]) __attribute__((always_inline)) {
       float sc[SC_QW];
       score_reduce<SC_QW>(acc, wv, sc);
+      const int off = (g == 0 && t >= 0) ? (p_begin + t * SC_PT + u * 32 + n) * 4 : int(0x80000000);
 #pragma unroll
-      for (int r = 0; r < SC_QW; ++r)  // written out only where visible and active
-        psb[wave * SC_QW + r][g == 0 ? (t & 31) * 32 + n : SC_PSEG + n] = sc[r];
+      for (int r = 0; r < SC_QW; ++r)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc[r]), dst[r], off, 0, 0);
     };
-    // Iteration t: the MFMAs of tile t (from LDS buffer t & 1) into one accumulator set while the epilogue of
-    // tile t-1 works on the other, so the matrix cores and the VALU overlap within a wave; then tile t+1 goes
-    // from registers into the other LDS buffer (last read in iteration t-1), tile t+3 starts loading, and one
-    // barrier closes the iteration.
-    auto iter = [&](int t, f32x16(&cur)[SC_QW], const f32x16(&prev)[SC_QW], u32x4(&R)[CHT])
-                    __attribute__((always_inline)) {
-      mma(t, cur);
-      // At t == t0 this writes slot 31 of psb from stale accumulators: the segment's tile 31 overwrites it
-      // later, or (a short last segment) its pools lie past the range and are never written out.  No branch.
-      epi(t - 1, prev);
-      store_tile((t + 1) & 1, R);
-      load_tile(t + 3, R);
-      __syncthreads();
-    };
-    // As in the decode kernel: loads and iterations are unconditional, no global store sits in the tile loop,
-    // and every tile's loads stay older than the next one's, so the loop's wait counts are exact.
-    u32x4 R0[CHT], R1[CHT];
+    // Load pipeline.  Vector-memory operations complete in issue order, so "tile t + 2 has landed" is a count:
+    // iteration t issues the loads of tile t + 3 first, then 2 * SC_QW score stores, and waits until at most
+    // 4 * SC_QW + CHT operations are outstanding -- the previous iteration's stores, this iteration's loads and
+    // stores -- before the barrier that publishes tile t + 2 to all waves.  Tile t + 1 is thus readable during
+    // iteration t, whose second column block refills the B registers with its first.  Scheduling barriers keep
+    // every vector-memory operation inside its part of the iteration (other instructions may cross them).
+    constexpr int PIN = 0x38F;  // ALU, VALU, SALU, MFMA and LDS instructions may cross; vector memory may not
+    int pg[CHT];
     f32x16 accA[SC_QW], accB[SC_QW];
 #pragma unroll
     for (int r = 0; r < SC_QW; ++r) accA[r] = accB[r] = f32x16{};
-    load_tile(0, R0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_tile(1, R1);
-    store_tile(0, R0);
-    load_tile(2, R0);
-    __syncthreads();
-    // segments of 32 tiles: their scores collect in psb and are written out (coalesced) after the segment
-    for (int t0 = 0; t0 < ntile; t0 += 32) {
-      const int t1 = min(t0 + 32, ntile);
-      int t = t0;
-      for (; t < t1; t += 2) {
-        iter(t, accA, accB, R1);
-        iter(t + 1, accB, accA, R0);
-      }
-      epi(t - 1, accB);  // the segment's last tile computed (t - 1 is odd: accB)
-      __syncthreads();
-      const int sp0 = p_begin + t0 * 32;  // first pool of the segment
-      for (int e = tid; e < SC_QG * SC_PSEG; e += 256) {
-        const int qr = e / SC_PSEG, i = e - qr * SC_PSEG;
-        if (((active >> qr) & 1u) && sp0 + i < min(nc_s[qr], p_end))
-          scores[int64_t(r0 + qr) * ld + sp0 + i] = psb[qr][i];
-      }
-      __syncthreads();  // psb is written out before the next segment reuses it
+    tile_pages(0, pg);
+    load_tile(0, 0, pg);
+    tile_pages(1, pg);
+    load_tile(1, 1, pg);
+    tile_pages(2, pg);
+    load_tile(2, 2, pg);
+    epi(-1, 0, accA);  // warm-up: the stores an iteration before the first would have issued (all dropped)
+    epi(-1, 1, accB);
+    tile_pages(3, pg);
+    __builtin_amdgcn_sched_barrier(PIN);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(CHT + 2 * SC_QW));  // tiles 0 and 1
+    __builtin_amdgcn_s_barrier();
+    read_kb(tile_buf(0), kb);
+    constexpr int HALF = 32 * PT::CPR * 16;  // byte offset of the second column block
+    auto iter = [&](int t, int buf) __attribute__((always_inline)) {
+      // buffer (buf + 3) % 4 was last read in iteration t - 1, which every wave has finished
+      load_tile(t + 3, (buf + 3) % SC_NBUF, pg);
+      __builtin_amdgcn_sched_barrier(PIN);
+      tile_pages(t + 4, pg);
+      __builtin_amdgcn_sched_barrier(0);
+      half(accA, accB, tile_buf(buf) + HALF, t - 1, 1);
+      half(accB, accA, tile_buf((buf + 1) % SC_NBUF), t, 0);
+      __builtin_amdgcn_sched_barrier(PIN);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * SC_QW + CHT));  // tile t + 2
+      __builtin_amdgcn_s_barrier();
+    };
+    // unrolled by the buffer count, so every LDS address offset is a constant
+    for (int t = 0;;) {
+      iter(t, 0);
+      if (++t >= ntile) break;
+      iter(t, 1);
+      if (++t >= ntile) break;
+      iter(t, 2);
+      if (++t >= ntile) break;
+      iter(t, 3);
+      if (++t >= ntile) break;
     }
+    epi(ntile - 1, 1, accB);
+    // drain the loads still in flight into LDS before the buffers are reused
+    __builtin_amdgcn_s_waitcnt(0);
   }
 }
 
 template <class T, int D>
 static void launch_score_t(const ScoreLaunch& a, bool prefill, int chunk, int n_chunks, int n_groups,
                            hipStream_t s) {
-  const dim3 grid(unsigned(int64_t(n_groups) * n_chunks)), block(256);
+  const dim3 grid(unsigned(int64_t(n_groups) * n_chunks)), block(prefill ? SC_PTHREADS : 256);
   if (prefill)
     score_prefill_kernel<T, D><<<grid, block, 0, s>>>((const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp,
                                                       (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.n_q, a.Hi, a.P,
@@ -364,13 +481,13 @@ kp_status launch_score(const ScoreLaunch& a, hipStream_t s) {
   const int64_t ncmax = (int64_t(a.max_pos) + 1) / a.P;
   if (a.n_q == 0 || ncmax == 0) return KP_OK;
   const int64_t ppp = int64_t(1) << a.log2_ppp;
-  // prefill shape when the caller promises runs of >= 8 queries of one sequence
-  const bool prefill = a.group >= SC_QG;
+  // prefill shape when the caller promises runs of >= 8 queries of one sequence (a block takes 16)
+  const bool prefill = a.group >= 8;
   const int64_t n_groups = prefill ? (a.n_q + SC_QG - 1) / SC_QG : a.n_q;
-  // pools per block: a multiple of 128 sized for about 4096 (decode) or 2048 (prefill) blocks, at most
+  // pools per block: a multiple of 128 sized for about 4096 (decode) or 1024 (prefill) blocks, at most
   // SC_MAXCHUNK (decode) or SC_PMAXCHUNK (prefill), and (decode) at most 64 pages per wave or (prefill)
   // SC_MAXPG pages per block
-  const int64_t target = prefill ? 2048 : 4096;  // decode: many short blocks even out rows of unequal length
+  const int64_t target = prefill ? 1024 : 4096;  // decode: many short blocks even out rows of unequal length
   int64_t chunk = (ncmax * n_groups + target - 1) / target;
   chunk = ((chunk + 127) / 128) * 128;
   if (chunk < 128) chunk = 128;
