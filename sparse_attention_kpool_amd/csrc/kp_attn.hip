@@ -12,8 +12,11 @@
 // block-table lookup per pool) in LDS, so no gathered load waits on another global load.
 //
 // The 8 waves form a two-stage pipeline over 32-slot blocks, one barrier per block:
-//   load   every thread keeps 16-byte chunks of the V-wide value rows in registers four blocks ahead (a wave
-//          covers one whole 1 KiB row per instruction) and writes them to a 3-deep ring of row-major LDS
+//   load   bf16 rows of 512 value columns (attn_dma_kernel): each wave brings four whole 1 KiB rows per block
+//          straight from global memory into LDS (one wave-wide 16-byte direct load per row, no register
+//          staging), two blocks ahead in a ring of four buffers whose rows are XOR-swizzled so that both
+//          products read them without bank conflicts.  Other shapes (attn_kernel): every thread keeps 16-byte
+//          chunks of the rows in registers four blocks ahead and writes them to a 3-deep ring of padded LDS
 //          buffers.
 //   S      waves 0..3 (S waves), block j: wave w owns heads 16w..16w+15 and computes S^T = C . Q^T on
 //          16x16x32 bf16 MFMA (tokens = M, heads = N, channels = K); its Q fragments stay in registers.  Online
@@ -25,13 +28,17 @@
 //          transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane s points at 4 channels of token
 //          8g + s/4 and lane i receives channel i of those 4 tokens.
 // Each SIMD runs one S wave and one O wave, so the two products overlap on the matrix core.  S waves keep Q in
-// the same register bank in which O waves keep their accumulators.
+// the same register bank in which O waves keep their accumulators.  Without register staging (attn_dma_kernel)
+// S waves keep twelve C-fragment reads in flight ahead of their MFMAs and O waves read a block's C^T and P
+// fragments before theirs, so LDS latency stays off the MFMA chains.
 // A query's selection is split over several blocks when the batch is small (split s takes every n_split-th
 // selected pool from the s-th on).  Splits write unnormalised partials (O, running max, running sum) that a
 // second kernel merges in split order, so results are deterministic.
 //
 // Bound: HBM (the gather of 1 KiB of bf16 value columns per token feeds 2 x 64 heads x 512 MACs: 128 flop/B,
 // between the VALU and MFMA ridges, hence MFMA for both products).
+#include <type_traits>
+
 #include "kp_device.hpp"
 #include "kp_internal.hpp"
 
@@ -55,7 +62,8 @@ struct AttnShape {
   static constexpr int CPR = V / EPC;                                 // chunks per value row
   static constexpr int CHUNKS = AT_NT * CPR;                          // chunks per block
   static constexpr int CHT = (CHUNKS + AT_THREADS - 1) / AT_THREADS;  // chunks per thread per block
-  static constexpr int RS = V + EPC;                                  // LDS row stride (+16 B against conflicts)
+  static constexpr bool SWZ = sizeof(T) == 2 && CPR % 64 == 0;       // XOR-swizzled rows (see attn_swz)
+  static constexpr int RS = SWZ ? V : V + EPC;                        // LDS row stride (else +16 B against conflicts)
   static constexpr int PS = AT_NT + EPC;                              // P row stride
   static constexpr int VW = V / 4;                                    // value channels per O wave
   static constexpr int MT = VW / 16;                                  // 16-channel tiles per O wave
@@ -66,6 +74,48 @@ struct AttnShape {
   static_assert(VW % 16 == 0, "value width must split into 16-channel tiles per O wave");
   static_assert((SK * KPL * int(sizeof(T))) % 16 == 0, "Q fragments fill whole 16-byte units");
 };
+
+// Position of chunk c in LDS row r of a swizzled block: c ^ attn_swz(r), with the permutation
+// pi(r) = 2 (r mod 4) + 8 ((r >> 3) mod 2) + ((r >> 2) mod 2) of the row's last four bits.  Sixteen consecutive rows
+// then put one chunk on sixteen distinct 4-bank groups (the S product's 16-byte reads), and the rows {0..3, 8..11}
+// (or {4..7, 12..15}) that one half-wave's transposed 8-byte reads touch put an aligned 32-byte window on eight
+// distinct 8-bank groups (the O product): both conflict-free in a 64-bank LDS, without padding.  With 1 KiB rows
+// in 256-byte aligned buffers, each read address is a per-lane base XOR a constant.
+__device__ __forceinline__ int attn_swz(int r) { return 2 * (r & 3) + 8 * ((r >> 3) & 1) + ((r >> 2) & 1); }
+
+// LDS byte offset of a pointer into shared memory, and a load from such an offset
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+template <class F>
+__device__ __forceinline__ F lds_load(uint32_t off) {
+  return *reinterpret_cast<__attribute__((address_space(3))) const F*>(uintptr_t(off));
+}
+__device__ __forceinline__ bf16x8 lds_tr_pair(uint32_t o1, uint32_t o2) {
+  const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t(o1)));
+  const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t(o2)));
+  const uint2 u1 = __builtin_bit_cast(uint2, v1), u2 = __builtin_bit_cast(uint2, v2);
+  return __builtin_bit_cast(bf16x8, make_uint4(u1.x, u1.y, u2.x, u2.y));
+}
+
+// One wave-wide 16-byte direct load from global memory into LDS: lane l's 16 bytes at `src` land at LDS byte
+// offset lds + 16 l.  Written as assembly so the compiler adds no waits of its own: the loop waits with explicit
+// vector-memory counts.  The instruction writes no VGPR; M0 carries the LDS offset (one wait state after it is
+// written).  (M0 is a reserved register: the compiler warns that clobbering it may be unsafe, but it keeps no
+// value in M0 across these statements -- this file makes no other use of it.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void attn_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding (lgkm and exp free)
+constexpr int attn_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// 1 KiB of zeros: the source row of a slot with no token (past the split or past the query), so the O product
+// multiplies its zero weight by zeros, never by whatever a cache row holds
+__device__ __align__(16) uint32_t attn_zero_row[256];
 
 // A-operand fragment of C^T (channels c0 .. c0+15 x tokens 8g .. 8g+7 of k-step s) from the row-major block.
 template <class T, int RS>
@@ -80,6 +130,48 @@ __device__ __forceinline__ typename Elem<T>::frag ct_frag(const T* blk, int c0, 
     return __builtin_bit_cast(bf16x8, make_uint4(u1.x, u1.y, u2.x, u2.y));
   } else {
     return blk[(8 * g + s) * RS + c0 + l16];
+  }
+}
+
+// O-wave epilogue: the output of the wave's channels for every head -- normalised (one split) or as an
+// unnormalised partial with its running max and sum (several splits)
+template <class T, int V, int HT>
+__device__ __forceinline__ void attn_write_out(const f32x4 (&bank)[AttnShape<T, V, HT>::NB], int qi, int sp,
+                                               int n_split, int H, int wl, int l16, int g, const float* m_s,
+                                               const float* l_s, T* __restrict__ out, float* __restrict__ lse,
+                                               float* __restrict__ part_o, float* __restrict__ part_ml) {
+  using S = AttnShape<T, V, HT>;
+#pragma unroll
+  for (int nt = 0; nt < HT; ++nt) {
+    const int h = 16 * nt + l16;
+    if (h >= H) continue;
+    const float mh = m_s[h], lh = l_s[h];
+    if (n_split == 1) {
+      const float inv = 1.f / lh;
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt) {
+        const f32x4 o = bank[mt * HT + nt] * inv;
+        T* op = out + (int64_t(qi) * H + h) * V + wl * S::VW + 16 * mt + 4 * g;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        } else {
+          *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+      }
+      if (lse && wl == 0 && g == 0) lse[int64_t(qi) * H + h] = (mh + log2f(lh)) * LN2;
+    } else {
+      const int64_t base = int64_t(qi * n_split + sp) * H + h;
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt) {
+        const f32x4 o = bank[mt * HT + nt];
+        *reinterpret_cast<float4*>(part_o + base * V + wl * S::VW + 16 * mt + 4 * g) =
+            make_float4(o[0], o[1], o[2], o[3]);
+      }
+      if (wl == 0 && g == 0) {
+        part_ml[base * 2 + 0] = mh;
+        part_ml[base * 2 + 1] = lh;
+      }
+    }
   }
 }
 
@@ -352,39 +444,281 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
   }
   __syncthreads();
   if (!o_wave) return;
+  attn_write_out<T, V, HT>(bank, qi, sp, n_split, H, wl, l16, g, m_s, l_s, out, lse, part_o, part_ml);
+}
 
-#pragma unroll
-  for (int nt = 0; nt < HT; ++nt) {
-    const int h = 16 * nt + l16;
-    if (h >= H) continue;
-    const float mh = m_s[h], lh = l_s[h];
-    if (n_split == 1) {
-      const float inv = 1.f / lh;
-#pragma unroll
-      for (int mt = 0; mt < S::MT; ++mt) {
-        const f32x4 o = bank[mt * HT + nt] * inv;
-        T* op = out + (int64_t(qi) * H + h) * V + wl * S::VW + 16 * mt + 4 * g;
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-        } else {
-          *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
-        }
+// ---------------------------------------------------------------------------------------------------------------
+// bf16 latent rows of V = 512 value columns: the same split, slots and two-role pipeline as attn_kernel, with the
+// value rows going straight from global memory into LDS (one wave-wide 16-byte direct load per 1 KiB row, no
+// register staging), two blocks ahead in a ring of four swizzled 32 KiB buffers.  The registers this frees let
+// the S waves keep twelve C-fragment reads in flight ahead of their MFMAs, and the O waves read all of a block's
+// C^T and P fragments before theirs.
+// ---------------------------------------------------------------------------------------------------------------
+constexpr int AD_NBUF = 4;        // LDS block buffers: S reads block j, O reads j - 1, j + 1 and j + 2 land
+constexpr int AD_MAXPOOL = 2048;  // pools of one split held in the LDS pool table
+constexpr int AD_DIST = 12;       // S waves: C-fragment reads in flight ahead of the MFMAs
+
+template <int HT>
+__global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
+    const bf16* __restrict__ latent, int L, const int32_t* __restrict__ bt, int bt_stride, int log2_pt,
+    const bf16* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int log2P, int k, int H, float scale_log2,
+    int n_split, bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  using T = bf16;
+  constexpr int V = 512;
+  using S = AttnShape<T, V, HT>;
+  using E = Elem<T>;
+  using F = typename E::frag;
+  static_assert(S::SWZ && S::RS == V && S::CPR == 64 && S::CHUNKS == 4 * AT_THREADS && S::OK == 1,
+                "one 1 KiB swizzled row per wave instruction, four rows per wave and block");
+  __shared__ __align__(1024) T crm[AD_NBUF][AT_NT * V];
+  __shared__ __align__(16) T ps[2][16 * HT * S::PS];
+  __shared__ int32_t prow_s[AD_MAXPOOL];  // cache row of each pool's first token
+  __shared__ uint8_t pnt_s[AD_MAXPOOL];   // tokens of the pool at or before the query (0: none)
+  __shared__ float alpha_s[2][64];
+  __shared__ uint32_t resc_s[2];
+  __shared__ float m_s[64];
+  __shared__ float l_s[64];
+  __shared__ uint32_t vmask_s[AT_MAXSLOT / AT_NT];  // valid-slot mask of every block of the split
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // the same value, known to be wave-uniform
+  const int l16 = lane & 15, g = lane >> 4;
+  const bool o_wave = wave >= 4;
+  const int wl = wave & 3;  // index within the wave's role
+  const int qi = blockIdx.x / n_split;
+  const int sp = blockIdx.x - qi * n_split;
+  const int seq = q_seq[qi];
+  const int pos = q_pos[qi];
+  const int P = 1 << log2P;
+  // split sp takes the selected pools sp, sp + n_split, sp + 2 n_split, ... (as attn_kernel)
+  // The first selection entry of each thread is loaded right away, with the selection count rather than after
+  // it (an entry past the count is read but not used; every index stays inside the row of k entries).
+  const int32_t* qsel = sel + int64_t(qi) * k + sp;
+  const int kq = (k - sp + n_split - 1) / n_split;  // entries of the row this split strides over
+  const int p_first = tid < kq ? qsel[int64_t(tid) * n_split] : -1;
+  const int ns_pools = n_sel[qi];
+  const int my_pools = ns_pools > sp ? (ns_pools - sp + n_split - 1) / n_split : 0;
+  const int nsl = my_pools * P;  // slots of this split
+
+  if (nsl == 0) {  // an empty split (this query selected fewer tokens)
+    if (n_split > 1) {
+      for (int h = tid; h < H; h += AT_THREADS) {
+        part_ml[(int64_t(qi * n_split + sp) * H + h) * 2 + 0] = -INFINITY;
+        part_ml[(int64_t(qi * n_split + sp) * H + h) * 2 + 1] = 0.f;
       }
-      if (lse && wl == 0 && g == 0) lse[int64_t(qi) * H + h] = (mh + log2f(lh)) * LN2;
     } else {
-      const int64_t base = int64_t(qi * n_split + sp) * H + h;
+      for (int64_t e = tid; e < int64_t(H) * V; e += AT_THREADS) out[int64_t(qi) * H * V + e] = E::from_f32(0.f);
+      if (lse)
+        for (int h = tid; h < H; h += AT_THREADS) lse[int64_t(qi) * H + h] = -INFINITY;
+    }
+    return;
+  }
+  const int nblk = (nsl + AT_NT - 1) / AT_NT;
+
+  // Register bank, as in attn_kernel: Q^T fragments on an S wave (bank[0 .. QB)), accumulators on an O wave.  The
+  // Q loads go out before the pool table's dependent ones.
+  f32x4 bank[S::NB];
 #pragma unroll
-      for (int mt = 0; mt < S::MT; ++mt) {
-        const f32x4 o = bank[mt * HT + nt];
-        *reinterpret_cast<float4*>(part_o + base * V + wl * S::VW + 16 * mt + 4 * g) =
-            make_float4(o[0], o[1], o[2], o[3]);
-      }
-      if (wl == 0 && g == 0) {
-        part_ml[base * 2 + 0] = mh;
-        part_ml[base * 2 + 1] = lh;
-      }
+  for (int b = 0; b < S::NB; ++b) bank[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool s_active = !o_wave && wl < HT;
+  if (s_active) {
+    const int h = 16 * wl + l16;
+    if (h < H) {
+      const T* qp = q + (int64_t(qi) * H + h) * L + g * (V / 4);
+#pragma unroll
+      for (int s = 0; s < S::SK; ++s) bank[s] = __builtin_bit_cast(f32x4, E::frag_load(qp + s * S::KPL));
     }
   }
+  // Pool table: cache row of every pool's first token and how many of its tokens the query sees (the tail pool is
+  // cut at the query), one block-table lookup per pool; and the valid-slot mask of every block, OR-ed over the
+  // 32 / P consecutive lanes that hold the block's pools (no LDS round trip).
+  {
+    const int pt_mask = (1 << log2_pt) - 1;
+    const int ppb = AT_NT >> log2P;  // pools per block (P <= 32)
+    for (int j0 = 0; j0 < my_pools; j0 += AT_THREADS) {
+      const int j = j0 + tid;
+      const bool valid = j < my_pools;
+      const int p = j0 == 0 ? p_first : (valid ? qsel[int64_t(j) * n_split] : -1);
+      int nt = 0, row = 0;
+      if (valid && p >= 0) {
+        const int first = p << log2P;
+        nt = max(min(P, pos - first + 1), 0);
+        if (nt > 0) row = bt[int64_t(seq) * bt_stride + (first >> log2_pt)] * (pt_mask + 1) + (first & pt_mask);
+      }
+      if (valid) {
+        prow_s[j] = row;
+        pnt_s[j] = uint8_t(nt);
+      }
+      uint32_t bits = (nt >= 32 ? 0xffffffffu : (1u << nt) - 1u) << ((j & (ppb - 1)) << log2P);
+      for (int o = 1; o < ppb; o <<= 1) bits |= uint32_t(__shfl_xor(int(bits), o));
+      if (valid && (j & (ppb - 1)) == 0) vmask_s[j / ppb] = bits;
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  __syncthreads();  // pool table and masks ready
+
+  // cache row of slot t (0..31) of block b, or -1 (past the split or past the query)
+  auto slot_entry = [&](int b, int t) __attribute__((always_inline)) -> int {
+    const int rel = b * AT_NT + t;
+    const int pool = min(rel >> log2P, AD_MAXPOOL - 1), w = rel & (P - 1);
+    return (rel < nsl && w < int(pnt_s[pool])) ? prow_s[pool] + w : -1;
+  };
+  __builtin_amdgcn_s_waitcnt(0);  // every prologue load is in: only block loads are in flight from here
+  // rows of the slots this wave loads for block b, one per lane (lane i < CHT: slot CHT w + i), read a whole
+  // iteration before their loads so the table lookups never delay them
+  auto block_rows = [&](int b) __attribute__((always_inline)) -> int {
+    return slot_entry(b, wave_u * S::CHT + (lane & (S::CHT - 1)));
+  };
+  // Block b into buffer b % 4: wave w brings slots 4w .. 4w+3, one row per instruction; lane l takes chunk
+  // l ^ attn_swz(slot) of the row, so LDS position l holds it (see attn_swz).  An invalid slot reads the zero row.
+  auto load_block = [&](int b, int rows) __attribute__((always_inline)) {
+    const uint32_t base = lds_off(crm[b % AD_NBUF]);
+#pragma unroll
+    for (int i = 0; i < S::CHT; ++i) {
+      const int slot = wave_u * S::CHT + i;
+      const int e = __builtin_amdgcn_readlane(rows, i);
+      const int c = lane ^ attn_swz(slot);
+      const void* src = e >= 0 ? static_cast<const void*>(latent + int64_t(e) * L + c * S::EPC)
+                               : static_cast<const void*>(attn_zero_row + 4 * lane);
+      attn_dma16(src, base + uint32_t(slot * V * int(sizeof(T))));
+    }
+  };
+
+  auto s_phase = [&](int j) __attribute__((always_inline)) {
+    const T* blk = crm[j % AD_NBUF];
+    f32x4 sa[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sa[t][0] = sa[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // fragment f = t * SK + s: row 16t + l16, chunk g * CPR/4 + s, at byte (row base + g * CPR/4 * 16 +
+    // 16 attn_swz(l16)) ^ (16 s) (rows 16t + l16 share their last four bits with l16)
+    const uint32_t a0 = lds_off(blk + l16 * S::RS + g * (V / 4)) + 16 * attn_swz(l16);
+    auto rd = [&](int f) __attribute__((always_inline)) -> F {
+      return lds_load<F>((a0 + (f / S::SK) * 16 * S::RS * int(sizeof(T))) ^ (16 * (f % S::SK)));
+    };
+    F cf[AD_DIST];
+#pragma unroll
+    for (int f = 0; f < AD_DIST; ++f) cf[f] = rd(f);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead: the scheduler would sink them to their uses
+#pragma unroll
+    for (int f = 0; f < 2 * S::SK; ++f) {
+      const int t = f / S::SK, s = f % S::SK;
+      sa[t][s & 1] = mfma16(cf[f % AD_DIST], __builtin_bit_cast(F, bank[s]), sa[t][s & 1]);
+      if (f + AD_DIST < 2 * S::SK) cf[f % AD_DIST] = rd(f + AD_DIST);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane holds head 16*wl + l16, slots 16t + 4g + i
+    const uint32_t vm = vmask_s[j];
+    float x[2][4];
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = 16 * t + 4 * g + i;
+        x[t][i] = ((vm >> slot) & 1u) ? (sa[t][0][i] + sa[t][1][i]) * scale_log2 : -INFINITY;
+        lmax = fmaxf(lmax, x[t][i]);
+      }
+    // lazy running max, as in attn_kernel
+    float alpha = 1.f;
+    const bool raise = __ballot(lmax > m_run + LAZY_MAX) != 0;
+    if (raise) {
+      float bmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      const float m_new = (bmax > m_run + LAZY_MAX) ? bmax : m_run;
+      alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      if (g == 0) alpha_s[j & 1][16 * wl + l16] = alpha;
+    }
+    float rsum = 0.f;
+    float pv[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[t][i] = (x[t][i] == -INFINITY) ? 0.f : fast_exp2(x[t][i] - m_run);
+        rsum += pv[t][i];
+      }
+    l_run = l_run * alpha + rsum;
+    T* prow = ps[j & 1] + (16 * wl + l16) * S::PS;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      *reinterpret_cast<uint2*>(prow + 16 * t + 4 * g) =
+          make_uint2(pack_bf16x2(pv[t][0], pv[t][1]), pack_bf16x2(pv[t][2], pv[t][3]));
+    if (lane == 0) reinterpret_cast<uint8_t*>(&resc_s[j & 1])[wl] = raise ? 1 : 0;
+  };
+
+  // the transposed reads of tokens r1 = 8g + l16/4 and r2 = r1 + 4 at channels c0 + 4a (a = l16 mod 4,
+  // c0 = wl * VW + 16 mt) sit at byte base_i ^ (32 mt) of a block, base_i fixed per lane (see attn_swz)
+  uint32_t tb1, tb2;
+  {
+    const int e = l16 >> 2, a = l16 & 3;
+    const int r1 = 8 * g + e, r2 = r1 + 4, x1 = attn_swz(r1), x2 = attn_swz(r2);
+    const uint32_t b = wl * S::VW * 2 + 8 * (a & 1);
+    tb1 = b + r1 * S::RS * 2 + 32 * (x1 >> 1) + 16 * ((a >> 1) ^ (x1 & 1));
+    tb2 = b + r2 * S::RS * 2 + 32 * (x2 >> 1) + 16 * ((a >> 1) ^ (x2 & 1));
+  }
+  auto o_phase = [&](int j) __attribute__((always_inline)) {
+    const uint32_t blk = lds_off(crm[j % AD_NBUF]);
+    const T* pb = ps[j & 1];
+    // rescale only the head tiles whose running max moved
+    const uint32_t rf = resc_s[j & 1];
+    if (rf) {
+#pragma unroll
+      for (int nt = 0; nt < HT; ++nt) {
+        if ((rf >> (8 * nt)) & 0xffu) {
+          const float a = alpha_s[j & 1][16 * nt + l16];
+#pragma unroll
+          for (int mt = 0; mt < S::MT; ++mt) bank[mt * HT + nt] *= a;
+        }
+      }
+    }
+    // O^T[channels of this wave][heads] += C^T . P^T over the block's 32 tokens: all fragments first
+    F bq[HT];
+#pragma unroll
+    for (int nt = 0; nt < HT; ++nt) bq[nt] = E::frag_load(pb + (16 * nt + l16) * S::PS + 8 * g);
+    F av[S::MT];
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt) av[mt] = lds_tr_pair((blk + tb1) ^ (32 * mt), (blk + tb2) ^ (32 * mt));
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < HT; ++nt) bank[mt * HT + nt] = mfma16(av[mt], bq[nt], bank[mt * HT + nt]);
+  };
+
+  // Iteration j: wait for this wave's loads of block j (those of block j + 1 stay in flight), publish it with the
+  // barrier -- after which every wave is past iteration j - 1, so buffer (j + 2) % 4, last read by O(j - 2),
+  // is free -- start block j + 2, then S(j) on S waves and O(j - 1) on O waves.  Loads are unconditional (a
+  // block past the end reads the zero row), so every iteration issues the same count and the wait is exact.
+  load_block(0, block_rows(0));
+  load_block(1, block_rows(1));
+  int rows_next = block_rows(2);
+  for (int j = 0; j <= nblk; ++j) {
+    __builtin_amdgcn_s_waitcnt(attn_vmcnt(S::CHT));
+    __syncthreads();
+    load_block(j + 2, rows_next);
+    rows_next = block_rows(j + 3);
+    if (o_wave) {
+      if (j >= 1) o_phase(j - 1);
+    } else if (s_active && j < nblk) {
+      s_phase(j);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may land in LDS after the block ends
+
+  if (s_active) {
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (g == 0) {
+      m_s[16 * wl + l16] = m_run;
+      l_s[16 * wl + l16] = l_run;
+    }
+  }
+  __syncthreads();
+  if (!o_wave) return;
+  attn_write_out<T, V, HT>(bank, qi, sp, n_split, H, wl, l16, g, m_s, l_s, out, lse, part_o, part_ml);
 }
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s per (query, head), with
@@ -440,11 +774,11 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const float* _
 
 int attn_splits(int P, int k, int n_q) {
   // about one block per CU (256), at most 32 splits, at least one pool per split, and few enough pools per
-  // split (ceil(k / splits) <= AT_MAXSLOT / P) for the LDS slot table
+  // split (ceil(k / splits) <= AT_MAXSLOT / P, and <= AD_MAXPOOL) for the LDS slot and pool tables
   int64_t want = (256 + int64_t(n_q) - 1) / (n_q > 0 ? n_q : 1);
   if (want > k) want = k;
   if (want > 32) want = 32;
-  const int64_t per_split = AT_MAXSLOT / P;
+  const int64_t per_split = AT_MAXSLOT / P < AD_MAXPOOL ? AT_MAXSLOT / P : AD_MAXPOOL;
   const int64_t min_splits = (int64_t(k) + per_split - 1) / per_split;
   if (want < min_splits) want = min_splits;
   return want < 1 ? 1 : int(want);
@@ -466,9 +800,14 @@ static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
     part_ml = part_o + size_t(a.n_q) * ns * a.H * a.V;
   }
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  attn_kernel<T, V, HT><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
-      (const T*)a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
-      ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml);
+  if constexpr (std::is_same<T, bf16>::value && V == 512)
+    attn_dma_kernel<HT><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
+        (const T*)a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
+        ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml);
+  else
+    attn_kernel<T, V, HT><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
+        (const T*)a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
+        ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml);
   kp_status st = check_launch("sparse_mla_attn");
   if (st != KP_OK || ns == 1) return st;
   const int hpb = CB_THREADS / (a.V / 4);
