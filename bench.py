@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the KPool-DSA layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--legs decode,128k,prefill]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--legs decode,128k,long1m,prefill]
 
 A step is one pass of the whole layer -- kpool_compress (pools completing this step) -> dsa_indexer_score ->
 dsa_topk_select -> sparse_mla_attn -- over one batch, enqueued on one stream through the C ABI.
@@ -152,7 +152,7 @@ class Leg:
 
 
 STAGE_KERNELS = {"score": ["kp::score_decode_kernel<kp::bf16, 128>"],
-                 "attend": ["kp::attn_kernel<kp::bf16, 512, 4>", "kp::attn_combine_kernel<kp::bf16>"]}
+                 "attend": ["kp::attn_dma_kernel<4>", "kp::attn_combine_kernel<kp::bf16>"]}
 
 
 def measured_traffic(stage: str):
@@ -246,7 +246,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,128k,prefill,copy")
+    ap.add_argument("--legs", default="decode,128k,long1m,prefill,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=16)
     args = ap.parse_args()
@@ -297,6 +297,18 @@ def main():
         res["decode128k"] = {"tokens_per_s": round(1 / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
                              "hbm_gbs": round(sum(by.values()) / (ms * 1e-3) / 1e9, 1),
                              "stages_ms": {k: round(v, 5) for k, v in st.items()}}
+        leg.free()
+    if "long1m" in legs:
+        print("[bench] long1m leg: 8 sequences at context 1048576", file=sys.stderr, flush=True)
+        w5 = W["long1m"]
+        leg = Leg(w5, copies=2)
+        ms = leg.time_steps(args.steps, args.warmup)
+        st = leg.time_stages(args.steps)
+        by = decode_bytes(w5)
+        gbs = sum(by.values()) / (ms * 1e-3) / 1e9
+        res["long1m"] = {"tokens_per_s": round(w5.n_q / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+                         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "stages_ms": {k: round(v, 5) for k, v in st.items()}, "stage_bytes": by}
         leg.free()
     if "prefill" in legs:
         print("[bench] prefill leg: 4096 queries on 65536 tokens", file=sys.stderr, flush=True)

@@ -267,23 +267,34 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(const uint32_t* 
                                                                 int32_t* __restrict__ sel,
                                                                 int32_t* __restrict__ n_sel) {
   __shared__ TkSync sy;
+  __shared__ int32_t kept[TK_MAXN / 2];  // candidate positions of the kept pools, in output order (b <= k)
   const int q = blockIdx.x;
   int n_c, r, tau, b;
   tk_geometry(q_pos[q], P, k, ld, n_c, r, tau, b);
   int32_t* out = sel + int64_t(q) * k;
   // Every chunk before the row's last non-empty one is longer than b (chunks hold at least 4k pools, or all
-  // 32768) and kept exactly b candidates, so candidate i sits in chunk i / b at i % b.
-  const int bb = max(b, 0);
+  // 32768) and kept exactly b candidates, so candidate i sits in chunk i / b at i % b.  (The quotient comes from
+  // a float reciprocal, corrected to the exact one: i < 2^15, so the estimate is off by at most one.)
+  const int bb = max(b, 1);
   int n2 = 0;
-  for (int c = 0; c < n_chunks; ++c) n2 += min(bb, max(0, min(chunk_len, n_c - c * chunk_len)));
+  for (int c = 0; c < n_chunks; ++c) n2 += min(max(b, 0), max(0, min(chunk_len, n_c - c * chunk_len)));
   const int64_t rowc = int64_t(q) * n_chunks * k;
-  auto cand = [&](int i) __attribute__((always_inline)) -> int64_t { return rowc + int64_t(i / bb) * k + i % bb; };
+  const float inv_bb = 1.f / float(bb);
+  auto cand = [&](int i) __attribute__((always_inline)) -> int64_t {
+    int c = int(float(i) * inv_bb);
+    c -= (c * bb > i) ? 1 : 0;
+    c += ((c + 1) * bb <= i) ? 1 : 0;
+    return rowc + int64_t(c) * k + (i - c * bb);
+  };
   if (b >= n2) {
     for (int i = threadIdx.x; i < n2; i += TK_THREADS) out[i] = cand_idx[cand(i)];
   } else if (b > 0) {
     TkKeys<NJ> K;  // straight from the candidates: every lane issues all its loads at once
     tk_load(K, n2, [&](int i) __attribute__((always_inline)) { return cand_key[cand(i)]; });
-    tk_select(sy, K, b, [&](int at, int i, uint32_t) __attribute__((always_inline)) { out[at] = cand_idx[cand(i)]; });
+    // the selection records positions; the pool ids are then read for all kept pools at once, instead of one
+    // dependent global load per step of the selection's emit loop
+    tk_select(sy, K, b, [&](int at, int i, uint32_t) __attribute__((always_inline)) { kept[at] = i; });
+    for (int at = threadIdx.x; at < b; at += TK_THREADS) out[at] = cand_idx[cand(kept[at])];
   }
   tk_finish(out, n_sel, q, k, max(b, 0), r, tau);
 }
