@@ -723,45 +723,66 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s per (query, head), with
 // M the max of m_s over non-empty splits, summed in split order.  128 threads per block, 4 channels (one float4)
-// per thread, V / 4 threads per head; the partials of four splits are loaded at once, unconditionally (an empty
-// split's O was never written: its weight is 0 and a select drops it).
+// per thread, V / 4 threads per head.  The block first brings every split's (m, l) of its heads into LDS in one
+// parallel pass, one thread per head turns them into weights, then each thread reads its partials eight splits
+// at a time, unconditionally (an empty split's O was never written: its weight is 0 and a select drops it).
 constexpr int CB_THREADS = 128;
+constexpr int CB_MAXSPLIT = 32;  // attn_splits never returns more
 
 template <class T>
 __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml, int n_split,
                                                                   int H, int V, T* __restrict__ out,
                                                                   float* __restrict__ lse) {
+  __shared__ float w_s[CB_THREADS / 16][CB_MAXSPLIT];  // per head of the block (at most CB_THREADS / 16), split
+  __shared__ float l_s[CB_THREADS / 16][CB_MAXSPLIT];
+  __shared__ float inv_s[CB_THREADS / 16], lse_s[CB_THREADS / 16];
   const int tph = V / 4;                    // threads per head
   const int hpb = CB_THREADS / tph;         // heads per block
   const int bpq = (H + hpb - 1) / hpb;      // blocks per query
   const int qi = blockIdx.x / bpq;
-  const int h = (blockIdx.x - qi * bpq) * hpb + int(threadIdx.x) / tph;
-  if (h >= H) return;
-  const int c = (int(threadIdx.x) % tph) * 4;
-  const float* ml = part_ml + (int64_t(qi) * n_split * H + h) * 2;   // split s at ml + s * 2H
-  const float* po = part_o + (int64_t(qi) * n_split * H + h) * V + c; // split s at po + s * H * V
+  const int h0 = (blockIdx.x - qi * bpq) * hpb;
+  const int tid = threadIdx.x;
   const int64_t mls = int64_t(H) * 2, pos_ = int64_t(H) * V;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s)
-    if (ml[s * mls + 1] > 0.f) M = fmaxf(M, ml[s * mls]);
-  float wsum = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto add = [&](float m, float l, f32x4 o) __attribute__((always_inline)) {
-    const float w = l > 0.f ? exp2f(m - M) : 0.f;
-    wsum += l > 0.f ? l * w : 0.f;
-    acc += l > 0.f ? w * o : f32x4{0.f, 0.f, 0.f, 0.f};
-  };
-  int s = 0;
-  for (; s + 4 <= n_split; s += 4) {
-    f32x4 o[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = *reinterpret_cast<const f32x4*>(po + (s + u) * pos_);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) add(ml[(s + u) * mls], ml[(s + u) * mls + 1], o[u]);
+  for (int t = tid; t < hpb * n_split; t += CB_THREADS) {
+    const int hh = t / n_split, sp = t - hh * n_split, h = min(h0 + hh, H - 1);
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + (int64_t(qi) * n_split * H + h) * 2 + sp * mls);
+    w_s[hh][sp] = ml.x;
+    l_s[hh][sp] = ml.y;
   }
-  for (; s < n_split; ++s) add(ml[s * mls], ml[s * mls + 1], *reinterpret_cast<const f32x4*>(po + s * pos_));
-  const float inv = 1.f / wsum;
+  __syncthreads();
+  if (tid < hpb) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < n_split; ++sp)
+      if (l_s[tid][sp] > 0.f) M = fmaxf(M, w_s[tid][sp]);
+    float wsum = 0.f;
+    for (int sp = 0; sp < n_split; ++sp) {
+      const float l = l_s[tid][sp];
+      const float w = l > 0.f ? exp2f(w_s[tid][sp] - M) : 0.f;
+      w_s[tid][sp] = w;
+      wsum += l > 0.f ? l * w : 0.f;
+    }
+    inv_s[tid] = 1.f / wsum;
+    lse_s[tid] = (M + log2f(wsum)) * LN2;
+  }
+  __syncthreads();
+  const int hh = tid / tph, h = h0 + hh;
+  if (h >= H) return;
+  const int c = (tid % tph) * 4;
+  const float* po = part_o + (int64_t(qi) * n_split * H + h) * V + c;  // split s at po + s * H * V
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_split; s0 += 8) {
+    f32x4 o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] = *reinterpret_cast<const f32x4*>(po + min(s0 + u, n_split - 1) * pos_);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = s0 + u;
+      const float w = sp < n_split ? w_s[hh][sp] : 0.f;
+      acc += (sp < n_split && l_s[hh][sp] > 0.f) ? w * o[u] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  const float inv = inv_s[hh];
   T* op = out + (int64_t(qi) * H + h) * V + c;
   if constexpr (sizeof(T) == 2) {
     *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
@@ -769,7 +790,7 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const float* _
   } else {
     *reinterpret_cast<float4*>(op) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   }
-  if (lse && c == 0) lse[int64_t(qi) * H + h] = (M + log2f(wsum)) * LN2;
+  if (lse && c == 0) lse[int64_t(qi) * H + h] = lse_s[hh];
 }
 
 int attn_splits(int P, int k, int n_q) {
@@ -819,6 +840,11 @@ static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
 
 kp_status launch_attn(const AttnLaunch& a, hipStream_t s) {
   if (a.n_q == 0) return KP_OK;
+  if (attn_splits(a.P, a.k, a.n_q) > CB_MAXSPLIT) {
+    set_error("sparse_mla_attn: topk %d pools of %d tokens needs more than %d splits per query", a.k, a.P,
+              CB_MAXSPLIT);
+    return KP_ERR_UNSUPPORTED;
+  }
   if (int64_t(a.n_q) * attn_splits(a.P, a.k, a.n_q) > 0x7fffffff) {
     set_error("sparse_mla_attn: too many queries for one launch");
     return KP_ERR_INVALID_ARG;
