@@ -258,27 +258,42 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(const float* __r
   }
 }
 
-// Step 2 of a two-step row: the final b among the chunks' candidates, taken in chunk order (ascending ids).
-template <int NJ>
+constexpr int TK_TREE_CAND = 8192;  // candidates one merge block takes when a row's chunks are merged in a tree
+
+// Step 2 of a two-step row: the b best among chunk candidates, taken in chunk order (ascending ids).
+//   FINAL   one block per row over all n_chunks chunks: writes the selection (sel, n_sel, tail, padding).
+//   !FINAL  one block per (row, group of `group` consecutive chunks): writes that group's b best candidates
+//           (key, pool id), ascending, in the chunk-candidate layout -- so a row of many chunks is merged as a
+//           tree, and the final merge reads each group as one chunk of group * chunk_len pools.
+// Exact: an element of the row's top b is in the top b of any subset of the row that holds it.
+template <int NJ, bool FINAL>
 __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(const uint32_t* __restrict__ cand_key,
                                                                 const int32_t* __restrict__ cand_idx, int64_t ld,
                                                                 const int32_t* __restrict__ q_pos, int P, int k,
-                                                                int n_chunks, int chunk_len,
+                                                                int n_chunks, int chunk_len, int group,
                                                                 int32_t* __restrict__ sel,
-                                                                int32_t* __restrict__ n_sel) {
+                                                                int32_t* __restrict__ n_sel,
+                                                                uint32_t* __restrict__ grp_key,
+                                                                int32_t* __restrict__ grp_idx) {
   __shared__ TkSync sy;
-  __shared__ int32_t kept[TK_MAXN / 2];  // candidate positions of the kept pools, in output order (b <= k)
-  const int q = blockIdx.x;
+  __shared__ int32_t kept[FINAL ? TK_MAXN / 2 : TK_TREE_CAND / 2];  // candidate positions kept, in order (b <= k)
+  __shared__ uint32_t kept_key[FINAL ? 1 : TK_TREE_CAND / 2];
+  const int n_groups = FINAL ? 1 : (n_chunks + group - 1) / group;
+  const int q = blockIdx.x / n_groups;
+  const int G = blockIdx.x - q * n_groups;
+  const int c0 = FINAL ? 0 : G * group;
+  const int c1 = FINAL ? n_chunks : min(c0 + group, n_chunks);
   int n_c, r, tau, b;
   tk_geometry(q_pos[q], P, k, ld, n_c, r, tau, b);
   int32_t* out = sel + int64_t(q) * k;
+  const int64_t ob = (int64_t(q) * n_groups + G) * k;  // !FINAL: this group's output candidates
   // Every chunk before the row's last non-empty one is longer than b (chunks hold at least 4k pools, or all
-  // 32768) and kept exactly b candidates, so candidate i sits in chunk i / b at i % b.  (The quotient comes from
-  // a float reciprocal, corrected to the exact one: i < 2^15, so the estimate is off by at most one.)
+  // 32768) and kept exactly b candidates, so candidate i sits in chunk c0 + i / b at i % b.  (The quotient comes
+  // from a float reciprocal, corrected to the exact one: i < 2^15, so the estimate is off by at most one.)
   const int bb = max(b, 1);
   int n2 = 0;
-  for (int c = 0; c < n_chunks; ++c) n2 += min(max(b, 0), max(0, min(chunk_len, n_c - c * chunk_len)));
-  const int64_t rowc = int64_t(q) * n_chunks * k;
+  for (int c = c0; c < c1; ++c) n2 += min(max(b, 0), max(0, min(chunk_len, n_c - c * chunk_len)));
+  const int64_t rowc = (int64_t(q) * n_chunks + c0) * k;
   const float inv_bb = 1.f / float(bb);
   auto cand = [&](int i) __attribute__((always_inline)) -> int64_t {
     int c = int(float(i) * inv_bb);
@@ -287,16 +302,33 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(const uint32_t* 
     return rowc + int64_t(c) * k + (i - c * bb);
   };
   if (b >= n2) {
-    for (int i = threadIdx.x; i < n2; i += TK_THREADS) out[i] = cand_idx[cand(i)];
+    for (int i = threadIdx.x; i < n2; i += TK_THREADS) {
+      if constexpr (FINAL) {
+        out[i] = cand_idx[cand(i)];
+      } else {
+        grp_key[ob + i] = cand_key[cand(i)];
+        grp_idx[ob + i] = cand_idx[cand(i)];
+      }
+    }
   } else if (b > 0) {
     TkKeys<NJ> K;  // straight from the candidates: every lane issues all its loads at once
     tk_load(K, n2, [&](int i) __attribute__((always_inline)) { return cand_key[cand(i)]; });
     // the selection records positions; the pool ids are then read for all kept pools at once, instead of one
     // dependent global load per step of the selection's emit loop
-    tk_select(sy, K, b, [&](int at, int i, uint32_t) __attribute__((always_inline)) { kept[at] = i; });
-    for (int at = threadIdx.x; at < b; at += TK_THREADS) out[at] = cand_idx[cand(kept[at])];
+    tk_select(sy, K, b, [&](int at, int i, uint32_t key) __attribute__((always_inline)) {
+      kept[at] = i;
+      if constexpr (!FINAL) kept_key[at] = key;
+    });
+    for (int at = threadIdx.x; at < b; at += TK_THREADS) {
+      if constexpr (FINAL) {
+        out[at] = cand_idx[cand(kept[at])];
+      } else {
+        grp_key[ob + at] = kept_key[at];
+        grp_idx[ob + at] = cand_idx[cand(kept[at])];
+      }
+    }
   }
-  tk_finish(out, n_sel, q, k, max(b, 0), r, tau);
+  if constexpr (FINAL) tk_finish(out, n_sel, q, k, max(b, 0), r, tau);
 }
 
 // Chunk length of the row split (a multiple of 256; n_chunks = 1 means one block per row).  A row longer than
@@ -328,7 +360,9 @@ static int tk_chunks(int P, int k, int n_q, int max_pos) {
 size_t topk_workspace(int P, int k, int n_q, int max_pos) {
   const int nch = tk_chunks(P, k, n_q, max_pos);
   if (nch <= 1) return 0;
-  return size_t(n_q) * nch * k * (sizeof(uint32_t) + sizeof(int32_t));
+  const int group = TK_TREE_CAND / (k > 0 ? k : 1);
+  const int n_groups = (nch > group && group >= 2) ? (nch + group - 1) / group : 0;
+  return size_t(n_q) * (nch + n_groups) * k * (sizeof(uint32_t) + sizeof(int32_t));
 }
 
 // keys per lane for n keys in one block: the smallest of 16, 32, 64 that holds them
@@ -336,6 +370,7 @@ static int tk_nj(int64_t n) { return n <= 16 * 64 * TK_WAVES ? 16 : n <= 32 * 64
 
 template <int NJ>
 static kp_status launch_topk_nj(const TopkLaunch& a, int nch, int clen, int merge_nj, hipStream_t s) {
+  // (nch, clen and merge_nj describe the merge input; a tree merge below replaces them with its groups')
   if (nch <= 1) {
     topk_row_kernel<NJ><<<dim3(unsigned(a.n_q)), dim3(TK_THREADS), 0, s>>>(a.scores, a.ld, a.q_pos, a.P, a.k, a.sel,
                                                                            a.n_sel);
@@ -347,16 +382,32 @@ static kp_status launch_topk_nj(const TopkLaunch& a, int nch, int clen, int merg
       a.scores, a.ld, a.q_pos, a.P, a.k, nch, clen, cand_key, cand_idx);
   kp_status st = check_launch("dsa_topk_select (chunks)");
   if (st != KP_OK) return st;
+  // many chunks of a large k: merge groups of TK_TREE_CAND / k chunks first, then the groups
+  const int group = TK_TREE_CAND / a.k;
+  if (nch > group && group >= 2) {
+    const int n_groups = (nch + group - 1) / group;
+    uint32_t* grp_key = reinterpret_cast<uint32_t*>(cand_idx + size_t(a.n_q) * nch * a.k);
+    int32_t* grp_idx = reinterpret_cast<int32_t*>(grp_key + size_t(a.n_q) * n_groups * a.k);
+    topk_merge_kernel<16, false><<<dim3(unsigned(int64_t(a.n_q) * n_groups)), dim3(TK_THREADS), 0, s>>>(
+        cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k, nch, clen, group, nullptr, nullptr, grp_key, grp_idx);
+    st = check_launch("dsa_topk_select (group merge)");
+    if (st != KP_OK) return st;
+    cand_key = grp_key;
+    cand_idx = grp_idx;
+    nch = n_groups;
+    clen *= group;
+    merge_nj = tk_nj(int64_t(nch) * a.k);
+  }
   const dim3 grid(unsigned(a.n_q)), block(TK_THREADS);
   if (merge_nj == 16)
-    topk_merge_kernel<16><<<grid, block, 0, s>>>(cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k, nch, clen, a.sel,
-                                                 a.n_sel);
+    topk_merge_kernel<16, true><<<grid, block, 0, s>>>(cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k, nch, clen, 1,
+                                                       a.sel, a.n_sel, nullptr, nullptr);
   else if (merge_nj == 32)
-    topk_merge_kernel<32><<<grid, block, 0, s>>>(cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k, nch, clen, a.sel,
-                                                 a.n_sel);
+    topk_merge_kernel<32, true><<<grid, block, 0, s>>>(cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k, nch, clen, 1,
+                                                       a.sel, a.n_sel, nullptr, nullptr);
   else
-    topk_merge_kernel<64><<<grid, block, 0, s>>>(cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k, nch, clen, a.sel,
-                                                 a.n_sel);
+    topk_merge_kernel<64, true><<<grid, block, 0, s>>>(cand_key, cand_idx, a.ld, a.q_pos, a.P, a.k, nch, clen, 1,
+                                                       a.sel, a.n_sel, nullptr, nullptr);
   return check_launch("dsa_topk_select (merge)");
 }
 
