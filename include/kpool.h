@@ -164,6 +164,9 @@ kp_status dsa_topk_select(const kp_dims* dims, const kp_queries* queries, const 
  *   out: device [n_q, H, V] storage dtype (rounded once, nearest-even); lse: device fp32 [n_q, H] or NULL.
  *   Accumulation in fp32; softmax weights enter the value product in the storage dtype.
  *   workspace: device, at least sparse_mla_workspace_size bytes (split-KV partials; NULL when that is 0).
+ *     When a query's selection is split over several blocks (batches too small to fill the GPU), each split's
+ *     unnormalised partial output is stored in the storage dtype before the merge, so the output of such a
+ *     query is rounded twice; the running max and sum stay fp32.
  *   Limit: a query's selection is split over at most 32 blocks of at most min(8192 / P, 2048) pools, so
  *     topk <= 32 * min(8192 / P, 2048) (65536 pools at P = 4), else KP_ERR_UNSUPPORTED.
  *   Errors: KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED (V, H, dtype, topk), KP_ERR_WORKSPACE.

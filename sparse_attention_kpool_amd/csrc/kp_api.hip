@@ -204,7 +204,7 @@ kp_status dsa_topk_select(const kp_dims* dims, const kp_queries* queries, const 
 
 size_t sparse_mla_workspace_size(const kp_dims* dims, const kp_queries* queries) {
   if (!dims || !queries || queries->n_q <= 0 || dims->pool < 1 || dims->topk < 1) return 0;
-  return attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q);
+  return attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)));
 }
 
 kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
@@ -226,7 +226,7 @@ kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_q
   KP_REQUIRE(q && sel && n_sel && out, KP_ERR_INVALID_ARG, "%s: NULL q, sel, n_sel or out", fn);
   KP_REQUIRE(aligned(q) && aligned(sel) && aligned(n_sel) && aligned(out) && (!lse || aligned(lse)),
              KP_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
-  const size_t ws_need = attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q);
+  const size_t ws_need = attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)));
   KP_REQUIRE(ws_bytes >= ws_need && (ws_need == 0 || (workspace && aligned(workspace))), KP_ERR_WORKSPACE,
              "%s: workspace of %zu bytes < %zu required", fn, ws_bytes, ws_need);
   AttnLaunch a{};

@@ -139,7 +139,7 @@ template <class T, int V, int HT>
 __device__ __forceinline__ void attn_write_out(const f32x4 (&bank)[AttnShape<T, V, HT>::NB], int qi, int sp,
                                                int n_split, int H, int wl, int l16, int g, const float* m_s,
                                                const float* l_s, T* __restrict__ out, float* __restrict__ lse,
-                                               float* __restrict__ part_o, float* __restrict__ part_ml) {
+                                               T* __restrict__ part_o, float* __restrict__ part_ml) {
   using S = AttnShape<T, V, HT>;
 #pragma unroll
   for (int nt = 0; nt < HT; ++nt) {
@@ -164,8 +164,12 @@ __device__ __forceinline__ void attn_write_out(const f32x4 (&bank)[AttnShape<T, 
 #pragma unroll
       for (int mt = 0; mt < S::MT; ++mt) {
         const f32x4 o = bank[mt * HT + nt];
-        *reinterpret_cast<float4*>(part_o + base * V + wl * S::VW + 16 * mt + 4 * g) =
-            make_float4(o[0], o[1], o[2], o[3]);
+        T* pp = part_o + base * V + wl * S::VW + 16 * mt + 4 * g;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint2*>(pp) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        } else {
+          *reinterpret_cast<float4*>(pp) = make_float4(o[0], o[1], o[2], o[3]);
+        }
       }
       if (wl == 0 && g == 0) {
         part_ml[base * 2 + 0] = mh;
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     const T* __restrict__ latent, int L, const int32_t* __restrict__ bt, int bt_stride, int log2_pt,
     const T* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int log2P, int k, int H, float scale_log2,
-    int n_split, T* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    int n_split, T* __restrict__ out, float* __restrict__ lse, T* __restrict__ part_o,
     float* __restrict__ part_ml) {
   using S = AttnShape<T, V, HT>;
   using E = Elem<T>;
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
     const bf16* __restrict__ latent, int L, const int32_t* __restrict__ bt, int bt_stride, int log2_pt,
     const bf16* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int log2P, int k, int H, float scale_log2,
-    int n_split, bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    int n_split, bf16* __restrict__ out, float* __restrict__ lse, bf16* __restrict__ part_o,
     float* __restrict__ part_ml) {
   using T = bf16;
   constexpr int V = 512;
@@ -722,67 +726,65 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
 }
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s per (query, head), with
-// M the max of m_s over non-empty splits, summed in split order.  128 threads per block, 4 channels (one float4)
-// per thread, V / 4 threads per head.  The block first brings every split's (m, l) of its heads into LDS in one
-// parallel pass, one thread per head turns them into weights, then each thread reads its partials eight splits
-// at a time, unconditionally (an empty split's O was never written: its weight is 0 and a select drops it).
+// M the max of m_s over non-empty splits, both sums taken in split order.  Each split's O is stored in the cache
+// dtype (rounded once, as the output is), its (m, l) in fp32.  128 threads per block, 4 channels per thread, V / 4
+// threads per head.  Every thread issues the loads of all its splits' partial O and (m, l) at once (PER >= the
+// split count registers of each; an empty split's O was never written, so its value is dropped by a select) and
+// computes its head's weights itself: no LDS, no barrier, one wait on memory.
 constexpr int CB_THREADS = 128;
 constexpr int CB_MAXSPLIT = 32;  // attn_splits never returns more
 
-template <class T>
-__global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const float* __restrict__ part_o,
+template <class T, int PER>
+__global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml, int n_split,
                                                                   int H, int V, T* __restrict__ out,
                                                                   float* __restrict__ lse) {
-  __shared__ float w_s[CB_THREADS / 16][CB_MAXSPLIT];  // per head of the block (at most CB_THREADS / 16), split
-  __shared__ float l_s[CB_THREADS / 16][CB_MAXSPLIT];
-  __shared__ float inv_s[CB_THREADS / 16], lse_s[CB_THREADS / 16];
+  static_assert(PER <= CB_MAXSPLIT, "splits per thread");
+  // raw 4-channel partial: 4 bf16 in two dwords, or 4 floats
+  using Raw = typename std::conditional<sizeof(T) == 2, uint2, f32x4>::type;
   const int tph = V / 4;                    // threads per head
   const int hpb = CB_THREADS / tph;         // heads per block
   const int bpq = (H + hpb - 1) / hpb;      // blocks per query
   const int qi = blockIdx.x / bpq;
-  const int h0 = (blockIdx.x - qi * bpq) * hpb;
   const int tid = threadIdx.x;
-  const int64_t mls = int64_t(H) * 2, pos_ = int64_t(H) * V;
-  for (int t = tid; t < hpb * n_split; t += CB_THREADS) {
-    const int hh = t / n_split, sp = t - hh * n_split, h = min(h0 + hh, H - 1);
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + (int64_t(qi) * n_split * H + h) * 2 + sp * mls);
-    w_s[hh][sp] = ml.x;
-    l_s[hh][sp] = ml.y;
-  }
-  __syncthreads();
-  if (tid < hpb) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < n_split; ++sp)
-      if (l_s[tid][sp] > 0.f) M = fmaxf(M, w_s[tid][sp]);
-    float wsum = 0.f;
-    for (int sp = 0; sp < n_split; ++sp) {
-      const float l = l_s[tid][sp];
-      const float w = l > 0.f ? exp2f(w_s[tid][sp] - M) : 0.f;
-      w_s[tid][sp] = w;
-      wsum += l > 0.f ? l * w : 0.f;
-    }
-    inv_s[tid] = 1.f / wsum;
-    lse_s[tid] = (M + log2f(wsum)) * LN2;
-  }
-  __syncthreads();
-  const int hh = tid / tph, h = h0 + hh;
-  if (h >= H) return;
+  const int h = (blockIdx.x - qi * bpq) * hpb + tid / tph;
   const int c = (tid % tph) * 4;
-  const float* po = part_o + (int64_t(qi) * n_split * H + h) * V + c;  // split s at po + s * H * V
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < n_split; s0 += 8) {
-    f32x4 o[8];
+  const int64_t mls = int64_t(H) * 2, pos_ = int64_t(H) * V;
+  if (h >= H) return;
+  const int64_t row = int64_t(qi) * n_split * H + h;  // split s: O at part_o + (row + s * H) * V, (m, l) likewise
+  const T* po = part_o + row * V + c;
+  const float* pm = part_ml + row * 2;
+  Raw o[PER];
+  float2 ml[PER];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) o[u] = *reinterpret_cast<const f32x4*>(po + min(s0 + u, n_split - 1) * pos_);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int sp = s0 + u;
-      const float w = sp < n_split ? w_s[hh][sp] : 0.f;
-      acc += (sp < n_split && l_s[hh][sp] > 0.f) ? w * o[u] : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < PER; ++u) {
+    if (u < n_split) {
+      o[u] = *reinterpret_cast<const Raw*>(po + u * pos_);
+      ml[u] = *reinterpret_cast<const float2*>(pm + u * mls);
     }
   }
-  const float inv = inv_s[hh];
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (u < n_split && ml[u].y > 0.f) M = fmaxf(M, ml[u].x);
+  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    if (u < n_split && ml[u].y > 0.f) {
+      const float w = exp2f(ml[u].x - M);
+      wsum += ml[u].y * w;
+      f32x4 v;
+      if constexpr (sizeof(T) == 2) {
+        v = f32x4{__uint_as_float(o[u].x << 16), __uint_as_float(o[u].x & 0xffff0000u),
+                  __uint_as_float(o[u].y << 16), __uint_as_float(o[u].y & 0xffff0000u)};
+      } else {
+        v = o[u];
+      }
+      acc += w * v;
+    }
+  }
+  const float inv = 1.f / wsum;
   T* op = out + (int64_t(qi) * H + h) * V + c;
   if constexpr (sizeof(T) == 2) {
     *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
@@ -790,7 +792,7 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const float* _
   } else {
     *reinterpret_cast<float4*>(op) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   }
-  if (lse && c == 0) lse[int64_t(qi) * H + h] = lse_s[hh];
+  if (lse && c == 0) lse[int64_t(qi) * H + h] = (M + log2f(wsum)) * LN2;
 }
 
 int attn_splits(int P, int k, int n_q) {
@@ -805,20 +807,21 @@ int attn_splits(int P, int k, int n_q) {
   return want < 1 ? 1 : int(want);
 }
 
-size_t attn_workspace(int P, int k, int H, int V, int n_q) {
+size_t attn_workspace(int P, int k, int H, int V, int n_q, int esize) {
   const int ns = attn_splits(P, k, n_q);
   if (ns <= 1) return 0;
-  return size_t(n_q) * ns * H * (size_t(V) + 2) * sizeof(float);
+  // partial O in the cache dtype, then (m, l) in fp32 (n_q * ns * H * V * esize is a multiple of 8: V is even)
+  return size_t(n_q) * ns * H * (size_t(V) * esize + 2 * sizeof(float));
 }
 
 template <class T, int V, int HT>
 static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
   const int ns = attn_splits(a.P, a.k, a.n_q);
-  float* part_o = nullptr;
+  T* part_o = nullptr;
   float* part_ml = nullptr;
   if (ns > 1) {
-    part_o = reinterpret_cast<float*>(a.ws);
-    part_ml = part_o + size_t(a.n_q) * ns * a.H * a.V;
+    part_o = reinterpret_cast<T*>(a.ws);
+    part_ml = reinterpret_cast<float*>(part_o + size_t(a.n_q) * ns * a.H * a.V);
   }
   const float scale_log2 = a.scale * 1.4426950408889634f;
   if constexpr (std::is_same<T, bf16>::value && V == 512)
@@ -833,8 +836,12 @@ static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
   if (st != KP_OK || ns == 1) return st;
   const int hpb = CB_THREADS / (a.V / 4);
   const int64_t cblocks = int64_t(a.n_q) * ((a.H + hpb - 1) / hpb);
-  attn_combine_kernel<T><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H, a.V,
-                                                                                (T*)a.out, a.lse);
+  if (ns <= 8)
+    attn_combine_kernel<T, 8><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H, a.V,
+                                                                                   (T*)a.out, a.lse);
+  else
+    attn_combine_kernel<T, CB_MAXSPLIT><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(
+        part_o, part_ml, ns, a.H, a.V, (T*)a.out, a.lse);
   return check_launch("sparse_mla_attn (split merge)");
 }
 

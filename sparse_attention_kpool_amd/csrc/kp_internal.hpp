@@ -77,7 +77,7 @@ struct AttnLaunch {
 };
 // Number of split-KV partitions per query for a call shape (a pure function of its arguments).
 int attn_splits(int P, int k, int n_q);
-size_t attn_workspace(int P, int k, int H, int V, int n_q);
+size_t attn_workspace(int P, int k, int H, int V, int n_q, int esize);
 kp_status launch_attn(const AttnLaunch& a, hipStream_t s);
 
 }  // namespace kp
