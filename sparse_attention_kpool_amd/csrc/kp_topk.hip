@@ -23,6 +23,8 @@
 // desc, index asc) is in the top b of its chunk.  Rows longer than 32768 pools (up to 16 chunks of at most
 // 32768, 16 b <= 32768) always take two steps; so do rows of a small batch, whose chunks then spread over more
 // blocks.
+#include <type_traits>
+
 #include "kp_device.hpp"
 #include "kp_internal.hpp"
 
@@ -32,10 +34,11 @@ constexpr int TK_THREADS = 512;
 constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int TK_MAXN = 32768;          // keys of one block: 64 per lane
 constexpr int TK_MAXCHUNKS = 16;        // chunks of a two-step row
+static_assert(TK_THREADS * 4 == 2048, "every histogram bin has one owner thread");
 
 // LDS state of one selection.
 struct TkSync {
-  uint32_t hist[2048];
+  uint32_t hist[2048];  // 11-bit digits; thread t of TK_THREADS owns bins 4t .. 4t+3
   uint32_t wa[TK_WAVES], wb[TK_WAVES];
   uint32_t digit, remaining;
 };
@@ -63,128 +66,195 @@ __device__ __forceinline__ void tk_load(TkKeys<NJ>& K, int n, Load load) {
   }
 }
 
+// Cross-lane steps on the DPP paths (no LDS): `old` is what a lane keeps when its source lane is outside its
+// 16-lane row.  Controls: quad_perm [1,0,3,2] = 0xB1 and [2,3,0,1] = 0x4E, row_shr:n = 0x110 + n,
+// row_mirror = 0x140, row_half_mirror = 0x141.
+template <int CTRL>
+__device__ __forceinline__ uint32_t tk_dpp(uint32_t old, uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Min and max over the wave (uniform results): within each row by DPP, then the four row values by readlane.
+__device__ __forceinline__ void tk_wave_minmax(uint32_t& mn, uint32_t& mx) {
+  mn = min(mn, tk_dpp<0xB1>(0xFFFFFFFFu, mn));
+  mx = max(mx, tk_dpp<0xB1>(0u, mx));
+  mn = min(mn, tk_dpp<0x4E>(0xFFFFFFFFu, mn));
+  mx = max(mx, tk_dpp<0x4E>(0u, mx));
+  mn = min(mn, tk_dpp<0x141>(0xFFFFFFFFu, mn));
+  mx = max(mx, tk_dpp<0x141>(0u, mx));
+  mn = min(mn, tk_dpp<0x140>(0xFFFFFFFFu, mn));
+  mx = max(mx, tk_dpp<0x140>(0u, mx));
+  mn = min(min(uint32_t(__builtin_amdgcn_readlane(int(mn), 0)), uint32_t(__builtin_amdgcn_readlane(int(mn), 16))),
+           min(uint32_t(__builtin_amdgcn_readlane(int(mn), 32)), uint32_t(__builtin_amdgcn_readlane(int(mn), 48))));
+  mx = max(max(uint32_t(__builtin_amdgcn_readlane(int(mx), 0)), uint32_t(__builtin_amdgcn_readlane(int(mx), 16))),
+           max(uint32_t(__builtin_amdgcn_readlane(int(mx), 32)), uint32_t(__builtin_amdgcn_readlane(int(mx), 48))));
+}
+
+// Inclusive prefix sum over the lanes of the wave; `total` gets the wave's sum (uniform).
+__device__ __forceinline__ uint32_t tk_wave_scan(uint32_t v, uint32_t& total) {
+  v += tk_dpp<0x111>(0u, v);
+  v += tk_dpp<0x112>(0u, v);
+  v += tk_dpp<0x114>(0u, v);
+  v += tk_dpp<0x118>(0u, v);  // inclusive within each 16-lane row
+  const uint32_t r0 = uint32_t(__builtin_amdgcn_readlane(int(v), 15));
+  const uint32_t r1 = uint32_t(__builtin_amdgcn_readlane(int(v), 31));
+  const uint32_t r2 = uint32_t(__builtin_amdgcn_readlane(int(v), 47));
+  const uint32_t r3 = uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+  const int row = (threadIdx.x & 63) >> 4;
+  total = r0 + r1 + r2 + r3;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // Selects the `budget` largest of the block's n keys (0 < budget < n) and calls emit(out_pos, i, key) for each
 // kept index i, out_pos ascending with i.
 template <int NJ, class Emit>
 __device__ void tk_select(TkSync& sy, const TkKeys<NJ>& K, int budget, Emit emit) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   auto valid = [&](int j) __attribute__((always_inline)) { return 64 * j + lane < K.cnt; };
+  // thread t owns bins 4t .. 4t+3: it zeroes them here and, after reading them, in every pass
+  u32x4* own = reinterpret_cast<u32x4*>(sy.hist) + tid;
+  *own = u32x4{0u, 0u, 0u, 0u};
 
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     mn = min(mn, valid(j) ? K.k[j] : 0xFFFFFFFFu);
-    mx = max(mx, valid(j) ? K.k[j] : 0u);
+    mx = max(mx, K.k[j]);  // slots past cnt hold 0
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    mn = min(mn, uint32_t(__shfl_xor(int(mn), off)));
-    mx = max(mx, uint32_t(__shfl_xor(int(mx), off)));
-  }
+  tk_wave_minmax(mn, mx);
   if (lane == 0) {
     sy.wa[wv] = mn;
     sy.wb[wv] = mx;
   }
-  __syncthreads();
+  __syncthreads();  // also orders the zeroing of the bins before the first pass's atomics
 #pragma unroll
   for (int w = 0; w < TK_WAVES; ++w) {
     mn = min(mn, sy.wa[w]);
     mx = max(mx, sy.wb[w]);
   }
-  __syncthreads();
   // bits [0, lo) vary; bits at and above lo are common to every key and fixed in `prefix`
   int lo = (mn == mx) ? 0 : 32 - __clz(int(mn ^ mx));
   uint32_t mask = lo == 32 ? 0u : ~((1u << lo) - 1u);
   uint32_t prefix = mn & mask;
   uint32_t remaining = uint32_t(budget);
+  // wa / wb are written next after a pass's first barrier, which every thread reaches after the reads above;
+  // with no pass, the compaction writes them: wait for the reads here
+  if (lo == 0) __syncthreads();
+  // Each pass: histogram of the next (up to) 11 bits of the keys that match `prefix` (LDS integer atomics, so
+  // their order does not matter); every thread reads its 4 bins and zeroes them for the next pass; a block-wide
+  // prefix over the threads (thread order = digit order) finds the bin where the count from the top reaches
+  // `remaining`.  Three barriers per pass: digit / remaining are written next two barriers later.  Slots past
+  // cnt take part as keys of value 0: below every other key, they never move the budget-th largest key while
+  // budget < cnt, and the compaction tells them apart when that key is 0.
   while (lo > 0) {
     const int width = min(11, lo);
     const int shift = lo - width;
     const uint32_t dmask = (1u << width) - 1u;
-    for (int j = tid; j < 2048; j += TK_THREADS) sy.hist[j] = 0;
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      if (valid(j) && (K.k[j] & mask) == prefix) atomicAdd(&sy.hist[(K.k[j] >> shift) & dmask], 1u);
+      if ((K.k[j] & mask) == prefix) atomicAdd(&sy.hist[(K.k[j] >> shift) & dmask], 1u);
     __syncthreads();
-    // thread t owns digits 4t .. 4t+3; `above` counts keys with a higher digit than its range
-    uint32_t c[4], mine = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = 4 * tid + j;
-      c[j] = d <= int(dmask) ? sy.hist[d] : 0u;
-      mine += c[j];
-    }
-    // inclusive prefix over threads (thread order = digit order), then count from the top
-    uint32_t inc = mine;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t u = uint32_t(__shfl_up(int(inc), off));
-      if (lane >= off) inc += u;
-    }
-    if (lane == 63) sy.wa[wv] = inc;
+    const bool owns = 4 * tid <= int(dmask);
+    const u32x4 c = owns ? *own : u32x4{0u, 0u, 0u, 0u};
+    if (owns) *own = u32x4{0u, 0u, 0u, 0u};
+    const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+    uint32_t wtot;
+    const uint32_t inc = tk_wave_scan(mine, wtot);
+    if (lane == 0) sy.wa[wv] = wtot;
     __syncthreads();
     uint32_t before = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < TK_WAVES; ++w) {
-      before += (w < wv) ? sy.wa[w] : 0u;
-      total += sy.wa[w];
+      const uint32_t t = sy.wa[w];
+      before += (w < wv) ? t : 0u;
+      total += t;
     }
-    const uint32_t above = total - (before + inc);
+    const uint32_t above = total - (before + inc);  // keys in higher bins than this thread's
     if (above < remaining && remaining <= above + mine) {
       uint32_t acc = above;
-      for (int j = 3; j >= 0; --j) {
-        if (acc + c[j] >= remaining) {
-          sy.digit = uint32_t(4 * tid + j);
-          sy.remaining = remaining - acc;
-          break;
+      int d = 3;
+      if (acc + c[3] < remaining) {
+        acc += c[3];
+        d = 2;
+        if (acc + c[2] < remaining) {
+          acc += c[2];
+          d = 1;
+          if (acc + c[1] < remaining) {
+            acc += c[1];
+            d = 0;
+          }
         }
-        acc += c[j];
       }
+      sy.digit = uint32_t(4 * tid + d);
+      sy.remaining = remaining - acc;
     }
     __syncthreads();
     prefix |= sy.digit << shift;
     mask |= dmask << shift;
     remaining = sy.remaining;
     lo = shift;
-    __syncthreads();
   }
   const uint32_t T = prefix;
   const uint32_t need_eq = remaining;
 
-  // compaction: per-wave counts, one exchange, then each wave emits its range in index order
-  uint32_t gt = 0, eq = 0;
+  // compaction: per-wave counts of keys >= T and == T, one exchange, then each wave emits its range in index
+  // order.  Slots past cnt hold 0, so they need telling apart only when T is 0.
+  auto compact = [&](auto check) __attribute__((always_inline)) {
+    constexpr bool CHECK = decltype(check)::value;
+    auto in = [&](int j) __attribute__((always_inline)) { return CHECK ? valid(j) : true; };
+    uint32_t ge = 0, eq = 0;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    gt += uint32_t(__popcll(__ballot(valid(j) && K.k[j] > T)));
-    eq += uint32_t(__popcll(__ballot(valid(j) && K.k[j] == T)));
-  }
-  if (lane == 0) {
-    sy.wa[wv] = gt;
-    sy.wb[wv] = eq;
-  }
-  __syncthreads();
-  uint32_t gt_before = 0, eq_before = 0;
-#pragma unroll
-  for (int w = 0; w < TK_WAVES; ++w)
-    if (w < wv) {
-      gt_before += sy.wa[w];
-      eq_before += sy.wb[w];
+    for (int j = 0; j < NJ; ++j) {
+      ge += uint32_t(__popcll(__ballot(in(j) && K.k[j] >= T)));
+      eq += uint32_t(__popcll(__ballot(in(j) && K.k[j] == T)));
     }
-  // kept before this wave: all greater keys plus the first need_eq equal keys in index order
-  uint32_t at = gt_before + min(eq_before, need_eq);
-  uint32_t eq_seen = eq_before;
-  const uint64_t below = (uint64_t(1) << lane) - 1;
+    if (lane == 0) {
+      sy.wa[wv] = ge;
+      sy.wb[wv] = eq;
+    }
+    __syncthreads();
+    uint32_t ge_before = 0, eq_before = 0, eq_total = 0;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const bool is_eq = valid(j) && K.k[j] == T;
-    const uint64_t eqm = __ballot(is_eq);
-    const uint32_t eq_rank = eq_seen + uint32_t(__popcll(eqm & below));
-    const bool take = (valid(j) && K.k[j] > T) || (is_eq && eq_rank < need_eq);
-    const uint64_t tm = __ballot(take);
-    if (take) emit(int(at + uint32_t(__popcll(tm & below))), K.lo + 64 * j + lane, K.k[j]);
-    at += uint32_t(__popcll(tm));
-    eq_seen += uint32_t(__popcll(eqm));
+    for (int w = 0; w < TK_WAVES; ++w) {
+      const uint32_t a = sy.wa[w], e = sy.wb[w];
+      ge_before += (w < wv) ? a : 0u;
+      eq_before += (w < wv) ? e : 0u;
+      eq_total += e;
+    }
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    if (NJ < 64 && need_eq == eq_total) {
+      // every copy of T is kept: a key is kept iff it is >= T (blocks of 64 keys per lane have registers for one
+      // emit loop only and always take the general one)
+      uint32_t at = ge_before;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bool take = in(j) && K.k[j] >= T;
+        const uint64_t tm = __ballot(take);
+        if (take) emit(int(at + uint32_t(__popcll(tm & below))), K.lo + 64 * j + lane, K.k[j]);
+        at += uint32_t(__popcll(tm));
+      }
+    } else {
+      // kept before this wave: all greater keys plus the first need_eq equal keys in index order
+      uint32_t at = (ge_before - eq_before) + min(eq_before, need_eq);
+      uint32_t eq_seen = eq_before;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bool is_eq = in(j) && K.k[j] == T;
+        const uint64_t eqm = __ballot(is_eq);
+        const uint32_t eq_rank = eq_seen + uint32_t(__popcll(eqm & below));
+        const bool take = K.k[j] > T || (is_eq && eq_rank < need_eq);  // a slot past cnt is never > T
+        const uint64_t tm = __ballot(take);
+        if (take) emit(int(at + uint32_t(__popcll(tm & below))), K.lo + 64 * j + lane, K.k[j]);
+        at += uint32_t(__popcll(tm));
+        eq_seen += uint32_t(__popcll(eqm));
+      }
+    }
+  };
+  if constexpr (NJ >= 64) {
+    compact(std::true_type{});  // one form only, for the same reason
+  } else {
+    if (T == 0u) compact(std::true_type{});
+    else compact(std::false_type{});
   }
   __syncthreads();
 }
@@ -234,6 +304,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(const float* __r
                                                                 uint32_t* __restrict__ cand_key,
                                                                 int32_t* __restrict__ cand_idx) {
   __shared__ TkSync sy;
+  __shared__ __align__(16) uint32_t st_key[TK_MAXN / 2];  // b <= k <= TK_MAXN / 2 for a row of >= 2 chunks
+  __shared__ __align__(16) uint32_t st_idx[TK_MAXN / 2];
   const int q = blockIdx.x / n_chunks;
   const int c = blockIdx.x - q * n_chunks;
   int n_c, r, tau, b;
@@ -251,10 +323,31 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(const float* __r
   } else {
     TkKeys<NJ> K;
     tk_load(K, len, [&](int i) __attribute__((always_inline)) { return score_key(row[i]); });
+    // the kept candidates are staged in LDS and then written out with whole-row 16-byte stores
     tk_select(sy, K, b, [&](int at, int i, uint32_t key) __attribute__((always_inline)) {
-      cand_key[cb + at] = key;
-      cand_idx[cb + at] = base + i;
+      st_key[at] = key;
+      st_idx[at] = base + i;
     });
+    uint32_t* ok = cand_key + cb;
+    uint32_t* oi = reinterpret_cast<uint32_t*>(cand_idx + cb);
+    if ((cb & 3) == 0) {
+      for (int i = 4 * threadIdx.x; i < b; i += 4 * TK_THREADS) {
+        if (i + 4 <= b) {
+          *reinterpret_cast<u32x4*>(ok + i) = *reinterpret_cast<const u32x4*>(st_key + i);
+          *reinterpret_cast<u32x4*>(oi + i) = *reinterpret_cast<const u32x4*>(st_idx + i);
+        } else {
+          for (int e = i; e < b; ++e) {
+            ok[e] = st_key[e];
+            oi[e] = st_idx[e];
+          }
+        }
+      }
+    } else {
+      for (int i = threadIdx.x; i < b; i += TK_THREADS) {
+        ok[i] = st_key[i];
+        oi[i] = st_idx[i];
+      }
+    }
   }
 }
 
