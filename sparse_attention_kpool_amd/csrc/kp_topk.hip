@@ -105,8 +105,8 @@ __device__ __forceinline__ uint32_t tk_wave_scan(uint32_t v, uint32_t& total) {
   return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
-// Selects the `budget` largest of the block's n keys (0 < budget < n) and calls emit(out_pos, i, key) for each
-// kept index i, out_pos ascending with i.
+// Selects the `budget` largest of the block's n keys (0 < budget < n) and calls emit(out_pos, j, i, key) for each
+// kept index i (held in the caller's register slot j), out_pos ascending with i.
 template <int NJ, class Emit>
 __device__ void tk_select(TkSync& sy, const TkKeys<NJ>& K, int budget, Emit emit) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -230,7 +230,7 @@ __device__ void tk_select(TkSync& sy, const TkKeys<NJ>& K, int budget, Emit emit
       for (int j = 0; j < NJ; ++j) {
         const bool take = in(j) && K.k[j] >= T;
         const uint64_t tm = __ballot(take);
-        if (take) emit(int(at + uint32_t(__popcll(tm & below))), K.lo + 64 * j + lane, K.k[j]);
+        if (take) emit(int(at + uint32_t(__popcll(tm & below))), j, K.lo + 64 * j + lane, K.k[j]);
         at += uint32_t(__popcll(tm));
       }
     } else {
@@ -244,7 +244,7 @@ __device__ void tk_select(TkSync& sy, const TkKeys<NJ>& K, int budget, Emit emit
         const uint32_t eq_rank = eq_seen + uint32_t(__popcll(eqm & below));
         const bool take = K.k[j] > T || (is_eq && eq_rank < need_eq);  // a slot past cnt is never > T
         const uint64_t tm = __ballot(take);
-        if (take) emit(int(at + uint32_t(__popcll(tm & below))), K.lo + 64 * j + lane, K.k[j]);
+        if (take) emit(int(at + uint32_t(__popcll(tm & below))), j, K.lo + 64 * j + lane, K.k[j]);
         at += uint32_t(__popcll(tm));
         eq_seen += uint32_t(__popcll(eqm));
       }
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const float* __res
   } else if (b > 0) {
     TkKeys<NJ> K;
     tk_load(K, n_c, [&](int i) __attribute__((always_inline)) { return score_key(row[i]); });
-    tk_select(sy, K, b, [&](int at, int i, uint32_t) __attribute__((always_inline)) { out[at] = i; });
+    tk_select(sy, K, b, [&](int at, int, int i, uint32_t) __attribute__((always_inline)) { out[at] = i; });
   }
   tk_finish(out, n_sel, q, k, max(b, 0), r, tau);
 }
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(const float* __r
     TkKeys<NJ> K;
     tk_load(K, len, [&](int i) __attribute__((always_inline)) { return score_key(row[i]); });
     // the kept candidates are staged in LDS and then written out with whole-row 16-byte stores
-    tk_select(sy, K, b, [&](int at, int i, uint32_t key) __attribute__((always_inline)) {
+    tk_select(sy, K, b, [&](int at, int, int i, uint32_t key) __attribute__((always_inline)) {
       st_key[at] = key;
       st_idx[at] = base + i;
     });
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(const uint32_t* 
                                                                 uint32_t* __restrict__ grp_key,
                                                                 int32_t* __restrict__ grp_idx) {
   __shared__ TkSync sy;
-  __shared__ int32_t kept[FINAL ? TK_MAXN / 2 : TK_TREE_CAND / 2];  // candidate positions kept, in order (b <= k)
+  __shared__ int32_t kept[FINAL ? TK_MAXN / 2 : TK_TREE_CAND / 2];  // kept pool ids (or positions), in order
   __shared__ uint32_t kept_key[FINAL ? 1 : TK_TREE_CAND / 2];
   const int n_groups = FINAL ? 1 : (n_chunks + group - 1) / group;
   const int q = blockIdx.x / n_groups;
@@ -406,18 +406,37 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(const uint32_t* 
   } else if (b > 0) {
     TkKeys<NJ> K;  // straight from the candidates: every lane issues all its loads at once
     tk_load(K, n2, [&](int i) __attribute__((always_inline)) { return cand_key[cand(i)]; });
-    // the selection records positions; the pool ids are then read for all kept pools at once, instead of one
-    // dependent global load per step of the selection's emit loop
-    tk_select(sy, K, b, [&](int at, int i, uint32_t key) __attribute__((always_inline)) {
-      kept[at] = i;
-      if constexpr (!FINAL) kept_key[at] = key;
-    });
-    for (int at = threadIdx.x; at < b; at += TK_THREADS) {
-      if constexpr (FINAL) {
-        out[at] = cand_idx[cand(kept[at])];
-      } else {
-        grp_key[ob + at] = kept_key[at];
-        grp_idx[ob + at] = cand_idx[cand(kept[at])];
+    if constexpr (NJ <= 32) {
+      // the pool ids are loaded with the keys, so the kept ones go straight to LDS and leave in order with
+      // coalesced stores
+      TkKeys<NJ> Ix;
+      tk_load(Ix, n2, [&](int i) __attribute__((always_inline)) { return uint32_t(cand_idx[cand(i)]); });
+      tk_select(sy, K, b, [&](int at, int j, int, uint32_t key) __attribute__((always_inline)) {
+        kept[at] = int32_t(Ix.k[j]);
+        if constexpr (!FINAL) kept_key[at] = key;
+      });
+      for (int at = threadIdx.x; at < b; at += TK_THREADS) {
+        if constexpr (FINAL) {
+          out[at] = kept[at];
+        } else {
+          grp_key[ob + at] = kept_key[at];
+          grp_idx[ob + at] = kept[at];
+        }
+      }
+    } else {
+      // no registers for the ids: the selection records positions, then the ids of all kept pools are read at
+      // once
+      tk_select(sy, K, b, [&](int at, int, int i, uint32_t key) __attribute__((always_inline)) {
+        kept[at] = i;
+        if constexpr (!FINAL) kept_key[at] = key;
+      });
+      for (int at = threadIdx.x; at < b; at += TK_THREADS) {
+        if constexpr (FINAL) {
+          out[at] = cand_idx[cand(kept[at])];
+        } else {
+          grp_key[ob + at] = kept_key[at];
+          grp_idx[ob + at] = cand_idx[cand(kept[at])];
+        }
       }
     }
   }
