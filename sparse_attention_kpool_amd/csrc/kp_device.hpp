@@ -99,4 +99,29 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Cross-lane step on the DPP paths (no LDS): `old` is what a lane keeps when its source lane is outside its 16-lane
+// row.  Controls: quad_perm [1,0,3,2] = 0xB1 and [2,3,0,1] = 0x4E, row_shr:n = 0x110 + n, row_mirror = 0x140,
+// row_half_mirror = 0x141.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Inclusive prefix sum over the lanes of the wave (row scans by DPP, then the row totals by readlane); `total`
+// gets the wave's sum (uniform).
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v, uint32_t& total) {
+  v += dpp_u32<0x111>(0u, v);
+  v += dpp_u32<0x112>(0u, v);
+  v += dpp_u32<0x114>(0u, v);
+  v += dpp_u32<0x118>(0u, v);  // inclusive within each 16-lane row
+  const uint32_t r0 = uint32_t(__builtin_amdgcn_readlane(int(v), 15));
+  const uint32_t r1 = uint32_t(__builtin_amdgcn_readlane(int(v), 31));
+  const uint32_t r2 = uint32_t(__builtin_amdgcn_readlane(int(v), 47));
+  const uint32_t r3 = uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+  const int row = (threadIdx.x & 63) >> 4;
+  total = r0 + r1 + r2 + r3;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 }  // namespace kp
+

@@ -15,9 +15,9 @@
 // another global load.
 //
 // Two kernels:
-//   decode   one query per block; each wave streams its own quarter of the block's pool range through a
-//            private LDS tile (32-pool tiles, kept two ahead in registers), with no block-wide barrier in the
-//            loop.
+//   decode   a persistent grid (two 4-wave blocks per compute unit): the 32-pool tiles of all queries are split
+//            into one contiguous range per wave of about equal length; a wave streams its range query by query
+//            through a private LDS tile (tiles kept two ahead in registers), with no block-wide barrier.
 //   prefill  16 consecutive queries per block that the caller says share a sequence (a prefill chunk); each
 //            64-pool tile goes straight from global memory into LDS (no register staging), four tiles in
 //            flight, and is computed by all 8 waves for 2 queries each.  If the queries turn out to belong to
@@ -110,92 +110,151 @@ __device__ __forceinline__ void score_tiles(const typename Elem<T>::frag (&qa)[Q
   score_reduce<QW>(acc, wv, sc);
 }
 
-constexpr int SC_MAXCHUNK = 4096;    // pools per decode block (each wave's scores are buffered in LDS)
+constexpr int SC_MAXCHUNK = 4096;    // decode: scores buffered in LDS per block (SC_MAXCHUNK / 4 per wave)
+constexpr int SC_DBLOCKS_PER_CU = 2;  // decode: persistent blocks of 4 waves per compute unit
 
 // ---------------------------------------------------------------------------------------------------------------
-// decode: grid = n_q x n_chunks; a block covers `chunk_pools` pools of one query, a wave `chunk_pools / 4`
-// (at most 64 pages, so the wave's page ids fit one register per lane)
+// decode: a persistent grid; the 32-pool tiles of all queries, taken query by query, are split into one contiguous
+// range per wave of about equal length, so rows of any length mix keep every wave streaming.  A wave covers its
+// range as segments, one per query it touches (and at most 31 tiles and 63 pages each): per segment it loads the
+// query's fragments and page ids once, streams the tiles through its private LDS tile two ahead in registers, and
+// writes the segment's scores out.  No block-wide barrier: waves run independently.
 // ---------------------------------------------------------------------------------------------------------------
 template <class T, int D>
 __global__ __launch_bounds__(256) void score_decode_kernel(
     const T* __restrict__ pooled, const int32_t* __restrict__ bt, int bt_stride, int log2_ppp,
     const T* __restrict__ q_idx, const float* __restrict__ w, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_pos, int Hi, int P, float* __restrict__ scores, int64_t ld, int chunk_pools,
-    int n_chunks) {
+    const int32_t* __restrict__ q_pos, int n_q, int Hi, int P, float* __restrict__ scores, int64_t ld) {
   using S = ScoreShape<T, D>;
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int CHT = S::TCH / 64;  // chunks per lane per tile
   __shared__ __align__(16) T tiles[4][32 * S::RS];
-  __shared__ float sbuf[4][SC_MAXCHUNK / 4];  // each wave's scores, written out after its loop
+  __shared__ float sbuf[4][SC_MAXCHUNK / 4];  // each wave's scores of one segment, written out after its loop
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
-  const int qi = blockIdx.x / n_chunks;
-  const int chunk = blockIdx.x - qi * n_chunks;
-  const int seq = q_seq[qi];
-  const int n_c = int(min(int64_t((q_pos[qi] + 1) / P), ld));  // ld bounds a row
-  const int sub = chunk_pools / 4;
-  const int w_begin = chunk * chunk_pools + wave * sub;
-  const int w_end = min(w_begin + sub, n_c);
-  if (w_begin >= w_end) return;  // no block-wide barrier below: waves finish independently
+  const int64_t n_waves = int64_t(gridDim.x) * 4;
+  const int64_t gw = int64_t(blockIdx.x) * 4 + wave;
+  auto pools_of = [&](int q) __attribute__((always_inline)) {
+    return int(min(int64_t((q_pos[q] + 1) / P), ld));  // ld bounds a row
+  };
 
-  F qa[1][S::STEPS];
-  float wv[1][16];
-  score_query_frags<T, D>(q_idx, w, qi, true, Hi, n, g, qa[0], wv[0]);
-
-  // page id of each page the wave touches: lane l holds page (w_begin >> log2_ppp) + l
-  const int pg0 = w_begin >> log2_ppp;
-  const int npg = ((w_end - 1) >> log2_ppp) - pg0 + 1;
-  const int page_reg = lane < npg ? bt[int64_t(seq) * bt_stride + pg0 + lane] : 0;
-  const int ppp_mask = (1 << log2_ppp) - 1;
-  // The first tile needs the page ids anyway: wait for every prologue load here, so that only tile loads are
-  // in flight in the loop and the compiler's wait counts there stay exact.
-  __builtin_amdgcn_s_waitcnt(0);
+  // total tiles, then the query holding this wave's first tile (64 queries per step, one per lane; with at most
+  // 64 queries one scan serves both, and the sequence ids come with it)
+  int64_t total = 0;
+  uint32_t nt0 = 0, inc0 = 0;
+  int seq0 = 0;
+  for (int q0 = 0; q0 < n_q; q0 += 64) {
+    const int q = q0 + lane;
+    const uint32_t nt = q < n_q ? uint32_t((pools_of(q) + 31) / 32) : 0u;
+    if (q0 == 0) seq0 = q < n_q ? q_seq[q] : 0;
+    uint32_t sum;
+    const uint32_t inc = wave_scan_u32(nt, sum);
+    if (q0 == 0) {
+      nt0 = nt;
+      inc0 = inc;
+    }
+    total += sum;
+  }
+  const int64_t t_begin = gw * total / n_waves, t_end = (gw + 1) * total / n_waves;
+  if (t_begin >= t_end) return;
+  int qc = 0, tc = 0;  // query and tile of the cursor
+  if (n_q <= 64) {
+    const uint64_t m = __ballot(int64_t(inc0) > t_begin);
+    const int l = __builtin_ctzll(m);
+    qc = l;
+    tc = int(t_begin - int64_t(__builtin_amdgcn_readlane(int(inc0 - nt0), l)));
+  } else {
+    int64_t before = 0;
+    for (int q0 = 0; q0 < n_q; q0 += 64) {
+      const int q = q0 + lane;
+      const uint32_t nt = q < n_q ? uint32_t((pools_of(q) + 31) / 32) : 0u;
+      uint32_t sum;
+      const uint32_t inc = wave_scan_u32(nt, sum);
+      if (before + sum > t_begin) {
+        const uint64_t m = __ballot(before + inc > t_begin);
+        const int l = __builtin_ctzll(m);
+        qc = q0 + l;
+        tc = int(t_begin - before - int64_t(__builtin_amdgcn_readlane(int(inc - nt), l)));
+        break;
+      }
+      before += sum;
+    }
+  }
 
   T* tile = tiles[wave];
-  const int ntile = (w_end - w_begin + 31) / 32;
-  // Loads and steps are unconditional (a tile past the range re-reads a valid pool) and no global store sits in
-  // the loop (stores share the load counter and would force full drains): the compiler's wait counts stay exact
-  // and a wave waits only for the tile it stores to LDS, never for the one loaded after it.
   float* sb = sbuf[wave];
-  auto load_tile = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
+  const int ppp_mask = (1 << log2_ppp) - 1;
+  int64_t left = t_end - t_begin;
+  while (left > 0 && qc < n_q) {
+    const int n_c = pools_of(qc);
+    const int nt = (n_c + 31) / 32;
+    // tiles of this segment: the scores fit the wave's buffer (32 tiles), and the pools span at most 64 pages
+    // (one page id per lane)
+    int seg = int(min(int64_t(min(nt - tc, SC_MAXCHUNK / 4 / 32)), left));
+    while (seg > 1 && (((min((tc + seg) * 32, n_c) - 1) >> log2_ppp) - ((tc * 32) >> log2_ppp)) >= 64) --seg;
+    if (seg > 0) {
+      const int qi = qc;
+      const int seq = qi < 64 ? __builtin_amdgcn_readlane(seq0, qi) : q_seq[qi];
+      const int w_begin = tc * 32, w_end = min(w_begin + seg * 32, n_c);
+      F qa[1][S::STEPS];
+      float wv[1][16];
+      score_query_frags<T, D>(q_idx, w, qi, true, Hi, n, g, qa[0], wv[0]);
+      // page id of each page the segment touches: lane l holds page (w_begin >> log2_ppp) + l
+      const int pg0 = w_begin >> log2_ppp;
+      const int npg = ((w_end - 1) >> log2_ppp) - pg0 + 1;
+      const int page_reg = lane < npg ? bt[int64_t(seq) * bt_stride + pg0 + lane] : 0;
+      // The first tile needs the page ids anyway: wait for every prologue load here, so that only tile loads are
+      // in flight in the loop and the compiler's wait counts there stay exact.
+      __builtin_amdgcn_s_waitcnt(0);
+      // Loads and steps are unconditional (a tile past the range re-reads a valid pool) and no global store sits in
+      // the loop (stores share the load counter and would force full drains): a wave waits only for the tile it
+      // stores to LDS, never for the one loaded after it.
+      auto load_tile = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < CHT; ++i) {
-      const int c = i * 64 + lane;
-      int pool = w_begin + t * 32 + c / S::CPR;
-      pool = pool < w_end ? pool : w_begin;  // past the range: re-read a valid pool, never scored
-      const int page = __shfl(page_reg, (pool >> log2_ppp) - pg0);
-      const int64_t row = (int64_t(page) << log2_ppp) + (pool & ppp_mask);
-      R[i] = *reinterpret_cast<const u32x4*>(pooled + row * D + (c % S::CPR) * S::EPC);
+        for (int i = 0; i < CHT; ++i) {
+          const int c = i * 64 + lane;
+          int pool = w_begin + t * 32 + c / S::CPR;
+          pool = pool < w_end ? pool : w_begin;  // past the range: re-read a valid pool, never scored
+          const int page = __shfl(page_reg, (pool >> log2_ppp) - pg0);
+          const int64_t row = (int64_t(page) << log2_ppp) + (pool & ppp_mask);
+          R[i] = *reinterpret_cast<const u32x4*>(pooled + row * D + (c % S::CPR) * S::EPC);
+        }
+      };
+      auto step = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < CHT; ++i) {
+          const int c = i * 64 + lane;
+          *reinterpret_cast<u32x4*>(tile + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
+        }
+        load_tile(t + 2, R);
+        F kb[S::STEPS];
+        const T* kp = tile + n * S::RS + g * (D / 2);
+#pragma unroll
+        for (int s = 0; s < S::STEPS; ++s) kb[s] = E::frag_load(kp + s * S::KPL);
+        float sc[1];
+        score_tiles<T, D, 1>(qa, kb, wv, sc);
+        if (g == 0) sb[t * 32 + n] = sc[0];  // slots past the range are never written out
+      };
+      u32x4 R0[CHT], R1[CHT];
+      load_tile(0, R0);
+      __builtin_amdgcn_sched_barrier(0);  // keep tile 0's loads older than tile 1's, as in the loop
+      load_tile(1, R1);
+      for (int t = 0; t < seg; t += 2) {
+        step(t, R0);
+        step(t + 1, R1);
+      }
+      float* srow = scores + int64_t(qi) * ld + w_begin;
+      for (int i = lane; i < w_end - w_begin; i += 64) srow[i] = sb[i];
+      left -= seg;
+      tc += seg;
     }
-  };
-  auto step = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < CHT; ++i) {
-      const int c = i * 64 + lane;
-      *reinterpret_cast<u32x4*>(tile + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
+    if (tc >= nt) {
+      ++qc;
+      tc = 0;
     }
-    load_tile(t + 2, R);
-    F kb[S::STEPS];
-    const T* kp = tile + n * S::RS + g * (D / 2);
-#pragma unroll
-    for (int s = 0; s < S::STEPS; ++s) kb[s] = E::frag_load(kp + s * S::KPL);
-    float sc[1];
-    score_tiles<T, D, 1>(qa, kb, wv, sc);
-    if (g == 0) sb[t * 32 + n] = sc[0];  // slots past the range are never written out
-  };
-
-  u32x4 R0[CHT], R1[CHT];
-  load_tile(0, R0);
-  __builtin_amdgcn_sched_barrier(0);  // keep tile 0's loads older than tile 1's, as in the loop
-  load_tile(1, R1);
-  for (int t = 0; t < ntile; t += 2) {
-    step(t, R0);
-    step(t + 1, R1);
   }
-  float* srow = scores + int64_t(qi) * ld + w_begin;
-  for (int i = lane; i < w_end - w_begin; i += 64) srow[i] = sb[i];
 }
 
 // ---------------------------------------------------------------------------------------------------------------
@@ -465,16 +524,28 @@ __global__ __launch_bounds__(SC_PTHREADS, 2) void score_prefill_kernel(
 
 template <class T, int D>
 static void launch_score_t(const ScoreLaunch& a, bool prefill, int chunk, int n_chunks, int n_groups,
-                           hipStream_t s) {
-  const dim3 grid(unsigned(int64_t(n_groups) * n_chunks)), block(prefill ? SC_PTHREADS : 256);
+                           int decode_blocks, hipStream_t s) {
   if (prefill)
-    score_prefill_kernel<T, D><<<grid, block, 0, s>>>((const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp,
-                                                      (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.n_q, a.Hi, a.P,
-                                                      a.scores, a.ld, chunk, n_chunks);
+    score_prefill_kernel<T, D><<<dim3(unsigned(int64_t(n_groups) * n_chunks)), dim3(SC_PTHREADS), 0, s>>>(
+        (const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp, (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.n_q, a.Hi,
+        a.P, a.scores, a.ld, chunk, n_chunks);
   else
-    score_decode_kernel<T, D><<<grid, block, 0, s>>>((const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp,
-                                                     (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.Hi, a.P,
-                                                     a.scores, a.ld, chunk, n_chunks);
+    score_decode_kernel<T, D><<<dim3(unsigned(decode_blocks)), dim3(256), 0, s>>>(
+        (const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp, (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.n_q, a.Hi,
+        a.P, a.scores, a.ld);
+}
+
+// compute units of the current device (looked up once per device)
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
 }
 
 kp_status launch_score(const ScoreLaunch& a, hipStream_t s) {
@@ -483,16 +554,29 @@ kp_status launch_score(const ScoreLaunch& a, hipStream_t s) {
   const int64_t ppp = int64_t(1) << a.log2_ppp;
   // prefill shape when the caller promises runs of >= 8 queries of one sequence (a block takes 16)
   const bool prefill = a.group >= 8;
-  const int64_t n_groups = prefill ? (a.n_q + SC_QG - 1) / SC_QG : a.n_q;
-  // pools per block: a multiple of 128 sized for about 4096 (decode) or 1024 (prefill) blocks, at most
-  // SC_MAXCHUNK (decode) or SC_PMAXCHUNK (prefill), and (decode) at most 64 pages per wave or (prefill)
-  // SC_MAXPG pages per block
-  const int64_t target = prefill ? 1024 : 4096;  // decode: many short blocks even out rows of unequal length
-  int64_t chunk = (ncmax * n_groups + target - 1) / target;
+  if (!prefill) {
+    // persistent decode grid: SC_DBLOCKS_PER_CU blocks per compute unit, fewer when the tiles are few (at least
+    // about four tiles per wave, counted on the longest row)
+    const int64_t tiles_ub = int64_t(a.n_q) * ((ncmax + 31) / 32);
+    int64_t blocks = int64_t(SC_DBLOCKS_PER_CU) * cu_count();
+    const int64_t few = (tiles_ub + 15) / 16;
+    if (few < blocks) blocks = few < 1 ? 1 : few;
+    if (a.dtype == KP_DTYPE_BF16) {
+      if (a.D == 128) launch_score_t<bf16, 128>(a, false, 0, 0, 0, int(blocks), s);
+      else launch_score_t<bf16, 32>(a, false, 0, 0, 0, int(blocks), s);
+    } else {
+      launch_score_t<float, 32>(a, false, 0, 0, 0, int(blocks), s);
+    }
+    return check_launch("dsa_indexer_score");
+  }
+  const int64_t n_groups = (a.n_q + SC_QG - 1) / SC_QG;
+  // pools per block: a multiple of 128 sized for about 1024 blocks, at most SC_PMAXCHUNK, and SC_MAXPG pages per
+  // block
+  int64_t chunk = (ncmax * n_groups + 1023) / 1024;
   chunk = ((chunk + 127) / 128) * 128;
   if (chunk < 128) chunk = 128;
-  if (chunk > (prefill ? SC_PMAXCHUNK : SC_MAXCHUNK)) chunk = prefill ? SC_PMAXCHUNK : SC_MAXCHUNK;
-  const int64_t cap = prefill ? int64_t(SC_MAXPG - 1) * ppp : 4 * 63 * ppp;
+  if (chunk > SC_PMAXCHUNK) chunk = SC_PMAXCHUNK;
+  const int64_t cap = int64_t(SC_MAXPG - 1) * ppp;
   while (chunk > 128 && chunk > cap) chunk -= 128;
   if (chunk > cap) {
     set_error("dsa_indexer_score: pages of %lld pooled rows are too small", (long long)ppp);
@@ -504,10 +588,10 @@ kp_status launch_score(const ScoreLaunch& a, hipStream_t s) {
     return KP_ERR_INVALID_ARG;
   }
   if (a.dtype == KP_DTYPE_BF16) {
-    if (a.D == 128) launch_score_t<bf16, 128>(a, prefill, int(chunk), int(n_chunks), int(n_groups), s);
-    else launch_score_t<bf16, 32>(a, prefill, int(chunk), int(n_chunks), int(n_groups), s);
+    if (a.D == 128) launch_score_t<bf16, 128>(a, true, int(chunk), int(n_chunks), int(n_groups), 0, s);
+    else launch_score_t<bf16, 32>(a, true, int(chunk), int(n_chunks), int(n_groups), 0, s);
   } else {
-    launch_score_t<float, 32>(a, prefill, int(chunk), int(n_chunks), int(n_groups), s);
+    launch_score_t<float, 32>(a, true, int(chunk), int(n_chunks), int(n_groups), 0, s);
   }
   return check_launch("dsa_indexer_score");
 }

@@ -66,43 +66,20 @@ __device__ __forceinline__ void tk_load(TkKeys<NJ>& K, int n, Load load) {
   }
 }
 
-// Cross-lane steps on the DPP paths (no LDS): `old` is what a lane keeps when its source lane is outside its
-// 16-lane row.  Controls: quad_perm [1,0,3,2] = 0xB1 and [2,3,0,1] = 0x4E, row_shr:n = 0x110 + n,
-// row_mirror = 0x140, row_half_mirror = 0x141.
-template <int CTRL>
-__device__ __forceinline__ uint32_t tk_dpp(uint32_t old, uint32_t v) {
-  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(v), CTRL, 0xF, 0xF, false));
-}
-
 // Min and max over the wave (uniform results): within each row by DPP, then the four row values by readlane.
 __device__ __forceinline__ void tk_wave_minmax(uint32_t& mn, uint32_t& mx) {
-  mn = min(mn, tk_dpp<0xB1>(0xFFFFFFFFu, mn));
-  mx = max(mx, tk_dpp<0xB1>(0u, mx));
-  mn = min(mn, tk_dpp<0x4E>(0xFFFFFFFFu, mn));
-  mx = max(mx, tk_dpp<0x4E>(0u, mx));
-  mn = min(mn, tk_dpp<0x141>(0xFFFFFFFFu, mn));
-  mx = max(mx, tk_dpp<0x141>(0u, mx));
-  mn = min(mn, tk_dpp<0x140>(0xFFFFFFFFu, mn));
-  mx = max(mx, tk_dpp<0x140>(0u, mx));
+  mn = min(mn, dpp_u32<0xB1>(0xFFFFFFFFu, mn));
+  mx = max(mx, dpp_u32<0xB1>(0u, mx));
+  mn = min(mn, dpp_u32<0x4E>(0xFFFFFFFFu, mn));
+  mx = max(mx, dpp_u32<0x4E>(0u, mx));
+  mn = min(mn, dpp_u32<0x141>(0xFFFFFFFFu, mn));
+  mx = max(mx, dpp_u32<0x141>(0u, mx));
+  mn = min(mn, dpp_u32<0x140>(0xFFFFFFFFu, mn));
+  mx = max(mx, dpp_u32<0x140>(0u, mx));
   mn = min(min(uint32_t(__builtin_amdgcn_readlane(int(mn), 0)), uint32_t(__builtin_amdgcn_readlane(int(mn), 16))),
            min(uint32_t(__builtin_amdgcn_readlane(int(mn), 32)), uint32_t(__builtin_amdgcn_readlane(int(mn), 48))));
   mx = max(max(uint32_t(__builtin_amdgcn_readlane(int(mx), 0)), uint32_t(__builtin_amdgcn_readlane(int(mx), 16))),
            max(uint32_t(__builtin_amdgcn_readlane(int(mx), 32)), uint32_t(__builtin_amdgcn_readlane(int(mx), 48))));
-}
-
-// Inclusive prefix sum over the lanes of the wave; `total` gets the wave's sum (uniform).
-__device__ __forceinline__ uint32_t tk_wave_scan(uint32_t v, uint32_t& total) {
-  v += tk_dpp<0x111>(0u, v);
-  v += tk_dpp<0x112>(0u, v);
-  v += tk_dpp<0x114>(0u, v);
-  v += tk_dpp<0x118>(0u, v);  // inclusive within each 16-lane row
-  const uint32_t r0 = uint32_t(__builtin_amdgcn_readlane(int(v), 15));
-  const uint32_t r1 = uint32_t(__builtin_amdgcn_readlane(int(v), 31));
-  const uint32_t r2 = uint32_t(__builtin_amdgcn_readlane(int(v), 47));
-  const uint32_t r3 = uint32_t(__builtin_amdgcn_readlane(int(v), 63));
-  const int row = (threadIdx.x & 63) >> 4;
-  total = r0 + r1 + r2 + r3;
-  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
 // Selects the `budget` largest of the block's n keys (0 < budget < n) and calls emit(out_pos, j, i, key) for each
@@ -159,7 +136,7 @@ __device__ void tk_select(TkSync& sy, const TkKeys<NJ>& K, int budget, Emit emit
     if (owns) *own = u32x4{0u, 0u, 0u, 0u};
     const uint32_t mine = c[0] + c[1] + c[2] + c[3];
     uint32_t wtot;
-    const uint32_t inc = tk_wave_scan(mine, wtot);
+    const uint32_t inc = wave_scan_u32(mine, wtot);
     if (lane == 0) sy.wa[wv] = wtot;
     __syncthreads();
     uint32_t before = 0, total = 0;
