@@ -26,6 +26,8 @@
 //
 // Bound: decode is HBM-bound (the pooled-key stream, 256 B per pool at D = 128 bf16 for 32 x 128 MACs, i.e.
 // 32 flop/B: above the VALU ridge, so the contraction runs on MFMA); prefill is MFMA-bound.
+#include <type_traits>
+
 #include "kp_device.hpp"
 #include "kp_internal.hpp"
 
@@ -195,9 +197,11 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
     int seg = int(min(int64_t(min(nt - tc, SC_MAXCHUNK / 4 / 32)), left));
     while (seg > 1 && (((min((tc + seg) * 32, n_c) - 1) >> log2_ppp) - ((tc * 32) >> log2_ppp)) >= 64) --seg;
     if (seg > 0) {
-      const int qi = qc;
+      // (the segment's bounds are wave-uniform: pinned to scalar registers so the load addresses stay scalar)
+      const int qi = __builtin_amdgcn_readfirstlane(qc);
       const int seq = qi < 64 ? __builtin_amdgcn_readlane(seq0, qi) : q_seq[qi];
-      const int w_begin = tc * 32, w_end = min(w_begin + seg * 32, n_c);
+      const int w_begin = __builtin_amdgcn_readfirstlane(tc * 32);
+      const int w_end = __builtin_amdgcn_readfirstlane(min(w_begin + seg * 32, n_c));
       F qa[1][S::STEPS];
       float wv[1][16];
       score_query_frags<T, D>(q_idx, w, qi, true, Hi, n, g, qa[0], wv[0]);
@@ -211,40 +215,55 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
       // Loads and steps are unconditional (a tile past the range re-reads a valid pool) and no global store sits in
       // the loop (stores share the load counter and would force full drains): a wave waits only for the tile it
       // stores to LDS, never for the one loaded after it.
-      auto load_tile = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
+      auto run = [&](auto scalar_pages) __attribute__((always_inline)) {
+        // scalar_pages: 256-byte pooled rows and pages of >= 4 rows, so the 4 rows of one wave load lie in one
+        // page: its id is uniform (a readlane) and the address a scalar base plus lane * 16.
+        auto load_tile = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < CHT; ++i) {
-          const int c = i * 64 + lane;
-          int pool = w_begin + t * 32 + c / S::CPR;
-          pool = pool < w_end ? pool : w_begin;  // past the range: re-read a valid pool, never scored
-          const int page = __shfl(page_reg, (pool >> log2_ppp) - pg0);
-          const int64_t row = (int64_t(page) << log2_ppp) + (pool & ppp_mask);
-          R[i] = *reinterpret_cast<const u32x4*>(pooled + row * D + (c % S::CPR) * S::EPC);
+          for (int i = 0; i < CHT; ++i) {
+            if constexpr (decltype(scalar_pages)::value) {
+              int p4 = w_begin + t * 32 + 4 * i;
+              p4 = p4 < w_end ? p4 : w_begin;  // past the range: re-read valid pools, never scored
+              const int page = __builtin_amdgcn_readlane(page_reg, (p4 >> log2_ppp) - pg0);
+              const char* rp = reinterpret_cast<const char*>(pooled) +
+                               ((int64_t(page) << log2_ppp) + (p4 & ppp_mask)) * int64_t(D * sizeof(T));
+              R[i] = *reinterpret_cast<const u32x4*>(rp + lane * 16);
+            } else {
+              const int c = i * 64 + lane;
+              int pool = w_begin + t * 32 + c / S::CPR;
+              pool = pool < w_end ? pool : w_begin;  // past the range: re-read a valid pool, never scored
+              const int page = __shfl(page_reg, (pool >> log2_ppp) - pg0);
+              const int64_t row = (int64_t(page) << log2_ppp) + (pool & ppp_mask);
+              R[i] = *reinterpret_cast<const u32x4*>(pooled + row * D + (c % S::CPR) * S::EPC);
+            }
+          }
+        };
+        auto step = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < CHT; ++i) {
+            const int c = i * 64 + lane;
+            *reinterpret_cast<u32x4*>(tile + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
+          }
+          load_tile(t + 2, R);
+          F kb[S::STEPS];
+          const T* kp = tile + n * S::RS + g * (D / 2);
+#pragma unroll
+          for (int s = 0; s < S::STEPS; ++s) kb[s] = E::frag_load(kp + s * S::KPL);
+          float sc[1];
+          score_tiles<T, D, 1>(qa, kb, wv, sc);
+          if (g == 0) sb[t * 32 + n] = sc[0];  // slots past the range are never written out
+        };
+        u32x4 R0[CHT], R1[CHT];
+        load_tile(0, R0);
+        __builtin_amdgcn_sched_barrier(0);  // keep tile 0's loads older than tile 1's, as in the loop
+        load_tile(1, R1);
+        for (int t = 0; t < seg; t += 2) {
+          step(t, R0);
+          step(t + 1, R1);
         }
       };
-      auto step = [&](int t, u32x4(&R)[CHT]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < CHT; ++i) {
-          const int c = i * 64 + lane;
-          *reinterpret_cast<u32x4*>(tile + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
-        }
-        load_tile(t + 2, R);
-        F kb[S::STEPS];
-        const T* kp = tile + n * S::RS + g * (D / 2);
-#pragma unroll
-        for (int s = 0; s < S::STEPS; ++s) kb[s] = E::frag_load(kp + s * S::KPL);
-        float sc[1];
-        score_tiles<T, D, 1>(qa, kb, wv, sc);
-        if (g == 0) sb[t * 32 + n] = sc[0];  // slots past the range are never written out
-      };
-      u32x4 R0[CHT], R1[CHT];
-      load_tile(0, R0);
-      __builtin_amdgcn_sched_barrier(0);  // keep tile 0's loads older than tile 1's, as in the loop
-      load_tile(1, R1);
-      for (int t = 0; t < seg; t += 2) {
-        step(t, R0);
-        step(t + 1, R1);
-      }
+      if (S::CPR == 16 && log2_ppp >= 2) run(std::true_type{});
+      else run(std::false_type{});
       float* srow = scores + int64_t(qi) * ld + w_begin;
       for (int i = lane; i < w_end - w_begin; i += 64) srow[i] = sb[i];
       left -= seg;

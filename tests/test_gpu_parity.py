@@ -114,6 +114,8 @@ SMALL = {
     "small_decode_pool16": lambda: _small_decode("small_decode_pool16", P=16, k=128),
     "small_decode_pool1": lambda: _small_decode("small_decode_pool1", ctx=(5, 300, 2500), P=1, k=512),
     "small_decode_contig": lambda: _small_decode("small_decode_contig", page_perm_seed=None, page_tokens=1 << 15),
+    # pages of 2 pooled rows: a 4-row wave load of the decode scorer crosses pages (per-lane page lookup)
+    "small_decode_page8": lambda: _small_decode("small_decode_page8", ctx=(37, 1000, 4099, 9001), page_tokens=8),
     # a small batch with k far below its rows: the rows are split over many top-k blocks (chunks of 256 pools)
     "small_decode_k64": lambda: _small_decode("small_decode_k64", ctx=(10001, 17, 9999, 4099), k=64),
     "small_bf16_narrow": lambda: ks.scaled(_small_decode("small_bf16_narrow", ctx=(3, 64, 777, 5000)), D=32, Hi=1,
