@@ -109,7 +109,9 @@ typedef struct {
  *   keys, gates: device [n_src, P, D]; pool i reads source row src[i] (src NULL: row i).  A decode step passes
  *     its per-sequence ring of pending key/gate rows directly, with src = the sequences whose pool completes.
  *   ape: device [P, D].  pool_seq, pool_id: device [n_pools].
- *   Errors: KP_ERR_INVALID_ARG on null pointers (n_pools > 0) or bad dims.
+ *   gates and ape may each be NULL, meaning zero gate logits / a zero position term.  Both NULL is the
+ *     non-learned pooling [MAX glm5_next API page, index_kpool_compress off]: the plain mean of the pool's keys.
+ *   Errors: KP_ERR_INVALID_ARG on null keys, pool_seq or pool_id (n_pools > 0) or bad dims.
  */
 kp_status kpool_compress(const kp_dims* dims, const kp_cache* cache, int32_t n_pools, const void* keys,
                          const void* gates, const int32_t* src, const void* ape, const int32_t* pool_seq,

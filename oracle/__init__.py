@@ -13,6 +13,7 @@ from .kpool_dsa import (  # noqa: F401
     bf16_round,
     store_round,
     pool_compress,
+    pool_mean,
     pool_geometry,
     indexer_scores,
     select_pools,

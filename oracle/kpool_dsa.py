@@ -79,6 +79,16 @@ def pool_compress(keys, gates, ape) -> np.ndarray:
     return (a * keys).sum(axis=1)
 
 
+def pool_mean(keys) -> np.ndarray:
+    """Pooled keys of complete pools without the learned weighting.
+
+    [MAX ``glm5_next`` API page, ``index_kpool_compress``]: with the flag off, a pool's key is the plain mean of its
+    tokens' keys.  keys: [n_pools, P, D] -> [n_pools, D], unrounded float64.
+    """
+    keys = np.asarray(keys, dtype=np.float64)
+    return keys.sum(axis=1) / keys.shape[1]
+
+
 # ----------------------------------------------------------------------------------------------------------
 # positions (R4, R5)
 # ----------------------------------------------------------------------------------------------------------

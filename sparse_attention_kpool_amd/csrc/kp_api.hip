@@ -103,8 +103,9 @@ kp_status kpool_compress(const kp_dims* dims, const kp_cache* cache, int32_t n_p
   if (st != KP_OK) return st;
   KP_REQUIRE(n_pools >= 0, KP_ERR_INVALID_ARG, "%s: n_pools < 0", fn);
   if (n_pools == 0) return KP_OK;
-  KP_REQUIRE(keys && gates && ape && pool_seq && pool_id, KP_ERR_INVALID_ARG, "%s: NULL input", fn);
-  KP_REQUIRE(aligned(keys) && aligned(gates) && aligned(ape), KP_ERR_INVALID_ARG, "%s: misaligned input", fn);
+  KP_REQUIRE(keys && pool_seq && pool_id, KP_ERR_INVALID_ARG, "%s: NULL input", fn);
+  KP_REQUIRE(aligned(keys) && (!gates || aligned(gates)) && (!ape || aligned(ape)), KP_ERR_INVALID_ARG,
+             "%s: misaligned input", fn);
   CompressLaunch a{};
   a.dtype = dims->dtype;
   a.P = dims->pool;

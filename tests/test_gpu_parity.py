@@ -208,6 +208,44 @@ def test_workspace_reuse_across_query_counts():
     _free()
 
 
+def test_compress_plain_mean():
+    """Pooling without the learned weights (gates and ape NULL) against the oracle's plain mean: bit-exact on
+    dyadic keys (every step exact in fp32), within one bf16 ulp on random bf16 keys; and NULL gates / ape write
+    the same rows as explicit zeros."""
+    import sparse_attention_kpool_amd as K
+    wl = _small_decode("plain_mean", ctx=(64, 1000))
+    run = DeviceRun(wl)
+    P, D = wl.P, wl.D
+    rng = np.random.default_rng(21)
+    seqs = np.array([0] * 16 + [1] * 8, np.int32)
+    pids = np.array(list(range(16)) + list(range(100, 108)), np.int32)
+    n = len(seqs)
+    dev = lambda a: torch.from_numpy(a).to("cuda")
+    for kind in ("dyadic", "random"):
+        if kind == "dyadic":
+            keys = rng.integers(-64, 65, size=(n, P, D)).astype(np.float64) / 8.0
+        else:
+            keys = O.bf16_round(rng.standard_normal((n, P, D)) * 3.0)
+        kt = dev(keys.astype(np.float32)).to(torch.bfloat16).contiguous()
+        K.kpool_compress(run.dims, run.cache, kt, None, None, dev(seqs), dev(pids))
+        torch.cuda.synchronize()
+        ref = O.store_round(O.pool_mean(keys), "bf16")
+        for t in range(n):
+            got = run.pooled_rows(int(seqs[t]), [int(pids[t])])[0]
+            if kind == "dyadic":
+                np.testing.assert_array_equal(got, ref[t], err_msg=f"plain mean, pool {t}")
+            else:
+                ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(ref[t]), 1e-30))[1] - 8)
+                assert (np.abs(got - ref[t]) <= ulp).all(), f"plain mean, pool {t}"
+        first = run.pooled.clone()
+        zeros = torch.zeros_like(kt)
+        K.kpool_compress(run.dims, run.cache, kt, zeros, zeros[0], dev(seqs), dev(pids))
+        torch.cuda.synchronize()
+        assert torch.equal(first, run.pooled), "NULL gates/ape differ from explicit zeros"
+    del run
+    _free()
+
+
 def test_empty_calls():
     """n_q = 0 and n_pools = 0 are valid and write nothing."""
     import sparse_attention_kpool_amd as K

@@ -76,6 +76,22 @@ def test_pool_zero_gate_is_mean():
     np.testing.assert_allclose(got, keys.mean(axis=1), rtol=1e-14, atol=1e-14)
 
 
+def test_pool_mean_worked_example():
+    """Plain-mean pooling on a hand-computed pool: tokens (1, 10), (2, 20), (4, 40), (9, -30) -> (4, 10)."""
+    keys = np.array([[[1.0, 10.0], [2.0, 20.0], [4.0, 40.0], [9.0, -30.0]]])
+    np.testing.assert_array_equal(O.pool_mean(keys), [[4.0, 10.0]])
+    # P = 16 pools (the other pool size): sixteen tokens 0 .. 15 average to 7.5
+    np.testing.assert_array_equal(O.pool_mean(np.arange(16.0).reshape(1, 16, 1)), [[7.5]])
+
+
+def test_pool_mean_is_zero_gate_compress():
+    """The plain mean is the learned pooling with gate = ape = 0 (uniform softmax weights)."""
+    rng = np.random.default_rng(12)
+    keys = rng.standard_normal((9, 4, 8))
+    np.testing.assert_allclose(O.pool_mean(keys), O.pool_compress(keys, np.zeros_like(keys), np.zeros((4, 8))),
+                               rtol=1e-14, atol=1e-14)
+
+
 def test_pool_dominant_gate_limit():
     """One gate logit 60 above the rest: the pooled key is that token's key (weights of the rest < e^-50)."""
     rng = np.random.default_rng(3)
