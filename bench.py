@@ -51,10 +51,11 @@ def decode_bytes(wl) -> dict:
       compress  per completing pool: P key + P gate rows in (2*P*D*es), one pooled row out (D*es)
       score     per query: the pooled-key scan D*es*n_c, its index query Hi*D*es and weights Hi*4
       topk      per query: the selection written, k*4
-      attend    per query: the V-wide value columns of every attended token V*es*|S|, the query's nope part
-                H*V*es, the output H*V*es, the selection read k*4
+      attend    per query: the V-wide value columns of every attended token V*les*|S| (les = 1 for an fp8
+                latent cache, else es), the query's nope part H*V*es, the output H*V*es, the selection read k*4
     Score rows and split-KV partials are intermediate traffic, not algorithmic."""
     es = 2 if wl.dtype == "bf16" else 4
+    les = 1 if wl.latent_fp8 else es
     P, D, Hi, k, H, V = wl.P, wl.D, wl.Hi, wl.k, wl.H, wl.V
     n_complete = sum(t // P - nf // P for t, nf in zip(wl.ctx, wl.new_from))
     out = dict(compress=n_complete * (2 * P * D * es + D * es), score=0, topk=0, attend=0)
@@ -62,7 +63,7 @@ def decode_bytes(wl) -> dict:
         n_c = (pos + 1) // P
         out["score"] += D * es * n_c + Hi * D * es + Hi * 4
         out["topk"] += k * 4
-        out["attend"] += V * es * attended(pos, P, k) + 2 * H * V * es + k * 4
+        out["attend"] += V * les * attended(pos, P, k) + 2 * H * V * es + k * 4
     return out
 
 
@@ -86,9 +87,9 @@ class Leg:
         self.d = d
         self.dims = K.Dims(pool=wl.P, idx_dim=wl.D, idx_heads=wl.Hi, topk=wl.k, heads=wl.H, latent_dim=wl.L,
                            v_dim=wl.V, page_tokens=wl.page_tokens, dtype=wl.dtype, scale=wl.scale)
-        self.caches = [K.Cache(latent=d.latent, pooled=d.pooled, block_table=d.block_table)]
+        self.caches = [K.Cache(latent=d.latent, pooled=d.pooled, block_table=d.block_table, latent_scale=wl.kv_scale)]
         for _ in range(copies - 1):
-            self.caches.append(K.Cache(latent=d.latent.clone(), pooled=d.pooled.clone(),
+            self.caches.append(K.Cache(latent=d.latent.clone(), pooled=d.pooled.clone(), latent_scale=wl.kv_scale,
                                        block_table=d.block_table))
         if group is None:
             group = wl.n_q if len(set(wl.q_seq.tolist())) == 1 else 1
@@ -137,8 +138,12 @@ class Leg:
             K.dsa_topk_select(self.dims, self.queries, L.scores[:n_q], L.sel[:n_q], L.n_sel[:n_q],
                               workspace=L.ws_topk)
             ev[3].record()
-            K.sparse_mla_attn(self.dims, cache, self.queries, self.d.q, L.sel[:n_q], L.n_sel[:n_q], self.out,
-                              lse=self.lse, workspace=L.ws_attn)
+            if cache.latent.dtype == torch.uint8:
+                K.sparse_mla_attn_fp8(self.dims, cache, self.queries, self.d.q, L.sel[:n_q], L.n_sel[:n_q],
+                                      cache.latent_scale, self.out, lse=self.lse, workspace=L.ws_attn)
+            else:
+                K.sparse_mla_attn(self.dims, cache, self.queries, self.d.q, L.sel[:n_q], L.n_sel[:n_q], self.out,
+                                  lse=self.lse, workspace=L.ws_attn)
             ev[4].record()
             torch.cuda.synchronize()
             for j, n in enumerate(names):
@@ -246,7 +251,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,128k,long1m,prefill,copy")
+    ap.add_argument("--legs", default="decode,128k,long1m,fp8,prefill,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=16)
     args = ap.parse_args()
@@ -309,6 +314,19 @@ def main():
         res["long1m"] = {"tokens_per_s": round(w5.n_q / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
                          "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                          "stages_ms": {k: round(v, 5) for k, v in st.items()}, "stage_bytes": by}
+        leg.free()
+    if "fp8" in legs:
+        print("[bench] fp8 leg: the 64-sequence decode over an fp8 (E4M3) latent cache", file=sys.stderr, flush=True)
+        w8 = W["batch64_fp8"]
+        leg = Leg(w8, copies=2)
+        ms = leg.time_steps(args.steps, args.warmup)
+        st = leg.time_stages(args.steps)
+        by = decode_bytes(w8)
+        gbs = sum(by.values()) / (ms * 1e-3) / 1e9
+        res["decode_fp8_latent"] = {"tokens_per_s": round(w8.n_q / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+                                    "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                                    "kv_scale": w8.kv_scale, "stages_ms": {k: round(v, 5) for k, v in st.items()},
+                                    "stage_bytes": by}
         leg.free()
     if "prefill" in legs:
         print("[bench] prefill leg: 4096 queries on 65536 tokens", file=sys.stderr, flush=True)

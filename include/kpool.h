@@ -178,6 +178,20 @@ kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_q
                           const int32_t* sel, const int32_t* n_sel, void* out, float* lse, void* workspace,
                           size_t ws_bytes, void* stream);
 
+/*
+ * sparse_mla_attn_fp8 -- sparse_mla_attn over an fp8 latent cache.
+ *   [MAX glm5_next API page, declared_state_dtype(): the KV cache format may put the MLA latent in fp8;
+ *   DEFAULT_ENCODING: float8_e4m3fn]; [metrale glm5_next_load/loader.rs page: each sparse-attention layer carries
+ *   a kv_scale].  cache->latent holds OCP E4M3 ("e4m3fn") codes, latent_dim bytes per token; the latent row of a
+ *   token is the decoded codes times kv_scale (a host scalar, finite and > 0).  Everything else -- the formula,
+ *   q (bf16), sel / n_sel, out (bf16), lse, workspace (sparse_mla_workspace_size), limits -- is as in
+ *   sparse_mla_attn.  Built for dims->dtype bf16 with v_dim 512 only.
+ *   Errors: KP_ERR_INVALID_ARG (kv_scale, buffers), KP_ERR_UNSUPPORTED (shape), KP_ERR_WORKSPACE.
+ */
+kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
+                              const int32_t* sel, const int32_t* n_sel, float kv_scale, void* out, float* lse,
+                              void* workspace, size_t ws_bytes, void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  Owned by the library. */
 const char* kp_last_error(void);
 

@@ -94,6 +94,14 @@ def normal_table(dtype: str) -> np.ndarray:
     return _TABLES[dtype]
 
 
+def fp8_codes(key: int, idx):
+    """E4M3 codes from the hash: random sign, exponent field 4..7, random 3-bit mantissa -- magnitudes in
+    [0.125, 1.875], never NaN.  uint8 numpy array, or an int64 torch tensor for a torch ``idx``."""
+    h = hash32(key, idx)
+    c = (((h >> 31) & 1) << 7) | ((4 + ((h >> 24) & 3)) << 3) | ((h >> 16) & 7)
+    return c.astype(np.uint8) if isinstance(c, np.ndarray) else c
+
+
 def normal(key: int, idx, dtype: str, table=None):
     """N(0,1) draws (numpy float32 on the host; pass ``table`` as a device tensor for torch)."""
     h = hash32(key, idx) >> 16
@@ -134,6 +142,8 @@ class Workload:
     key_per_token: bool = False      # general instance: keys drawn per token (else constant per pool)
     page_perm_seed: Optional[int] = None   # None: pages placed in order; else a seeded random permutation
     w_scale: float = 1.0             # multiplies the head weights (0 makes every score 0: a pure tie-break case)
+    latent_fp8: bool = False         # latent cache of OCP E4M3 codes (value = code value * kv_scale)
+    kv_scale: float = 1.0            # scale of the fp8 latent cache
     extra: dict = field(default_factory=dict)
 
     @property
@@ -189,7 +199,8 @@ def cfg3_contexts() -> np.ndarray:
 
 
 def workloads() -> dict:
-    """The five published workload shapes (plus the 128K single-sequence decode point)."""
+    """The five published workload shapes, plus the 128K single-sequence decode point and the batch-64 decode over
+    an fp8 latent cache."""
     w = {}
     # tiny prefill, fp32: all 64 positions of one sequence are queries and all tokens are new
     w["tiny"] = Workload(name="tiny", dtype="f32", P=4, D=32, Hi=2, k=8, H=4, L=80, V=64, scale=1.0 / 8.0,
@@ -204,6 +215,8 @@ def workloads() -> dict:
                                q_seq=np.zeros(4096, np.int32), q_pos=np.arange(61440, 65536, dtype=np.int32),
                                seed=4)
     w["long1m"] = _decode("long1m", "bf16", [1 << 20] * 8, seed=5, page_perm_seed=55)
+    # the batch-64 decode over an fp8 (E4M3) latent cache with scale 1/2
+    w["batch64_fp8"] = scaled(w["batch64"], name="batch64_fp8", latent_fp8=True, kv_scale=0.5)
     return w
 
 
@@ -274,6 +287,14 @@ def host_q(wl: Workload, seq, pos) -> np.ndarray:
     return v
 
 
+def host_latent_codes(wl: Workload, seq: int, toks: np.ndarray) -> np.ndarray:
+    """Fp8 latent rows [len(toks), L] as E4M3 codes (uint8); columns V..L-1 hold code 0."""
+    idx = _seqtok(seq, toks)[:, None] * wl.L + np.arange(wl.L, dtype=np.int64)[None, :]
+    c = fp8_codes(wl.key("lat8"), idx)
+    c[:, wl.V:] = 0
+    return c
+
+
 def host_latent(wl: Workload, seq: int, toks: np.ndarray) -> np.ndarray:
     """Latent rows [len(toks), L]; columns V..L-1 are zero."""
     idx = _seqtok(seq, toks)[:, None] * wl.L + np.arange(wl.L, dtype=np.int64)[None, :]
@@ -315,7 +336,7 @@ def device_caches(wl: Workload, device, chunk_pages: int = 1024):
     seq_np, lpg_np = page_owner(wl)
     n_pages, pt, P = wl.n_pages(), wl.page_tokens, wl.P
     ppp = pt // P
-    latent = torch.empty((n_pages, pt, wl.L), dtype=dt, device=device)
+    latent = torch.empty((n_pages, pt, wl.L), dtype=torch.uint8 if wl.latent_fp8 else dt, device=device)
     pooled = torch.zeros((n_pages, ppp, wl.D), dtype=dt, device=device)
     table = torch.from_numpy(normal_table(wl.dtype)).to(device)
     seq_t = torch.from_numpy(seq_np).to(device)
@@ -331,13 +352,19 @@ def device_caches(wl: Workload, device, chunk_pages: int = 1024):
         s = seq_t[p0:p1]
         tok = lpg_t[p0:p1, None] * pt + tok_in_page[None, :]                       # [c, pt]
         idx = ((s[:, None] * TMAX + tok)[:, :, None] * wl.L + colL[None, None, :])  # [c, pt, L]
-        if wl.latent_int:
-            v = uniform_int(klat, idx, -4, 4).to(torch.float32)
+        if wl.latent_fp8:
+            c = fp8_codes(wl.key("lat8"), idx)
+            c[:, :, wl.V:] = 0
+            latent[p0:p1] = c.to(torch.uint8)
+            del idx, c
         else:
-            v = table[hash32(klat, idx) >> 16]
-        v[:, :, wl.V:] = 0
-        latent[p0:p1] = v.to(dt)
-        del idx, v
+            if wl.latent_int:
+                v = uniform_int(klat, idx, -4, 4).to(torch.float32)
+            else:
+                v = table[hash32(klat, idx) >> 16]
+            v[:, :, wl.V:] = 0
+            latent[p0:p1] = v.to(dt)
+            del idx, v
         pool = lpg_t[p0:p1, None] * ppp + pool_in_page[None, :]                      # [c, ppp]
         idx = ((s[:, None] * TMAX + pool)[:, :, None] * wl.D + colD[None, None, :])
         kv = uniform_int(kpool, idx, -4, 4).to(torch.float32)

@@ -12,6 +12,7 @@ leave open are listed with each function.
 from .kpool_dsa import (  # noqa: F401
     bf16_round,
     store_round,
+    fp8_e4m3_decode,
     pool_compress,
     pool_mean,
     pool_geometry,

@@ -61,6 +61,21 @@ def store_round(x, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 ("e4m3fn") codes as float64: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits;
+    exponent field 0 is subnormal (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN; there are no infinities.
+    The fp8 latent cache stores these codes; a row's values are the decoded codes times the cache's scale.
+    Written from the format's definition.
+    """
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
 # ----------------------------------------------------------------------------------------------------------
 # stage 1: pool compression (R1, R2, R4)
 # ----------------------------------------------------------------------------------------------------------

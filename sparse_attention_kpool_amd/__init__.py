@@ -5,7 +5,7 @@ memory and the current stream; nothing else.  There is no fallback: if libkpool.
 every call raises.
 
 The four calls keep the C names:
-    kpool_compress, dsa_indexer_score, dsa_topk_select, sparse_mla_attn
+    kpool_compress, dsa_indexer_score, dsa_topk_select, sparse_mla_attn (sparse_mla_attn_fp8 over an fp8 latent cache)
 plus the workspace queries dsa_topk_workspace_size and sparse_mla_workspace_size.  Outputs and workspaces are
 caller-allocated tensors, as in the C ABI.
 """
@@ -21,10 +21,11 @@ LIB_PATH = os.path.join(PKG, "libkpool.so")
 
 KP_OK, KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED, KP_ERR_WORKSPACE, KP_ERR_LAUNCH = 0, -1, -2, -3, -4
 KP_DTYPE_F32, KP_DTYPE_BF16 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk_select",
-            "sparse_mla_workspace_size", "sparse_mla_attn", "kp_last_error", "kp_abi_version")
+            "sparse_mla_workspace_size", "sparse_mla_attn", "sparse_mla_attn_fp8", "kp_last_error",
+            "kp_abi_version")
 
 
 class KpError(RuntimeError):
@@ -73,7 +74,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_mla_workspace_size.argtypes = [D, Q]
     lib.sparse_mla_workspace_size.restype = sz
     lib.sparse_mla_attn.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn"):
+    lib.sparse_mla_attn_fp8.argtypes = [D, C, Q, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_fp8"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kp_last_error.restype = ctypes.c_char_p
     lib.kp_abi_version.restype = i32
@@ -110,9 +112,10 @@ class Dims:
 
 @dataclass
 class Cache:
-    latent: object = None        # torch tensor [n_pages, page_tokens, L]
+    latent: object = None        # torch tensor [n_pages, page_tokens, L] (uint8: E4M3 codes, see latent_scale)
     pooled: object = None        # torch tensor [n_pages, page_tokens / P, D]
     block_table: object = None   # torch int32 tensor [n_seq, stride]
+    latent_scale: float = 1.0    # scale of an fp8 latent cache (row value = decoded code * latent_scale)
 
     def c(self) -> _Cache:
         return _Cache(_ptr(self.latent), _ptr(self.pooled), _ptr(self.block_table),
@@ -191,3 +194,13 @@ def sparse_mla_attn(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, o
                                                      ctypes.byref(queries.c()), _ptr(q), _ptr(sel), _ptr(n_sel),
                                                      _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                                      _stream(stream)))
+
+
+def sparse_mla_attn_fp8(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, kv_scale: float, out, lse=None,
+                        workspace=None, stream=None) -> None:
+    """As sparse_mla_attn, over a latent cache of E4M3 codes (cache.latent uint8) scaled by kv_scale."""
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    _check("sparse_mla_attn_fp8", load().sparse_mla_attn_fp8(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+                                                             ctypes.byref(queries.c()), _ptr(q), _ptr(sel),
+                                                             _ptr(n_sel), float(kv_scale), _ptr(out), _ptr(lse),
+                                                             _ptr(workspace), ws_bytes, _stream(stream)))

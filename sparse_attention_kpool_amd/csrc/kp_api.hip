@@ -1,6 +1,7 @@
 // The extern "C" entry points declared in include/kpool.h: argument validation, then one launcher per call.
 // Nothing here touches device memory or synchronises; a validation failure launches nothing.
 #include <stdarg.h>
+#include <math.h>
 #include <stdio.h>
 
 #include "kp_internal.hpp"
@@ -89,7 +90,7 @@ using namespace kp;
 
 extern "C" {
 
-int32_t kp_abi_version(void) { return 1; }
+int32_t kp_abi_version(void) { return 2; }
 
 const char* kp_last_error(void) { return g_err; }
 
@@ -208,10 +209,10 @@ size_t sparse_mla_workspace_size(const kp_dims* dims, const kp_queries* queries)
   return attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)));
 }
 
-kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
-                          const int32_t* sel, const int32_t* n_sel, void* out, float* lse, void* workspace,
-                          size_t ws_bytes, void* stream) {
-  const char* fn = "sparse_mla_attn";
+// Shared body of sparse_mla_attn and sparse_mla_attn_fp8 (fp8: latent rows of latent_dim E4M3 codes).
+static kp_status attn_call(const char* fn, bool fp8, float kv_scale, const kp_dims* dims, const kp_cache* cache,
+                           const kp_queries* queries, const void* q, const int32_t* sel, const int32_t* n_sel,
+                           void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
   kp_status st = check_dims(dims, fn);
   if (st != KP_OK) return st;
   st = check_queries(queries, fn);
@@ -219,15 +220,25 @@ kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_q
   if (queries->n_q == 0) return KP_OK;
   st = check_cache(cache, true, false, fn);
   if (st != KP_OK) return st;
-  KP_REQUIRE(attn_built(dims), KP_ERR_UNSUPPORTED, "%s: v_dim %d with dtype %d is not built (bf16: 512, 64; f32: 64)",
-             fn, dims->v_dim, dims->dtype);
+  if (fp8) {
+    KP_REQUIRE(dims->dtype == KP_DTYPE_BF16 && dims->v_dim == 512, KP_ERR_UNSUPPORTED,
+               "%s: built for bf16 queries and output with v_dim 512 (got dtype %d, v_dim %d)", fn, dims->dtype,
+               dims->v_dim);
+    KP_REQUIRE(kv_scale > 0.f && kv_scale < INFINITY, KP_ERR_INVALID_ARG, "%s: kv_scale must be finite and > 0",
+               fn);
+  } else {
+    KP_REQUIRE(attn_built(dims), KP_ERR_UNSUPPORTED,
+               "%s: v_dim %d with dtype %d is not built (bf16: 512, 64; f32: 64)", fn, dims->v_dim, dims->dtype);
+  }
   KP_REQUIRE(dims->heads <= 64, KP_ERR_UNSUPPORTED, "%s: heads %d > 64", fn, dims->heads);
-  KP_REQUIRE((int64_t(dims->latent_dim) * int64_t(elem_size(dims))) % 16 == 0, KP_ERR_INVALID_ARG,
+  const int64_t lat_es = fp8 ? 1 : int64_t(elem_size(dims));
+  KP_REQUIRE((int64_t(dims->latent_dim) * lat_es) % 16 == 0, KP_ERR_INVALID_ARG,
              "%s: latent rows must be a multiple of 16 bytes (latent_dim %d)", fn, dims->latent_dim);
   KP_REQUIRE(q && sel && n_sel && out, KP_ERR_INVALID_ARG, "%s: NULL q, sel, n_sel or out", fn);
   KP_REQUIRE(aligned(q) && aligned(sel) && aligned(n_sel) && aligned(out) && (!lse || aligned(lse)),
              KP_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
-  const size_t ws_need = attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)));
+  const size_t ws_need =
+      attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)));
   KP_REQUIRE(ws_bytes >= ws_need && (ws_need == 0 || (workspace && aligned(workspace))), KP_ERR_WORKSPACE,
              "%s: workspace of %zu bytes < %zu required", fn, ws_bytes, ws_need);
   AttnLaunch a{};
@@ -242,6 +253,8 @@ kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_q
   a.log2_pt = ilog2(dims->page_tokens);
   a.bt_stride = cache->bt_stride;
   a.scale = dims->scale;
+  a.latent_fp8 = fp8 ? 1 : 0;
+  a.kv_scale = fp8 ? kv_scale : 1.f;
   a.latent = cache->latent;
   a.bt = cache->block_table;
   a.q = q;
@@ -254,6 +267,20 @@ kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_q
   a.ws = workspace;
   a.ws_bytes = ws_bytes;
   return launch_attn(a, (hipStream_t)stream);
+}
+
+kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
+                          const int32_t* sel, const int32_t* n_sel, void* out, float* lse, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  return attn_call("sparse_mla_attn", false, 1.f, dims, cache, queries, q, sel, n_sel, out, lse, workspace, ws_bytes,
+                   stream);
+}
+
+kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
+                              const int32_t* sel, const int32_t* n_sel, float kv_scale, void* out, float* lse,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  return attn_call("sparse_mla_attn_fp8", true, kv_scale, dims, cache, queries, q, sel, n_sel, out, lse, workspace,
+                   ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -134,12 +134,14 @@ __device__ __forceinline__ typename Elem<T>::frag ct_frag(const T* blk, int c0, 
 }
 
 // O-wave epilogue: the output of the wave's channels for every head -- normalised (one split) or as an
-// unnormalised partial with its running max and sum (several splits)
+// unnormalised partial with its running max and sum (several splits).  The accumulated O is multiplied by oscale
+// on the way out (the scale of an fp8 latent cache; 1 otherwise).
 template <class T, int V, int HT>
 __device__ __forceinline__ void attn_write_out(const f32x4 (&bank)[AttnShape<T, V, HT>::NB], int qi, int sp,
                                                int n_split, int H, int wl, int l16, int g, const float* m_s,
                                                const float* l_s, T* __restrict__ out, float* __restrict__ lse,
-                                               T* __restrict__ part_o, float* __restrict__ part_ml) {
+                                               T* __restrict__ part_o, float* __restrict__ part_ml,
+                                               float oscale = 1.f) {
   using S = AttnShape<T, V, HT>;
 #pragma unroll
   for (int nt = 0; nt < HT; ++nt) {
@@ -147,7 +149,7 @@ __device__ __forceinline__ void attn_write_out(const f32x4 (&bank)[AttnShape<T, 
     if (h >= H) continue;
     const float mh = m_s[h], lh = l_s[h];
     if (n_split == 1) {
-      const float inv = 1.f / lh;
+      const float inv = oscale / lh;
 #pragma unroll
       for (int mt = 0; mt < S::MT; ++mt) {
         const f32x4 o = bank[mt * HT + nt] * inv;
@@ -163,7 +165,7 @@ __device__ __forceinline__ void attn_write_out(const f32x4 (&bank)[AttnShape<T, 
       const int64_t base = int64_t(qi * n_split + sp) * H + h;
 #pragma unroll
       for (int mt = 0; mt < S::MT; ++mt) {
-        const f32x4 o = bank[mt * HT + nt];
+        const f32x4 o = bank[mt * HT + nt] * oscale;
         T* pp = part_o + base * V + wl * S::VW + 16 * mt + 4 * g;
         if constexpr (sizeof(T) == 2) {
           *reinterpret_cast<uint2*>(pp) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
@@ -462,14 +464,23 @@ constexpr int AD_NBUF = 4;        // LDS block buffers: S reads block j, O reads
 constexpr int AD_MAXPOOL = 2048;  // pools of one split held in the LDS pool table
 constexpr int AD_DIST = 12;       // S waves: C-fragment reads in flight ahead of the MFMAs
 
-template <int HT>
+// FP8: the latent cache holds OCP E4M3 codes (1 byte per element; value = code value * its scale).  Then every wave
+// loads its 4 rows (512 B each, one 1 KiB wave load per 2 rows) of each block into registers three blocks ahead,
+// converts every code to bf16 once -- exactly: E4M3 values are bf16 values -- and writes the same swizzled bf16
+// block the direct loads produce, two blocks ahead of the S phase, so the S and O phases are unchanged.  The cache
+// scale is folded into the softmax scale and applied to O on the way out.
+template <int HT, bool FP8>
 __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
-    const bf16* __restrict__ latent, int L, const int32_t* __restrict__ bt, int bt_stride, int log2_pt,
+    const void* __restrict__ latent_v, int L, const int32_t* __restrict__ bt, int bt_stride, int log2_pt,
     const bf16* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int log2P, int k, int H, float scale_log2,
     int n_split, bf16* __restrict__ out, float* __restrict__ lse, bf16* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, float oscale) {
   using T = bf16;
+  // S waves: C-fragment reads in flight ahead of the MFMAs (fewer with fp8: the staging registers take the rest)
+  constexpr int DIST = FP8 ? 6 : AD_DIST;
+  const bf16* latent = static_cast<const bf16*>(latent_v);
+  const uint8_t* latent8 = static_cast<const uint8_t*>(latent_v);
   constexpr int V = 512;
   using S = AttnShape<T, V, HT>;
   using E = Elem<T>;
@@ -602,15 +613,15 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
     auto rd = [&](int f) __attribute__((always_inline)) -> F {
       return lds_load<F>((a0 + (f / S::SK) * 16 * S::RS * int(sizeof(T))) ^ (16 * (f % S::SK)));
     };
-    F cf[AD_DIST];
+    F cf[DIST];
 #pragma unroll
-    for (int f = 0; f < AD_DIST; ++f) cf[f] = rd(f);
+    for (int f = 0; f < DIST; ++f) cf[f] = rd(f);
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead: the scheduler would sink them to their uses
 #pragma unroll
     for (int f = 0; f < 2 * S::SK; ++f) {
       const int t = f / S::SK, s = f % S::SK;
-      sa[t][s & 1] = mfma16(cf[f % AD_DIST], __builtin_bit_cast(F, bank[s]), sa[t][s & 1]);
-      if (f + AD_DIST < 2 * S::SK) cf[f % AD_DIST] = rd(f + AD_DIST);
+      sa[t][s & 1] = mfma16(cf[f % DIST], __builtin_bit_cast(F, bank[s]), sa[t][s & 1]);
+      if (f + DIST < 2 * S::SK) cf[f % DIST] = rd(f + DIST);
       __builtin_amdgcn_sched_barrier(0);
     }
     // lane holds head 16*wl + l16, slots 16t + 4g + i
@@ -696,21 +707,102 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
   // barrier -- after which every wave is past iteration j - 1, so buffer (j + 2) % 4, last read by O(j - 2),
   // is free -- start block j + 2, then S(j) on S waves and O(j - 1) on O waves.  Loads are unconditional (a
   // block past the end reads the zero row), so every iteration issues the same count and the wait is exact.
-  load_block(0, block_rows(0));
-  load_block(1, block_rows(1));
-  int rows_next = block_rows(2);
-  for (int j = 0; j <= nblk; ++j) {
-    __builtin_amdgcn_s_waitcnt(attn_vmcnt(S::CHT));
-    __syncthreads();
-    load_block(j + 2, rows_next);
-    rows_next = block_rows(j + 3);
-    if (o_wave) {
-      if (j >= 1) o_phase(j - 1);
-    } else if (s_active && j < nblk) {
-      s_phase(j);
+  if constexpr (!FP8) {
+    load_block(0, block_rows(0));
+    load_block(1, block_rows(1));
+    int rows_next = block_rows(2);
+    for (int j = 0; j <= nblk; ++j) {
+      __builtin_amdgcn_s_waitcnt(attn_vmcnt(S::CHT));
+      __syncthreads();
+      load_block(j + 2, rows_next);
+      rows_next = block_rows(j + 3);
+      if (o_wave) {
+        if (j >= 1) o_phase(j - 1);
+      } else if (s_active && j < nblk) {
+        s_phase(j);
+      }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // no load may land in LDS after the block ends
+  } else {
+    // Wave w brings slots 4w .. 4w + 3 of each block (as the direct loads do): load i covers slot 4w + 2i (lanes
+    // 0..31) and 4w + 2i + 1 (lanes 32..63), lane l taking the 16 codes of channels 16 (l % 32) .. + 15.
+    // Lane j < 4 of fp8_rows(b) holds the cache row of slot 4w + j of block b (-1: none).
+    auto fp8_rows = [&](int b) __attribute__((always_inline)) -> int {
+      return slot_entry(b, 4 * wave_u + (lane & 3));
+    };
+    auto load8 = [&](int rows, u32x4(&R)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int e0 = __builtin_amdgcn_readlane(rows, 2 * i), e1 = __builtin_amdgcn_readlane(rows, 2 * i + 1);
+        const int e = lane < 32 ? e0 : e1;
+        const uint8_t* src = e >= 0 ? latent8 + int64_t(e) * L + 16 * (lane & 31)
+                                    : reinterpret_cast<const uint8_t*>(attn_zero_row) + 16 * (lane & 31);
+        R[i] = *reinterpret_cast<const u32x4*>(src);
+      }
+    };
+    // codes -> bf16 into buffer b % 4: the 16 codes of lane l are bf16 chunks 2 (l % 32) and 2 (l % 32) + 1 of
+    // its slot's row, stored at chunk position c ^ attn_swz(slot) as the direct loads place them
+    auto store8 = [&](int b, const u32x4(&R)[2]) __attribute__((always_inline)) {
+      T* blk = crm[b % AD_NBUF];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int slot = 4 * wave_u + 2 * i + (lane >> 5);
+        const int c = 2 * (lane & 31);
+        uint32_t h[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(R[i][d]), false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(R[i][d]), true);
+          h[2 * d] = pack_bf16x2(lo[0], lo[1]);
+          h[2 * d + 1] = pack_bf16x2(hi[0], hi[1]);
+        }
+        T* row = blk + slot * V;
+        *reinterpret_cast<u32x4*>(row + ((c ^ attn_swz(slot)) * S::EPC)) = u32x4{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<u32x4*>(row + (((c + 1) ^ attn_swz(slot)) * S::EPC)) = u32x4{h[4], h[5], h[6], h[7]};
+      }
+    };
+    // blocks in flight, block b in R[b % 3] (a fourth would not fit the registers beside the S and O state)
+    u32x4 R0[2], R1[2], R2[2];
+    load8(fp8_rows(0), R0);
+    load8(fp8_rows(1), R1);
+    load8(fp8_rows(2), R2);
+    __builtin_amdgcn_s_waitcnt(attn_vmcnt(4));
+    store8(0, R0);
+    load8(fp8_rows(3), R0);
+    __builtin_amdgcn_s_waitcnt(attn_vmcnt(4));
+    store8(1, R1);
+    load8(fp8_rows(4), R1);
+    // Iteration j: the barrier publishes block j + 1 (written in iteration j - 1); after it every wave is past
+    // iteration j - 1, so buffer (j + 2) % 4, last read by S(j - 2) and O(j - 2), is free: each wave writes its
+    // rows of block j + 2 into it from registers and loads block j + 5 in their place, then O waves run O(j - 1)
+    // and S waves S(j).  Loads are unconditional (a block past the end reads the zero row), so the wait for the
+    // oldest block is exact.
+    auto iter = [&](int j, u32x4(&R)[2]) __attribute__((always_inline)) {
+      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(attn_vmcnt(4));
+      store8(j + 2, R);
+      load8(fp8_rows(j + 5), R);
+      if (o_wave) {
+        if (j >= 1) o_phase(j - 1);
+      } else if (s_active && j < nblk) {
+        s_phase(j);
+      }
+    };
+    // unrolled by the register ring, so every register index is a constant (a block in flight must stay in its
+    // registers: moving them would wait for its loads); the scheduling barriers keep the copies apart
+    for (int j = 0;;) {
+      iter(j, R2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (++j > nblk) break;
+      iter(j, R0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (++j > nblk) break;
+      iter(j, R1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (++j > nblk) break;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // no load may land in LDS after the block ends
 
   if (s_active) {
     l_run += __shfl_xor(l_run, 16);
@@ -722,7 +814,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
   }
   __syncthreads();
   if (!o_wave) return;
-  attn_write_out<T, V, HT>(bank, qi, sp, n_split, H, wl, l16, g, m_s, l_s, out, lse, part_o, part_ml);
+  attn_write_out<T, V, HT>(bank, qi, sp, n_split, H, wl, l16, g, m_s, l_s, out, lse, part_o, part_ml, oscale);
 }
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s per (query, head), with
@@ -824,11 +916,17 @@ static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
     part_ml = reinterpret_cast<float*>(part_o + size_t(a.n_q) * ns * a.H * a.V);
   }
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  if constexpr (std::is_same<T, bf16>::value && V == 512)
-    attn_dma_kernel<HT><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
-        (const T*)a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
-        ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml);
-  else
+  if constexpr (std::is_same<T, bf16>::value && V == 512) {
+    if (a.latent_fp8)  // the cache scale multiplies every logit and the output
+      attn_dma_kernel<HT, true><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
+          a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
+          ilog2(a.P), a.k, a.H, scale_log2 * a.kv_scale, ns, (T*)a.out, a.lse, part_o, part_ml, a.kv_scale);
+    else
+      attn_dma_kernel<HT, false><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
+          a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
+          ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml, 1.f);
+  } else
+
     attn_kernel<T, V, HT><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
         (const T*)a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
         ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml);
@@ -847,6 +945,10 @@ static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
 
 kp_status launch_attn(const AttnLaunch& a, hipStream_t s) {
   if (a.n_q == 0) return KP_OK;
+  if (a.latent_fp8 && !(a.dtype == KP_DTYPE_BF16 && a.V == 512)) {
+    set_error("sparse_mla_attn_fp8: built for bf16 queries with v_dim 512 only");
+    return KP_ERR_UNSUPPORTED;
+  }
   if (attn_splits(a.P, a.k, a.n_q) > CB_MAXSPLIT) {
     set_error("sparse_mla_attn: topk %d pools of %d tokens needs more than %d splits per query", a.k, a.P,
               CB_MAXSPLIT);

@@ -63,6 +63,8 @@ kp_status launch_topk(const TopkLaunch& a, hipStream_t s);
 struct AttnLaunch {
   int dtype, P, H, L, V, k, n_q, max_pos, log2_pt, bt_stride;
   float scale;
+  int latent_fp8;   // latent cache of E4M3 codes (bf16 queries and output, V = 512)
+  float kv_scale;   // its scale (value = code value * kv_scale)
   const void* latent;
   const int32_t* bt;
   const void* q;

@@ -12,7 +12,7 @@ from typing import Optional
 import torch
 
 from . import (Cache, Dims, Queries, dsa_indexer_score, dsa_topk_select, dsa_topk_workspace_size, kpool_compress,
-               sparse_mla_attn, sparse_mla_workspace_size)
+               sparse_mla_attn, sparse_mla_attn_fp8, sparse_mla_workspace_size)
 
 
 @dataclass
@@ -64,5 +64,9 @@ class KPoolDSALayer:
         scores = self.scores[:n_q]
         dsa_indexer_score(self.dims, cache, queries, q_idx, w, scores)
         dsa_topk_select(self.dims, queries, scores, self.sel[:n_q], self.n_sel[:n_q], workspace=self.ws_topk)
-        sparse_mla_attn(self.dims, cache, queries, q, self.sel[:n_q], self.n_sel[:n_q], out, lse=lse,
-                        workspace=self.ws_attn)
+        if cache.latent.dtype == torch.uint8:   # an fp8 (E4M3) latent cache
+            sparse_mla_attn_fp8(self.dims, cache, queries, q, self.sel[:n_q], self.n_sel[:n_q], cache.latent_scale,
+                                out, lse=lse, workspace=self.ws_attn)
+        else:
+            sparse_mla_attn(self.dims, cache, queries, q, self.sel[:n_q], self.n_sel[:n_q], out, lse=lse,
+                            workspace=self.ws_attn)

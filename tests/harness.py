@@ -29,7 +29,7 @@ class DeviceRun:
         self.inputs = d
         self.bt_np = d.block_table_np
         self.latent, self.pooled = d.latent, d.pooled
-        self.cache = K.Cache(latent=d.latent, pooled=d.pooled, block_table=d.block_table)
+        self.cache = K.Cache(latent=d.latent, pooled=d.pooled, block_table=d.block_table, latent_scale=wl.kv_scale)
         if group is None:
             group = wl.n_q if len(set(wl.q_seq.tolist())) == 1 else 1
         self.queries = K.Queries(seq=d.q_seq, pos=d.q_pos, max_pos=wl.max_pos(), group=group)
@@ -97,7 +97,11 @@ def oracle_query(wl: ks.Workload, j: int, pooled=None, sel=None):
     use_sel = own_sel if sel is None else sel
     toks = O.attended_tokens(use_sel, i, wl.P)
     q = ks.host_q(wl, s, i)[0]
-    out, lse = O.sparse_mla(q, ks.host_latent(wl, s, toks), wl.scale, wl.V)
+    if wl.latent_fp8:   # the cache holds E4M3 codes; a row's values are the decoded codes times the cache scale
+        rows = O.fp8_e4m3_decode(ks.host_latent_codes(wl, s, toks)) * wl.kv_scale
+    else:
+        rows = ks.host_latent(wl, s, toks)
+    out, lse = O.sparse_mla(q, rows, wl.scale, wl.V)
     return dict(scores=scores, sel=own_sel, tokens=toks, out=out, lse=lse, n_c=n_c, r=r, tau=tau)
 
 

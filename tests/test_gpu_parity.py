@@ -114,6 +114,10 @@ SMALL = {
     "small_decode_pool16": lambda: _small_decode("small_decode_pool16", P=16, k=128),
     "small_decode_pool1": lambda: _small_decode("small_decode_pool1", ctx=(5, 300, 2500), P=1, k=512),
     "small_decode_contig": lambda: _small_decode("small_decode_contig", page_perm_seed=None, page_tokens=1 << 15),
+    # fp8 (E4M3) latent cache with a scale: attention through sparse_mla_attn_fp8
+    "small_decode_fp8": lambda: _small_decode("small_decode_fp8", latent_fp8=True, kv_scale=0.5),
+    "two_step_fp8": lambda: _small_decode("two_step_fp8", ctx=(140001, 3001, 131076), latent_fp8=True,
+                                          kv_scale=0.25),
     # pages of 2 pooled rows: a 4-row wave load of the decode scorer crosses pages (per-lane page lookup)
     "small_decode_page8": lambda: _small_decode("small_decode_page8", ctx=(37, 1000, 4099, 9001), page_tokens=8),
     # a small batch with k far below its rows: the rows are split over many top-k blocks (chunks of 256 pools)

@@ -398,3 +398,26 @@ def test_layer_causality():
         assert max(a["tokens"]) <= i
         if (i + 1) % P:
             assert max(a["tokens"]) == i                        # the incomplete tail reaches the query itself
+
+# ----------------------------------------------------------------------------------------------------------
+# fp8 latent codes (OCP E4M3)
+# ----------------------------------------------------------------------------------------------------------
+def test_fp8_e4m3_published_values():
+    """Landmarks of the E4M3 format: 1.0, 1.5, 2.0, 3.75, the largest finite value 448, the smallest normal 2^-6,
+    the smallest subnormal 2^-9, the signed zero and NaN."""
+    d = O.fp8_e4m3_decode
+    assert d(0x38) == 1.0 and d(0x3C) == 1.5 and d(0x40) == 2.0 and d(0x47) == 3.75
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0
+    assert d(0x08) == 2.0 ** -6 and d(0x07) == 7 * 2.0 ** -9 and d(0x01) == 2.0 ** -9
+    assert d(0x00) == 0.0 and d(0x80) == 0.0 and np.signbit(d(0x80)) and d(0xB8) == -1.0
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+
+
+def test_fp8_e4m3_order_and_count():
+    """Codes 0x00..0x7E decode strictly increasing (the magnitude order of the encoding), the negative half
+    mirrors them, and there are 253 distinct finite values (+0 and -0 equal)."""
+    pos = O.fp8_e4m3_decode(np.arange(0x7F))
+    assert (np.diff(pos) > 0).all()
+    np.testing.assert_array_equal(O.fp8_e4m3_decode(np.arange(0x80, 0xFF)), -pos)
+    vals = O.fp8_e4m3_decode(np.arange(256))
+    assert len(np.unique(vals[~np.isnan(vals)])) == 253

@@ -45,6 +45,24 @@ def test_device_fill_matches_host_rows():
         np.testing.assert_array_equal(row, want)
 
 
+def test_device_fill_fp8_latent_codes():
+    """An fp8 latent cache filled through torch holds the host generator's E4M3 codes; codes stay finite with
+    magnitudes in [0.125, 1.875] and the rotary columns hold code 0."""
+    import oracle as O
+    wl = ks.scaled(ks.workloads()["batch64"], ctx=[300, 77], new_from=[299, 76], q_seq=np.arange(2, dtype=np.int32),
+                   q_pos=np.array([299, 76], np.int32), latent_fp8=True, kv_scale=0.5)
+    lat, _ = ks.device_caches(wl, "cpu", chunk_pages=2)
+    assert lat.dtype == torch.uint8
+    bt = wl.block_table()
+    for s, t in [(0, 5), (1, 70), (0, 299)]:
+        row = lat[bt[s, t // 64], t % 64].numpy()
+        np.testing.assert_array_equal(row, ks.host_latent_codes(wl, s, np.array([t]))[0])
+    codes = ks.host_latent_codes(wl, 0, np.arange(300))
+    v = O.fp8_e4m3_decode(codes)
+    assert not np.isnan(v).any() and (v[:, wl.V:] == 0).all()
+    assert np.abs(v[:, :wl.V]).min() == 0.125 and np.abs(v[:, :wl.V]).max() == 1.875
+
+
 def test_batch64_contexts():
     t = ks.cfg3_contexts()
     assert int(t.sum()) == 4151643 and int(t.min()) == 8375 and int(t.max()) == 127811
