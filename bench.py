@@ -157,7 +157,7 @@ class Leg:
 
 
 STAGE_KERNELS = {"score": ["kp::score_decode_kernel<kp::bf16, 128>"],
-                 "attend": ["kp::attn_dma_kernel<4>", "kp::attn_combine_kernel<kp::bf16, 8>"]}
+                 "attend": ["kp::attn_dma_kernel<4, false>", "kp::attn_combine_kernel<kp::bf16, 8>"]}
 
 
 def measured_traffic(stage: str):

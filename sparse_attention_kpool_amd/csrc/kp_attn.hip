@@ -813,8 +813,42 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
     }
   }
   __syncthreads();
-  if (!o_wave) return;
-  attn_write_out<T, V, HT>(bank, qi, sp, n_split, H, wl, l16, g, m_s, l_s, out, lse, part_o, part_ml, oscale);
+  // Write-out through LDS (the ring is free now): O waves store their scaled O as bf16 rows of 1040 B (1 KiB of
+  // channels plus 16 B, which keeps the 16 heads of one store on distinct banks); then all threads copy the rows
+  // out with 16-byte stores.  A (query, split)'s H x V outputs are contiguous, so the copy is one 64 KiB run.
+  constexpr int SROW = V + 8;  // staging row stride, elements
+  static_assert(64 * SROW * int(sizeof(T)) <= AD_NBUF * AT_NT * V * int(sizeof(T)), "staging fits the ring");
+  T* stg = &crm[0][0];  // the whole ring, as one array
+  if (o_wave) {
+#pragma unroll
+    for (int nt = 0; nt < HT; ++nt) {
+      const int h = 16 * nt + l16;
+      if (h >= H) continue;
+      const float f = n_split == 1 ? oscale / l_s[h] : oscale;
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt) {
+        const f32x4 o = bank[mt * HT + nt] * f;
+        *reinterpret_cast<uint2*>(stg + h * SROW + wl * S::VW + 16 * mt + 4 * g) =
+            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+      }
+    }
+  }
+  __syncthreads();
+  T* dst = n_split == 1 ? out + int64_t(qi) * H * V : part_o + int64_t(qi * n_split + sp) * H * V;
+  for (int i = tid; i < H * (V / S::EPC); i += AT_THREADS) {
+    const int h = i / (V / S::EPC), c = i % (V / S::EPC);
+    *reinterpret_cast<u32x4*>(dst + int64_t(h) * V + c * S::EPC) =
+        *reinterpret_cast<const u32x4*>(stg + h * SROW + c * S::EPC);
+  }
+  if (tid < H) {
+    if (n_split == 1) {
+      if (lse) lse[int64_t(qi) * H + tid] = (m_s[tid] + log2f(l_s[tid])) * LN2;
+    } else {
+      const int64_t base = int64_t(qi * n_split + sp) * H + tid;
+      part_ml[base * 2 + 0] = m_s[tid];
+      part_ml[base * 2 + 1] = l_s[tid];
+    }
+  }
 }
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s per (query, head), with
