@@ -179,6 +179,20 @@ kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_q
                           size_t ws_bytes, void* stream);
 
 /*
+ * sparse_mla_attn_shared -- sparse_mla_attn with selections shared between queries (MTP drafts).
+ *   [MAX glm5_next API page, index_share_for_mtp_iteration: the MTP draft layer reuses the target's top-k
+ *   selection; GLM-5.3-Flash model card, "Raw config fields": index_share_for_mtp_iteration true].  Query i attends
+ *   the tokens of the pools in selection row sel_row[i] of sel / n_sel (rows as written by dsa_topk_select for
+ *   the target queries), cut at its own position: the tail of a selected pool counts up to pos[i], and a pool the
+ *   target did not select (for instance one the draft's position has just entered) is not attended.  With
+ *   sel_row[i] = i this is sparse_mla_attn.  sel_row: device int32 [n_q], each in [0, rows of sel).  Workspace,
+ *   outputs, limits and errors as in sparse_mla_attn; KP_ERR_INVALID_ARG on a NULL sel_row (n_q > 0).
+ */
+kp_status sparse_mla_attn_shared(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries,
+                                 const void* q, const int32_t* sel, const int32_t* n_sel, const int32_t* sel_row,
+                                 void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * sparse_mla_attn_fp8 -- sparse_mla_attn over an fp8 latent cache.
  *   [MAX glm5_next API page, declared_state_dtype(): the KV cache format may put the MLA latent in fp8;
  *   DEFAULT_ENCODING: float8_e4m3fn]; [metrale glm5_next_load/loader.rs page: each sparse-attention layer carries

@@ -21,11 +21,11 @@ LIB_PATH = os.path.join(PKG, "libkpool.so")
 
 KP_OK, KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED, KP_ERR_WORKSPACE, KP_ERR_LAUNCH = 0, -1, -2, -3, -4
 KP_DTYPE_F32, KP_DTYPE_BF16 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk_select",
-            "sparse_mla_workspace_size", "sparse_mla_attn", "sparse_mla_attn_fp8", "kp_last_error",
-            "kp_abi_version")
+            "sparse_mla_workspace_size", "sparse_mla_attn", "sparse_mla_attn_shared", "sparse_mla_attn_fp8",
+            "kp_last_error", "kp_abi_version")
 
 
 class KpError(RuntimeError):
@@ -75,7 +75,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_mla_workspace_size.restype = sz
     lib.sparse_mla_attn.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sparse_mla_attn_fp8.argtypes = [D, C, Q, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
-    for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_fp8"):
+    lib.sparse_mla_attn_shared.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_shared",
+              "sparse_mla_attn_fp8"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kp_last_error.restype = ctypes.c_char_p
     lib.kp_abi_version.restype = i32
@@ -194,6 +196,16 @@ def sparse_mla_attn(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, o
                                                      ctypes.byref(queries.c()), _ptr(q), _ptr(sel), _ptr(n_sel),
                                                      _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                                      _stream(stream)))
+
+
+def sparse_mla_attn_shared(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, sel_row, out, lse=None,
+                           workspace=None, stream=None) -> None:
+    """As sparse_mla_attn, query i attending selection row sel_row[i] (int32 [n_q]) cut at its own position."""
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    _check("sparse_mla_attn_shared", load().sparse_mla_attn_shared(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+                                                                   ctypes.byref(queries.c()), _ptr(q), _ptr(sel),
+                                                                   _ptr(n_sel), _ptr(sel_row), _ptr(out), _ptr(lse),
+                                                                   _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def sparse_mla_attn_fp8(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, kv_scale: float, out, lse=None,

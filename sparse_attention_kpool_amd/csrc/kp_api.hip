@@ -90,7 +90,7 @@ using namespace kp;
 
 extern "C" {
 
-int32_t kp_abi_version(void) { return 2; }
+int32_t kp_abi_version(void) { return 3; }
 
 const char* kp_last_error(void) { return g_err; }
 
@@ -212,7 +212,8 @@ size_t sparse_mla_workspace_size(const kp_dims* dims, const kp_queries* queries)
 // Shared body of sparse_mla_attn and sparse_mla_attn_fp8 (fp8: latent rows of latent_dim E4M3 codes).
 static kp_status attn_call(const char* fn, bool fp8, float kv_scale, const kp_dims* dims, const kp_cache* cache,
                            const kp_queries* queries, const void* q, const int32_t* sel, const int32_t* n_sel,
-                           void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+                           const int32_t* sel_row, void* out, float* lse, void* workspace, size_t ws_bytes,
+                           void* stream) {
   kp_status st = check_dims(dims, fn);
   if (st != KP_OK) return st;
   st = check_queries(queries, fn);
@@ -235,7 +236,8 @@ static kp_status attn_call(const char* fn, bool fp8, float kv_scale, const kp_di
   KP_REQUIRE((int64_t(dims->latent_dim) * lat_es) % 16 == 0, KP_ERR_INVALID_ARG,
              "%s: latent rows must be a multiple of 16 bytes (latent_dim %d)", fn, dims->latent_dim);
   KP_REQUIRE(q && sel && n_sel && out, KP_ERR_INVALID_ARG, "%s: NULL q, sel, n_sel or out", fn);
-  KP_REQUIRE(aligned(q) && aligned(sel) && aligned(n_sel) && aligned(out) && (!lse || aligned(lse)),
+  KP_REQUIRE(aligned(q) && aligned(sel) && aligned(n_sel) && aligned(out) && (!lse || aligned(lse)) &&
+                 (!sel_row || aligned(sel_row)),
              KP_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
   const size_t ws_need =
       attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)));
@@ -262,6 +264,7 @@ static kp_status attn_call(const char* fn, bool fp8, float kv_scale, const kp_di
   a.q_pos = queries->pos;
   a.sel = sel;
   a.n_sel = n_sel;
+  a.sel_row = sel_row;
   a.out = out;
   a.lse = lse;
   a.ws = workspace;
@@ -272,15 +275,23 @@ static kp_status attn_call(const char* fn, bool fp8, float kv_scale, const kp_di
 kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
                           const int32_t* sel, const int32_t* n_sel, void* out, float* lse, void* workspace,
                           size_t ws_bytes, void* stream) {
-  return attn_call("sparse_mla_attn", false, 1.f, dims, cache, queries, q, sel, n_sel, out, lse, workspace, ws_bytes,
-                   stream);
+  return attn_call("sparse_mla_attn", false, 1.f, dims, cache, queries, q, sel, n_sel, nullptr, out, lse, workspace,
+                   ws_bytes, stream);
+}
+
+kp_status sparse_mla_attn_shared(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries,
+                                 const void* q, const int32_t* sel, const int32_t* n_sel, const int32_t* sel_row,
+                                 void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  KP_REQUIRE(sel_row || !queries || queries->n_q == 0, KP_ERR_INVALID_ARG, "sparse_mla_attn_shared: NULL sel_row");
+  return attn_call("sparse_mla_attn_shared", false, 1.f, dims, cache, queries, q, sel, n_sel, sel_row, out, lse,
+                   workspace, ws_bytes, stream);
 }
 
 kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
                               const int32_t* sel, const int32_t* n_sel, float kv_scale, void* out, float* lse,
                               void* workspace, size_t ws_bytes, void* stream) {
-  return attn_call("sparse_mla_attn_fp8", true, kv_scale, dims, cache, queries, q, sel, n_sel, out, lse, workspace,
-                   ws_bytes, stream);
+  return attn_call("sparse_mla_attn_fp8", true, kv_scale, dims, cache, queries, q, sel, n_sel, nullptr, out, lse,
+                   workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -185,7 +185,8 @@ template <class T, int V, int HT>
 __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     const T* __restrict__ latent, int L, const int32_t* __restrict__ bt, int bt_stride, int log2_pt,
     const T* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int log2P, int k, int H, float scale_log2,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, const int32_t* __restrict__ sel_row,
+    int log2P, int k, int H, float scale_log2,
     int n_split, T* __restrict__ out, float* __restrict__ lse, T* __restrict__ part_o,
     float* __restrict__ part_ml) {
   using S = AttnShape<T, V, HT>;
@@ -205,13 +206,14 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
   const bool o_wave = wave >= 4;
   const int wl = wave & 3;  // index within the wave's role
   const int qi = blockIdx.x / n_split;
+  const int srow = sel_row ? sel_row[qi] : qi;  // the selection row this query attends (shared by MTP drafts)
   const int sp = blockIdx.x - qi * n_split;
   const int seq = q_seq[qi];
   const int pos = q_pos[qi];
   const int P = 1 << log2P;
   // Split sp takes the selected pools sp, sp + n_split, sp + 2 n_split, ...: interleaved rather than
   // contiguous, so the blocks of one query read spread-out parts of its (ascending) selection at a time.
-  const int ns_pools = n_sel[qi];
+  const int ns_pools = n_sel[srow];
   const int my_pools = ns_pools > sp ? (ns_pools - sp + n_split - 1) / n_split : 0;
   const int s_begin = 0;
   const int s_end = my_pools * P;
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
   // Slot table: cache row of every slot of the split, -1 for a slot past the query (the cut tail pool).  One
   // block-table lookup per pool, done once; in the loop a slot's row is then a single LDS read.
   {
-    const int32_t* qsel = sel + int64_t(qi) * k + sp;
+    const int32_t* qsel = sel + int64_t(srow) * k + sp;
     const int pt_mask = (1 << log2_pt) - 1;
     for (int j = tid; j < (nsl >> log2P); j += AT_THREADS) {
       const int p = qsel[int64_t(j) * n_split];
@@ -473,7 +475,8 @@ template <int HT, bool FP8>
 __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
     const void* __restrict__ latent_v, int L, const int32_t* __restrict__ bt, int bt_stride, int log2_pt,
     const bf16* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int log2P, int k, int H, float scale_log2,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, const int32_t* __restrict__ sel_row,
+    int log2P, int k, int H, float scale_log2,
     int n_split, bf16* __restrict__ out, float* __restrict__ lse, bf16* __restrict__ part_o,
     float* __restrict__ part_ml, float oscale) {
   using T = bf16;
@@ -503,6 +506,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
   const bool o_wave = wave >= 4;
   const int wl = wave & 3;  // index within the wave's role
   const int qi = blockIdx.x / n_split;
+  const int srow = sel_row ? sel_row[qi] : qi;  // the selection row this query attends (shared by MTP drafts)
   const int sp = blockIdx.x - qi * n_split;
   const int seq = q_seq[qi];
   const int pos = q_pos[qi];
@@ -510,10 +514,10 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
   // split sp takes the selected pools sp, sp + n_split, sp + 2 n_split, ... (as attn_kernel)
   // The first selection entry of each thread is loaded right away, with the selection count rather than after
   // it (an entry past the count is read but not used; every index stays inside the row of k entries).
-  const int32_t* qsel = sel + int64_t(qi) * k + sp;
+  const int32_t* qsel = sel + int64_t(srow) * k + sp;
   const int kq = (k - sp + n_split - 1) / n_split;  // entries of the row this split strides over
   const int p_first = tid < kq ? qsel[int64_t(tid) * n_split] : -1;
-  const int ns_pools = n_sel[qi];
+  const int ns_pools = n_sel[srow];
   const int my_pools = ns_pools > sp ? (ns_pools - sp + n_split - 1) / n_split : 0;
   const int nsl = my_pools * P;  // slots of this split
 
@@ -953,16 +957,17 @@ static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
   if constexpr (std::is_same<T, bf16>::value && V == 512) {
     if (a.latent_fp8)  // the cache scale multiplies every logit and the output
       attn_dma_kernel<HT, true><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
-          a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
+          a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel, a.sel_row,
           ilog2(a.P), a.k, a.H, scale_log2 * a.kv_scale, ns, (T*)a.out, a.lse, part_o, part_ml, a.kv_scale);
     else
       attn_dma_kernel<HT, false><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
-          a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
+          a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel, a.sel_row,
           ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml, 1.f);
   } else
 
     attn_kernel<T, V, HT><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
         (const T*)a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel,
+        a.sel_row,
         ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml);
   kp_status st = check_launch("sparse_mla_attn");
   if (st != KP_OK || ns == 1) return st;

@@ -72,6 +72,7 @@ struct AttnLaunch {
   const int32_t* q_pos;
   const int32_t* sel;
   const int32_t* n_sel;
+  const int32_t* sel_row;  // query i attends selection row sel_row[i] (NULL: row i)
   void* out;
   float* lse;
   void* ws;

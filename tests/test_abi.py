@@ -21,6 +21,7 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_fp8",
+              "sparse_mla_attn_shared",
               "dsa_topk_workspace_size", "sparse_mla_workspace_size", "kp_last_error", "kp_abi_version"):
         assert f in names
     assert set(names) == set(K.EXPORTED)

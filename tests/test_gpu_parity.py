@@ -212,6 +212,46 @@ def test_workspace_reuse_across_query_counts():
     _free()
 
 
+def test_mtp_shared_selection():
+    """MTP drafts reusing their targets' selections (sparse_mla_attn_shared): targets at T-2, drafts at T-1 of the
+    same sequences.  A target reading its own row reproduces sparse_mla_attn bit for bit; a draft matches the oracle
+    over the target's selected pools cut at the draft's own position (so with T-1 = 9000 the draft's new pool,
+    which the target could not select, is not attended)."""
+    import sparse_attention_kpool_amd as K
+    ctx = [37, 1000, 4099, 9001]
+    n = len(ctx)
+    base = ks.workloads()["batch64"]
+    wl = ks.scaled(base, name="mtp_shared", ctx=ctx, new_from=[t - 2 for t in ctx],
+                   q_seq=np.array(list(range(n)) * 2, np.int32),
+                   q_pos=np.array([t - 2 for t in ctx] + [t - 1 for t in ctx], np.int32), page_perm_seed=7)
+    _say("[case mtp_shared] targets at T-2, drafts at T-1")
+    run = DeviceRun(wl).run()
+    check_run(run, list(range(2 * n)))
+    n_q = wl.n_q
+    sel_row = torch.tensor(list(range(n)) * 2, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(run.out)
+    lse = torch.empty_like(run.lse)
+    K.sparse_mla_attn_shared(run.dims, run.cache, run.queries, run.q, run.layer.sel[:n_q], run.layer.n_sel[:n_q],
+                             sel_row, out, lse=lse, workspace=run.layer.ws_attn)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:n], run.out[:n]) and torch.equal(lse[:n], run.lse[:n]), "target rows differ"
+    tol_abs, tol_rel = attn_tolerance(wl.dtype)
+    for d in range(n, 2 * n):
+        t = d - n
+        s, i = int(wl.q_seq[d]), int(wl.q_pos[d])
+        sel_t, ns = run.sel_row(t)
+        toks = O.attended_tokens(sel_t[:ns], i, wl.P)
+        ref_out, ref_lse = O.sparse_mla(ks.host_q(wl, s, i)[0], ks.host_latent(wl, s, toks), wl.scale, wl.V)
+        got = out[d].float().cpu().numpy()
+        assert np.abs(got - ref_out).max() <= tol_abs, f"draft {d}: max-abs"
+        assert rel_rms(got, ref_out) <= tol_rel, f"draft {d}: rel-RMS"
+        np.testing.assert_allclose(lse[d].cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-3, err_msg=f"draft {d} lse")
+        if i == 9000:
+            assert 9000 not in set(toks.tolist()), "the draft's new pool must not be attended"
+    del run
+    _free()
+
+
 def test_compress_plain_mean():
     """Pooling without the learned weights (gates and ape NULL) against the oracle's plain mean: bit-exact on
     dyadic keys (every step exact in fp32), within one bf16 ulp on random bf16 keys; and NULL gates / ape write
