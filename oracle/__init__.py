@@ -22,3 +22,9 @@ from .kpool_dsa import (  # noqa: F401
     sparse_mla,
     LayerOracle,
 )
+from .projections import (  # noqa: F401
+    linear,
+    indexer_project,
+    mla_absorb_q,
+    mla_unabsorb_o,
+)

@@ -421,3 +421,78 @@ def test_fp8_e4m3_order_and_count():
     np.testing.assert_array_equal(O.fp8_e4m3_decode(np.arange(0x80, 0xFF)), -pos)
     vals = O.fp8_e4m3_decode(np.arange(256))
     assert len(np.unique(vals[~np.isnan(vals)])) == 253
+
+
+# ---- dense projections (oracle/projections.py) ----
+
+def test_linear_bruteforce_python():
+    """alpha * a @ w^T against a pure-Python triple loop on a tiny case (brute force; catches a transposed w)."""
+    rng = np.random.default_rng(11)
+    a = rng.integers(-5, 6, size=(3, 7)).astype(float)
+    w = rng.integers(-5, 6, size=(4, 7)).astype(float)
+    got = O.linear(a, w, alpha=0.5)
+    for m in range(3):
+        for n in range(4):
+            acc = 0.0
+            for kk in range(7):
+                acc += a[m][kk] * w[n][kk]
+            assert got[m, n] == 0.5 * acc
+
+
+def test_absorbed_query_scores_equal_explicit_keys():
+    """Absorption: (W_UK[h]^T q) . c == q . (W_UK[h] c) for every head and latent row (associativity).  A
+    transposed W_UK or a wrong head index breaks the equality."""
+    rng = np.random.default_rng(12)
+    T, H, dn, V, n = 3, 4, 6, 10, 5
+    q_nope = rng.standard_normal((T, H, dn))
+    w_uk = rng.standard_normal((H, dn, V))
+    c = rng.standard_normal((n, V))
+    q_lat = O.mla_absorb_q(q_nope, w_uk)
+    for h in range(H):
+        k_nope = c @ w_uk[h].T  # [n, dn]: the explicit keys of head h
+        np.testing.assert_allclose(q_lat[:, h, :] @ c.T, q_nope[:, h, :] @ k_nope.T, rtol=1e-12, atol=1e-12)
+
+
+def test_unabsorbed_output_equals_explicit_values():
+    """Un-absorption: W_UV[h] (sum_t p_t c_t) == sum_t p_t (W_UV[h] c_t) for probability weights p."""
+    rng = np.random.default_rng(13)
+    T, H, dv, V, n = 2, 3, 5, 9, 7
+    w_uv = rng.standard_normal((H, dv, V))
+    c = rng.standard_normal((n, V))
+    p = rng.random((T, H, n))
+    p /= p.sum(axis=2, keepdims=True)
+    o_lat = np.einsum("thn,nv->thv", p, c)
+    got = O.mla_unabsorb_o(o_lat, w_uv)
+    for t in range(T):
+        for h in range(H):
+            vals = c @ w_uv[h].T  # [n, dv]: the explicit values of head h
+            np.testing.assert_allclose(got[t, h], p[t, h] @ vals, rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_project_key_then_gate_and_head_major():
+    """Key | gate order of the shared projection (llama.cpp PR, "What I implemented new") and the head-major
+    layout of the index query, on selector weights whose outputs are known in closed form."""
+    rng = np.random.default_rng(14)
+    T, hidden, q_rank, Hi, D = 3, 16, 12, 2, 4
+    x = rng.integers(-8, 9, size=(T, hidden)).astype(float)
+    cq = rng.integers(-8, 9, size=(T, q_rank)).astype(float)
+    w_kg = np.zeros((2 * D, hidden))
+    for d in range(D):
+        w_kg[d, d] = 1.0          # key channel d = x[:, d]
+        w_kg[D + d, D + d] = -2.0  # gate channel d = -2 x[:, D + d]
+    w_q = np.zeros((Hi * D, q_rank))
+    for h in range(Hi):
+        for d in range(D):
+            w_q[h * D + d, (3 * h + d) % q_rank] = 1.0
+    w_w = np.zeros((Hi, hidden))
+    w_w[0, hidden - 1] = 1.0
+    w_w[1, 0] = 3.0
+    q_idx, w, keys, gates = O.indexer_project(x, cq, w_q, w_w, w_kg, Hi, D)
+    assert q_idx.shape == (T, Hi, D) and w.shape == (T, Hi) and keys.shape == (T, D) and gates.shape == (T, D)
+    np.testing.assert_array_equal(keys, x[:, :D])
+    np.testing.assert_array_equal(gates, -2.0 * x[:, D:2 * D])
+    for h in range(Hi):
+        for d in range(D):
+            np.testing.assert_array_equal(q_idx[:, h, d], cq[:, (3 * h + d) % q_rank])
+    np.testing.assert_array_equal(w[:, 0], x[:, hidden - 1])
+    np.testing.assert_array_equal(w[:, 1], 3.0 * x[:, 0])
