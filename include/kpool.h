@@ -8,6 +8,9 @@
  *   dsa_topk_select    causal top-k pools per query, the incomplete tail pool always kept
  *   sparse_mla_attn    nope-only absorbed MLA of each query over the tokens of its selected pools
  *
+ * and, beside them, kp_linear: the dense projections that feed and follow the path (indexer query, head
+ * weights and key | gate; the MLA query absorb and output un-absorb).
+ *
  * Sources (page title, section):
  *   [MAX "max.pipelines.architectures.glm5_next" API page]: fields index_kpool (tokens per scoring pool),
  *     index_kpool_always_select_tail, index_kpool_compress (gate logits plus a learned intra-pool position
@@ -205,6 +208,36 @@ kp_status sparse_mla_attn_shared(const kp_dims* dims, const kp_cache* cache, con
 kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
                               const int32_t* sel, const int32_t* n_sel, float kv_scale, void* out, float* lse,
                               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * kp_linear -- the dense projections beside the sparse path, as one strided-batched bf16 product
+ *     C[b][m][n] = alpha * sum_k A[b][m][k] * W[b][n][k]     (0 <= b < batch, m < M, n < N, k < K)
+ *   [llama.cpp PR, "What I implemented new": the indexer cache holds key | gate per token; the indexer and the
+ *   MLA low-rank paths are kept unquantized]; [MAX glm5_next API page, compute_dtype: the indexer and kv_b_proj
+ *   run in the compute dtype]; [GLM-5.3-Flash model card, "Raw config fields": hidden_size 4096, q_lora_rank
+ *   1536, qk_nope_head_dim 256, v_head_dim 256].  Absorbed MLA (the layer's specification): head h's key and
+ *   value of a latent row c are W_UK[h] c and W_UV[h] c, so the query enters latent space as W_UK[h]^T q and the
+ *   latent output leaves it as W_UV[h] o.
+ *   A: device bf16, row m of batch b at A + b*stride_a + m*lda (elements), k contiguous.
+ *   W: device bf16, row n of batch b at W + b*stride_w + n*ldw, k contiguous (a weight stored output-major).
+ *   C: device, c_dtype (KP_DTYPE_BF16: rounded once, nearest-even; KP_DTYPE_F32), row m at C + b*stride_c +
+ *     m*ldc, n contiguous.  A stride of 0 reuses one matrix for every batch entry.
+ *   Accumulation is fp32 over k in an order that does not depend on M, N or the batch.
+ *   The layer's projections (T tokens, hidden 4096, q_lora 1536, Hi = 32, D = 128, H = 64, dn = dv = 256):
+ *     index query   A = cq [T, 1536], W = W_iq [Hi*D, 1536] (head-major rows)  -> C = q_idx [T, Hi*D] bf16
+ *     head weights  A = x [T, 4096],  W = W_w [Hi, 4096]                       -> C = w [T, Hi] f32
+ *     key, gate     A = x [T, 4096],  W = rows 0..D-1 / D..2D-1 of W_kg [2D, 4096] -> C = keys / gates [T, D]
+ *     absorb        batch H: A = q_nope + h*dn (lda H*dn), W = W_UK[h]^T [V, dn] (stride V*dn)
+ *                   -> C = q + h*L (ldc H*L): columns 0..V-1 of each query row; the rotary columns V..L-1 are
+ *                   not written (keep them zero)
+ *     un-absorb     batch H: A = out + h*V (lda H*V), W = W_UV[h] [dv, V] (stride dv*V) -> C = o + h*dv
+ *   Limits: K a multiple of 64; lda, ldw, stride_a, stride_w multiples of 8; ldc, stride_c multiples of 4;
+ *   lda, ldw >= K; ldc >= N; every operand 16-byte aligned.  batch, M or N = 0 is a valid empty call.
+ *   Errors: KP_ERR_INVALID_ARG (pointers, strides, alignment, c_dtype, alpha not finite), KP_ERR_UNSUPPORTED (K).
+ */
+kp_status kp_linear(int32_t batch, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int64_t stride_a,
+                    const void* W, int64_t ldw, int64_t stride_w, void* C, int64_t ldc, int64_t stride_c,
+                    int32_t c_dtype, float alpha, void* stream);
 
 /* Message of the last failed call on this thread ("" if none).  Owned by the library. */
 const char* kp_last_error(void);

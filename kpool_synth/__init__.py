@@ -110,6 +110,19 @@ def normal(key: int, idx, dtype: str, table=None):
     return table[h]
 
 
+def host_matrix(seed: int, name: str, shape, kind: str = "normal", scale: float = 1.0) -> np.ndarray:
+    """Seeded float32 array of bf16 values for one named operand.  kind 'int': integers in [-4, 4] (exact in
+    bf16, and any sum of up to 2^20 of their products is exact in fp32); 'normal': N(0, 1) draws times `scale`
+    (a power of two keeps them bf16 values)."""
+    key = stream_key(seed, "matrix:" + name)
+    idx = np.arange(int(np.prod(shape)), dtype=np.int64)
+    if kind == "int":
+        v = uniform_int(key, idx, -4, 4).astype(np.float32)
+    else:
+        v = normal(key, idx, "bf16") * np.float32(scale)
+    return v.reshape(shape)
+
+
 # ----------------------------------------------------------------------------------------------------------
 # workloads
 # ----------------------------------------------------------------------------------------------------------

@@ -21,11 +21,11 @@ LIB_PATH = os.path.join(PKG, "libkpool.so")
 
 KP_OK, KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED, KP_ERR_WORKSPACE, KP_ERR_LAUNCH = 0, -1, -2, -3, -4
 KP_DTYPE_F32, KP_DTYPE_BF16 = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk_select",
             "sparse_mla_workspace_size", "sparse_mla_attn", "sparse_mla_attn_shared", "sparse_mla_attn_fp8",
-            "kp_last_error", "kp_abi_version")
+            "kp_linear", "kp_last_error", "kp_abi_version")
 
 
 class KpError(RuntimeError):
@@ -76,8 +76,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_mla_attn.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sparse_mla_attn_fp8.argtypes = [D, C, Q, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.sparse_mla_attn_shared.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kp_linear.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, ctypes.c_float,
+                              vp]
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_shared",
-              "sparse_mla_attn_fp8"):
+              "sparse_mla_attn_fp8", "kp_linear"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kp_last_error.restype = ctypes.c_char_p
     lib.kp_abi_version.restype = i32
@@ -216,3 +218,63 @@ def sparse_mla_attn_fp8(dims: Dims, cache: Cache, queries: Queries, q, sel, n_se
                                                              ctypes.byref(queries.c()), _ptr(q), _ptr(sel),
                                                              _ptr(n_sel), float(kv_scale), _ptr(out), _ptr(lse),
                                                              _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------------------------------------
+# the dense projections beside the path (kp_linear)
+# ----------------------------------------------------------------------------------------------------------
+def _mat3(t, name: str):
+    """(batch, rows, ld, batch stride) of a 2-D [rows, cols] or 3-D [batch, rows, cols] view, cols contiguous."""
+    if t.dim() == 2:
+        b, rows, ld, sb = 1, t.shape[0], t.stride(0), 0
+    elif t.dim() == 3:
+        b, rows, ld, sb = t.shape[0], t.shape[1], t.stride(1), t.stride(0)
+    else:
+        raise ValueError(f"kp_linear: {name} must be 2-D or 3-D")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"kp_linear: {name} needs a contiguous last dimension")
+    return b, rows, ld, sb
+
+
+def linear(a, w, out, alpha: float = 1.0, stream=None) -> None:
+    """out[b] = alpha * a[b] @ w[b]^T (kp_linear).  a [.., M, K] and w [.., N, K] bf16; out [.., M, N] bf16 or
+    float32.  2-D operands are shared by every batch entry; 3-D ones give the batch (views with any row and batch
+    strides, last dimension contiguous)."""
+    import torch
+    ba, M, lda, sa = _mat3(a, "a")
+    bw, N, ldw, sw = _mat3(w, "w")
+    bc, Mc, ldc, sc = _mat3(out, "out")
+    batch = max(ba, bw, bc)
+    if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("kp_linear: a and w must be bfloat16")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("kp_linear: out must be bfloat16 or float32")
+    if any(x not in (1, batch) for x in (ba, bw, bc)) or bc != batch or Mc != M or out.shape[-1] != N \
+            or w.shape[-1] != a.shape[-1]:
+        raise ValueError(f"kp_linear: shapes {tuple(a.shape)} x {tuple(w.shape)} -> {tuple(out.shape)} disagree")
+    c_dtype = KP_DTYPE_BF16 if out.dtype == torch.bfloat16 else KP_DTYPE_F32
+    _check("kp_linear", load().kp_linear(batch, M, N, a.shape[-1], _ptr(a), lda, sa, _ptr(w), ldw, sw, _ptr(out),
+                                         ldc, sc, c_dtype, float(alpha), _stream(stream)))
+
+
+def indexer_project(x, cq, w_q, w_w, w_kg, q_idx, w, keys, gates, stream=None) -> None:
+    """The indexer's projections: q_idx [T, Hi, D] = cq @ w_q^T (head-major), w [T, Hi] (float32) = x @ w_w^T,
+    keys | gates [T, D] = x @ w_kg^T split after D columns (key first)."""
+    T, D = x.shape[0], keys.shape[-1]
+    linear(cq, w_q, q_idx.view(T, -1), stream=stream)
+    linear(x, w_w, w, stream=stream)
+    linear(x, w_kg[:D], keys, stream=stream)
+    linear(x, w_kg[D:2 * D], gates, stream=stream)
+
+
+def mla_absorb_q(q_nope, w_uk_t, q, stream=None) -> None:
+    """Query in latent space, per head: q[t, h, :V] = W_UK[h]^T q_nope[t, h].  q_nope [T, H, dn] bf16, w_uk_t
+    [H, V, dn] (W_UK[h] transposed, prepared once), q [T, H, L] bf16 (columns V..L-1 are left as they are)."""
+    V = w_uk_t.shape[1]
+    linear(q_nope.transpose(0, 1), w_uk_t, q[:, :, :V].transpose(0, 1), stream=stream)
+
+
+def mla_unabsorb_o(o_lat, w_uv, o, stream=None) -> None:
+    """Head output from the latent output: o[t, h] = W_UV[h] o_lat[t, h].  o_lat [T, H, V] bf16, w_uv [H, dv, V],
+    o [T, H, dv] (bf16 or float32)."""
+    linear(o_lat.transpose(0, 1), w_uv, o.transpose(0, 1), stream=stream)

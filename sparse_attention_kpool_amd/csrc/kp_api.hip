@@ -90,7 +90,7 @@ using namespace kp;
 
 extern "C" {
 
-int32_t kp_abi_version(void) { return 3; }
+int32_t kp_abi_version(void) { return 4; }
 
 const char* kp_last_error(void) { return g_err; }
 
@@ -292,6 +292,42 @@ kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const 
                               void* workspace, size_t ws_bytes, void* stream) {
   return attn_call("sparse_mla_attn_fp8", true, kv_scale, dims, cache, queries, q, sel, n_sel, nullptr, out, lse,
                    workspace, ws_bytes, stream);
+}
+
+kp_status kp_linear(int32_t batch, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int64_t stride_a,
+                    const void* W, int64_t ldw, int64_t stride_w, void* C, int64_t ldc, int64_t stride_c,
+                    int32_t c_dtype, float alpha, void* stream) {
+  const char* fn = "kp_linear";
+  KP_REQUIRE(batch >= 0 && M >= 0 && N >= 0, KP_ERR_INVALID_ARG, "%s: negative batch, M or N", fn);
+  if (batch == 0 || M == 0 || N == 0) return KP_OK;
+  KP_REQUIRE(K >= 64 && K % 64 == 0, KP_ERR_UNSUPPORTED, "%s: K = %d is not a positive multiple of 64", fn, K);
+  KP_REQUIRE(c_dtype == KP_DTYPE_BF16 || c_dtype == KP_DTYPE_F32, KP_ERR_INVALID_ARG, "%s: bad c_dtype", fn);
+  KP_REQUIRE(A && W && C, KP_ERR_INVALID_ARG, "%s: NULL operand", fn);
+  KP_REQUIRE(aligned(A) && aligned(W) && aligned(C), KP_ERR_INVALID_ARG, "%s: misaligned operand", fn);
+  KP_REQUIRE(lda >= K && ldw >= K && ldc >= N, KP_ERR_INVALID_ARG, "%s: leading dimension below K or N", fn);
+  KP_REQUIRE(lda % 8 == 0 && ldw % 8 == 0 && stride_a % 8 == 0 && stride_w % 8 == 0 && stride_a >= 0 &&
+                 stride_w >= 0,
+             KP_ERR_INVALID_ARG, "%s: A / W row and batch strides must be non-negative multiples of 8", fn);
+  KP_REQUIRE(ldc % 4 == 0 && stride_c % 4 == 0 && stride_c >= 0, KP_ERR_INVALID_ARG,
+             "%s: C row and batch strides must be non-negative multiples of 4", fn);
+  KP_REQUIRE(isfinite(alpha), KP_ERR_INVALID_ARG, "%s: alpha is not finite", fn);
+  LinearLaunch a{};
+  a.batch = batch;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.c_dtype = c_dtype;
+  a.A = A;
+  a.lda = lda;
+  a.sa = stride_a;
+  a.W = W;
+  a.ldw = ldw;
+  a.sw = stride_w;
+  a.C = C;
+  a.ldc = ldc;
+  a.sc = stride_c;
+  a.alpha = alpha;
+  return launch_linear(a, (hipStream_t)stream);
 }
 
 }  // extern "C"

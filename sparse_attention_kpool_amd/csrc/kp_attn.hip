@@ -83,35 +83,13 @@ struct AttnShape {
 // in 256-byte aligned buffers, each read address is a per-lane base XOR a constant.
 __device__ __forceinline__ int attn_swz(int r) { return 2 * (r & 3) + 8 * ((r >> 3) & 1) + ((r >> 2) & 1); }
 
-// LDS byte offset of a pointer into shared memory, and a load from such an offset
-__device__ __forceinline__ uint32_t lds_off(const void* p) {
-  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
-}
-template <class F>
-__device__ __forceinline__ F lds_load(uint32_t off) {
-  return *reinterpret_cast<__attribute__((address_space(3))) const F*>(uintptr_t(off));
-}
+// Two LDS transpose reads (ds_read_b64_tr_b16) joined into one 8-element MFMA fragment
 __device__ __forceinline__ bf16x8 lds_tr_pair(uint32_t o1, uint32_t o2) {
   const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t(o1)));
   const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t(o2)));
   const uint2 u1 = __builtin_bit_cast(uint2, v1), u2 = __builtin_bit_cast(uint2, v2);
   return __builtin_bit_cast(bf16x8, make_uint4(u1.x, u1.y, u2.x, u2.y));
 }
-
-// One wave-wide 16-byte direct load from global memory into LDS: lane l's 16 bytes at `src` land at LDS byte
-// offset lds + 16 l.  Written as assembly so the compiler adds no waits of its own: the loop waits with explicit
-// vector-memory counts.  The instruction writes no VGPR; M0 carries the LDS offset (one wait state after it is
-// written).  (M0 is a reserved register: the compiler warns that clobbering it may be unsafe, but it keeps no
-// value in M0 across these statements -- this file makes no other use of it.)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void attn_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding (lgkm and exp free)
-constexpr int attn_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // 1 KiB of zeros: the source row of a slot with no token (past the split or past the query), so the O product
 // multiplies its zero weight by zeros, never by whatever a cache row holds
@@ -602,7 +580,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
       const int c = lane ^ attn_swz(slot);
       const void* src = e >= 0 ? static_cast<const void*>(latent + int64_t(e) * L + c * S::EPC)
                                : static_cast<const void*>(attn_zero_row + 4 * lane);
-      attn_dma16(src, base + uint32_t(slot * V * int(sizeof(T))));
+      lds_dma16(src, base + uint32_t(slot * V * int(sizeof(T))));
     }
   };
 
@@ -716,7 +694,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
     load_block(1, block_rows(1));
     int rows_next = block_rows(2);
     for (int j = 0; j <= nblk; ++j) {
-      __builtin_amdgcn_s_waitcnt(attn_vmcnt(S::CHT));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::CHT));
       __syncthreads();
       load_block(j + 2, rows_next);
       rows_next = block_rows(j + 3);
@@ -770,10 +748,10 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
     load8(fp8_rows(0), R0);
     load8(fp8_rows(1), R1);
     load8(fp8_rows(2), R2);
-    __builtin_amdgcn_s_waitcnt(attn_vmcnt(4));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
     store8(0, R0);
     load8(fp8_rows(3), R0);
-    __builtin_amdgcn_s_waitcnt(attn_vmcnt(4));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
     store8(1, R1);
     load8(fp8_rows(4), R1);
     // Iteration j: the barrier publishes block j + 1 (written in iteration j - 1); after it every wave is past
@@ -783,7 +761,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
     // oldest block is exact.
     auto iter = [&](int j, u32x4(&R)[2]) __attribute__((always_inline)) {
       __syncthreads();
-      __builtin_amdgcn_s_waitcnt(attn_vmcnt(4));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
       store8(j + 2, R);
       load8(fp8_rows(j + 5), R);
       if (o_wave) {

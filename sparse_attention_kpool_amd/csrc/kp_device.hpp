@@ -123,5 +123,29 @@ __device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v, uint32_t& total) {
   return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
+// LDS byte offset of a pointer into shared memory, and a load from such an offset
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+template <class F>
+__device__ __forceinline__ F lds_load(uint32_t off) {
+  return *reinterpret_cast<__attribute__((address_space(3))) const F*>(uintptr_t(off));
+}
+
+// One wave-wide 16-byte direct load from global memory into LDS: lane l's 16 bytes at `src` land at LDS byte
+// offset lds + 16 l.  Written as assembly so the compiler adds no waits of its own: callers wait with explicit
+// vector-memory counts.  The instruction writes no VGPR; M0 carries the LDS offset (one wait state after it is
+// written).  (M0 is a reserved register: the compiler warns that clobbering it may be unsafe, but it keeps no
+// value in M0 across these statements -- no kernel here makes other use of it.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding (lgkm and exp free)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 }  // namespace kp
 

@@ -83,4 +83,16 @@ int attn_splits(int P, int k, int n_q);
 size_t attn_workspace(int P, int k, int H, int V, int n_q, int esize);
 kp_status launch_attn(const AttnLaunch& a, hipStream_t s);
 
+struct LinearLaunch {
+  int batch, M, N, K, c_dtype;
+  const void* A;
+  int64_t lda, sa;
+  const void* W;
+  int64_t ldw, sw;
+  void* C;
+  int64_t ldc, sc;
+  float alpha;
+};
+kp_status launch_linear(const LinearLaunch& a, hipStream_t s);
+
 }  // namespace kp

@@ -304,21 +304,6 @@ struct PrefillTile {
   static_assert((SC_PTHREADS / CPR) % (SWZ + 1) == 0, "a thread's chunk position is the same in all its loads");
 };
 
-// One wave-wide 16-byte direct load from global memory into LDS: lane l's 16 bytes at `src` land at LDS byte
-// address lds + 16 * l.  Written as assembly so that the compiler, which cannot tell the LDS buffers of the tile
-// pipeline apart here, adds no waits of its own for it: callers wait with explicit vector-memory counts.  The
-// instruction writes no VGPR; M0 carries the LDS address (one wait state after it is written).
-// (M0 is a reserved register: the compiler warns that clobbering it may be unsafe, but it keeps no value in M0
-// across these statements -- this file makes no other use of it.)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding (lgkm and exp free)
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <class T, int D>
 __global__ __launch_bounds__(SC_PTHREADS, 2) void score_prefill_kernel(
@@ -433,7 +418,7 @@ __global__ __launch_bounds__(SC_PTHREADS, 2) void score_prefill_kernel(
         pool = pool < p_end ? pool : p_begin;
         const int64_t prow = (int64_t(pg[i]) << log2_ppp) + (pool & ppp_mask);
         const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(tile_buf(buf)));  // the LDS offset
-        dma16(pooled + prow * D + c * PT::EPC, lds + uint32_t((i * SC_PTHREADS + wave_u * 64) * 16));
+        lds_dma16(pooled + prow * D + c * PT::EPC, lds + uint32_t((i * SC_PTHREADS + wave_u * 64) * 16));
       }
     };
     F kb[S::STEPS];  // B operands of the column block being computed

@@ -21,7 +21,7 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_fp8",
-              "sparse_mla_attn_shared",
+              "sparse_mla_attn_shared", "kp_linear",
               "dsa_topk_workspace_size", "sparse_mla_workspace_size", "kp_last_error", "kp_abi_version"):
         assert f in names
     assert set(names) == set(K.EXPORTED)
@@ -129,3 +129,33 @@ def test_binding_raises_without_library(tmp_path, monkeypatch):
     with pytest.raises(RuntimeError, match="no CPU or PyTorch fallback"):
         K.load(str(tmp_path / "missing.so"))
     importlib.reload(K)
+
+
+def _linear(batch=1, M=64, N=64, k=128, A=FAKE, lda=128, sa=0, W=FAKE, ldw=128, sw=0, C=FAKE, ldc=64, sc=0,
+            c_dtype=K.KP_DTYPE_BF16, alpha=1.0):
+    return K.load().kp_linear(batch, M, N, k, A, lda, sa, W, ldw, sw, C, ldc, sc, c_dtype, alpha, None)
+
+
+def test_linear_validation():
+    """kp_linear rejects every bad argument before launching anything (no GPU is touched here)."""
+    ok_empty = [dict(batch=0), dict(M=0), dict(N=0), dict(M=0, A=None)]
+    for kw in ok_empty:
+        assert _linear(**kw) == K.KP_OK, kw
+    bad = [
+        (dict(batch=-1), K.KP_ERR_INVALID_ARG),
+        (dict(k=96, lda=96, ldw=96), K.KP_ERR_UNSUPPORTED),     # not a multiple of 64
+        (dict(k=0), K.KP_ERR_UNSUPPORTED),
+        (dict(c_dtype=7), K.KP_ERR_INVALID_ARG),
+        (dict(A=None), K.KP_ERR_INVALID_ARG),
+        (dict(W=FAKE + 8), K.KP_ERR_INVALID_ARG),               # misaligned
+        (dict(lda=64), K.KP_ERR_INVALID_ARG),                   # below K
+        (dict(ldc=60), K.KP_ERR_INVALID_ARG),                   # below N
+        (dict(lda=132), K.KP_ERR_INVALID_ARG),                  # not a multiple of 8
+        (dict(sw=4), K.KP_ERR_INVALID_ARG),
+        (dict(ldc=66), K.KP_ERR_INVALID_ARG),                   # not a multiple of 4
+        (dict(sc=-4), K.KP_ERR_INVALID_ARG),
+        (dict(alpha=float("inf")), K.KP_ERR_INVALID_ARG),
+    ]
+    for kw, code in bad:
+        assert _linear(**kw) == code, kw
+        assert "kp_linear" in K.last_error()

@@ -1,0 +1,163 @@
+"""GPU parity of kp_linear (the dense projections beside the path) against the oracle, through the C ABI.
+
+Shapes are the layer's (GLM-5.3-Flash model card: hidden 4096, q_lora 1536, 32 index heads x 128, 64 MLA heads,
+kv_lora 512, qk_nope = v_head = 256) at a decode step of 64 tokens, ragged token counts (several tiles plus a
+tail) and a 4096-token prefill chunk checked on sampled rows.
+Bar: integer-valued operands ('int') make every fp32 sum exact, so fp32 outputs are bit-exact and bf16 outputs
+equal the oracle's nearest-even rounding of the exact value.  Normal operands: |gpu - ref| <= 2^-8 |ref| +
+2^-14 sum_k |a_k w_k| for bf16 outputs (one rounding plus fp32 accumulation), 2^-14 sum_k |a_k w_k| for fp32.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kpool_synth as ks
+import oracle as O
+import sparse_attention_kpool_amd as K
+
+pytestmark = pytest.mark.gpu
+
+HIDDEN, Q_RANK, HI, D, H, V, DN, DV, L = 4096, 1536, 32, 128, 64, 512, 256, 256, 576
+SEED = 21
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(x, dtype=torch.bfloat16):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda", dtype)
+
+
+def _check(got, ref, abs_sum, out_bf16: bool, exact: bool, what: str):
+    got = np.asarray(got, dtype=np.float64)
+    if exact:
+        want = O.bf16_round(ref) if out_bf16 else ref
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {tuple(bad[0])}: {got[tuple(bad[0])]} vs " \
+                              f"{want[tuple(bad[0])]}"
+        return
+    tol = 2.0 ** -14 * abs_sum + (2.0 ** -8 * np.abs(ref) if out_bf16 else 0.0)
+    err = np.abs(got - ref)
+    worst = np.unravel_index(np.argmax(err - tol), err.shape)
+    assert np.all(err <= tol), f"{what}: error {err[worst]:.3g} > tol {tol[worst]:.3g} at {worst}"
+
+
+def _plain(T, N, K_, kind, out_dtype, tag, ldc=None, scale_a=1.0, scale_w=2.0 ** -6):
+    """One unbatched product A [T, K] x W [N, K]^T -> C [T, N] (row stride ldc)."""
+    _say(f"linear {tag}: T={T} N={N} K={K_} kind={kind} out={out_dtype}")
+    a = ks.host_matrix(SEED, f"{tag}:a", (T, K_), kind, 1.0 if kind == "int" else scale_a)
+    w = ks.host_matrix(SEED, f"{tag}:w", (N, K_), kind, 1.0 if kind == "int" else scale_w)
+    ldc = ldc or N
+    c_full = torch.full((T, ldc), 3.0, dtype=out_dtype, device="cuda")
+    c = c_full[:, :N]
+    K.linear(_dev(a), _dev(w), c, alpha=1.0)
+    torch.cuda.synchronize()
+    got = c.float().cpu().numpy()
+    ref = O.linear(a, w)
+    abs_sum = O.linear(np.abs(a), np.abs(w))
+    _check(got, ref, abs_sum, out_dtype == torch.bfloat16, kind == "int", tag)
+    if ldc > N:  # the padding columns are never written
+        assert torch.all(c_full[:, N:] == 3.0).item(), f"{tag}: wrote past column N"
+
+
+@pytest.mark.parametrize("kind", ["int", "normal"])
+def test_index_query_projection_decode(kind):
+    _plain(64, HI * D, Q_RANK, kind, torch.bfloat16, f"qidx-{kind}")
+
+
+@pytest.mark.parametrize("kind", ["int", "normal"])
+def test_head_weight_projection_fp32_out(kind):
+    _plain(64, HI, HIDDEN, kind, torch.float32, f"w-{kind}")
+
+
+def test_ragged_rows_and_columns():
+    """Token counts that leave a partial tile (77 in one 128-row tile; 300 over three) and a column count that
+    leaves a partial 4-column group (198, row stride 200)."""
+    _plain(77, 198, 512, "int", torch.bfloat16, "ragged77", ldc=200)
+    _plain(300, 198, 256, "int", torch.float32, "ragged300", ldc=200)
+    _plain(5, 70, 128, "normal", torch.bfloat16, "ragged5", ldc=72)
+    _plain(1, 64, 64, "int", torch.float32, "single")
+
+
+def test_indexer_projections_key_then_gate():
+    T = 64
+    _say(f"indexer_project: T={T}")
+    x = ks.host_matrix(SEED, "ip:x", (T, HIDDEN), "int")
+    cq = ks.host_matrix(SEED, "ip:cq", (T, Q_RANK), "int")
+    w_q = ks.host_matrix(SEED, "ip:wq", (HI * D, Q_RANK), "int")
+    w_w = ks.host_matrix(SEED, "ip:ww", (HI, HIDDEN), "int")
+    w_kg = ks.host_matrix(SEED, "ip:wkg", (2 * D, HIDDEN), "int")
+    q_idx = torch.empty((T, HI, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((T, HI), dtype=torch.float32, device="cuda")
+    keys = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    gates = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    K.indexer_project(_dev(x), _dev(cq), _dev(w_q), _dev(w_w), _dev(w_kg), q_idx, w, keys, gates)
+    torch.cuda.synchronize()
+    r_q, r_w, r_k, r_g = O.indexer_project(x, cq, w_q, w_w, w_kg, HI, D)
+    np.testing.assert_array_equal(q_idx.float().cpu().numpy(), O.bf16_round(r_q))
+    np.testing.assert_array_equal(w.cpu().numpy(), r_w)
+    np.testing.assert_array_equal(keys.float().cpu().numpy(), O.bf16_round(r_k))
+    np.testing.assert_array_equal(gates.float().cpu().numpy(), O.bf16_round(r_g))
+
+
+@pytest.mark.parametrize("T,kind", [(64, "int"), (64, "normal"), (300, "normal")])
+def test_mla_absorb_query(T, kind):
+    """q[t, h, :V] = W_UK[h]^T q_nope[t, h] for all 64 heads (one batch entry per head); the rotary columns of q
+    keep what they held."""
+    _say(f"mla_absorb_q: T={T} kind={kind}")
+    q_nope = ks.host_matrix(SEED, f"ab{T}:q", (T, H, DN), kind)
+    w_uk = ks.host_matrix(SEED, f"ab{T}:w", (H, DN, V), kind, 1.0 if kind == "int" else 2.0 ** -4)
+    q = torch.full((T, H, L), 5.0, dtype=torch.bfloat16, device="cuda")
+    w_uk_t = _dev(np.ascontiguousarray(np.transpose(w_uk, (0, 2, 1))))  # [H, V, dn], prepared once per layer
+    K.mla_absorb_q(_dev(q_nope), w_uk_t, q)
+    torch.cuda.synchronize()
+    got = q.float().cpu().numpy()
+    ref = O.mla_absorb_q(q_nope, w_uk)
+    abs_sum = O.mla_absorb_q(np.abs(q_nope), np.abs(w_uk))
+    _check(got[:, :, :V], ref, abs_sum, True, kind == "int", "absorb")
+    assert np.all(got[:, :, V:] == 5.0), "absorb wrote into the rotary columns"
+
+
+@pytest.mark.parametrize("T,kind", [(64, "int"), (64, "normal"), (77, "normal")])
+def test_mla_unabsorb_output(T, kind):
+    _say(f"mla_unabsorb_o: T={T} kind={kind}")
+    o_lat = ks.host_matrix(SEED, f"un{T}:o", (T, H, V), kind)
+    w_uv = ks.host_matrix(SEED, f"un{T}:w", (H, DV, V), kind, 1.0 if kind == "int" else 2.0 ** -4)
+    o = torch.empty((T, H, DV), dtype=torch.bfloat16, device="cuda")
+    K.mla_unabsorb_o(_dev(o_lat), _dev(w_uv), o)
+    torch.cuda.synchronize()
+    ref = O.mla_unabsorb_o(o_lat, w_uv)
+    abs_sum = O.mla_unabsorb_o(np.abs(o_lat), np.abs(w_uv))
+    _check(o.float().cpu().numpy(), ref, abs_sum, True, kind == "int", "unabsorb")
+
+
+def test_prefill_index_query_sampled_rows():
+    """The 4096-token prefill chunk through the 128 x 128 tile path; 256 sampled rows, every column."""
+    T = 4096
+    _say(f"linear prefill: T={T} N={HI * D} K={Q_RANK}")
+    a = ks.host_matrix(SEED, "pf:a", (T, Q_RANK), "normal")
+    w = ks.host_matrix(SEED, "pf:w", (HI * D, Q_RANK), "normal", 2.0 ** -6)
+    c = torch.empty((T, HI * D), dtype=torch.bfloat16, device="cuda")
+    K.linear(_dev(a), _dev(w), c)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(5).choice(T, 256, replace=False))
+    rows[0], rows[-1] = 0, T - 1
+    got = c[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    ref = O.linear(a[rows], w)
+    _check(got, ref, O.linear(np.abs(a[rows]), np.abs(w)), True, False, "prefill qidx")
+
+
+def test_linear_alpha_and_shared_weight_batch():
+    """alpha scales once before the rounding; a 2-D weight is shared by every batch entry (stride 0)."""
+    _say("linear alpha / shared weight")
+    a = ks.host_matrix(SEED, "al:a", (3, 40, 256), "int")
+    w = ks.host_matrix(SEED, "al:w", (96, 256), "int")
+    c = torch.empty((3, 40, 96), dtype=torch.float32, device="cuda")
+    K.linear(_dev(a), _dev(w), c, alpha=0.25)
+    torch.cuda.synchronize()
+    ref = np.stack([O.linear(a[b], w, alpha=0.25) for b in range(3)])
+    np.testing.assert_array_equal(c.cpu().numpy(), ref)
