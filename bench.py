@@ -244,6 +244,88 @@ def cpu_baseline(wl, n_sample: int, min_seconds: float = 10.0) -> dict:
                       f"layer per query (pool, score, select, attend) in float64 numpy; host input regeneration "
                       f"not timed"}
 
+# the dense projections beside the path (kp_linear) at the layer's shapes: hidden 4096, q_lora 1536, 32 index heads
+# x 128, 64 MLA heads, kv_lora 512, qk_nope = v_head = 256
+PROJ_HIDDEN, PROJ_QRANK, PROJ_HI, PROJ_D, PROJ_H, PROJ_V, PROJ_DN, PROJ_DV, PROJ_L = 4096, 1536, 32, 128, 64, 512, \
+    256, 256, 576
+
+
+def proj_leg(T: int, reps: int, split: bool = True) -> dict:
+    """Time each projection of a T-token step (HIP events around a graph replay of `reps` calls, mean per call)
+    and all five back to back.  Inputs: seeded N(0, 1) draws (weights x 2^-6) rounded to bf16."""
+    import torch
+    import sparse_attention_kpool_amd as K
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234 + T)
+
+    def mat(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=gen, device="cuda") * scale).to(torch.bfloat16)
+    hid, qr, Hi, D, H, V, dn, dv, L = (PROJ_HIDDEN, PROJ_QRANK, PROJ_HI, PROJ_D, PROJ_H, PROJ_V, PROJ_DN, PROJ_DV,
+                                       PROJ_L)
+    x, cq = mat(T, hid), mat(T, qr)
+    w_q, w_w, w_kg = mat(Hi * D, qr, scale=2 ** -6), mat(Hi, hid, scale=2 ** -6), mat(2 * D, hid, scale=2 ** -6)
+    q_nope, w_uk_t, w_uv = mat(T, H, dn), mat(H, V, dn, scale=2 ** -6), mat(H, dv, V, scale=2 ** -6)
+    o_lat = mat(T, H, V)
+    q_idx = torch.empty(T, Hi * D, dtype=torch.bfloat16, device="cuda")
+    w = torch.empty(T, Hi, dtype=torch.float32, device="cuda")
+    keys = torch.empty(T, D, dtype=torch.bfloat16, device="cuda")
+    gates = torch.empty(T, D, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(T, H, L, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty(T, H, dv, dtype=torch.bfloat16, device="cuda")
+    # one split-K workspace for all five
+    ws_n = max(K.linear_workspace_size(1, T, Hi * D, qr), K.linear_workspace_size(1, T, Hi, hid),
+               K.linear_workspace_size(1, T, D, hid), K.linear_workspace_size(H, T, V, dn),
+               K.linear_workspace_size(H, T, dv, V))
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device="cuda") if (ws_n and split) else None
+    # name: (call, flops, algorithmic bytes = operands read once + output written once)
+    calls = {
+        "index_query": (lambda: K.linear(cq, w_q, q_idx, workspace=ws), 2 * T * Hi * D * qr,
+                        2 * (T * qr + Hi * D * qr + T * Hi * D)),
+        "head_weights": (lambda: K.linear(x, w_w, w, workspace=ws), 2 * T * Hi * hid, 2 * (T * hid + Hi * hid) + 4 * T * Hi),
+        "key_gate": (lambda: (K.linear(x, w_kg[:D], keys, workspace=ws), K.linear(x, w_kg[D:], gates, workspace=ws)),
+                     2 * T * 2 * D * hid,
+                     2 * (2 * T * hid + 2 * D * hid + 2 * T * D)),
+        "absorb": (lambda: K.mla_absorb_q(q_nope, w_uk_t, q, workspace=ws), 2 * T * H * V * dn,
+                   2 * (T * H * dn + H * V * dn + T * H * V)),
+        "unabsorb": (lambda: K.mla_unabsorb_o(o_lat, w_uv, o, workspace=ws), 2 * T * H * dv * V,
+                     2 * (T * H * V + H * dv * V + T * H * dv)),
+    }
+
+    def timed(f):
+        # `reps` calls captured in one HIP graph and replayed: a decode-sized product runs for less time than one
+        # Python call takes to launch it, so timing eager calls would time the host
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) / reps * 1e3  # us
+    out = {"tokens": T, "calls": {}}
+    for name, (f, fl, by) in calls.items():
+        us = timed(f)
+        out["calls"][name] = {"us": round(us, 2), "tflops": round(fl / (us * 1e-6) / 1e12, 2),
+                              "gbs": round(by / (us * 1e-6) / 1e9, 1)}
+    us = timed(lambda: [f() for f, _, _ in calls.values()])
+    fl = sum(c[1] for c in calls.values())
+    by = sum(c[2] for c in calls.values())
+    out.update(us=round(us, 2), flops=fl, bytes=by, tflops=round(fl / (us * 1e-6) / 1e12, 2),
+               frac_of_bf16_peak=round(fl / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+               gbs=round(by / (us * 1e-6) / 1e9, 1), hbm_frac=round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+    del x, cq, w_q, w_w, w_kg, q_nope, w_uk_t, w_uv, o_lat, q_idx, w, keys, gates, q, o, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 
 # ----------------------------------------------------------------------------------------------------------
 def main():
@@ -251,7 +333,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,128k,long1m,fp8,prefill,copy")
+    ap.add_argument("--legs", default="decode,128k,long1m,fp8,prefill,proj,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=16)
     args = ap.parse_args()
@@ -340,6 +422,10 @@ def main():
                                   "ms": round(st["score"], 4), "flops": fl, "step_ms": round(ms, 4),
                                   "stages_ms": {k: round(v, 4) for k, v in st.items()}}
         leg.free()
+    if "proj" in legs:
+        print("[bench] proj leg: the five projections at 64 tokens (decode) and 4096 tokens (prefill)",
+              file=sys.stderr, flush=True)
+        res["projections"] = {"decode64": proj_leg(64, 200), "prefill4096": proj_leg(4096, 20)}
     if "copy" in legs:
         print("[bench] copy leg: 1 GiB device copy", file=sys.stderr, flush=True)
         n = 1 << 28

@@ -222,7 +222,12 @@ kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const 
  *   W: device bf16, row n of batch b at W + b*stride_w + n*ldw, k contiguous (a weight stored output-major).
  *   C: device, c_dtype (KP_DTYPE_BF16: rounded once, nearest-even; KP_DTYPE_F32), row m at C + b*stride_c +
  *     m*ldc, n contiguous.  A stride of 0 reuses one matrix for every batch entry.
- *   Accumulation is fp32 over k in an order that does not depend on M, N or the batch.
+ *   Accumulation is fp32; the result is a deterministic function of the operands and the call shape.
+ *   workspace (device, may be NULL, no initial contents): with at least kp_linear_workspace_size(batch, M, N, K)
+ *     bytes, a shape whose output tiles are too few to keep every compute unit streaming (a decode step) splits K
+ *     over several blocks that store fp32 partial tiles there; a second kernel on the same stream adds them in
+ *     split order.  Calls that share a workspace must not overlap (same stream, or ordered).  NULL or smaller: no
+ *     split, same formula (the sum may round differently).  A size of 0 means this shape never splits.
  *   The layer's projections (T tokens, hidden 4096, q_lora 1536, Hi = 32, D = 128, H = 64, dn = dv = 256):
  *     index query   A = cq [T, 1536], W = W_iq [Hi*D, 1536] (head-major rows)  -> C = q_idx [T, Hi*D] bf16
  *     head weights  A = x [T, 4096],  W = W_w [Hi, 4096]                       -> C = w [T, Hi] f32
@@ -234,10 +239,12 @@ kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const 
  *   Limits: K a multiple of 64; lda, ldw, stride_a, stride_w multiples of 8; ldc, stride_c multiples of 4;
  *   lda, ldw >= K; ldc >= N; every operand 16-byte aligned.  batch, M or N = 0 is a valid empty call.
  *   Errors: KP_ERR_INVALID_ARG (pointers, strides, alignment, c_dtype, alpha not finite), KP_ERR_UNSUPPORTED (K).
+ *   kp_linear_workspace_size: bytes of split-K workspace for a shape (0: never splits); host only.
  */
+size_t kp_linear_workspace_size(int32_t batch, int32_t M, int32_t N, int32_t K);
 kp_status kp_linear(int32_t batch, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int64_t stride_a,
                     const void* W, int64_t ldw, int64_t stride_w, void* C, int64_t ldc, int64_t stride_c,
-                    int32_t c_dtype, float alpha, void* stream);
+                    int32_t c_dtype, float alpha, void* workspace, size_t ws_bytes, void* stream);
 
 /* Message of the last failed call on this thread ("" if none).  Owned by the library. */
 const char* kp_last_error(void);

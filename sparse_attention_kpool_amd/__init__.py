@@ -25,7 +25,7 @@ ABI_VERSION = 4
 
 EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk_select",
             "sparse_mla_workspace_size", "sparse_mla_attn", "sparse_mla_attn_shared", "sparse_mla_attn_fp8",
-            "kp_linear", "kp_last_error", "kp_abi_version")
+            "kp_linear", "kp_linear_workspace_size", "kp_last_error", "kp_abi_version")
 
 
 class KpError(RuntimeError):
@@ -77,7 +77,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_mla_attn_fp8.argtypes = [D, C, Q, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.sparse_mla_attn_shared.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kp_linear.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, ctypes.c_float,
-                              vp]
+                              vp, sz, vp]
+    lib.kp_linear_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.kp_linear_workspace_size.restype = sz
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_shared",
               "sparse_mla_attn_fp8", "kp_linear"):
         getattr(lib, f).restype = ctypes.c_int
@@ -236,10 +238,16 @@ def _mat3(t, name: str):
     return b, rows, ld, sb
 
 
-def linear(a, w, out, alpha: float = 1.0, stream=None) -> None:
+def linear_workspace_size(batch: int, M: int, N: int, K: int) -> int:
+    """Bytes of split-K workspace kp_linear can use for this shape (0: it never splits)."""
+    return int(load().kp_linear_workspace_size(batch, M, N, K))
+
+
+def linear(a, w, out, alpha: float = 1.0, workspace=None, stream=None) -> None:
     """out[b] = alpha * a[b] @ w[b]^T (kp_linear).  a [.., M, K] and w [.., N, K] bf16; out [.., M, N] bf16 or
     float32.  2-D operands are shared by every batch entry; 3-D ones give the batch (views with any row and batch
-    strides, last dimension contiguous)."""
+    strides, last dimension contiguous).  workspace: a device tensor of at least linear_workspace_size(...) bytes
+    (any contents), reused across calls (None: no split-K)."""
     import torch
     ba, M, lda, sa = _mat3(a, "a")
     bw, N, ldw, sw = _mat3(w, "w")
@@ -253,28 +261,30 @@ def linear(a, w, out, alpha: float = 1.0, stream=None) -> None:
             or w.shape[-1] != a.shape[-1]:
         raise ValueError(f"kp_linear: shapes {tuple(a.shape)} x {tuple(w.shape)} -> {tuple(out.shape)} disagree")
     c_dtype = KP_DTYPE_BF16 if out.dtype == torch.bfloat16 else KP_DTYPE_F32
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     _check("kp_linear", load().kp_linear(batch, M, N, a.shape[-1], _ptr(a), lda, sa, _ptr(w), ldw, sw, _ptr(out),
-                                         ldc, sc, c_dtype, float(alpha), _stream(stream)))
+                                         ldc, sc, c_dtype, float(alpha), _ptr(workspace), ws_bytes,
+                                         _stream(stream)))
 
 
-def indexer_project(x, cq, w_q, w_w, w_kg, q_idx, w, keys, gates, stream=None) -> None:
+def indexer_project(x, cq, w_q, w_w, w_kg, q_idx, w, keys, gates, workspace=None, stream=None) -> None:
     """The indexer's projections: q_idx [T, Hi, D] = cq @ w_q^T (head-major), w [T, Hi] (float32) = x @ w_w^T,
     keys | gates [T, D] = x @ w_kg^T split after D columns (key first)."""
     T, D = x.shape[0], keys.shape[-1]
-    linear(cq, w_q, q_idx.view(T, -1), stream=stream)
-    linear(x, w_w, w, stream=stream)
-    linear(x, w_kg[:D], keys, stream=stream)
-    linear(x, w_kg[D:2 * D], gates, stream=stream)
+    linear(cq, w_q, q_idx.view(T, -1), workspace=workspace, stream=stream)
+    linear(x, w_w, w, workspace=workspace, stream=stream)
+    linear(x, w_kg[:D], keys, workspace=workspace, stream=stream)
+    linear(x, w_kg[D:2 * D], gates, workspace=workspace, stream=stream)
 
 
-def mla_absorb_q(q_nope, w_uk_t, q, stream=None) -> None:
+def mla_absorb_q(q_nope, w_uk_t, q, workspace=None, stream=None) -> None:
     """Query in latent space, per head: q[t, h, :V] = W_UK[h]^T q_nope[t, h].  q_nope [T, H, dn] bf16, w_uk_t
     [H, V, dn] (W_UK[h] transposed, prepared once), q [T, H, L] bf16 (columns V..L-1 are left as they are)."""
     V = w_uk_t.shape[1]
-    linear(q_nope.transpose(0, 1), w_uk_t, q[:, :, :V].transpose(0, 1), stream=stream)
+    linear(q_nope.transpose(0, 1), w_uk_t, q[:, :, :V].transpose(0, 1), workspace=workspace, stream=stream)
 
 
-def mla_unabsorb_o(o_lat, w_uv, o, stream=None) -> None:
+def mla_unabsorb_o(o_lat, w_uv, o, workspace=None, stream=None) -> None:
     """Head output from the latent output: o[t, h] = W_UV[h] o_lat[t, h].  o_lat [T, H, V] bf16, w_uv [H, dv, V],
     o [T, H, dv] (bf16 or float32)."""
-    linear(o_lat.transpose(0, 1), w_uv, o.transpose(0, 1), stream=stream)
+    linear(o_lat.transpose(0, 1), w_uv, o.transpose(0, 1), workspace=workspace, stream=stream)

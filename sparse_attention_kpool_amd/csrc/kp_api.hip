@@ -294,9 +294,13 @@ kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const 
                    workspace, ws_bytes, stream);
 }
 
+size_t kp_linear_workspace_size(int32_t batch, int32_t M, int32_t N, int32_t K) {
+  return linear_workspace(batch, M, N, K);
+}
+
 kp_status kp_linear(int32_t batch, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int64_t stride_a,
                     const void* W, int64_t ldw, int64_t stride_w, void* C, int64_t ldc, int64_t stride_c,
-                    int32_t c_dtype, float alpha, void* stream) {
+                    int32_t c_dtype, float alpha, void* workspace, size_t ws_bytes, void* stream) {
   const char* fn = "kp_linear";
   KP_REQUIRE(batch >= 0 && M >= 0 && N >= 0, KP_ERR_INVALID_ARG, "%s: negative batch, M or N", fn);
   if (batch == 0 || M == 0 || N == 0) return KP_OK;
@@ -311,6 +315,7 @@ kp_status kp_linear(int32_t batch, int32_t M, int32_t N, int32_t K, const void* 
   KP_REQUIRE(ldc % 4 == 0 && stride_c % 4 == 0 && stride_c >= 0, KP_ERR_INVALID_ARG,
              "%s: C row and batch strides must be non-negative multiples of 4", fn);
   KP_REQUIRE(isfinite(alpha), KP_ERR_INVALID_ARG, "%s: alpha is not finite", fn);
+  KP_REQUIRE(!workspace || aligned(workspace), KP_ERR_INVALID_ARG, "%s: misaligned workspace", fn);
   LinearLaunch a{};
   a.batch = batch;
   a.M = M;
@@ -327,6 +332,8 @@ kp_status kp_linear(int32_t batch, int32_t M, int32_t N, int32_t K, const void* 
   a.ldc = ldc;
   a.sc = stride_c;
   a.alpha = alpha;
+  a.ws = workspace;
+  a.ws_bytes = workspace ? ws_bytes : 0;
   return launch_linear(a, (hipStream_t)stream);
 }
 

@@ -92,7 +92,10 @@ struct LinearLaunch {
   void* C;
   int64_t ldc, sc;
   float alpha;
+  void* ws;  // split-K partials and per-tile counters (NULL: no split)
+  size_t ws_bytes;
 };
+size_t linear_workspace(int batch, int M, int N, int K);
 kp_status launch_linear(const LinearLaunch& a, hipStream_t s);
 
 }  // namespace kp

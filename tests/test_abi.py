@@ -21,7 +21,7 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_fp8",
-              "sparse_mla_attn_shared", "kp_linear",
+              "sparse_mla_attn_shared", "kp_linear", "kp_linear_workspace_size",
               "dsa_topk_workspace_size", "sparse_mla_workspace_size", "kp_last_error", "kp_abi_version"):
         assert f in names
     assert set(names) == set(K.EXPORTED)
@@ -132,8 +132,8 @@ def test_binding_raises_without_library(tmp_path, monkeypatch):
 
 
 def _linear(batch=1, M=64, N=64, k=128, A=FAKE, lda=128, sa=0, W=FAKE, ldw=128, sw=0, C=FAKE, ldc=64, sc=0,
-            c_dtype=K.KP_DTYPE_BF16, alpha=1.0):
-    return K.load().kp_linear(batch, M, N, k, A, lda, sa, W, ldw, sw, C, ldc, sc, c_dtype, alpha, None)
+            c_dtype=K.KP_DTYPE_BF16, alpha=1.0, ws=None, ws_bytes=0):
+    return K.load().kp_linear(batch, M, N, k, A, lda, sa, W, ldw, sw, C, ldc, sc, c_dtype, alpha, ws, ws_bytes, None)
 
 
 def test_linear_validation():
@@ -155,7 +155,23 @@ def test_linear_validation():
         (dict(ldc=66), K.KP_ERR_INVALID_ARG),                   # not a multiple of 4
         (dict(sc=-4), K.KP_ERR_INVALID_ARG),
         (dict(alpha=float("inf")), K.KP_ERR_INVALID_ARG),
+        (dict(ws=FAKE + 4, ws_bytes=1 << 20), K.KP_ERR_INVALID_ARG),  # misaligned workspace
     ]
     for kw, code in bad:
         assert _linear(**kw) == code, kw
         assert "kp_linear" in K.last_error()
+
+
+def test_linear_workspace_sizes():
+    """Decode-shaped products (few output tiles) ask for split-K workspace; shapes with enough tiles, or too short a
+    K, need none."""
+    ws = K.linear_workspace_size
+    assert ws(1, 64, 4096, 1536) > 0          # index query at a 64-token step: 64 tiles
+    assert ws(1, 64, 32, 4096) > 0            # head weights: one tile, long K
+    assert ws(1, 4096, 4096, 1536) == 0       # prefill: 1024 tiles
+    assert ws(64, 64, 512, 256) == 0          # absorb at a decode step: 512 tiles, 4 stages
+    assert ws(1, 64, 64, 64) == 0             # one stage: nothing to split
+    assert ws(0, 64, 64, 4096) == 0 and ws(1, 0, 64, 4096) == 0
+    # fp32 partial tiles: 64 x 64 per split of each tile
+    n = ws(1, 64, 32, 4096)
+    assert n > 0 and n % (64 * 64 * 4) == 0

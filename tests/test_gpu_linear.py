@@ -46,15 +46,23 @@ def _check(got, ref, abs_sum, out_bf16: bool, exact: bool, what: str):
     assert np.all(err <= tol), f"{what}: error {err[worst]:.3g} > tol {tol[worst]:.3g} at {worst}"
 
 
-def _plain(T, N, K_, kind, out_dtype, tag, ldc=None, scale_a=1.0, scale_w=2.0 ** -6):
-    """One unbatched product A [T, K] x W [N, K]^T -> C [T, N] (row stride ldc)."""
-    _say(f"linear {tag}: T={T} N={N} K={K_} kind={kind} out={out_dtype}")
+def _workspace(batch, M, N, K_):
+    """Split-K workspace for a shape, filled with a non-zero pattern: its contents must not matter."""
+    n = K.linear_workspace_size(batch, M, N, K_)
+    return torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda") if n else None
+
+
+def _plain(T, N, K_, kind, out_dtype, tag, ldc=None, scale_a=1.0, scale_w=2.0 ** -6, split=True):
+    """One unbatched product A [T, K] x W [N, K]^T -> C [T, N] (row stride ldc); split: pass the split-K
+    workspace the shape asks for (decode shapes split K over several blocks)."""
+    ws = _workspace(1, T, N, K_) if split else None
+    _say(f"linear {tag}: T={T} N={N} K={K_} kind={kind} out={out_dtype} split-K={ws is not None}")
     a = ks.host_matrix(SEED, f"{tag}:a", (T, K_), kind, 1.0 if kind == "int" else scale_a)
     w = ks.host_matrix(SEED, f"{tag}:w", (N, K_), kind, 1.0 if kind == "int" else scale_w)
     ldc = ldc or N
     c_full = torch.full((T, ldc), 3.0, dtype=out_dtype, device="cuda")
     c = c_full[:, :N]
-    K.linear(_dev(a), _dev(w), c, alpha=1.0)
+    K.linear(_dev(a), _dev(w), c, alpha=1.0, workspace=ws)
     torch.cuda.synchronize()
     got = c.float().cpu().numpy()
     ref = O.linear(a, w)
@@ -64,14 +72,31 @@ def _plain(T, N, K_, kind, out_dtype, tag, ldc=None, scale_a=1.0, scale_w=2.0 **
         assert torch.all(c_full[:, N:] == 3.0).item(), f"{tag}: wrote past column N"
 
 
-@pytest.mark.parametrize("kind", ["int", "normal"])
-def test_index_query_projection_decode(kind):
-    _plain(64, HI * D, Q_RANK, kind, torch.bfloat16, f"qidx-{kind}")
+@pytest.mark.parametrize("kind,split", [("int", True), ("normal", True), ("int", False), ("normal", False)])
+def test_index_query_projection_decode(kind, split):
+    _plain(64, HI * D, Q_RANK, kind, torch.bfloat16, f"qidx-{kind}", split=split)
 
 
-@pytest.mark.parametrize("kind", ["int", "normal"])
-def test_head_weight_projection_fp32_out(kind):
-    _plain(64, HI, HIDDEN, kind, torch.float32, f"w-{kind}")
+@pytest.mark.parametrize("kind,split", [("int", True), ("normal", True), ("normal", False)])
+def test_head_weight_projection_fp32_out(kind, split):
+    _plain(64, HI, HIDDEN, kind, torch.float32, f"w-{kind}", split=split)
+
+
+def test_split_k_workspace_reuse_across_shapes():
+    """One workspace (sized for the largest shape) serves consecutive calls of different shapes, whatever the
+    previous call left in it."""
+    _say("split-K workspace reuse")
+    shapes = [(64, HI * D, Q_RANK), (64, 2 * D, HIDDEN), (64, HI, HIDDEN), (48, HI * D, Q_RANK)]
+    n = max(K.linear_workspace_size(1, *s) for s in shapes)
+    ws = torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for i, (T, N, K_) in enumerate(shapes):
+            a = ks.host_matrix(SEED, f"re{i}:a", (T, K_), "int")
+            w = ks.host_matrix(SEED, f"re{i}:w", (N, K_), "int")
+            c = torch.empty((T, N), dtype=torch.float32, device="cuda")
+            K.linear(_dev(a), _dev(w), c, workspace=ws)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(c.cpu().numpy(), O.linear(a, w), err_msg=f"rep {rep} shape {i}")
 
 
 def test_ragged_rows_and_columns():
@@ -95,7 +120,10 @@ def test_indexer_projections_key_then_gate():
     w = torch.empty((T, HI), dtype=torch.float32, device="cuda")
     keys = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
     gates = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
-    K.indexer_project(_dev(x), _dev(cq), _dev(w_q), _dev(w_w), _dev(w_kg), q_idx, w, keys, gates)
+    n = max(K.linear_workspace_size(1, T, HI * D, Q_RANK), K.linear_workspace_size(1, T, HI, HIDDEN),
+            K.linear_workspace_size(1, T, D, HIDDEN))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    K.indexer_project(_dev(x), _dev(cq), _dev(w_q), _dev(w_w), _dev(w_kg), q_idx, w, keys, gates, workspace=ws)
     torch.cuda.synchronize()
     r_q, r_w, r_k, r_g = O.indexer_project(x, cq, w_q, w_w, w_kg, HI, D)
     np.testing.assert_array_equal(q_idx.float().cpu().numpy(), O.bf16_round(r_q))
@@ -128,7 +156,7 @@ def test_mla_unabsorb_output(T, kind):
     o_lat = ks.host_matrix(SEED, f"un{T}:o", (T, H, V), kind)
     w_uv = ks.host_matrix(SEED, f"un{T}:w", (H, DV, V), kind, 1.0 if kind == "int" else 2.0 ** -4)
     o = torch.empty((T, H, DV), dtype=torch.bfloat16, device="cuda")
-    K.mla_unabsorb_o(_dev(o_lat), _dev(w_uv), o)
+    K.mla_unabsorb_o(_dev(o_lat), _dev(w_uv), o, workspace=_workspace(H, T, DV, V))
     torch.cuda.synchronize()
     ref = O.mla_unabsorb_o(o_lat, w_uv)
     abs_sum = O.mla_unabsorb_o(np.abs(o_lat), np.abs(w_uv))
