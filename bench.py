@@ -251,8 +251,9 @@ PROJ_HIDDEN, PROJ_QRANK, PROJ_HI, PROJ_D, PROJ_H, PROJ_V, PROJ_DN, PROJ_DV, PROJ
 
 
 def proj_leg(T: int, reps: int, split: bool = True) -> dict:
-    """Time each projection of a T-token step (HIP events around a graph replay of `reps` calls, mean per call)
-    and all five back to back.  Inputs: seeded N(0, 1) draws (weights x 2^-6) rounded to bf16."""
+    """Time each projection of a T-token step (HIP events around a graph replay of `reps` calls, mean per call),
+    then the step's five as a layer launches them (one grouped launch before attention, the un-absorb after).
+    Inputs: seeded N(0, 1) draws (weights x 2^-6) rounded to bf16."""
     import torch
     import sparse_attention_kpool_amd as K
     gen = torch.Generator(device="cuda")
@@ -315,13 +316,25 @@ def proj_leg(T: int, reps: int, split: bool = True) -> dict:
         us = timed(f)
         out["calls"][name] = {"us": round(us, 2), "tflops": round(fl / (us * 1e-6) / 1e12, 2),
                               "gbs": round(by / (us * 1e-6) / 1e9, 1)}
-    us = timed(lambda: [f() for f, _, _ in calls.values()])
+    # as a layer step launches them: the four indexer products and the query absorb (all inputs ready before
+    # attention) in one grouped launch, the un-absorb after attention on its own
+    group = K.indexer_products(x, cq, w_q, w_w, w_kg, q_idx, w, keys, gates) + [K.absorb_product(q_nope, w_uk_t, q)]
+    gws_n = K.linear_group_workspace_size(group)
+    gws = torch.empty(max(gws_n, 16), dtype=torch.uint8, device="cuda") if (gws_n and split) else None
+    f_group = lambda: K.linear_group(group, workspace=gws)  # noqa: E731
+    us_g = timed(f_group)
+    fl_g = sum(calls[c][1] for c in ("index_query", "head_weights", "key_gate", "absorb"))
+    by_g = sum(calls[c][2] for c in ("index_query", "head_weights", "key_gate", "absorb"))
+    out["calls"]["pre_attention_group"] = {"us": round(us_g, 2), "tflops": round(fl_g / (us_g * 1e-6) / 1e12, 2),
+                                           "gbs": round(by_g / (us_g * 1e-6) / 1e9, 1)}
+    f_un = calls["unabsorb"][0]
+    us = timed(lambda: (f_group(), f_un()))
     fl = sum(c[1] for c in calls.values())
     by = sum(c[2] for c in calls.values())
     out.update(us=round(us, 2), flops=fl, bytes=by, tflops=round(fl / (us * 1e-6) / 1e12, 2),
                frac_of_bf16_peak=round(fl / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
                gbs=round(by / (us * 1e-6) / 1e9, 1), hbm_frac=round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
-    del x, cq, w_q, w_w, w_kg, q_nope, w_uk_t, w_uv, o_lat, q_idx, w, keys, gates, q, o, ws
+    del x, cq, w_q, w_w, w_kg, q_nope, w_uk_t, w_uv, o_lat, q_idx, w, keys, gates, q, o, ws, gws, group
     torch.cuda.empty_cache()
     return out
 

@@ -246,6 +246,34 @@ kp_status kp_linear(int32_t batch, int32_t M, int32_t N, int32_t K, const void* 
                     const void* W, int64_t ldw, int64_t stride_w, void* C, int64_t ldc, int64_t stride_c,
                     int32_t c_dtype, float alpha, void* workspace, size_t ws_bytes, void* stream);
 
+/* One product of a kp_linear_group call: the arguments of kp_linear (host struct, read during the call only). */
+typedef struct {
+  int32_t batch, M, N, K;
+  const void* A;
+  int64_t lda, stride_a;
+  const void* W;
+  int64_t ldw, stride_w;
+  void* C;
+  int64_t ldc, stride_c;
+  int32_t c_dtype;
+  float alpha;
+} kp_linear_problem;
+
+/*
+ * kp_linear_group -- up to 8 independent kp_linear products in one launch (plus one launch that adds split-K
+ *   partials, when any product splits): the products of one layer step that do not depend on each other (the
+ *   indexer's projections and the query absorb of a decode step) pay the launch cost once.  Each product is
+ *   exactly what kp_linear computes for the same arguments and workspace share (one tile shape serves the group,
+ *   chosen by its largest M, so a product may round differently than alone when the group mixes row counts).
+ *   problems: host array of n (0..8) products; their outputs must not overlap each other's inputs or outputs.
+ *   workspace: as in kp_linear, at least kp_linear_group_workspace_size(n, problems) bytes for full splitting
+ *   (products are given workspace in order; one that no longer fits runs unsplit).
+ *   Errors: as kp_linear, per product; KP_ERR_INVALID_ARG for n outside 0..8 or a NULL list.
+ */
+size_t kp_linear_group_workspace_size(int32_t n, const kp_linear_problem* problems);
+kp_status kp_linear_group(int32_t n, const kp_linear_problem* problems, void* workspace, size_t ws_bytes,
+                          void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  Owned by the library. */
 const char* kp_last_error(void);
 

@@ -25,7 +25,8 @@ ABI_VERSION = 4
 
 EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk_select",
             "sparse_mla_workspace_size", "sparse_mla_attn", "sparse_mla_attn_shared", "sparse_mla_attn_fp8",
-            "kp_linear", "kp_linear_workspace_size", "kp_last_error", "kp_abi_version")
+            "kp_linear", "kp_linear_workspace_size", "kp_linear_group", "kp_linear_group_workspace_size",
+            "kp_last_error", "kp_abi_version")
 
 
 class KpError(RuntimeError):
@@ -44,6 +45,14 @@ class _Dims(ctypes.Structure):
 class _Cache(ctypes.Structure):
     _fields_ = [("latent", ctypes.c_void_p), ("pooled", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("bt_stride", ctypes.c_int32)]
+
+
+class _LinearProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("M", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("stride_a", ctypes.c_int64),
+                ("W", ctypes.c_void_p), ("ldw", ctypes.c_int64), ("stride_w", ctypes.c_int64),
+                ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64), ("stride_c", ctypes.c_int64),
+                ("c_dtype", ctypes.c_int32), ("alpha", ctypes.c_float)]
 
 
 class _Queries(ctypes.Structure):
@@ -80,8 +89,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                               vp, sz, vp]
     lib.kp_linear_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.kp_linear_workspace_size.restype = sz
+    LP = ctypes.POINTER(_LinearProblem)
+    lib.kp_linear_group.argtypes = [i32, LP, vp, sz, vp]
+    lib.kp_linear_group_workspace_size.argtypes = [i32, LP]
+    lib.kp_linear_group_workspace_size.restype = sz
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_shared",
-              "sparse_mla_attn_fp8", "kp_linear"):
+              "sparse_mla_attn_fp8", "kp_linear", "kp_linear_group"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kp_last_error.restype = ctypes.c_char_p
     lib.kp_abi_version.restype = i32
@@ -243,11 +256,8 @@ def linear_workspace_size(batch: int, M: int, N: int, K: int) -> int:
     return int(load().kp_linear_workspace_size(batch, M, N, K))
 
 
-def linear(a, w, out, alpha: float = 1.0, workspace=None, stream=None) -> None:
-    """out[b] = alpha * a[b] @ w[b]^T (kp_linear).  a [.., M, K] and w [.., N, K] bf16; out [.., M, N] bf16 or
-    float32.  2-D operands are shared by every batch entry; 3-D ones give the batch (views with any row and batch
-    strides, last dimension contiguous).  workspace: a device tensor of at least linear_workspace_size(...) bytes
-    (any contents), reused across calls (None: no split-K)."""
+def _problem(a, w, out, alpha: float = 1.0) -> _LinearProblem:
+    """The kp_linear_problem of out[b] = alpha * a[b] @ w[b]^T (see linear)."""
     import torch
     ba, M, lda, sa = _mat3(a, "a")
     bw, N, ldw, sw = _mat3(w, "w")
@@ -261,27 +271,63 @@ def linear(a, w, out, alpha: float = 1.0, workspace=None, stream=None) -> None:
             or w.shape[-1] != a.shape[-1]:
         raise ValueError(f"kp_linear: shapes {tuple(a.shape)} x {tuple(w.shape)} -> {tuple(out.shape)} disagree")
     c_dtype = KP_DTYPE_BF16 if out.dtype == torch.bfloat16 else KP_DTYPE_F32
+    return _LinearProblem(batch, M, N, a.shape[-1], _ptr(a), lda, sa, _ptr(w), ldw, sw, _ptr(out), ldc, sc, c_dtype,
+                          float(alpha))
+
+
+def linear(a, w, out, alpha: float = 1.0, workspace=None, stream=None) -> None:
+    """out[b] = alpha * a[b] @ w[b]^T (kp_linear).  a [.., M, K] and w [.., N, K] bf16; out [.., M, N] bf16 or
+    float32.  2-D operands are shared by every batch entry; 3-D ones give the batch (views with any row and batch
+    strides, last dimension contiguous).  workspace: a device tensor of at least linear_workspace_size(...) bytes
+    (any contents), reused across calls (None: no split-K)."""
+    q = _problem(a, w, out, alpha)
     ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
-    _check("kp_linear", load().kp_linear(batch, M, N, a.shape[-1], _ptr(a), lda, sa, _ptr(w), ldw, sw, _ptr(out),
-                                         ldc, sc, c_dtype, float(alpha), _ptr(workspace), ws_bytes,
+    _check("kp_linear", load().kp_linear(q.batch, q.M, q.N, q.K, q.A, q.lda, q.stride_a, q.W, q.ldw, q.stride_w, q.C,
+                                         q.ldc, q.stride_c, q.c_dtype, q.alpha, _ptr(workspace), ws_bytes,
                                          _stream(stream)))
 
 
-def indexer_project(x, cq, w_q, w_w, w_kg, q_idx, w, keys, gates, workspace=None, stream=None) -> None:
-    """The indexer's projections: q_idx [T, Hi, D] = cq @ w_q^T (head-major), w [T, Hi] (float32) = x @ w_w^T,
-    keys | gates [T, D] = x @ w_kg^T split after D columns (key first)."""
+def _problems(products):
+    arr = (_LinearProblem * max(len(products), 1))()
+    for i, p in enumerate(products):
+        arr[i] = _problem(*p)
+    return arr
+
+
+def linear_group_workspace_size(products) -> int:
+    """Bytes of split-K workspace for a group of products [(a, w, out[, alpha]), ...]."""
+    return int(load().kp_linear_group_workspace_size(len(products), _problems(products)))
+
+
+def linear_group(products, workspace=None, stream=None) -> None:
+    """Up to 8 independent products [(a, w, out[, alpha]), ...] in one launch (kp_linear_group)."""
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    _check("kp_linear_group", load().kp_linear_group(len(products), _problems(products), _ptr(workspace), ws_bytes,
+                                                     _stream(stream)))
+
+
+def indexer_products(x, cq, w_q, w_w, w_kg, q_idx, w, keys, gates):
+    """The indexer's four products for linear_group: q_idx [T, Hi, D] = cq @ w_q^T (head-major), w [T, Hi] (float32)
+    = x @ w_w^T, keys | gates [T, D] = x @ w_kg^T split after D columns (key first)."""
     T, D = x.shape[0], keys.shape[-1]
-    linear(cq, w_q, q_idx.view(T, -1), workspace=workspace, stream=stream)
-    linear(x, w_w, w, workspace=workspace, stream=stream)
-    linear(x, w_kg[:D], keys, workspace=workspace, stream=stream)
-    linear(x, w_kg[D:2 * D], gates, workspace=workspace, stream=stream)
+    return [(cq, w_q, q_idx.view(T, -1)), (x, w_w, w), (x, w_kg[:D], keys), (x, w_kg[D:2 * D], gates)]
+
+
+def absorb_product(q_nope, w_uk_t, q):
+    """The query absorb as a product for linear_group (see mla_absorb_q)."""
+    V = w_uk_t.shape[1]
+    return (q_nope.transpose(0, 1), w_uk_t, q[:, :, :V].transpose(0, 1))
+
+
+def indexer_project(x, cq, w_q, w_w, w_kg, q_idx, w, keys, gates, workspace=None, stream=None) -> None:
+    """The indexer's projections in one grouped launch (see indexer_products)."""
+    linear_group(indexer_products(x, cq, w_q, w_w, w_kg, q_idx, w, keys, gates), workspace=workspace, stream=stream)
 
 
 def mla_absorb_q(q_nope, w_uk_t, q, workspace=None, stream=None) -> None:
     """Query in latent space, per head: q[t, h, :V] = W_UK[h]^T q_nope[t, h].  q_nope [T, H, dn] bf16, w_uk_t
     [H, V, dn] (W_UK[h] transposed, prepared once), q [T, H, L] bf16 (columns V..L-1 are left as they are)."""
-    V = w_uk_t.shape[1]
-    linear(q_nope.transpose(0, 1), w_uk_t, q[:, :, :V].transpose(0, 1), workspace=workspace, stream=stream)
+    linear(*absorb_product(q_nope, w_uk_t, q), workspace=workspace, stream=stream)
 
 
 def mla_unabsorb_o(o_lat, w_uv, o, workspace=None, stream=None) -> None:

@@ -294,47 +294,116 @@ kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const 
                    workspace, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+// validation of one product and its launch descriptor
+static kp_status linear_prepare(const kp_linear_problem& q, const char* fn, LinearLaunch& a) {
+  KP_REQUIRE(q.batch >= 0 && q.M >= 0 && q.N >= 0, KP_ERR_INVALID_ARG, "%s: negative batch, M or N", fn);
+  a = LinearLaunch{};
+  a.batch = q.batch;
+  a.M = q.M;
+  a.N = q.N;
+  a.K = q.K;
+  if (q.batch == 0 || q.M == 0 || q.N == 0) {  // empty: nothing is read or written
+    a.batch = a.M = a.N = 0;
+    return KP_OK;
+  }
+  KP_REQUIRE(q.K >= 64 && q.K % 64 == 0, KP_ERR_UNSUPPORTED, "%s: K = %d is not a positive multiple of 64", fn, q.K);
+  KP_REQUIRE(q.c_dtype == KP_DTYPE_BF16 || q.c_dtype == KP_DTYPE_F32, KP_ERR_INVALID_ARG, "%s: bad c_dtype", fn);
+  KP_REQUIRE(q.A && q.W && q.C, KP_ERR_INVALID_ARG, "%s: NULL operand", fn);
+  KP_REQUIRE(aligned(q.A) && aligned(q.W) && aligned(q.C), KP_ERR_INVALID_ARG, "%s: misaligned operand", fn);
+  KP_REQUIRE(q.lda >= q.K && q.ldw >= q.K && q.ldc >= q.N, KP_ERR_INVALID_ARG, "%s: leading dimension below K or N",
+             fn);
+  KP_REQUIRE(q.lda % 8 == 0 && q.ldw % 8 == 0 && q.stride_a % 8 == 0 && q.stride_w % 8 == 0 && q.stride_a >= 0 &&
+                 q.stride_w >= 0,
+             KP_ERR_INVALID_ARG, "%s: A / W row and batch strides must be non-negative multiples of 8", fn);
+  KP_REQUIRE(q.ldc % 4 == 0 && q.stride_c % 4 == 0 && q.stride_c >= 0, KP_ERR_INVALID_ARG,
+             "%s: C row and batch strides must be non-negative multiples of 4", fn);
+  KP_REQUIRE(isfinite(q.alpha), KP_ERR_INVALID_ARG, "%s: alpha is not finite", fn);
+  a.c_dtype = q.c_dtype;
+  a.A = q.A;
+  a.lda = q.lda;
+  a.sa = q.stride_a;
+  a.W = q.W;
+  a.ldw = q.ldw;
+  a.sw = q.stride_w;
+  a.C = q.C;
+  a.ldc = q.ldc;
+  a.sc = q.stride_c;
+  a.alpha = q.alpha;
+  return KP_OK;
+}
+
+static kp_status linear_group_prepare(int32_t n, const kp_linear_problem* problems, const char* fn,
+                                      LinearLaunch (&a)[8]) {
+  KP_REQUIRE(n >= 0 && n <= 8, KP_ERR_INVALID_ARG, "%s: %d products (1..8 per call)", fn, n);
+  KP_REQUIRE(n == 0 || problems, KP_ERR_INVALID_ARG, "%s: NULL problem list", fn);
+  for (int i = 0; i < n; ++i) {
+    const kp_status st = linear_prepare(problems[i], fn, a[i]);
+    if (st != KP_OK) return st;
+  }
+  return KP_OK;
+}
+
+extern "C" {
+
+size_t kp_linear_group_workspace_size(int32_t n, const kp_linear_problem* problems) {
+  LinearLaunch a[8];
+  if (linear_group_prepare(n, problems, "kp_linear_group_workspace_size", a) != KP_OK) return 0;
+  return linear_group_workspace(a, n);
+}
+
+kp_status kp_linear_group(int32_t n, const kp_linear_problem* problems, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  const char* fn = "kp_linear_group";
+  LinearLaunch a[8];
+  const kp_status st = linear_group_prepare(n, problems, fn, a);
+  if (st != KP_OK) return st;
+  KP_REQUIRE(!workspace || aligned(workspace), KP_ERR_INVALID_ARG, "%s: misaligned workspace", fn);
+  return launch_linear_group(a, n, workspace, workspace ? ws_bytes : 0, (hipStream_t)stream);
+}
+
+static kp_linear_problem one_problem(int32_t batch, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda,
+                                     int64_t stride_a, const void* W, int64_t ldw, int64_t stride_w, void* C,
+                                     int64_t ldc, int64_t stride_c, int32_t c_dtype, float alpha) {
+  kp_linear_problem q;
+  q.batch = batch;
+  q.M = M;
+  q.N = N;
+  q.K = K;
+  q.A = A;
+  q.lda = lda;
+  q.stride_a = stride_a;
+  q.W = W;
+  q.ldw = ldw;
+  q.stride_w = stride_w;
+  q.C = C;
+  q.ldc = ldc;
+  q.stride_c = stride_c;
+  q.c_dtype = c_dtype;
+  q.alpha = alpha;
+  return q;
+}
+
 size_t kp_linear_workspace_size(int32_t batch, int32_t M, int32_t N, int32_t K) {
-  return linear_workspace(batch, M, N, K);
+  // only the shape matters: stand-in operands that pass validation
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  const kp_linear_problem q = one_problem(batch, M, N, K, dummy, K, 0, dummy, K, 0, (void*)dummy, N + (4 - N % 4) % 4,
+                                          0, KP_DTYPE_F32, 1.f);
+  return kp_linear_group_workspace_size(1, &q);
 }
 
 kp_status kp_linear(int32_t batch, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int64_t stride_a,
                     const void* W, int64_t ldw, int64_t stride_w, void* C, int64_t ldc, int64_t stride_c,
                     int32_t c_dtype, float alpha, void* workspace, size_t ws_bytes, void* stream) {
+  const kp_linear_problem q =
+      one_problem(batch, M, N, K, A, lda, stride_a, W, ldw, stride_w, C, ldc, stride_c, c_dtype, alpha);
   const char* fn = "kp_linear";
-  KP_REQUIRE(batch >= 0 && M >= 0 && N >= 0, KP_ERR_INVALID_ARG, "%s: negative batch, M or N", fn);
-  if (batch == 0 || M == 0 || N == 0) return KP_OK;
-  KP_REQUIRE(K >= 64 && K % 64 == 0, KP_ERR_UNSUPPORTED, "%s: K = %d is not a positive multiple of 64", fn, K);
-  KP_REQUIRE(c_dtype == KP_DTYPE_BF16 || c_dtype == KP_DTYPE_F32, KP_ERR_INVALID_ARG, "%s: bad c_dtype", fn);
-  KP_REQUIRE(A && W && C, KP_ERR_INVALID_ARG, "%s: NULL operand", fn);
-  KP_REQUIRE(aligned(A) && aligned(W) && aligned(C), KP_ERR_INVALID_ARG, "%s: misaligned operand", fn);
-  KP_REQUIRE(lda >= K && ldw >= K && ldc >= N, KP_ERR_INVALID_ARG, "%s: leading dimension below K or N", fn);
-  KP_REQUIRE(lda % 8 == 0 && ldw % 8 == 0 && stride_a % 8 == 0 && stride_w % 8 == 0 && stride_a >= 0 &&
-                 stride_w >= 0,
-             KP_ERR_INVALID_ARG, "%s: A / W row and batch strides must be non-negative multiples of 8", fn);
-  KP_REQUIRE(ldc % 4 == 0 && stride_c % 4 == 0 && stride_c >= 0, KP_ERR_INVALID_ARG,
-             "%s: C row and batch strides must be non-negative multiples of 4", fn);
-  KP_REQUIRE(isfinite(alpha), KP_ERR_INVALID_ARG, "%s: alpha is not finite", fn);
+  LinearLaunch a;
+  const kp_status st = linear_prepare(q, fn, a);
+  if (st != KP_OK) return st;
   KP_REQUIRE(!workspace || aligned(workspace), KP_ERR_INVALID_ARG, "%s: misaligned workspace", fn);
-  LinearLaunch a{};
-  a.batch = batch;
-  a.M = M;
-  a.N = N;
-  a.K = K;
-  a.c_dtype = c_dtype;
-  a.A = A;
-  a.lda = lda;
-  a.sa = stride_a;
-  a.W = W;
-  a.ldw = ldw;
-  a.sw = stride_w;
-  a.C = C;
-  a.ldc = ldc;
-  a.sc = stride_c;
-  a.alpha = alpha;
-  a.ws = workspace;
-  a.ws_bytes = workspace ? ws_bytes : 0;
-  return launch_linear(a, (hipStream_t)stream);
+  return launch_linear_group(&a, 1, workspace, workspace ? ws_bytes : 0, (hipStream_t)stream);
 }
 
 }  // extern "C"

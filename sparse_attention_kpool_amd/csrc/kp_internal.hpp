@@ -92,10 +92,9 @@ struct LinearLaunch {
   void* C;
   int64_t ldc, sc;
   float alpha;
-  void* ws;  // split-K partials and per-tile counters (NULL: no split)
-  size_t ws_bytes;
 };
-size_t linear_workspace(int batch, int M, int N, int K);
-kp_status launch_linear(const LinearLaunch& a, hipStream_t s);
+// up to 8 products in one launch (plus one split-K reduce launch); one tile shape for all, by the largest M
+size_t linear_group_workspace(const LinearLaunch* probs, int n);
+kp_status launch_linear_group(const LinearLaunch* probs, int n, void* ws, size_t ws_bytes, hipStream_t s);
 
 }  // namespace kp

@@ -18,9 +18,9 @@
 //          stored), so every wave issues the same loads every stage and the waits are exact counts.
 //   math   wave (wn, wm) owns the BN/2 x BM/2 quarter of the tile: (BN/32) x (BM/32) MFMA tiles, BK/32 k-steps a
 //          stage.
-// Tiles are numbered m-fastest under one weight tile, and with a grid that is a multiple of 8 consecutive tile
-// numbers go to the same XCD (blocks are dealt to the 8 XCDs round-robin), so blocks sharing a weight tile share
-// that XCD's L2.
+// Tiles are numbered m-fastest under one weight tile, and each XCD takes a contiguous run of a product's tiles
+// (see linear_kernel), so blocks sharing a weight tile share that XCD's L2.  A grouped launch runs up to 8
+// independent products in one grid, each spread over all XCDs.
 //
 // Bound: the decode shapes (M = tokens of a step, tens) stream their weights once -- HBM; the prefill shapes
 // (M = thousands) are MFMA-bound at 2 M N K flop.
@@ -32,6 +32,7 @@ namespace kp {
 constexpr int LN_THREADS = 256;
 constexpr int LN_NBUF = 4;   // stage buffers
 constexpr int LN_AHEAD = 3;  // stages in flight ahead of the one being multiplied
+constexpr int LN_MAXGROUP = 8;  // products per grouped launch
 
 // A stage holds BK of k for every tile row: CPR = BK / 8 chunks of 16 bytes.  Chunk c of row r sits at position
 // c ^ ln_swz(r) of the row.  A fragment read takes one chunk of 16 consecutive rows; 16 / CPR consecutive rows
@@ -42,12 +43,56 @@ __device__ __forceinline__ int ln_swz(int r) {
   return (r / (16 / CPR)) & (CPR - 1);
 }
 
-template <int BM, int BN, int BK, class TC>
-__global__ __launch_bounds__(LN_THREADS) void linear_kernel(const bf16* __restrict__ A, int64_t lda, int64_t sa,
-                                                            const bf16* __restrict__ W, int64_t ldw, int64_t sw,
-                                                            TC* __restrict__ C, int64_t ldc, int64_t sc, int M,
-                                                            int N, int K, float alpha, int tiles_m, int tiles_n,
-                                                            int splits, int nk_per, f32x4* __restrict__ part) {
+// One product of a group as the kernels see it (host-filled; passed by value in the kernel arguments).
+struct LinearProb {
+  const bf16* A;
+  const bf16* W;
+  void* C;
+  f32x4* part;  // split-K partial tiles (splits > 1)
+  int64_t lda, sa, ldw, sw, ldc, sc;
+  int M, N, K, c_bf16, tiles_m, tiles_n, splits, nk_per;
+  float alpha;
+  int block0;   // first block of this product in the product grid (a multiple of 8)
+  int nblocks;  // its blocks (tiles x splits); the grid gives it nblocks rounded up to a multiple of 8
+  int rblock0;  // first block of its split-K reduction in the reduce grid
+};
+struct LinearGroup {
+  int n;
+  LinearProb p[LN_MAXGROUP];
+};
+
+// product of a block: the last one whose first block is at or below it (n <= 8, a uniform scalar walk)
+__device__ __forceinline__ int linear_find(const LinearGroup& g, int bid, bool reduce) {
+  int i = 0;
+  while (i + 1 < g.n && bid >= (reduce ? g.p[i + 1].rblock0 : g.p[i + 1].block0)) ++i;
+  return i;
+}
+
+// store 4 consecutive outputs n .. n+3 of row m (those below N)
+__device__ __forceinline__ void linear_store4(const LinearProb& P, int64_t off, int n, f32x4 v) {
+  if (P.c_bf16) {
+    bf16* dst = static_cast<bf16*>(P.C) + off;
+    if (n + 3 < P.N) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n + i < P.N) dst[i] = Elem<bf16>::from_f32(v[i]);
+    }
+  } else {
+    float* dst = static_cast<float*>(P.C) + off;
+    if (n + 3 < P.N) {
+      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n + i < P.N) dst[i] = v[i];
+    }
+  }
+}
+
+template <int BM, int BN, int BK>
+__global__ __launch_bounds__(LN_THREADS) void linear_kernel(const LinearGroup grp) {
   constexpr int CPR = BK / 8;                // 16-byte chunks per tile row and stage
   constexpr int RPI = 64 / CPR;              // tile rows per direct-load instruction (1 KiB)
   constexpr int LA = BM / (4 * RPI), LW = BN / (4 * RPI);  // direct-load instructions per wave per stage
@@ -57,21 +102,25 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const bf16* __restri
   __shared__ __align__(1024) bf16 sA[LN_NBUF][BM * BK];
   __shared__ __align__(1024) bf16 sW[LN_NBUF][BN * BK];
 
-  int bid = blockIdx.x;
-  if ((gridDim.x & 7) == 0) {
-    const int per = gridDim.x >> 3;
-    bid = (bid & 7) * per + (bid >> 3);
-  }
+  // Each product owns an 8-aligned range of 8 k blocks (blocks are dealt to the 8 XCDs round-robin, so every
+  // product spreads over all XCDs); inside it, slot j runs block (j mod 8) k + j / 8, so each XCD takes a
+  // contiguous run of the product's tiles (m-fastest under one weight tile: shared in that XCD's L2).  Slots
+  // past the product's blocks exit at once.
+  const LinearProb& P = grp.p[linear_find(grp, blockIdx.x, false)];
+  const int j = blockIdx.x - P.block0, per = (P.nblocks + 7) >> 3;
+  int bid = (j & 7) * per + (j >> 3);
+  if (bid >= P.nblocks) return;
+  const int M = P.M, N = P.N, K = P.K, splits = P.splits, nk_per = P.nk_per, tiles_m = P.tiles_m;
   const int sp = bid % splits;  // k-split of this block
   bid /= splits;
-  const int per_b = tiles_m * tiles_n;
+  const int per_b = tiles_m * P.tiles_n;
   const int b = bid / per_b;
   const int t = bid - b * per_b;
   const int tn = t / tiles_m, tm = t - tn * tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
-  A += b * sa;
-  W += b * sw;
-  C += b * sc;
+  const bf16* A = P.A + b * P.sa;
+  const bf16* W = P.W + b * P.sw;
+  const int64_t lda = P.lda, ldw = P.ldw;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -148,7 +197,7 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const bf16* __restri
   if (splits > 1) {
     // split K: store the fp32 partial tile in lane order, [tile][split][wave][n tile][m tile][lane]; the reduce
     // kernel adds the splits in order and writes the output
-    f32x4* pt = part + (int64_t(bid) * splits + sp) * (4 * TN * TM * 64) + (wave * TN * TM) * 64 + lane;
+    f32x4* pt = P.part + (int64_t(bid) * splits + sp) * (4 * TN * TM * 64) + (wave * TN * TM) * 64 + lane;
 #pragma unroll
     for (int a = 0; a < TN; ++a)
 #pragma unroll
@@ -164,19 +213,7 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const bf16* __restri
     for (int c = 0; c < TM; ++c) {
       const int m = m0 + wm * (BM / 2) + 16 * c + l16;
       if (m >= M || n >= N) continue;
-      const f32x4 v = acc[a][c] * alpha;
-      TC* dst = C + int64_t(m) * ldc + n;
-      if (n + 3 < N) {
-        if constexpr (sizeof(TC) == 2) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        } else {
-          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (n + i < N) dst[i] = Elem<TC>::from_f32(v[i]);
-      }
+      linear_store4(P, int64_t(b) * P.sc + int64_t(m) * P.ldc + n, n, acc[a][c] * P.alpha);
     }
   }
 }
@@ -185,39 +222,35 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const bf16* __restri
 // small, each split at least 4 stages long; a pure function of the shape
 // Split-K reduction: one thread per 4 outputs (one lane's f32x4 of one MFMA tile of one wave); the partials of the
 // splits are added in split order, scaled once and rounded once, and stored as the unsplit kernel stores them.
-template <int BM, int BN, class TC>
-__global__ __launch_bounds__(256) void linear_reduce_kernel(const f32x4* __restrict__ part, int splits,
-                                                            TC* __restrict__ C, int64_t ldc, int64_t sc, int M, int N,
-                                                            float alpha, int tiles_m, int tiles_n) {
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void linear_reduce_kernel(const LinearGroup grp) {
   constexpr int TN = BN / 32, TM = BM / 32, TILE = 4 * TN * TM * 64;
-  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;  // f32x4 index over all tiles
+  const LinearProb& P = grp.p[linear_find(grp, blockIdx.x, true)];
+  const int64_t e = int64_t(blockIdx.x - P.rblock0) * 256 + threadIdx.x;  // f32x4 index over the product's tiles
   const int64_t tile = e / TILE;
   const int r = int(e - tile * TILE);
   const int lane = r & 63, ac = (r >> 6) % (TN * TM), wave = (r >> 6) / (TN * TM);
   const int a = ac / TM, c = ac - a * TM;
-  const int per_b = tiles_m * tiles_n;
+  const int tiles_m = P.tiles_m, per_b = tiles_m * P.tiles_n, splits = P.splits;
   const int b = int(tile / per_b), t = int(tile - int64_t(b) * per_b);
   const int tn = t / tiles_m, tm = t - tn * tiles_m;
   const int wn = wave >> 1, wm = wave & 1, l16 = lane & 15, g = lane >> 4;
   const int n = tn * BN + wn * (BN / 2) + 16 * a + 4 * g;
   const int m = tm * BM + wm * (BM / 2) + 16 * c + l16;
-  if (m >= M || n >= N) return;
-  const f32x4* p = part + tile * splits * TILE + r;
+  if (m >= P.M || n >= P.N) return;
+  const f32x4* p = P.part + tile * splits * TILE + r;
+  // eight loads in flight at a time, added in split order
   f32x4 v = p[0];
-  for (int q = 1; q < splits; ++q) v += p[int64_t(q) * TILE];
-  v *= alpha;
-  TC* dst = C + int64_t(b) * sc + int64_t(m) * ldc + n;
-  if (n + 3 < N) {
-    if constexpr (sizeof(TC) == 2) {
-      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-    } else {
-      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-  } else {
+  for (int q = 1; q < splits; q += 8) {
+    f32x4 t8[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (n + i < N) dst[i] = Elem<TC>::from_f32(v[i]);
+    for (int j = 0; j < 8; ++j)
+      if (q + j < splits) t8[j] = p[int64_t(q + j) * TILE];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (q + j < splits) v += t8[j];
   }
+  linear_store4(P, int64_t(b) * P.sc + int64_t(m) * P.ldc + n, n, v * P.alpha);
 }
 
 // Tile shape for a call: a decode step (few rows) takes 64 x 64 tiles with 64-wide k stages (64 KiB of LDS, two
@@ -228,16 +261,28 @@ struct LinearTile {
 };
 static LinearTile linear_tile(int M) { return M <= 64 ? LinearTile{64, 64, 64} : LinearTile{128, 128, 32}; }
 
-// k-splits for a call shape: only when there are fewer output tiles than compute units, enough splits for about
-// two blocks per CU, each at least 4 stages long; a pure function of the shape
-static int linear_splits(const LinearTile& t, int batch, int M, int N, int K, int cus) {
-  const int64_t tiles = int64_t(batch) * ((M + t.BM - 1) / t.BM) * ((N + t.BN - 1) / t.BN);
-  if (tiles >= cus) return 1;
-  const int nk = K / t.BK;
-  int sp = int((2 * int64_t(cus) + tiles - 1) / tiles);
-  sp = max(1, min(sp, nk / 4));
-  const int per = (nk + sp - 1) / sp;
-  return (nk + per - 1) / per;  // every split non-empty
+// k-splits of a group's products, a pure function of the shapes.  The group's work is sum(tiles x stages); spread
+// over two blocks per CU it gives the stages each block slot runs on average (at least 4).  A product whose blocks
+// would run more than twice that is split down to about that many stages per block (the split-K reduction costs a
+// launch, so a product is split only where it would otherwise be the long pole).
+static void linear_splits(const LinearTile& t, const LinearLaunch* probs, int n, int cus, int* sp) {
+  int64_t work = 0;
+  for (int i = 0; i < n; ++i) {
+    const LinearLaunch& a = probs[i];
+    if (a.batch > 0 && a.M > 0 && a.N > 0)
+      work += int64_t(a.batch) * ((a.M + t.BM - 1) / t.BM) * ((a.N + t.BN - 1) / t.BN) * (a.K / t.BK);
+  }
+  const int64_t slots = 2 * int64_t(cus);
+  const int64_t avg = (work + slots - 1) / slots, load = avg > 4 ? avg : 4;
+  for (int i = 0; i < n; ++i) {
+    const int nk = probs[i].K / t.BK;
+    sp[i] = 1;
+    if (probs[i].batch <= 0 || probs[i].M <= 0 || probs[i].N <= 0 || nk <= 2 * load) continue;
+    const int want = int((nk + load - 1) / load);
+    const int s1 = max(1, min(want, nk / 4));  // at least 4 stages per split
+    const int per = (nk + s1 - 1) / s1;
+    sp[i] = (nk + per - 1) / per;  // every split non-empty
+  }
 }
 
 static int device_cus() {
@@ -252,61 +297,96 @@ static int device_cus() {
   return cus[dev];
 }
 
-size_t linear_workspace(int batch, int M, int N, int K) {
-  if (batch <= 0 || M <= 0 || N <= 0 || K < 64) return 0;
-  const LinearTile t = linear_tile(M);
-  const int sp = linear_splits(t, batch, M, N, K, 256);
-  if (sp <= 1) return 0;
-  const int64_t tiles = int64_t(batch) * ((M + t.BM - 1) / t.BM) * ((N + t.BN - 1) / t.BN);
-  return size_t(tiles) * sp * t.BM * t.BN * sizeof(float);
-}
-
 template <int BM, int BN, int BK>
-static kp_status launch_tile(const LinearLaunch& a, hipStream_t s) {
+static kp_status launch_group(const LinearLaunch* probs, int n, void* ws, size_t ws_bytes, hipStream_t s) {
   const LinearTile tl{BM, BN, BK};
-  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-  const int64_t tiles = int64_t(a.batch) * tiles_m * tiles_n;
-  int sp = 1;
-  f32x4* part = nullptr;
-  if (a.ws) {
-    // the split count is sized for 256 CUs (the workspace query cannot see the device); fewer fit the workspace
-    sp = linear_splits(tl, a.batch, a.M, a.N, a.K, min(device_cus(), 256));
-    const size_t need = size_t(tiles) * sp * BM * BN * sizeof(float);
-    if (sp > 1 && a.ws_bytes >= need) {
-      part = static_cast<f32x4*>(a.ws);
-    } else {
-      sp = 1;
+  int spl[LN_MAXGROUP];
+  linear_splits(tl, probs, n, min(device_cus(), 256), spl);  // the workspace query assumes 256 CUs
+  LinearGroup g{};
+  int64_t blocks = 0, rblocks = 0;
+  size_t ws_off = 0;
+  bool ws_ok = true;
+  for (int i = 0; i < n; ++i) {
+    const LinearLaunch& a = probs[i];
+    LinearProb& P = g.p[g.n];
+    const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    const int64_t tiles = int64_t(a.batch) * tiles_m * tiles_n;
+    if (tiles == 0) continue;
+    int sp = spl[i];
+    if (sp > 1) {
+      const size_t need = size_t(tiles) * sp * BM * BN * sizeof(float);
+      if (ws && ws_ok && ws_off + need <= ws_bytes) {
+        P.part = reinterpret_cast<f32x4*>(static_cast<char*>(ws) + ws_off);
+        ws_off += need;
+      } else {
+        ws_ok = false;  // a workspace too small for this and later products: no split from here on
+        sp = 1;
+      }
     }
+    P.A = static_cast<const bf16*>(a.A);
+    P.W = static_cast<const bf16*>(a.W);
+    P.C = a.C;
+    P.lda = a.lda;
+    P.sa = a.sa;
+    P.ldw = a.ldw;
+    P.sw = a.sw;
+    P.ldc = a.ldc;
+    P.sc = a.sc;
+    P.M = a.M;
+    P.N = a.N;
+    P.K = a.K;
+    P.c_bf16 = a.c_dtype == KP_DTYPE_BF16;
+    P.tiles_m = tiles_m;
+    P.tiles_n = tiles_n;
+    P.splits = sp;
+    P.nk_per = (a.K / BK + sp - 1) / sp;
+    P.alpha = a.alpha;
+    P.block0 = int(blocks);
+    P.nblocks = int(tiles * sp);  // below 2^31: the grid check after the loop covers it
+    P.rblock0 = int(rblocks);
+    blocks += (tiles * sp + 7) / 8 * 8;
+    if (sp > 1) rblocks += tiles * (BM * BN / 4) / 256;  // one thread per f32x4 of the partial tiles
+    if (blocks > 0x7fffffff || rblocks > 0x7fffffff) {
+      set_error("kp_linear: %lld blocks exceed the grid", (long long)blocks);
+      return KP_ERR_INVALID_ARG;
+    }
+    ++g.n;
   }
-  const int nk = a.K / BK, nk_per = (nk + sp - 1) / sp;
-  const int64_t blocks = tiles * sp;
-  if (blocks > 0x7fffffff) {
-    set_error("kp_linear: %lld blocks exceed the grid", (long long)blocks);
-    return KP_ERR_INVALID_ARG;
-  }
-  const int64_t rblocks = tiles * (BM * BN / 4) / 256;  // reduce: one thread per f32x4 of the partial tiles
-  if (a.c_dtype == KP_DTYPE_BF16) {
-    linear_kernel<BM, BN, BK, bf16><<<dim3(unsigned(blocks)), dim3(LN_THREADS), 0, s>>>(
-        (const bf16*)a.A, a.lda, a.sa, (const bf16*)a.W, a.ldw, a.sw, (bf16*)a.C, a.ldc, a.sc, a.M, a.N, a.K,
-        a.alpha, tiles_m, tiles_n, sp, nk_per, part);
-    if (sp > 1)
-      linear_reduce_kernel<BM, BN, bf16><<<dim3(unsigned(rblocks)), dim3(256), 0, s>>>(
-          part, sp, (bf16*)a.C, a.ldc, a.sc, a.M, a.N, a.alpha, tiles_m, tiles_n);
-  } else {
-    linear_kernel<BM, BN, BK, float><<<dim3(unsigned(blocks)), dim3(LN_THREADS), 0, s>>>(
-        (const bf16*)a.A, a.lda, a.sa, (const bf16*)a.W, a.ldw, a.sw, (float*)a.C, a.ldc, a.sc, a.M, a.N, a.K,
-        a.alpha, tiles_m, tiles_n, sp, nk_per, part);
-    if (sp > 1)
-      linear_reduce_kernel<BM, BN, float><<<dim3(unsigned(rblocks)), dim3(256), 0, s>>>(
-          part, sp, (float*)a.C, a.ldc, a.sc, a.M, a.N, a.alpha, tiles_m, tiles_n);
+  if (g.n == 0) return KP_OK;
+  linear_kernel<BM, BN, BK><<<dim3(unsigned(blocks)), dim3(LN_THREADS), 0, s>>>(g);
+  if (rblocks > 0) {
+    // a product without splits has no reduce blocks: its rblock0 equals the next one's, and linear_find (the last
+    // product whose first block is at or below) passes over it
+    linear_reduce_kernel<BM, BN><<<dim3(unsigned(rblocks)), dim3(256), 0, s>>>(g);
   }
   return check_launch("kp_linear");
 }
 
-kp_status launch_linear(const LinearLaunch& a, hipStream_t s) {
-  if (a.batch == 0 || a.M == 0 || a.N == 0) return KP_OK;
-  if (linear_tile(a.M).BM == 64) return launch_tile<64, 64, 64>(a, s);
-  return launch_tile<128, 128, 32>(a, s);
+size_t linear_group_workspace(const LinearLaunch* probs, int n) {
+  int maxM = 0;
+  for (int i = 0; i < n; ++i) maxM = max(maxM, probs[i].M);
+  if (maxM == 0) return 0;
+  const LinearTile t = linear_tile(maxM);
+  int spl[LN_MAXGROUP];
+  linear_splits(t, probs, n, 256, spl);
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    const LinearLaunch& a = probs[i];
+    const int sp = spl[i];
+    if (sp <= 1) continue;
+    const int64_t tiles = int64_t(a.batch) * ((a.M + t.BM - 1) / t.BM) * ((a.N + t.BN - 1) / t.BN);
+    total += size_t(tiles) * sp * t.BM * t.BN * sizeof(float);
+  }
+  return total;
+}
+
+kp_status launch_linear_group(const LinearLaunch* probs, int n, void* ws, size_t ws_bytes, hipStream_t s) {
+  int maxM = 0;
+  for (int i = 0; i < n; ++i) maxM = max(maxM, probs[i].M);
+  if (maxM == 0) return KP_OK;
+  // one tile shape for the whole group, chosen by its largest row count
+  if (linear_tile(maxM).BM == 64) return launch_group<64, 64, 64>(probs, n, ws, ws_bytes, s);
+  return launch_group<128, 128, 32>(probs, n, ws, ws_bytes, s);
 }
 
 }  // namespace kp

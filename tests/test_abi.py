@@ -21,7 +21,8 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_fp8",
-              "sparse_mla_attn_shared", "kp_linear", "kp_linear_workspace_size",
+              "sparse_mla_attn_shared", "kp_linear", "kp_linear_workspace_size", "kp_linear_group",
+              "kp_linear_group_workspace_size",
               "dsa_topk_workspace_size", "sparse_mla_workspace_size", "kp_last_error", "kp_abi_version"):
         assert f in names
     assert set(names) == set(K.EXPORTED)
@@ -128,7 +129,8 @@ def test_binding_raises_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(K, "_lib", None)
     with pytest.raises(RuntimeError, match="no CPU or PyTorch fallback"):
         K.load(str(tmp_path / "missing.so"))
-    importlib.reload(K)
+    monkeypatch.undo()
+    importlib.reload(K)  # a fresh module: the next load() binds the library to this module's ctypes classes
 
 
 def _linear(batch=1, M=64, N=64, k=128, A=FAKE, lda=128, sa=0, W=FAKE, ldw=128, sw=0, C=FAKE, ldc=64, sc=0,
@@ -175,3 +177,27 @@ def test_linear_workspace_sizes():
     # fp32 partial tiles: 64 x 64 per split of each tile
     n = ws(1, 64, 32, 4096)
     assert n > 0 and n % (64 * 64 * 4) == 0
+
+
+def test_linear_group_validation():
+    """kp_linear_group checks the product count, the list and every product before launching anything."""
+    lib = K.load()
+    good = K._LinearProblem(1, 64, 64, 128, FAKE, 128, 0, FAKE, 128, 0, FAKE, 64, 0, K.KP_DTYPE_BF16, 1.0)
+    bad_k = K._LinearProblem(1, 64, 64, 96, FAKE, 128, 0, FAKE, 128, 0, FAKE, 64, 0, K.KP_DTYPE_BF16, 1.0)
+    empty = K._LinearProblem(0, 64, 64, 96, None, 0, 0, None, 0, 0, None, 0, 0, 9, 1.0)  # never read
+    arr = (K._LinearProblem * 9)(*([good] * 9))
+    assert lib.kp_linear_group(0, arr, None, 0, None) == K.KP_OK
+    assert lib.kp_linear_group(9, arr, None, 0, None) == K.KP_ERR_INVALID_ARG
+    assert lib.kp_linear_group(-1, arr, None, 0, None) == K.KP_ERR_INVALID_ARG
+    assert lib.kp_linear_group(2, None, None, 0, None) == K.KP_ERR_INVALID_ARG
+    two = (K._LinearProblem * 2)(empty, bad_k)
+    assert lib.kp_linear_group(2, two, None, 0, None) == K.KP_ERR_UNSUPPORTED
+    assert "kp_linear_group" in K.last_error()
+    one_empty = (K._LinearProblem * 1)(empty)
+    assert lib.kp_linear_group(1, one_empty, None, 0, None) == K.KP_OK
+    # the group's workspace is the sum of its products' (same tile shape here)
+    pair = (K._LinearProblem * 2)(
+        K._LinearProblem(1, 64, 32, 4096, FAKE, 4096, 0, FAKE, 4096, 0, FAKE, 32, 0, K.KP_DTYPE_F32, 1.0),
+        K._LinearProblem(1, 64, 4096, 1536, FAKE, 1536, 0, FAKE, 1536, 0, FAKE, 4096, 0, K.KP_DTYPE_BF16, 1.0))
+    assert lib.kp_linear_group_workspace_size(2, pair) == \
+        K.linear_workspace_size(1, 64, 32, 4096) + K.linear_workspace_size(1, 64, 4096, 1536)

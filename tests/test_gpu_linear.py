@@ -189,3 +189,63 @@ def test_linear_alpha_and_shared_weight_batch():
     torch.cuda.synchronize()
     ref = np.stack([O.linear(a[b], w, alpha=0.25) for b in range(3)])
     np.testing.assert_array_equal(c.cpu().numpy(), ref)
+
+
+def test_group_mixed_products_and_short_workspace():
+    """One grouped launch of products with different shapes, output dtypes, splits and row counts (the group takes
+    the 128-row tile of its largest M); then the same group with a workspace that fits only the first product's
+    split, so the rest run unsplit.  Integer operands: every output is exact either way."""
+    _say("linear_group: mixed products")
+    shapes = [(64, 32, 4096, torch.float32), (200, 130, 256, torch.bfloat16), (64, HI * D, Q_RANK, torch.bfloat16),
+              (3, 8, 512, torch.float32)]
+    ops, refs = [], []
+    for i, (T, N, K_, dt) in enumerate(shapes):
+        a = ks.host_matrix(SEED, f"gr{i}:a", (T, K_), "int")
+        w = ks.host_matrix(SEED, f"gr{i}:w", (N, K_), "int")
+        ldc = -(-N // 4) * 4  # output rows padded to a multiple of 4 elements
+        ops.append((_dev(a), _dev(w), torch.empty((T, ldc), dtype=dt, device="cuda")[:, :N], 0.5))
+        refs.append(O.linear(a, w, alpha=0.5))
+    n = K.linear_group_workspace_size(ops)
+    for ws_bytes in (n, 16 * 1024):
+        ws = torch.full((max(ws_bytes, 16),), 0x55, dtype=torch.uint8, device="cuda") if ws_bytes else None
+        for _, _, c, _ in ops:
+            c.fill_(7.0)
+        K.linear_group(ops, workspace=ws)
+        torch.cuda.synchronize()
+        for (_, _, c, _), ref in zip(ops, refs):
+            want = O.bf16_round(ref) if c.dtype == torch.bfloat16 else ref
+            np.testing.assert_array_equal(c.float().cpu().numpy(), want, err_msg=f"workspace {ws_bytes}")
+
+
+def test_group_decode_step_products():
+    """The five products that precede attention in a decode step (index query, head weights, key, gate, query
+    absorb) in one grouped launch, normal operands, against the oracle."""
+    T = 64
+    _say(f"linear_group: decode-step products T={T}")
+    x = ks.host_matrix(SEED, "ds:x", (T, HIDDEN), "normal")
+    cq = ks.host_matrix(SEED, "ds:cq", (T, Q_RANK), "normal")
+    w_q = ks.host_matrix(SEED, "ds:wq", (HI * D, Q_RANK), "normal", 2.0 ** -6)
+    w_w = ks.host_matrix(SEED, "ds:ww", (HI, HIDDEN), "normal", 2.0 ** -6)
+    w_kg = ks.host_matrix(SEED, "ds:wkg", (2 * D, HIDDEN), "normal", 2.0 ** -6)
+    q_nope = ks.host_matrix(SEED, "ds:qn", (T, H, DN), "normal")
+    w_uk = ks.host_matrix(SEED, "ds:wuk", (H, DN, V), "normal", 2.0 ** -4)
+    q_idx = torch.empty((T, HI, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((T, HI), dtype=torch.float32, device="cuda")
+    keys = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    gates = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((T, H, L), dtype=torch.bfloat16, device="cuda")
+    w_uk_t = _dev(np.ascontiguousarray(np.transpose(w_uk, (0, 2, 1))))
+    prods = K.indexer_products(_dev(x), _dev(cq), _dev(w_q), _dev(w_w), _dev(w_kg), q_idx, w, keys, gates)
+    prods.append(K.absorb_product(_dev(q_nope), w_uk_t, q))
+    ws = torch.empty(max(K.linear_group_workspace_size(prods), 16), dtype=torch.uint8, device="cuda")
+    K.linear_group(prods, workspace=ws)
+    torch.cuda.synchronize()
+    r_q, r_w, r_k, r_g = O.indexer_project(x, cq, w_q, w_w, w_kg, HI, D)
+    a_q, a_w, a_k, a_g = O.indexer_project(np.abs(x), np.abs(cq), np.abs(w_q), np.abs(w_w), np.abs(w_kg), HI, D)
+    _check(q_idx.float().cpu().numpy(), r_q, a_q, True, False, "group q_idx")
+    _check(w.cpu().numpy(), r_w, a_w, False, False, "group w")
+    _check(keys.float().cpu().numpy(), r_k, a_k, True, False, "group keys")
+    _check(gates.float().cpu().numpy(), r_g, a_g, True, False, "group gates")
+    _check(q.float().cpu().numpy()[:, :, :V], O.mla_absorb_q(q_nope, w_uk),
+           O.mla_absorb_q(np.abs(q_nope), np.abs(w_uk)), True, False, "group absorb")
+    assert np.all(q.float().cpu().numpy()[:, :, V:] == 0.0)
