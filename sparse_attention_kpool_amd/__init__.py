@@ -294,6 +294,15 @@ def _problems(products):
     return arr
 
 
+def linear_shapes_workspace_size(shapes) -> int:
+    """Split-K workspace of a group given only its shapes [(batch, M, N, K, c_dtype), ...] (nothing is read)."""
+    arr = (_LinearProblem * max(len(shapes), 1))()
+    for i, (b, M, N, K, dt) in enumerate(shapes):
+        # stand-in operands: aligned, never dereferenced by the size query
+        arr[i] = _LinearProblem(b, M, N, K, 256, K, 0, 256, K, 0, 256, (N + 3) // 4 * 4, 0, dt, 1.0)
+    return int(load().kp_linear_group_workspace_size(len(shapes), arr))
+
+
 def linear_group_workspace_size(products) -> int:
     """Bytes of split-K workspace for a group of products [(a, w, out[, alpha]), ...]."""
     return int(load().kp_linear_group_workspace_size(len(products), _problems(products)))

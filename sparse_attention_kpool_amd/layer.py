@@ -1,8 +1,11 @@
-"""One KPool-DSA layer step over the C ABI: compress -> score -> select -> attend.
+"""One KPool-DSA layer step over the C ABI: compress -> score -> select -> attend, and the dense projections on
+either side of it.
 
 ``KPoolDSALayer`` sizes and owns the intermediate buffers (scores, selection, workspaces) once, at
 construction, for a maximum batch shape; ``step`` then only enqueues the four library calls on the current
-stream -- no allocation, no host synchronisation.  Caches, queries and outputs belong to the caller.
+stream -- no allocation, no host synchronisation.  ``LayerProjections`` does the same for the projections: one
+grouped launch before attention (index query, head weights, key | gate, query absorb) and the output un-absorb
+after it.  Caches, queries, weights and outputs belong to the caller.
 """
 from __future__ import annotations
 
@@ -11,8 +14,10 @@ from typing import Optional
 
 import torch
 
-from . import (Cache, Dims, Queries, dsa_indexer_score, dsa_topk_select, dsa_topk_workspace_size, kpool_compress,
-               sparse_mla_attn, sparse_mla_attn_fp8, sparse_mla_workspace_size)
+from . import (KP_DTYPE_BF16, KP_DTYPE_F32, Cache, Dims, Queries, absorb_product, dsa_indexer_score,
+               dsa_topk_select, dsa_topk_workspace_size, indexer_products, kpool_compress, linear_group,
+               linear_shapes_workspace_size, mla_unabsorb_o, sparse_mla_attn, sparse_mla_attn_fp8,
+               sparse_mla_workspace_size)
 
 
 @dataclass
@@ -70,3 +75,52 @@ class KPoolDSALayer:
         else:
             sparse_mla_attn(self.dims, cache, queries, q, self.sel[:n_q], self.n_sel[:n_q], out, lse=lse,
                             workspace=self.ws_attn)
+
+
+@dataclass
+class ProjectionWeights:
+    """The layer's dense weights, bf16, output-major (rows = outputs): w_q [Hi*D, q_lora] (index query, head-major),
+    w_w [Hi, hidden] (head weights), w_kg [2D, hidden] (key rows, then gate rows), w_uk_t [H, V, dn] (W_UK[h]
+    transposed, prepared once at load), w_uv [H, dv, V]."""
+    w_q: torch.Tensor
+    w_w: torch.Tensor
+    w_kg: torch.Tensor
+    w_uk_t: torch.Tensor
+    w_uv: torch.Tensor
+
+
+class LayerProjections:
+    """The projections of one layer for up to ``max_tokens`` tokens a step; the split-K workspace is sized once."""
+
+    def __init__(self, weights: ProjectionWeights, max_tokens: int, device):
+        self.wt = weights
+        Hi_D, q_rank = weights.w_q.shape
+        Hi, hidden = weights.w_w.shape
+        D2 = weights.w_kg.shape[0]
+        H, V, dn = weights.w_uk_t.shape
+        dv = weights.w_uv.shape[1]
+        need = 0
+        # the split rule depends on the token count: take the largest need over every count up to max_tokens
+        for T in range(1, max_tokens + 1):
+            pre = [(1, T, Hi_D, q_rank, KP_DTYPE_BF16), (1, T, Hi, hidden, KP_DTYPE_F32),
+                   (1, T, D2 // 2, hidden, KP_DTYPE_BF16), (1, T, D2 // 2, hidden, KP_DTYPE_BF16),
+                   (H, T, V, dn, KP_DTYPE_BF16)]
+            need = max(need, linear_shapes_workspace_size(pre),
+                       linear_shapes_workspace_size([(H, T, dv, V, KP_DTYPE_BF16)]))
+        self.ws = None if need == 0 else torch.empty(need, dtype=torch.uint8, device=device)
+        self.max_tokens = max_tokens
+
+    def pre_attention(self, x, cq, q_nope, q_idx, w, keys, gates, q) -> None:
+        """q_idx [T, Hi, D], w [T, Hi] (float32), keys / gates [T, D] and q[:, :, :V] [T, H, L] from the hidden
+        state x [T, hidden], the compressed query cq [T, q_lora] and q_nope [T, H, dn]: one grouped launch."""
+        if x.shape[0] > self.max_tokens:
+            raise ValueError("more tokens than the projections were sized for")
+        wt = self.wt
+        linear_group(indexer_products(x, cq, wt.w_q, wt.w_w, wt.w_kg, q_idx, w, keys, gates)
+                     + [absorb_product(q_nope, wt.w_uk_t, q)], workspace=self.ws)
+
+    def post_attention(self, o_lat, o) -> None:
+        """o [T, H, dv] from the latent attention output o_lat [T, H, V]."""
+        if o_lat.shape[0] > self.max_tokens:
+            raise ValueError("more tokens than the projections were sized for")
+        mla_unabsorb_o(o_lat, self.wt.w_uv, o, workspace=self.ws)

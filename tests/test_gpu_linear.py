@@ -249,3 +249,39 @@ def test_group_decode_step_products():
     _check(q.float().cpu().numpy()[:, :, :V], O.mla_absorb_q(q_nope, w_uk),
            O.mla_absorb_q(np.abs(q_nope), np.abs(w_uk)), True, False, "group absorb")
     assert np.all(q.float().cpu().numpy()[:, :, V:] == 0.0)
+
+
+@pytest.mark.parametrize("T", [64, 70])
+def test_layer_projections_object(T):
+    """LayerProjections (workspace sized once for up to 96 tokens): pre_attention's grouped launch and
+    post_attention's un-absorb against the oracle, integer operands (exact)."""
+    from sparse_attention_kpool_amd.layer import LayerProjections, ProjectionWeights
+    _say(f"LayerProjections: T={T}")
+    x = ks.host_matrix(SEED, f"lp{T}:x", (T, HIDDEN), "int")
+    cq = ks.host_matrix(SEED, f"lp{T}:cq", (T, Q_RANK), "int")
+    q_nope = ks.host_matrix(SEED, f"lp{T}:qn", (T, H, DN), "int")
+    o_lat = ks.host_matrix(SEED, f"lp{T}:ol", (T, H, V), "int")
+    w_q = ks.host_matrix(SEED, "lpw:q", (HI * D, Q_RANK), "int")
+    w_w = ks.host_matrix(SEED, "lpw:w", (HI, HIDDEN), "int")
+    w_kg = ks.host_matrix(SEED, "lpw:kg", (2 * D, HIDDEN), "int")
+    w_uk = ks.host_matrix(SEED, "lpw:uk", (H, DN, V), "int")
+    w_uv = ks.host_matrix(SEED, "lpw:uv", (H, DV, V), "int")
+    wt = ProjectionWeights(w_q=_dev(w_q), w_w=_dev(w_w), w_kg=_dev(w_kg),
+                           w_uk_t=_dev(np.ascontiguousarray(np.transpose(w_uk, (0, 2, 1)))), w_uv=_dev(w_uv))
+    proj = LayerProjections(wt, max_tokens=96, device="cuda")
+    q_idx = torch.empty((T, HI, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((T, HI), dtype=torch.float32, device="cuda")
+    keys = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    gates = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((T, H, L), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((T, H, DV), dtype=torch.bfloat16, device="cuda")
+    proj.pre_attention(_dev(x), _dev(cq), _dev(q_nope), q_idx, w, keys, gates, q)
+    proj.post_attention(_dev(o_lat), o)
+    torch.cuda.synchronize()
+    r_q, r_w, r_k, r_g = O.indexer_project(x, cq, w_q, w_w, w_kg, HI, D)
+    np.testing.assert_array_equal(q_idx.float().cpu().numpy(), O.bf16_round(r_q))
+    np.testing.assert_array_equal(w.cpu().numpy(), r_w)
+    np.testing.assert_array_equal(keys.float().cpu().numpy(), O.bf16_round(r_k))
+    np.testing.assert_array_equal(gates.float().cpu().numpy(), O.bf16_round(r_g))
+    np.testing.assert_array_equal(q.float().cpu().numpy()[:, :, :V], O.bf16_round(O.mla_absorb_q(q_nope, w_uk)))
+    np.testing.assert_array_equal(o.float().cpu().numpy(), O.bf16_round(O.mla_unabsorb_o(o_lat, w_uv)))
