@@ -119,6 +119,27 @@ class Leg:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
+    def time_steps_graph(self, steps: int) -> float:
+        """Mean ms per step with `steps` steps captured in one HIP graph and replayed: the GPU time of a step whose
+        kernels finish faster than Python can enqueue them (a single query)."""
+        torch = self.torch
+        for i in range(3):
+            self.step(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                self.step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) / steps
+
     def time_stages(self, steps: int) -> dict:
         """Mean ms per stage, events recorded between the four calls on the launch stream."""
         torch, K, L = self.torch, self.K, self.layer
@@ -394,9 +415,12 @@ def main():
         ms = leg.time_steps(max(args.steps, 50), args.warmup)
         st = leg.time_stages(max(args.steps, 50))
         by = decode_bytes(w1)
+        msg = leg.time_steps_graph(max(args.steps, 50))
         res["decode128k"] = {"tokens_per_s": round(1 / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
                              "hbm_gbs": round(sum(by.values()) / (ms * 1e-3) / 1e9, 1),
-                             "stages_ms": {k: round(v, 5) for k, v in st.items()}}
+                             "stages_ms": {k: round(v, 5) for k, v in st.items()},
+                             "graph": {"ms_per_step": round(msg, 5), "tokens_per_s": round(1 / (msg * 1e-3), 1),
+                                       "hbm_gbs": round(sum(by.values()) / (msg * 1e-3) / 1e9, 1)}}
         leg.free()
     if "long1m" in legs:
         print("[bench] long1m leg: 8 sequences at context 1048576", file=sys.stderr, flush=True)
