@@ -285,3 +285,45 @@ def test_layer_projections_object(T):
     np.testing.assert_array_equal(gates.float().cpu().numpy(), O.bf16_round(r_g))
     np.testing.assert_array_equal(q.float().cpu().numpy()[:, :, :V], O.bf16_round(O.mla_absorb_q(q_nope, w_uk)))
     np.testing.assert_array_equal(o.float().cpu().numpy(), O.bf16_round(O.mla_unabsorb_o(o_lat, w_uv)))
+
+
+def test_group_prefill_chunk_sampled_rows():
+    """The bench's prefill launch: the five pre-attention products of a 4096-token chunk in one grouped launch
+    (128 x 128 tiles, 9312 blocks) and the un-absorb; 96 sampled token rows of every output against the oracle."""
+    T = 4096
+    _say(f"linear_group: prefill chunk T={T}")
+    x = ks.host_matrix(SEED, "pc:x", (T, HIDDEN), "normal")
+    cq = ks.host_matrix(SEED, "pc:cq", (T, Q_RANK), "normal")
+    q_nope = ks.host_matrix(SEED, "pc:qn", (T, H, DN), "normal")
+    o_lat = ks.host_matrix(SEED, "pc:ol", (T, H, V), "normal")
+    w_q = ks.host_matrix(SEED, "pc:wq", (HI * D, Q_RANK), "normal", 2.0 ** -6)
+    w_w = ks.host_matrix(SEED, "pc:ww", (HI, HIDDEN), "normal", 2.0 ** -6)
+    w_kg = ks.host_matrix(SEED, "pc:wkg", (2 * D, HIDDEN), "normal", 2.0 ** -6)
+    w_uk = ks.host_matrix(SEED, "pc:wuk", (H, DN, V), "normal", 2.0 ** -4)
+    w_uv = ks.host_matrix(SEED, "pc:wuv", (H, DV, V), "normal", 2.0 ** -4)
+    q_idx = torch.empty((T, HI, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((T, HI), dtype=torch.float32, device="cuda")
+    keys = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    gates = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((T, H, L), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((T, H, DV), dtype=torch.bfloat16, device="cuda")
+    prods = K.indexer_products(_dev(x), _dev(cq), _dev(w_q), _dev(w_w), _dev(w_kg), q_idx, w, keys, gates)
+    prods.append(K.absorb_product(_dev(q_nope), _dev(np.ascontiguousarray(np.transpose(w_uk, (0, 2, 1)))), q))
+    n = K.linear_group_workspace_size(prods)
+    K.linear_group(prods, workspace=torch.empty(max(n, 16), dtype=torch.uint8, device="cuda"))
+    K.mla_unabsorb_o(_dev(o_lat), _dev(w_uv), o)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(9).choice(T, 96, replace=False))
+    rows[0], rows[-1] = 0, T - 1
+    r = torch.from_numpy(rows).cuda()
+    r_q, r_w, r_k, r_g = O.indexer_project(x[rows], cq[rows], w_q, w_w, w_kg, HI, D)
+    a_q, a_w, a_k, a_g = O.indexer_project(np.abs(x[rows]), np.abs(cq[rows]), np.abs(w_q), np.abs(w_w),
+                                           np.abs(w_kg), HI, D)
+    _check(q_idx[r].float().cpu().numpy(), r_q, a_q, True, False, "prefill q_idx")
+    _check(w[r].cpu().numpy(), r_w, a_w, False, False, "prefill w")
+    _check(keys[r].float().cpu().numpy(), r_k, a_k, True, False, "prefill keys")
+    _check(gates[r].float().cpu().numpy(), r_g, a_g, True, False, "prefill gates")
+    _check(q[r].float().cpu().numpy()[:, :, :V], O.mla_absorb_q(q_nope[rows], w_uk),
+           O.mla_absorb_q(np.abs(q_nope[rows]), np.abs(w_uk)), True, False, "prefill absorb")
+    _check(o[r].float().cpu().numpy(), O.mla_unabsorb_o(o_lat[rows], w_uv),
+           O.mla_unabsorb_o(np.abs(o_lat[rows]), np.abs(w_uv)), True, False, "prefill unabsorb")
