@@ -68,6 +68,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # torch's HIP runtime first: the library then binds to that same runtime (a process that loaded ROCm's own
+    # copy first would hold two, and kernels launched through one would see no device of the other)
+    import torch  # noqa: F401
     p = path or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m sparse_attention_kpool_amd.build` "
