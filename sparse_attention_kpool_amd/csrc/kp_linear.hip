@@ -10,7 +10,9 @@
 // Every operand is K-contiguous (a weight is stored output-major, as a linear layer keeps it), so both MFMA
 // operands are plain 16-byte row reads.  One block of 4 waves per BM x BN output tile.  The block computes the
 // tile transposed, D[n][m] = W . A^T on 16x16x32 bf16 MFMA (weight rows = M operand, activation rows = N
-// operand), so each lane ends with 4 consecutive output columns of one row: one 8- or 16-byte store.
+// operand), so each lane ends with 4 consecutive output columns of one row.  A bf16 output tile then goes through
+// LDS (the stage ring is free by then) and out as whole 16-byte row chunks: the 4096-token absorb and un-absorb,
+// which write 268 / 134 MB, ran 239 -> 195 and 207 -> 159 us with it; other outputs are stored from the lanes.
 //   load   k advances BK (64 or 32) at a time: one 2 BK-byte segment of every tile row per stage.  Each wave moves
 //          1 KiB of rows per direct global->LDS instruction (16 bytes a lane, no register staging) into a ring of
 //          NBUF stage buffers, NBUF - 1 stages ahead, with one barrier per stage.  Rows are XOR-swizzled (see ln_swz) so the
@@ -99,8 +101,11 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const LinearGroup gr
   constexpr int TN = BN / 32, TM = BM / 32;  // MFMA tiles per wave along n and m
   constexpr int KS = BK / 32;                // MFMA k-steps per stage
   static_assert(LA >= 1 && LW >= 1 && KS >= 1, "tile shape");
-  __shared__ __align__(1024) bf16 sA[LN_NBUF][BM * BK];
-  __shared__ __align__(1024) bf16 sW[LN_NBUF][BN * BK];
+  // one LDS array: the stage ring while the tile is multiplied, then the staging of its bf16 output
+  __shared__ __align__(1024) bf16 smem[LN_NBUF * (BM + BN) * BK];
+  bf16 (*sA)[BM * BK] = reinterpret_cast<bf16 (*)[BM * BK]>(smem);
+  bf16 (*sW)[BN * BK] = reinterpret_cast<bf16 (*)[BN * BK]>(smem + LN_NBUF * BM * BK);
+  static_assert(BM * BN <= LN_NBUF * (BM + BN) * BK, "the output tile fits the stage ring");
 
   // Each product owns an 8-aligned range of 8 k blocks (blocks are dealt to the 8 XCDs round-robin, so every
   // product spreads over all XCDs); inside it, slot j runs block (j mod 8) k + j / 8, so each XCD takes a
@@ -205,6 +210,38 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const LinearGroup gr
     return;
   }
 
+  if (P.c_bf16 && P.ldc % 8 == 0 && P.sc % 8 == 0) {
+    // bf16 output through LDS: the tile's rows are written as whole 16-byte chunks (chunk ch of row r at position
+    // ch ^ (r mod CH), so the 16 rows of one fragment store land on distinct banks), then copied out contiguously
+    constexpr int CH = BN / 8;
+    __syncthreads();  // every wave is done with the stage buffers
+#pragma unroll
+    for (int a = 0; a < TN; ++a) {
+      const int cc = wn * (BN / 2) + 16 * a + 4 * g;
+#pragma unroll
+      for (int c = 0; c < TM; ++c) {
+        const int r = wm * (BM / 2) + 16 * c + l16;
+        const f32x4 v = acc[a][c] * P.alpha;
+        *reinterpret_cast<uint2*>(smem + r * BN + 8 * ((cc >> 3) ^ (r & (CH - 1))) + (cc & 7)) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+    __syncthreads();
+    bf16* Cb = static_cast<bf16*>(P.C) + int64_t(b) * P.sc;
+    for (int i = threadIdx.x; i < BM * CH; i += LN_THREADS) {
+      const int r = i / CH, ch = i - r * CH;
+      const int m = m0 + r, n = n0 + 8 * ch;
+      if (m >= M || n >= N) continue;
+      const bf16* src = smem + r * BN + 8 * (ch ^ (r & (CH - 1)));
+      bf16* dst = Cb + int64_t(m) * P.ldc + n;
+      if (n + 8 <= N) {
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        for (int e = 0; e < N - n; ++e) dst[e] = src[e];
+      }
+    }
+    return;
+  }
   // lane holds D[n][m] for n = tile n + 4 g .. +3, m = tile m + l16
 #pragma unroll
   for (int a = 0; a < TN; ++a) {
@@ -218,8 +255,6 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const LinearGroup gr
   }
 }
 
-// k-splits for a call shape: enough blocks to keep every CU streaming (about 2 per CU) when the tile grid is
-// small, each split at least 4 stages long; a pure function of the shape
 // Split-K reduction: one thread per 4 outputs (one lane's f32x4 of one MFMA tile of one wave); the partials of the
 // splits are added in split order, scaled once and rounded once, and stored as the unsplit kernel stores them.
 template <int BM, int BN>
