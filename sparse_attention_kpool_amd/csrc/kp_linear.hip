@@ -289,14 +289,14 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const LinearGroup gr
 }
 
 // Tile shape for a call: a decode step (few rows) takes 64 x 64 tiles with 64-wide k stages in 3 buffers (48 KiB
-// of LDS, three blocks per CU); more rows take 128 x 128 tiles with 32-wide k stages in 2 buffers (32 KiB; three
-// blocks per CU, as many as the registers allow).  Several blocks per CU hide each other's load latency, first loads and last stores: measured
-// against 4 buffers (two blocks per CU), the 4096-token projections ran 598 -> 539 us and the 64-token ones
-// 22.7 -> 21.6 us.
+// of LDS, three blocks per CU); more rows take 128 x 128 tiles with 64-wide k stages in 2 buffers (64 KiB, two
+// blocks per CU).  Several blocks per CU hide each other's load latency, first loads and last stores.  Measured on
+// the 4096-token projections: 4 buffers of 32-wide stages 598 us, 2 buffers of 32-wide stages 539 us, 2 buffers of
+// 64-wide stages 415 us (with the LDS-staged output); the 64-token ones went 22.7 -> 21.4 us with 3 buffers.
 struct LinearTile {
   int BM, BN, BK;
 };
-static LinearTile linear_tile(int M) { return M <= 64 ? LinearTile{64, 64, 64} : LinearTile{128, 128, 32}; }
+static LinearTile linear_tile(int M) { return M <= 64 ? LinearTile{64, 64, 64} : LinearTile{128, 128, 64}; }
 
 // k-splits of a group's products, a pure function of the shapes.  The group's work is sum(tiles x stages); spread
 // over two blocks per CU it gives the stages each block slot runs on average (at least 4).  A product whose blocks
@@ -423,7 +423,7 @@ kp_status launch_linear_group(const LinearLaunch* probs, int n, void* ws, size_t
   if (maxM == 0) return KP_OK;
   // one tile shape for the whole group, chosen by its largest row count
   if (linear_tile(maxM).BM == 64) return launch_group<64, 64, 64, 3>(probs, n, ws, ws_bytes, s);
-  return launch_group<128, 128, 32, 2>(probs, n, ws, ws_bytes, s);
+  return launch_group<128, 128, 64, 2>(probs, n, ws, ws_bytes, s);
 }
 
 }  // namespace kp
