@@ -13,19 +13,21 @@
 // operand), so each lane ends with 4 consecutive output columns of one row.  A bf16 output tile then goes through
 // LDS (the stage ring is free by then) and out as whole 16-byte row chunks: the 4096-token absorb and un-absorb,
 // which write 268 / 134 MB, ran 239 -> 195 and 207 -> 159 us with it; other outputs are stored from the lanes.
-//   load   k advances BK (64 or 32) at a time: one 2 BK-byte segment of every tile row per stage.  Each wave moves
-//          1 KiB of rows per direct global->LDS instruction (16 bytes a lane, no register staging) into a ring of
-//          NBUF stage buffers, NBUF - 1 stages ahead, with one barrier per stage.  Rows are XOR-swizzled (see ln_swz) so the
-//          fragment reads are conflict-free.  Rows past M or N read row M-1 / N-1 (their results are never
-//          stored), so every wave issues the same loads every stage and the waits are exact counts.
+//   load   k advances BK at a time (64 for both tile shapes; the kernel also takes 32): one 2 BK-byte segment of
+//          every tile row per stage.  Each wave moves 1 KiB of rows per direct global->LDS instruction (16 bytes a
+//          lane, no register staging) into a ring of NBUF stage buffers, NBUF - 1 stages ahead, with one barrier
+//          per stage.  Rows are XOR-swizzled (see ln_swz) so the fragment reads are conflict-free.  Rows past M
+//          or N read row M-1 / N-1 (their results are never stored), so every wave issues the same loads every
+//          stage and the waits are exact counts.
 //   math   wave (wn, wm) owns the BN/2 x BM/2 quarter of the tile: (BN/32) x (BM/32) MFMA tiles, BK/32 k-steps a
 //          stage.
 // Tiles are numbered m-fastest under one weight tile, and each XCD takes a contiguous run of a product's tiles
 // (see linear_kernel), so blocks sharing a weight tile share that XCD's L2.  A grouped launch runs up to 8
 // independent products in one grid, each spread over all XCDs.
 //
-// Bound: the decode shapes (M = tokens of a step, tens) stream their weights once -- HBM; the prefill shapes
-// (M = thousands) are MFMA-bound at 2 M N K flop.
+// Bound: the decode shapes (M = tokens of a step, tens) stream their weights once -- HBM.  The prefill shapes
+// (M = thousands) are MFMA-bound at 2 M N K flop, except the absorb and un-absorb, whose outputs and inputs
+// (268 + 134 MB at 4096 tokens) put their HBM time above their MFMA time.
 #include "kp_device.hpp"
 #include "kp_internal.hpp"
 
