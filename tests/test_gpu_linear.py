@@ -327,3 +327,41 @@ def test_group_prefill_chunk_sampled_rows():
            O.mla_absorb_q(np.abs(q_nope[rows]), np.abs(w_uk)), True, False, "prefill absorb")
     _check(o[r].float().cpu().numpy(), O.mla_unabsorb_o(o_lat[rows], w_uv),
            O.mla_unabsorb_o(np.abs(o_lat[rows]), np.abs(w_uv)), True, False, "prefill unabsorb")
+
+
+def test_layer_chain_with_projections():
+    """The documented decode chain: LayerProjections.pre_attention -> KPoolDSALayer.step -> post_attention, on
+    real paged caches (three sequences of 29, 4096 and 7001 tokens).  Selector weights (identities) make the
+    projections return the seeded inputs exactly, so the layer's output must equal, bit for bit, that of the same
+    step fed those inputs directly."""
+    from harness import DeviceRun
+    from sparse_attention_kpool_amd.layer import LayerProjections, ProjectionWeights
+    _say("layer chain with projections")
+    base = ks.workloads()["batch64"]
+    ctx = [29, 4096, 7001]
+    wl = ks.scaled(base, name="chain", ctx=ctx, new_from=[t - 1 for t in ctx], q_seq=np.arange(3, dtype=np.int32),
+                   q_pos=np.array([t - 1 for t in ctx], np.int32), k=256, page_perm_seed=5)
+    run = DeviceRun(wl, device="cuda").run()
+    torch.cuda.synchronize()
+    T, hid = wl.n_q, 64
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    eye = lambda n: torch.eye(n, **bf)  # noqa: E731
+    x = torch.zeros((T, hid), **bf)
+    x[:, :HI] = run.w.to(torch.bfloat16)  # head weights lie on a 2^-8 grid below 1: exact in bf16
+    wt = ProjectionWeights(w_q=eye(HI * D), w_w=eye(hid)[:HI].contiguous(), w_kg=torch.zeros((2 * D, hid), **bf),
+                           w_uk_t=eye(V).expand(H, V, V).contiguous(), w_uv=eye(V).expand(H, V, V).contiguous())
+    proj = LayerProjections(wt, max_tokens=T, device="cuda")
+    q_idx = torch.empty((T, HI, D), **bf)
+    w = torch.empty((T, HI), dtype=torch.float32, device="cuda")
+    keys, gates = torch.empty((T, D), **bf), torch.empty((T, D), **bf)
+    q = torch.zeros((T, H, L), **bf)
+    proj.pre_attention(x, run.q_idx.reshape(T, HI * D), run.q[:, :, :V].contiguous(), q_idx, w, keys, gates, q)
+    out = torch.empty_like(run.out)
+    lse = torch.empty_like(run.lse)
+    run.layer.step(run.cache, run.queries, q_idx, w, q, out, lse=lse, compress=run.compress)
+    o = torch.empty((T, H, V), **bf)
+    proj.post_attention(out, o)
+    torch.cuda.synchronize()
+    assert torch.equal(q_idx, run.q_idx) and torch.equal(w, run.w) and torch.equal(q, run.q)
+    assert torch.equal(out, run.out) and torch.equal(lse, run.lse)
+    assert torch.equal(o, out)
