@@ -213,8 +213,9 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const LinearGroup gr
   }
 
   if (P.c_bf16 && P.ldc % 8 == 0 && P.sc % 8 == 0) {
-    // bf16 output through LDS: the tile's rows are written as whole 16-byte chunks (chunk ch of row r at position
-    // ch ^ (r mod CH), so the 16 rows of one fragment store land on distinct banks), then copied out contiguously
+    // bf16 output through LDS: chunk ch (16 bytes) of tile row r sits at position ch ^ (r mod CH), which spreads the
+    // 16 rows of one fragment store over distinct bank groups (BN = 128; two rows per group at BN = 64); then the
+    // rows are copied out as whole 16-byte chunks
     constexpr int CH = BN / 8;
     __syncthreads();  // every wave is done with the stage buffers
 #pragma unroll
