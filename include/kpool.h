@@ -224,9 +224,8 @@ kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const 
  *     m*ldc, n contiguous.  A stride of 0 reuses one matrix for every batch entry.
  *   Accumulation is fp32; the result is a deterministic function of the operands and the call shape.
  *   workspace (device, may be NULL, no initial contents): with at least kp_linear_workspace_size(batch, M, N, K)
- *     bytes, a shape whose output tiles are too few to keep every compute unit streaming (a decode step) splits K
- *     over several blocks that store fp32 partial tiles there; a second kernel on the same stream adds them in
- *     split order.  Calls that share a workspace must not overlap (same stream, or ordered).  NULL or smaller: no
+ *     bytes, a shape whose few output tiles would each stream a long K (a decode step) splits K over several
+ *     blocks that store fp32 partial tiles there; a second kernel on the same stream adds them in split order.  Calls that share a workspace must not overlap (same stream, or ordered).  NULL or smaller: no
  *     split, same formula (the sum may round differently).  A size of 0 means this shape never splits.
  *   The layer's projections (T tokens, hidden 4096, q_lora 1536, Hi = 32, D = 128, H = 64, dn = dv = 256):
  *     index query   A = cq [T, 1536], W = W_iq [Hi*D, 1536] (head-major rows)  -> C = q_idx [T, Hi*D] bf16
@@ -262,12 +261,13 @@ typedef struct {
 /*
  * kp_linear_group -- up to 8 independent kp_linear products in one launch (plus one launch that adds split-K
  *   partials, when any product splits): the products of one layer step that do not depend on each other (the
- *   indexer's projections and the query absorb of a decode step) pay the launch cost once.  Each product is
- *   exactly what kp_linear computes for the same arguments and workspace share (one tile shape serves the group,
- *   chosen by its largest M, so a product may round differently than alone when the group mixes row counts).
+ *   indexer's projections and the query absorb of a decode step) pay the launch cost once.  Each product follows
+ *   kp_linear's formula and contract.  Its tile shape (chosen by the group's largest M) and its K split (chosen
+ *   from the whole group's work) can differ from a kp_linear call of its own, and so can the rounding of its sums;
+ *   for a given group the result is deterministic.
  *   problems: host array of n (0..8) products; their outputs must not overlap each other's inputs or outputs.
  *   workspace: as in kp_linear, at least kp_linear_group_workspace_size(n, problems) bytes for full splitting
- *   (products are given workspace in order; one that no longer fits runs unsplit).
+ *   (products are given workspace in order; from the first that no longer fits on, they run unsplit).
  *   Errors: as kp_linear, per product; KP_ERR_INVALID_ARG for n outside 0..8 or a NULL list.
  */
 size_t kp_linear_group_workspace_size(int32_t n, const kp_linear_problem* problems);
