@@ -172,8 +172,9 @@ kp_status dsa_topk_select(const kp_dims* dims, const kp_queries* queries, const 
  *     When a query's selection is split over several blocks (batches too small to fill the GPU), each split's
  *     unnormalised partial output is stored in the storage dtype before the merge, so the output of such a
  *     query is rounded twice; the running max and sum stay fp32.
- *   Limit: a query's selection is split over at most 32 blocks of at most min(8192 / P, 2048) pools, so
- *     topk <= 32 * min(8192 / P, 2048) (65536 pools at P = 4), else KP_ERR_UNSUPPORTED.
+ *   Limit: a query's selection (plus the one pool sparse_mla_attn_shared may add) is split over at most 32
+ *     blocks of at most min(8320 / P, 2064) pools, so topk + 1 <= 32 * min(8320 / P, 2064) (66048 pools at P = 4),
+ *     else KP_ERR_UNSUPPORTED.  Only the first min(n_sel, topk) entries of a row are read.
  *   Errors: KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED (V, H, dtype, topk), KP_ERR_WORKSPACE.
  */
 size_t sparse_mla_workspace_size(const kp_dims* dims, const kp_queries* queries);
@@ -184,10 +185,15 @@ kp_status sparse_mla_attn(const kp_dims* dims, const kp_cache* cache, const kp_q
 /*
  * sparse_mla_attn_shared -- sparse_mla_attn with selections shared between queries (MTP drafts).
  *   [MAX glm5_next API page, index_share_for_mtp_iteration: the MTP draft layer reuses the target's top-k
- *   selection; GLM-5.3-Flash model card, "Raw config fields": index_share_for_mtp_iteration true].  Query i attends
- *   the tokens of the pools in selection row sel_row[i] of sel / n_sel (rows as written by dsa_topk_select for
- *   the target queries), cut at its own position: the tail of a selected pool counts up to pos[i], and a pool the
- *   target did not select (for instance one the draft's position has just entered) is not attended.  With
+ *   selection; GLM-5.3-Flash model card, "Raw config fields": index_share_for_mtp_iteration true]; [MAX glm5_next
+ *   API page, index_kpool_always_select_tail: the incomplete trailing pool is always visible].  Query i (at
+ *   position pos[i]) attends
+ *     - the tokens of the pools in selection row sel_row[i] of sel / n_sel (rows as written by dsa_topk_select
+ *       for the target queries), each pool cut at pos[i]; and
+ *     - its own incomplete trailing pool tau = pos[i] / P (tokens P*tau .. pos[i]) when (pos[i] + 1) mod P != 0
+ *       and the row does not hold tau.  The shared item is the target's top-k pick; the forced tail is not a
+ *       pick, so a draft always sees its own pending tokens, itself included (it may attend topk + 1 pools).
+ *   A row's own query reads the same set as sparse_mla_attn (its row already holds its incomplete tail), so with
  *   sel_row[i] = i this is sparse_mla_attn.  sel_row: device int32 [n_q], each in [0, rows of sel).  Workspace,
  *   outputs, limits and errors as in sparse_mla_attn; KP_ERR_INVALID_ARG on a NULL sel_row (n_q > 0).
  */

@@ -19,6 +19,7 @@ from .kpool_dsa import (  # noqa: F401
     indexer_scores,
     select_pools,
     attended_tokens,
+    shared_attended_tokens,
     sparse_mla,
     LayerOracle,
 )

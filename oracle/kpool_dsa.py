@@ -27,6 +27,7 @@ Readings taken here (each one lives in exactly one function):
   R5  the tail pool is forced only when it is incomplete, i.e. when (i+1) mod P != 0.
   R6  the forced tail uses one of the k slots.
   R7  inside the tail pool only tokens <= i are attended.
+  R24 a query reusing another query's selection row (an MTP draft) keeps its own incomplete tail visible.
   R8  ranking order is (score descending, pool index ascending).
   R9  the selection is reported as ascending pool ids.
   R14 attention keys are the full latent rows; values are their first V columns.
@@ -167,6 +168,23 @@ def attended_tokens(sel, i: int, P: int) -> np.ndarray:
             if t <= i:
                 toks.append(t)
     return np.asarray(toks, dtype=np.int64)
+
+
+def shared_attended_tokens(sel, i: int, P: int) -> np.ndarray:
+    """Token ids a query at position i attends when it reuses another query's selection row ``sel``.
+
+    [MAX ``glm5_next`` API page, ``index_share_for_mtp_iteration``]: an MTP draft reuses its target's top-k
+    selection.  [same page, ``index_kpool_always_select_tail``]: the incomplete trailing pool is always visible.
+    The shared item is the target's top-k pick; the draft's own incomplete tail is not a pick, so it stays visible:
+    the draft attends every token <= i of the row's pools, plus tokens P*tau .. i of its own pool tau = i // P
+    when (i+1) mod P != 0 and the row does not already hold tau.  A query reading its own selection gets exactly
+    ``attended_tokens`` (its selection already holds its incomplete tail).
+    """
+    n_c, r, tau = pool_geometry(i, P)
+    pools = [int(p) for p in np.asarray(sel, dtype=np.int64)]
+    if r and tau not in pools:
+        pools.append(tau)
+    return attended_tokens(np.sort(np.asarray(pools, dtype=np.int64)), i, P)
 
 
 def sparse_mla(q, rows, scale: float, V: int):

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, "libkpool.so")
 
 KP_OK, KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED, KP_ERR_WORKSPACE, KP_ERR_LAUNCH = 0, -1, -2, -3, -4
 KP_DTYPE_F32, KP_DTYPE_BF16 = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk_select",
             "sparse_mla_workspace_size", "sparse_mla_attn", "sparse_mla_attn_shared", "sparse_mla_attn_fp8",
@@ -174,12 +174,72 @@ def _check(fn: str, status: int) -> None:
         raise KpError(fn, status, last_error())
 
 
+def _want(fn: str, name: str, t, dtypes, shape, rows_only: bool = False, min_rows: bool = False):
+    """Raise ValueError unless `t` is a device tensor of one of `dtypes` with `shape` (None = any extent; with
+    min_rows the first extent is a lower bound: the kernels touch rows below it only) that the kernels can address
+    densely: contiguous, or (rows_only) a 2-D view whose rows are contiguous."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{fn}: {name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{fn}: {name} must be on the GPU (got {t.device})")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{fn}: {name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    bad = len(shape) != t.dim()
+    for d, (e, a) in enumerate(zip(shape, t.shape)):
+        if e is not None and (a < e if (min_rows and d == 0) else a != e):
+            bad = True
+    if bad:
+        want = "[" + ", ".join("*" if e is None else (f">={e}" if min_rows and d == 0 else str(e))
+                               for d, e in enumerate(shape)) + "]"
+        raise ValueError(f"{fn}: {name} has shape {list(t.shape)}, expected {want}")
+    if rows_only:
+        if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1) or (t.shape[0] > 1 and t.stride(0) < t.shape[1]):
+            raise ValueError(f"{fn}: {name} needs contiguous rows")
+    elif not t.is_contiguous():
+        raise ValueError(f"{fn}: {name} must be contiguous")
+    return t
+
+
+def _storage(dims: "Dims"):
+    import torch
+    return (torch.bfloat16,) if dims.dtype == "bf16" else (torch.float32,)
+
+
+def _i32():
+    import torch
+    return (torch.int32,)
+
+
+def _check_queries(fn: str, queries: "Queries") -> int:
+    n = int(queries.seq.numel())
+    _want(fn, "queries.seq", queries.seq, _i32(), (n,))
+    _want(fn, "queries.pos", queries.pos, _i32(), (n,))
+    return n
+
+
 # ----------------------------------------------------------------------------------------------------------
 # the four calls
 # ----------------------------------------------------------------------------------------------------------
 def kpool_compress(dims: Dims, cache: Cache, keys, gates, ape, pool_seq, pool_id, src=None, stream=None) -> None:
     """Pooled keys of complete pools -> rows (pool_seq[i], pool_id[i]) of cache.pooled (see include/kpool.h)."""
+    import torch
+    fn = "kpool_compress"
     n = int(pool_seq.numel())
+    st = _storage(dims)
+    _want(fn, "pool_seq", pool_seq, _i32(), (n,))
+    _want(fn, "pool_id", pool_id, _i32(), (n,))
+    _want(fn, "cache.pooled", cache.pooled, st, (None, dims.page_tokens // dims.pool, dims.idx_dim))
+    if n:
+        _want(fn, "keys", keys, st, (None, dims.pool, dims.idx_dim))
+        if gates is not None:
+            _want(fn, "gates", gates, st, tuple(keys.shape))
+        if ape is not None:
+            _want(fn, "ape", ape, st, (dims.pool, dims.idx_dim))
+        if src is not None:
+            _want(fn, "src", src, _i32(), (n,))
+        elif keys.shape[0] < n:
+            raise ValueError(f"{fn}: keys holds {keys.shape[0]} pools, fewer than the {n} to compress")
     _check("kpool_compress", load().kpool_compress(ctypes.byref(dims.c()), ctypes.byref(cache.c()), n,
                                                    _ptr(keys), _ptr(gates), _ptr(src), _ptr(ape), _ptr(pool_seq),
                                                    _ptr(pool_id), _stream(stream)))
@@ -187,6 +247,13 @@ def kpool_compress(dims: Dims, cache: Cache, keys, gates, ape, pool_seq, pool_id
 
 def dsa_indexer_score(dims: Dims, cache: Cache, queries: Queries, q_idx, w, scores, stream=None) -> None:
     """scores[q, p] for p < (pos[q] + 1) / P; scores is fp32 [n_q, ld]."""
+    import torch
+    fn = "dsa_indexer_score"
+    n = _check_queries(fn, queries)
+    _want(fn, "q_idx", q_idx, _storage(dims), (n, dims.idx_heads, dims.idx_dim), min_rows=True)
+    _want(fn, "w", w, (torch.float32,), (n, dims.idx_heads), min_rows=True)
+    _want(fn, "scores", scores, (torch.float32,), (n, None), rows_only=True, min_rows=True)
+    _want(fn, "cache.pooled", cache.pooled, _storage(dims), (None, dims.page_tokens // dims.pool, dims.idx_dim))
     _check("dsa_indexer_score", load().dsa_indexer_score(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
                                                          ctypes.byref(queries.c()), _ptr(q_idx), _ptr(w),
                                                          _ptr(scores), int(scores.stride(0)), _stream(stream)))
@@ -198,6 +265,14 @@ def dsa_topk_workspace_size(dims: Dims, queries: Queries) -> int:
 
 def dsa_topk_select(dims: Dims, queries: Queries, scores, sel, n_sel, workspace=None, stream=None) -> None:
     """sel [n_q, k] int32 ascending pool ids padded with -1; n_sel [n_q] int32."""
+    import torch
+    fn = "dsa_topk_select"
+    n = _check_queries(fn, queries)
+    _want(fn, "scores", scores, (torch.float32,), (n, None), rows_only=True, min_rows=True)
+    _want(fn, "sel", sel, _i32(), (n, dims.topk), min_rows=True)
+    _want(fn, "n_sel", n_sel, _i32(), (n,), min_rows=True)
+    if workspace is not None:
+        _want(fn, "workspace", workspace, (workspace.dtype,), tuple(workspace.shape))
     ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     _check("dsa_topk_select", load().dsa_topk_select(ctypes.byref(dims.c()), ctypes.byref(queries.c()),
                                                      _ptr(scores), int(scores.stride(0)), _ptr(sel), _ptr(n_sel),
@@ -208,9 +283,29 @@ def sparse_mla_workspace_size(dims: Dims, queries: Queries) -> int:
     return int(load().sparse_mla_workspace_size(ctypes.byref(dims.c()), ctypes.byref(queries.c())))
 
 
+def _check_attn(fn: str, dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, out, lse, workspace,
+                fp8: bool = False, sel_row=None) -> None:
+    import torch
+    n = _check_queries(fn, queries)
+    st = _storage(dims)
+    _want(fn, "cache.latent", cache.latent, (torch.uint8,) if fp8 else st, (None, dims.page_tokens, dims.latent_dim))
+    _want(fn, "q", q, st, (n, dims.heads, dims.latent_dim), min_rows=True)
+    rows = n if sel_row is None else None
+    _want(fn, "sel", sel, _i32(), (rows, dims.topk), min_rows=True)
+    _want(fn, "n_sel", n_sel, _i32(), (sel.shape[0],), min_rows=True)
+    if sel_row is not None:
+        _want(fn, "sel_row", sel_row, _i32(), (n,))
+    _want(fn, "out", out, st, (n, dims.heads, dims.v_dim), min_rows=True)
+    if lse is not None:
+        _want(fn, "lse", lse, (torch.float32,), (n, dims.heads), min_rows=True)
+    if workspace is not None:
+        _want(fn, "workspace", workspace, (workspace.dtype,), tuple(workspace.shape))
+
+
 def sparse_mla_attn(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, out, lse=None, workspace=None,
                     stream=None) -> None:
     """out [n_q, H, V] (storage dtype), lse [n_q, H] fp32 (optional)."""
+    _check_attn("sparse_mla_attn", dims, cache, queries, q, sel, n_sel, out, lse, workspace)
     ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     _check("sparse_mla_attn", load().sparse_mla_attn(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
                                                      ctypes.byref(queries.c()), _ptr(q), _ptr(sel), _ptr(n_sel),
@@ -220,7 +315,9 @@ def sparse_mla_attn(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, o
 
 def sparse_mla_attn_shared(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, sel_row, out, lse=None,
                            workspace=None, stream=None) -> None:
-    """As sparse_mla_attn, query i attending selection row sel_row[i] (int32 [n_q]) cut at its own position."""
+    """As sparse_mla_attn, query i attending selection row sel_row[i] (int32 [n_q]) cut at its own position, plus its
+    own incomplete trailing pool (see include/kpool.h)."""
+    _check_attn("sparse_mla_attn_shared", dims, cache, queries, q, sel, n_sel, out, lse, workspace, sel_row=sel_row)
     ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     _check("sparse_mla_attn_shared", load().sparse_mla_attn_shared(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
                                                                    ctypes.byref(queries.c()), _ptr(q), _ptr(sel),
@@ -231,6 +328,7 @@ def sparse_mla_attn_shared(dims: Dims, cache: Cache, queries: Queries, q, sel, n
 def sparse_mla_attn_fp8(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, kv_scale: float, out, lse=None,
                         workspace=None, stream=None) -> None:
     """As sparse_mla_attn, over a latent cache of E4M3 codes (cache.latent uint8) scaled by kv_scale."""
+    _check_attn("sparse_mla_attn_fp8", dims, cache, queries, q, sel, n_sel, out, lse, workspace, fp8=True)
     ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     _check("sparse_mla_attn_fp8", load().sparse_mla_attn_fp8(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
                                                              ctypes.byref(queries.c()), _ptr(q), _ptr(sel),

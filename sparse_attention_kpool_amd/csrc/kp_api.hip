@@ -90,7 +90,7 @@ using namespace kp;
 
 extern "C" {
 
-int32_t kp_abi_version(void) { return 4; }
+int32_t kp_abi_version(void) { return 5; }
 
 const char* kp_last_error(void) { return g_err; }
 

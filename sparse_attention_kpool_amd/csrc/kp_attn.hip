@@ -47,7 +47,7 @@ namespace kp {
 constexpr int AT_NT = 32;         // token slots per block
 constexpr int AT_THREADS = 512;   // 4 S waves + 4 O waves
 constexpr int AT_DEPTH = 4;       // blocks in flight from HBM (register-staged)
-constexpr int AT_MAXSLOT = 8192;  // token slots of one split held in the LDS slot table
+constexpr int AT_MAXSLOT = 8192 + 128;  // token slots of one split held in the LDS slot table (k pools + 1)
 constexpr float LN2 = 0.69314718055994530942f;
 // log2 headroom before the running max is raised: weights up to 2^64 stay far inside the fp32 / bf16 exponent
 // range, so the accumulators are rescaled only when a later block's max beats the running one by 2^64.
@@ -94,6 +94,27 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(uint32_t o1, uint32_t o2) {
 // 1 KiB of zeros: the source row of a slot with no token (past the split or past the query), so the O product
 // multiplies its zero weight by zeros, never by whatever a cache row holds
 __device__ __align__(16) uint32_t attn_zero_row[256];
+
+// Pools a query attends from its selection row: the row's first n_row entries (n_row = min(n_sel, k), so a count
+// beyond the row is never trusted) and, for a query that reads another query's row (an MTP draft sharing its
+// target's selection), its own trailing pool tau = pos / P when that pool is incomplete ((pos + 1) mod P != 0) and
+// the row lacks it.  The shared item is the target's top-k pick; the incomplete tail is not a pick but is always
+// visible, so a draft always sees its own pending tokens -- itself included.  Returns the entry count; entry
+// n_row, when present, is `extra`.  With `shared` set every thread of the block must call it (one barrier).
+__device__ __forceinline__ int attn_row_pools(const int32_t* __restrict__ row, int n_row, bool shared, int pos,
+                                              int log2P, int& extra) {
+  extra = -1;
+  if (!shared) return n_row;
+  const int tau = pos >> log2P;
+  int has = 0;
+  for (int j = threadIdx.x; j < n_row; j += blockDim.x) has |= row[j] == tau ? 1 : 0;
+  has = __syncthreads_or(has);
+  if (has == 0 && ((pos + 1) & ((1 << log2P) - 1)) != 0) {
+    extra = tau;
+    return n_row + 1;
+  }
+  return n_row;
+}
 
 // A-operand fragment of C^T (channels c0 .. c0+15 x tokens 8g .. 8g+7 of k-step s) from the row-major block.
 template <class T, int RS>
@@ -191,7 +212,9 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
   const int P = 1 << log2P;
   // Split sp takes the selected pools sp, sp + n_split, sp + 2 n_split, ...: interleaved rather than
   // contiguous, so the blocks of one query read spread-out parts of its (ascending) selection at a time.
-  const int ns_pools = n_sel[srow];
+  const int n_row = min(n_sel[srow], k);
+  int extra;
+  const int ns_pools = attn_row_pools(sel + int64_t(srow) * k, n_row, sel_row != nullptr, pos, log2P, extra);
   const int my_pools = ns_pools > sp ? (ns_pools - sp + n_split - 1) / n_split : 0;
   const int s_begin = 0;
   const int s_end = my_pools * P;
@@ -218,7 +241,8 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
     const int32_t* qsel = sel + int64_t(srow) * k + sp;
     const int pt_mask = (1 << log2_pt) - 1;
     for (int j = tid; j < (nsl >> log2P); j += AT_THREADS) {
-      const int p = qsel[int64_t(j) * n_split];
+      const int gj = sp + j * n_split;  // entry of the row
+      const int p = gj < n_row ? qsel[int64_t(j) * n_split] : extra;
       int nt = 0, row = 0;
       if (p >= 0) {
         const int first = p << log2P;
@@ -441,7 +465,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
 // C^T and P fragments before theirs.
 // ---------------------------------------------------------------------------------------------------------------
 constexpr int AD_NBUF = 4;        // LDS block buffers: S reads block j, O reads j - 1, j + 1 and j + 2 land
-constexpr int AD_MAXPOOL = 2048;  // pools of one split held in the LDS pool table
+constexpr int AD_MAXPOOL = 2048 + 16;  // pools of one split held in the LDS pool table (k pools + 1)
 constexpr int AD_DIST = 12;       // S waves: C-fragment reads in flight ahead of the MFMAs
 
 // FP8: the latent cache holds OCP E4M3 codes (1 byte per element; value = code value * its scale).  Then every wave
@@ -495,7 +519,9 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
   const int32_t* qsel = sel + int64_t(srow) * k + sp;
   const int kq = (k - sp + n_split - 1) / n_split;  // entries of the row this split strides over
   const int p_first = tid < kq ? qsel[int64_t(tid) * n_split] : -1;
-  const int ns_pools = n_sel[srow];
+  const int n_row = min(n_sel[srow], k);
+  int extra;  // a shared row's added tail pool (entry n_row), or -1
+  const int ns_pools = attn_row_pools(sel + int64_t(srow) * k, n_row, sel_row != nullptr, pos, log2P, extra);
   const int my_pools = ns_pools > sp ? (ns_pools - sp + n_split - 1) / n_split : 0;
   const int nsl = my_pools * P;  // slots of this split
 
@@ -537,7 +563,8 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
     for (int j0 = 0; j0 < my_pools; j0 += AT_THREADS) {
       const int j = j0 + tid;
       const bool valid = j < my_pools;
-      const int p = j0 == 0 ? p_first : (valid ? qsel[int64_t(j) * n_split] : -1);
+      const int gj = sp + j * n_split;  // entry of the row
+      const int p = gj >= n_row ? (valid ? extra : -1) : j0 == 0 ? p_first : qsel[int64_t(j) * n_split];
       int nt = 0, row = 0;
       if (valid && p >= 0) {
         const int first = p << log2P;
@@ -657,6 +684,35 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
     tb1 = b + r1 * S::RS * 2 + 32 * (x1 >> 1) + 16 * ((a >> 1) ^ (x1 & 1));
     tb2 = b + r2 * S::RS * 2 + 32 * (x2 >> 1) + 16 * ((a >> 1) ^ (x2 & 1));
   }
+  // O waves read a block's C^T fragments in the iteration that publishes it (beside S on the same block) and
+  // multiply them one iteration later, so a block's buffer is free one iteration earlier than if O read it itself
+  auto o_read = [&](int j, F(&av)[S::MT]) __attribute__((always_inline)) {
+    const uint32_t blk = lds_off(crm[j % AD_NBUF]);
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt) av[mt] = lds_tr_pair((blk + tb1) ^ (32 * mt), (blk + tb2) ^ (32 * mt));
+  };
+  auto o_mma = [&](int j, const F(&av)[S::MT]) __attribute__((always_inline)) {
+    const T* pb = ps[j & 1];
+    // rescale only the head tiles whose running max moved
+    const uint32_t rf = resc_s[j & 1];
+    if (rf) {
+#pragma unroll
+      for (int nt = 0; nt < HT; ++nt) {
+        if ((rf >> (8 * nt)) & 0xffu) {
+          const float a = alpha_s[j & 1][16 * nt + l16];
+#pragma unroll
+          for (int mt = 0; mt < S::MT; ++mt) bank[mt * HT + nt] *= a;
+        }
+      }
+    }
+    F bq[HT];
+#pragma unroll
+    for (int nt = 0; nt < HT; ++nt) bq[nt] = E::frag_load(pb + (16 * nt + l16) * S::PS + 8 * g);
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < HT; ++nt) bank[mt * HT + nt] = mfma16(av[mt], bq[nt], bank[mt * HT + nt]);
+  };
   auto o_phase = [&](int j) __attribute__((always_inline)) {
     const uint32_t blk = lds_off(crm[j % AD_NBUF]);
     const T* pb = ps[j & 1];
@@ -685,23 +741,43 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
       for (int nt = 0; nt < HT; ++nt) bank[mt * HT + nt] = mfma16(av[mt], bq[nt], bank[mt * HT + nt]);
   };
 
-  // Iteration j: wait for this wave's loads of block j (those of block j + 1 stay in flight), publish it with the
-  // barrier -- after which every wave is past iteration j - 1, so buffer (j + 2) % 4, last read by O(j - 2),
-  // is free -- start block j + 2, then S(j) on S waves and O(j - 1) on O waves.  Loads are unconditional (a
-  // block past the end reads the zero row), so every iteration issues the same count and the wait is exact.
+  // Iteration j: wait for this wave's loads of block j (those of blocks j + 1 and j + 2 stay in flight), publish
+  // it with the barrier -- after which every wave is past iteration j - 1, so buffer (j + 3) % 4, last read in
+  // iteration j - 1 (by S(j - 1) and by the O waves' fragment reads), is free -- start block j + 3, then S(j) on S
+  // waves; O waves read block j's C^T fragments and multiply block j - 1's (read in iteration j - 1).  Three blocks
+  // stay in flight from HBM per compute unit.  Loads are unconditional (a block past the end reads the zero row),
+  // so every iteration issues the same count and the wait is exact.  (The barrier's release fence waits for each
+  // wave's LDS reads, so no read of a buffer is still pending when its next block is started.)
   if constexpr (!FP8) {
     load_block(0, block_rows(0));
     load_block(1, block_rows(1));
-    int rows_next = block_rows(2);
-    for (int j = 0; j <= nblk; ++j) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::CHT));
+    load_block(2, block_rows(2));
+    int rows_next = block_rows(3);
+    auto publish = [&](int j) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::CHT));
       __syncthreads();
-      load_block(j + 2, rows_next);
-      rows_next = block_rows(j + 3);
-      if (o_wave) {
-        if (j >= 1) o_phase(j - 1);
-      } else if (s_active && j < nblk) {
-        s_phase(j);
+      load_block(j + 3, rows_next);
+      rows_next = block_rows(j + 4);
+    };
+    // One loop per role (the role is wave-uniform and both loops pass the same barriers), so the O waves' two
+    // fragment sets and the S waves' read-ahead never hold registers at the same time.
+    if (o_wave) {
+      F avA[S::MT], avB[S::MT];
+      // unrolled by two, so each fragment set keeps its registers
+      for (int j = 0;;) {
+        publish(j);
+        if (j < nblk) o_read(j, avA);
+        if (j >= 1) o_mma(j - 1, avB);
+        if (++j > nblk) break;
+        publish(j);
+        if (j < nblk) o_read(j, avB);
+        o_mma(j - 1, avA);
+        if (++j > nblk) break;
+      }
+    } else {
+      for (int j = 0; j <= nblk; ++j) {
+        publish(j);
+        if (s_active && j < nblk) s_phase(j);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // no load may land in LDS after the block ends
@@ -905,12 +981,13 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __res
 
 int attn_splits(int P, int k, int n_q) {
   // about one block per CU (256), at most 32 splits, at least one pool per split, and few enough pools per
-  // split (ceil(k / splits) <= AT_MAXSLOT / P, and <= AD_MAXPOOL) for the LDS slot and pool tables
+  // split (ceil((k + 1) / splits) <= AT_MAXSLOT / P, and <= AD_MAXPOOL) for the LDS slot and pool tables -- a
+  // row shared by an MTP draft may carry the draft's own tail pool beyond its k entries
   int64_t want = (256 + int64_t(n_q) - 1) / (n_q > 0 ? n_q : 1);
   if (want > k) want = k;
   if (want > 32) want = 32;
   const int64_t per_split = AT_MAXSLOT / P < AD_MAXPOOL ? AT_MAXSLOT / P : AD_MAXPOOL;
-  const int64_t min_splits = (int64_t(k) + per_split - 1) / per_split;
+  const int64_t min_splits = (int64_t(k) + 1 + per_split - 1) / per_split;
   if (want < min_splits) want = min_splits;
   return want < 1 ? 1 : int(want);
 }

@@ -13,6 +13,39 @@ import sparse_attention_kpool_amd as K
 from sparse_attention_kpool_amd.layer import CompressInput, KPoolDSALayer
 
 
+# Guard bands: every output buffer of a parity run sits inside a larger allocation filled with a sentinel; after the
+# run, the words before and after it must be untouched (a kernel writing out of bounds fails the test).
+GUARD_ELEMS = 256
+SENTINEL = {torch.float32: 0x7FC0DEAD, torch.int32: 0x5A5A5A5A, torch.bfloat16: 0x7FC1}
+
+
+class Guarded:
+    """A tensor of `shape` placed GUARD_ELEMS elements into a sentinel-filled buffer of GUARD_ELEMS extra elements on
+    each side."""
+
+    def __init__(self, shape, dtype, device):
+        n = 1
+        for e in shape:
+            n *= int(e)
+        self.n, self.dtype = n, dtype
+        raw = torch.empty(n + 2 * GUARD_ELEMS, dtype=dtype, device=device)
+        self._bits(raw).fill_(SENTINEL[dtype])
+        self.raw = raw
+        self.t = raw[GUARD_ELEMS:GUARD_ELEMS + n].view(*shape)
+
+    @staticmethod
+    def _bits(t):
+        return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+    def intact(self) -> bool:
+        b = self._bits(self.raw)
+        pre, post = b[:GUARD_ELEMS], b[GUARD_ELEMS + self.n:]
+        ref = SENTINEL[self.dtype]
+        if self.dtype == torch.bfloat16:
+            ref = ref - (1 << 16) if ref >= (1 << 15) else ref
+        return bool((pre == ref).all().item() and (post == ref).all().item())
+
+
 def dims_of(wl: ks.Workload) -> K.Dims:
     return K.Dims(pool=wl.P, idx_dim=wl.D, idx_heads=wl.Hi, topk=wl.k, heads=wl.H, latent_dim=wl.L, v_dim=wl.V,
                   page_tokens=wl.page_tokens, dtype=wl.dtype, scale=wl.scale)
@@ -39,14 +72,36 @@ class DeviceRun:
             keys=d.c_keys, gates=d.c_gates, ape=d.ape, pool_seq=d.c_seq, pool_id=d.c_pool)
         self.layer = KPoolDSALayer(self.dims, self.dev, max_q=wl.n_q, max_pos=max(wl.max_pos(), 0))
         tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
-        self.out = torch.empty((wl.n_q, wl.H, wl.V), dtype=tdt, device=self.dev)
-        self.lse = torch.empty((wl.n_q, wl.H), dtype=torch.float32, device=self.dev)
+        # every output the step writes sits between guard bands; the layer's own intermediates are swapped for
+        # guarded ones of the same shape, and the score rows start out as the sentinel, so columns a query cannot
+        # see (p >= n_c) are checked to stay unwritten
+        L = self.layer
+        self.guards = {
+            "scores": Guarded(tuple(L.scores.shape), torch.float32, self.dev),
+            "sel": Guarded(tuple(L.sel.shape), torch.int32, self.dev),
+            "n_sel": Guarded(tuple(L.n_sel.shape), torch.int32, self.dev),
+            "out": Guarded((wl.n_q, wl.H, wl.V), tdt, self.dev),
+            "lse": Guarded((wl.n_q, wl.H), torch.float32, self.dev),
+        }
+        L.scores, L.sel, L.n_sel = self.guards["scores"].t, self.guards["sel"].t, self.guards["n_sel"].t
+        self.out, self.lse = self.guards["out"].t, self.guards["lse"].t
 
     def run(self):
         self.layer.step(self.cache, self.queries, self.q_idx, self.w, self.q, self.out, lse=self.lse,
                         compress=self.compress)
         torch.cuda.synchronize()
         return self
+
+    def check_guards(self):
+        """Every guard band intact, and no score written at or past a query's visible complete pools."""
+        for name, g in self.guards.items():
+            assert g.intact(), f"{name}: a kernel wrote outside the buffer"
+        wl = self.wl
+        n_c = torch.from_numpy(((wl.q_pos.astype(np.int64) + 1) // wl.P)).to(self.dev)
+        sc = self.layer.scores[:wl.n_q].view(torch.int32)
+        col = torch.arange(sc.shape[1], device=self.dev)[None, :]
+        tail = col >= n_c[:, None]
+        assert bool((sc[tail] == SENTINEL[torch.float32]).all().item()), "a score was written past n_c"
 
     # ---- host copies of what the device produced -----------------------------------------------------
     def pooled_rows(self, s: int, pools) -> np.ndarray:

@@ -267,6 +267,46 @@ def test_selection_invariants(seed):
     assert O.select_pools(s, i, P, n_c + 1).tolist() == list(range(n_c + (1 if r else 0)))
 
 
+def test_shared_selection_hand_cases():
+    """MTP draft reusing a target's selection (hand-worked, P = 4): the draft sees every token <= its position of
+    the target's pools, plus its own incomplete trailing pool, which is never a top-k pick but always visible."""
+    P = 4
+    # target at 22 selected pools 0 and 5 (5 = its incomplete tail, tokens 20..22)
+    # draft at 23 completes pool 5: tokens 0..3 and 20..23, nothing added
+    assert O.shared_attended_tokens([0, 5], 23, P).tolist() == [0, 1, 2, 3, 20, 21, 22, 23]
+    # draft at 24 starts pool 6, which the target could not select: tokens of 0 and 5, then token 24 itself
+    assert O.shared_attended_tokens([0, 5], 24, P).tolist() == [0, 1, 2, 3, 20, 21, 22, 23, 24]
+    # draft at 26 (pool 6 holds 24..26): all three pending tokens
+    assert O.shared_attended_tokens([2, 5], 26, P).tolist() == [8, 9, 10, 11, 20, 21, 22, 23, 24, 25, 26]
+    # a row that already holds the draft's pool adds nothing; its pool is cut at the draft
+    assert O.shared_attended_tokens([1, 6], 25, P).tolist() == [4, 5, 6, 7, 24, 25]
+    # an empty row: only the pending tokens
+    assert O.shared_attended_tokens([], 9, P).tolist() == [8, 9]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_shared_selection_invariants(seed):
+    """A query reading its own selection attends exactly what attended_tokens gives; a draft reading an earlier
+    target's selection always attends itself, attends no token after itself, and every target token it sees was
+    selected by the target or is one of its own pending tokens."""
+    rng = np.random.default_rng(300 + seed)
+    P = 4
+    i_t = int(rng.integers(0, 300))
+    n_c, r, tau = O.pool_geometry(i_t, P)
+    s = rng.standard_normal(n_c)
+    for k in (1, 2, 5, 50):
+        sel = O.select_pools(s, i_t, P, k)
+        assert O.shared_attended_tokens(sel, i_t, P).tolist() == O.attended_tokens(sel, i_t, P).tolist()
+        for d in (1, 2, 3):
+            i = i_t + d
+            toks = O.shared_attended_tokens(sel, i, P).tolist()
+            assert i in toks                                    # the draft always sees itself
+            assert max(toks) == i and len(set(toks)) == len(toks)
+            own_pool = i // P
+            for t in toks:
+                assert t // P in sel.tolist() or t // P == own_pool
+
+
 # ----------------------------------------------------------------------------------------------------------
 # attention
 # ----------------------------------------------------------------------------------------------------------
