@@ -202,6 +202,24 @@ kp_status sparse_mla_attn_shared(const kp_dims* dims, const kp_cache* cache, con
                                  void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sparse_mla_attn_noalloc -- sparse_mla_attn with no workspace argument and no allocation.
+ *   For callers that cannot allocate device memory or pass a workspace: code under HIP graph capture, tight
+ *   serving loops, harnesses that forbid allocation.  Same formula, kernels, split count and results as
+ *   sparse_mla_attn (bit for bit); the split-KV partials go to a static device array of KP_NOALLOC_SCRATCH_BYTES
+ *   that the library holds on each GPU it runs on until the process ends (its address is looked up on the first
+ *   call on each device).  The call allocates nothing.
+ *   Every call on a GPU shares that GPU's array and it keeps the last call's contents (nothing in it needs to start
+ *   at zero): calls that overlap on one GPU (different streams, or threads) race and must be ordered by the caller.
+ *   Limit: sparse_mla_workspace_size(dims, queries) <= KP_NOALLOC_SCRATCH_BYTES (every query count at the model's
+ *   dims, H = 64, V = 512, topk = 2048 in bf16, needs at most 33.7 MB), else KP_ERR_WORKSPACE and nothing runs.
+ *   Errors: as sparse_mla_attn; KP_ERR_LAUNCH also when the array's address cannot be looked up.
+ */
+#define KP_NOALLOC_SCRATCH_BYTES (36u << 20)
+kp_status sparse_mla_attn_noalloc(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries,
+                                  const void* q, const int32_t* sel, const int32_t* n_sel, void* out, float* lse,
+                                  void* stream);
+
+/*
  * sparse_mla_attn_fp8 -- sparse_mla_attn over an fp8 latent cache.
  *   [MAX glm5_next API page, declared_state_dtype(): the KV cache format may put the MLA latent in fp8;
  *   DEFAULT_ENCODING: float8_e4m3fn]; [metrale glm5_next_load/loader.rs page: each sparse-attention layer carries

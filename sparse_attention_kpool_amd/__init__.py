@@ -25,6 +25,7 @@ ABI_VERSION = 5
 
 EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk_select",
             "sparse_mla_workspace_size", "sparse_mla_attn", "sparse_mla_attn_shared", "sparse_mla_attn_fp8",
+            "sparse_mla_attn_noalloc",
             "kp_linear", "kp_linear_workspace_size", "kp_linear_group", "kp_linear_group_workspace_size",
             "kp_last_error", "kp_abi_version")
 
@@ -88,6 +89,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_mla_attn.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sparse_mla_attn_fp8.argtypes = [D, C, Q, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.sparse_mla_attn_shared.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sparse_mla_attn_noalloc.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp]
     lib.kp_linear.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, ctypes.c_float,
                               vp, sz, vp]
     lib.kp_linear_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -97,7 +99,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kp_linear_group_workspace_size.argtypes = [i32, LP]
     lib.kp_linear_group_workspace_size.restype = sz
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_shared",
-              "sparse_mla_attn_fp8", "kp_linear", "kp_linear_group"):
+              "sparse_mla_attn_fp8", "sparse_mla_attn_noalloc", "kp_linear", "kp_linear_group"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kp_last_error.restype = ctypes.c_char_p
     lib.kp_abi_version.restype = i32
@@ -323,6 +325,20 @@ def sparse_mla_attn_shared(dims: Dims, cache: Cache, queries: Queries, q, sel, n
                                                                    ctypes.byref(queries.c()), _ptr(q), _ptr(sel),
                                                                    _ptr(n_sel), _ptr(sel_row), _ptr(out), _ptr(lse),
                                                                    _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 36 << 20    # KP_NOALLOC_SCRATCH_BYTES of include/kpool.h
+
+
+def sparse_mla_attn_noalloc(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, out, lse=None,
+                            stream=None) -> None:
+    """As sparse_mla_attn with no workspace: the split-KV partials use the library's static per-device scratch of
+    NOALLOC_SCRATCH_BYTES (calls that overlap on one GPU race; see include/kpool.h)."""
+    _check_attn("sparse_mla_attn_noalloc", dims, cache, queries, q, sel, n_sel, out, lse, None)
+    _check("sparse_mla_attn_noalloc", load().sparse_mla_attn_noalloc(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+                                                                     ctypes.byref(queries.c()), _ptr(q), _ptr(sel),
+                                                                     _ptr(n_sel), _ptr(out), _ptr(lse),
+                                                                     _stream(stream)))
 
 
 def sparse_mla_attn_fp8(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, kv_scale: float, out, lse=None,

@@ -287,6 +287,29 @@ kp_status sparse_mla_attn_shared(const kp_dims* dims, const kp_cache* cache, con
                    workspace, ws_bytes, stream);
 }
 
+kp_status sparse_mla_attn_noalloc(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries,
+                                  const void* q, const int32_t* sel, const int32_t* n_sel, void* out, float* lse,
+                                  void* stream) {
+  const char* fn = "sparse_mla_attn_noalloc";
+  kp_status st = check_dims(dims, fn);
+  if (st != KP_OK) return st;
+  st = check_queries(queries, fn);
+  if (st != KP_OK) return st;
+  if (queries->n_q == 0) return KP_OK;
+  const size_t need =
+      attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)));
+  KP_REQUIRE(need <= size_t(KP_NOALLOC_SCRATCH_BYTES), KP_ERR_WORKSPACE,
+             "%s: this call needs %zu bytes of split-KV scratch, more than the %zu bytes held per device "
+             "(use sparse_mla_attn with a workspace)",
+             fn, need, size_t(KP_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (need > 0) {
+    st = attn_noalloc_scratch(&ws);
+    if (st != KP_OK) return st;
+  }
+  return attn_call(fn, false, 1.f, dims, cache, queries, q, sel, n_sel, nullptr, out, lse, ws, need, stream);
+}
+
 kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
                               const int32_t* sel, const int32_t* n_sel, float kv_scale, void* out, float* lse,
                               void* workspace, size_t ws_bytes, void* stream) {

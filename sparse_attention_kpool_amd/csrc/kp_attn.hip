@@ -37,6 +37,7 @@
 //
 // Bound: HBM (the gather of 1 KiB of bf16 value columns per token feeds 2 x 64 heads x 512 MACs: 128 flop/B,
 // between the VALU and MFMA ridges, hence MFMA for both products).
+#include <mutex>
 #include <type_traits>
 
 #include "kp_device.hpp"
@@ -997,6 +998,35 @@ size_t attn_workspace(int P, int k, int H, int V, int n_q, int esize) {
   if (ns <= 1) return 0;
   // partial O in the cache dtype, then (m, l) in fp32 (n_q * ns * H * V * esize is a multiple of 8: V is even)
   return size_t(n_q) * ns * H * (size_t(V) * esize + 2 * sizeof(float));
+}
+
+// Split-KV partials of sparse_mla_attn_noalloc: one array per device, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is a stand-in, not a device address); it uses the address
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[KP_NOALLOC_SCRATCH_BYTES];
+
+kp_status attn_noalloc_scratch(void** ptr) {
+  constexpr int MAXDEV = 64;
+  static void* addr[MAXDEV] = {nullptr};
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= MAXDEV) {
+    set_error("sparse_mla_attn_noalloc: no usable current device (%s)", hipGetErrorString(e));
+    return KP_ERR_LAUNCH;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error("sparse_mla_attn_noalloc: scratch address lookup failed on device %d: %s", dev, hipGetErrorString(e));
+      return KP_ERR_LAUNCH;
+    }
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return KP_OK;
 }
 
 template <class T, int V, int HT>

@@ -82,6 +82,9 @@ struct AttnLaunch {
 int attn_splits(int P, int k, int n_q);
 size_t attn_workspace(int P, int k, int H, int V, int n_q, int esize);
 kp_status launch_attn(const AttnLaunch& a, hipStream_t s);
+// Device address of the current device's static split-KV scratch (KP_NOALLOC_SCRATCH_BYTES), looked up on the
+// first call per device.
+kp_status attn_noalloc_scratch(void** ptr);
 
 struct LinearLaunch {
   int batch, M, N, K, c_dtype;

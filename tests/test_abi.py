@@ -21,7 +21,7 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_fp8",
-              "sparse_mla_attn_shared", "kp_linear", "kp_linear_workspace_size", "kp_linear_group",
+              "sparse_mla_attn_shared", "sparse_mla_attn_noalloc", "kp_linear", "kp_linear_workspace_size", "kp_linear_group",
               "kp_linear_group_workspace_size",
               "dsa_topk_workspace_size", "sparse_mla_workspace_size", "kp_last_error", "kp_abi_version"):
         assert f in names
@@ -113,6 +113,28 @@ def test_topk_and_attn_validation():
     assert st == K.KP_ERR_UNSUPPORTED
     st = lib.sparse_mla_attn(ctypes.byref(_dims(latent_dim=577)), ctypes.byref(_cache()), ctypes.byref(q), FAKE,
                              FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert st == K.KP_ERR_INVALID_ARG
+
+
+def test_noalloc_limits():
+    """sparse_mla_attn_noalloc: every query count at the model's dims fits its static scratch; a call that needs more
+    (a huge top-k forces many splits) is rejected with KP_ERR_WORKSPACE before anything runs, and argument
+    errors come back as they do from sparse_mla_attn."""
+    lib = K.load()
+    d = _dims()
+    worst = max(lib.sparse_mla_workspace_size(ctypes.byref(d), ctypes.byref(_queries(n_q=n))) for n in range(1, 600))
+    assert 0 < worst <= K.NOALLOC_SCRATCH_BYTES and worst == 510 * 64 * (512 * 2 + 8)
+    st = lib.sparse_mla_attn_noalloc(ctypes.byref(_dims(topk=65536)), ctypes.byref(_cache()),
+                                     ctypes.byref(_queries(n_q=64)), FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == K.KP_ERR_WORKSPACE and "scratch" in K.last_error()
+    st = lib.sparse_mla_attn_noalloc(ctypes.byref(_dims(pool=3)), ctypes.byref(_cache()), ctypes.byref(_queries()),
+                                     FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == K.KP_ERR_INVALID_ARG
+    st = lib.sparse_mla_attn_noalloc(ctypes.byref(_dims(v_dim=128)), ctypes.byref(_cache()),
+                                     ctypes.byref(_queries(n_q=4096)), FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == K.KP_ERR_UNSUPPORTED
+    st = lib.sparse_mla_attn_noalloc(ctypes.byref(d), ctypes.byref(_cache()), ctypes.byref(_queries(n_q=4096)),
+                                     FAKE, None, FAKE, FAKE, None, None)
     assert st == K.KP_ERR_INVALID_ARG
 
 
