@@ -134,9 +134,13 @@ __device__ __forceinline__ F lds_load(uint32_t off) {
 
 // One wave-wide 16-byte direct load from global memory into LDS: lane l's 16 bytes at `src` land at LDS byte
 // offset lds + 16 l.  Written as assembly so the compiler adds no waits of its own: callers wait with explicit
-// vector-memory counts.  The instruction writes no VGPR; M0 carries the LDS offset (one wait state after it is
-// written).  (M0 is a reserved register: the compiler warns that clobbering it may be unsafe, but it keeps no
-// value in M0 across these statements -- no kernel here makes other use of it.)
+// vector-memory counts.  (The compiler's own builtin for this load makes it wait for every outstanding load --
+// vmcnt(0) -- before the next barrier or LDS read, which would serialise the pipelines built on it.)  The
+// instruction writes no VGPR; M0 carries the LDS offset (one wait state after it is written).
+// M0 is a reserved register and the compiler does not preserve one named in a clobber list, so this is safe only
+// while compiled code keeps no value of its own in M0 across these statements.  None of these kernels leads it to
+// use M0 at all (no indirect register indexing, messages, GWS or append / consume LDS operations): the compiled
+// code's only M0 writes are these statements', which tests/test_m0_usage.py checks on the generated assembly.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
