@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the KPool-DSA layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--legs decode,128k,long1m,prefill]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--legs decode,ceiling,32k,...]
 
 A step is one pass of the whole layer -- kpool_compress (pools completing this step) -> dsa_indexer_score ->
 dsa_topk_select -> sparse_mla_attn -- over one batch, enqueued on one stream through the C ABI.
@@ -11,12 +11,22 @@ Legs (inputs are seeded synthetic data already resident in HBM when timing start
            full layer dims (index 32 x 128, pool 4, top-k 2048, 64 MLA heads on a 576 latent), bf16.
            `value` = decode tokens/s = 64 / step time.  Two copies of the caches alternate between steps so the
            256 MB Infinity Cache cannot serve one step from the previous one.
+  ceiling  (with decode / long1m) the read-only gather of the step's own rows -- the attended tokens' 1 KiB value
+           rows and the scanned 4 KiB pooled-key pages -- through kp_read_rows: what HBM delivers for these access
+           patterns with nothing else running, the practical ceiling the stages are compared with.
+  32k      one sequence at context 32,768 (latency-bound: its 10.6 MB is below what fills the machine),
+           rotating 40 cache copies; also timed as a HIP graph replay.
   128k     one sequence at context 131,072 (the exact 128K point), rotating 40 cache copies.
+  long1m   8 sequences at context 1,048,576.
+  fp8      the 64-sequence decode over an fp8 (E4M3) latent cache.
+  proj     the dense projections beside the path, at 64 and 4096 tokens.
   prefill  4096 new queries on 65,536 tokens: the indexer's TFLOP/s against the bf16 MFMA peak, and the
            whole prefill step.
   copy     a plain 1 GiB device-to-device copy: the achievable-bandwidth reference, and the kernel of known
            traffic against which the FETCH_SIZE / WRITE_SIZE counters are scaled.
-Rank 0 prints one JSON line.  Algorithmic bytes/flops count what the method must move or compute; the
+Step times: `ms_per_step` is the mean over the whole timed region (the headline `value` is 64 / that); the median
+and min of the per-step times come with it.  The CPU baseline is the oracle on this machine's host cores (see
+`cpu_baseline`).  Rank 0 prints one JSON line.  Algorithmic bytes/flops count what the method must move or compute; the
 derivation is in the docstrings of `decode_bytes` and `prefill_flops`.
 """
 from __future__ import annotations
@@ -105,19 +115,21 @@ class Leg:
         self.layer.step(self.caches[i % len(self.caches)], self.queries, self.d.q_idx, self.d.w, self.d.q,
                         self.out, lse=self.lse, compress=self.compress)
 
-    def time_steps(self, steps: int, warmup: int) -> float:
-        """Mean ms per step over `steps` back-to-back steps (HIP events on the launch stream)."""
+    def time_steps(self, steps: int, warmup: int) -> dict:
+        """ms per step over `steps` back-to-back steps: the mean over the whole timed region, and the median and min
+        of the per-step times (HIP events recorded between the steps on the launch stream)."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
         for i in range(steps):
             self.step(i)
-        e1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return {"mean": ev[0].elapsed_time(ev[steps]) / steps, "median": float(np.median(per)), "min": min(per)}
 
     def time_steps_graph(self, steps: int) -> float:
         """Mean ms per step with `steps` steps captured in one HIP graph and replayed: the GPU time of a step whose
@@ -171,6 +183,54 @@ class Leg:
                 acc[n] += ev[j].elapsed_time(ev[j + 1])
         return {n: acc[n] / steps for n in names}
 
+    def attended_rows(self):
+        """Physical latent rows of every token the last step attended (int32, in each query's selection order)."""
+        torch, wl = self.torch, self.wl
+        P, pt = wl.P, wl.page_tokens
+        bt = self.d.block_table.long()
+        out = []
+        for j in range(wl.n_q):
+            s, pos = int(wl.q_seq[j]), int(wl.q_pos[j])
+            ns = int(self.layer.n_sel[j].item())
+            p = self.layer.sel[j, :ns].long()
+            tok = (p[:, None] * P + torch.arange(P, device="cuda")[None, :]).reshape(-1)
+            tok = tok[tok <= pos]
+            out.append(bt[s, tok // pt] * pt + tok % pt)
+        return torch.cat(out).to(torch.int32).contiguous()
+
+    def scanned_pages(self):
+        """Physical pages of every query's visible complete pools (the pooled-key pages the scorer streams)."""
+        torch, wl = self.torch, self.wl
+        ppp = wl.page_tokens // wl.P
+        out = []
+        for j in range(wl.n_q):
+            s, n_c = int(wl.q_seq[j]), (int(wl.q_pos[j]) + 1) // wl.P
+            out.append(self.d.block_table[s, :(n_c + ppp - 1) // ppp])
+        return torch.cat(out).to(torch.int32).contiguous()
+
+    def time_read_rows(self, which: str, reps: int = 20) -> dict:
+        """The gather-bandwidth reference (kp_read_rows) over this workload's own rows: 'attend' = the attended
+        tokens' 1 KiB value rows of the latent cache, 'score' = the scanned 4 KiB pages of the pooled cache;
+        alternating cache copies, as the steps do."""
+        torch, K = self.torch, self.K
+        if which == "attend":
+            rows, nbytes, bufs = self.attended_rows(), 1024, [c.latent.view(-1, self.wl.L) for c in self.caches]
+        else:
+            rows, nbytes, bufs = self.scanned_pages(), 4096, [c.pooled for c in self.caches]
+        for i in range(3):
+            K.read_rows(bufs[i % len(bufs)], nbytes, rows)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            K.read_rows(bufs[i % len(bufs)], nbytes, rows)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        b = rows.numel() * nbytes
+        return {"rows": int(rows.numel()), "bytes": int(b), "ms": round(ms, 5), "gbs": round(b / (ms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
     def free(self):
         del self.caches, self.layer, self.d
         self.torch.cuda.synchronize()
@@ -212,58 +272,107 @@ def roofline(stage_ms: dict, stage_bytes: dict) -> dict:
 # ----------------------------------------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded sample of the decode step
 # ----------------------------------------------------------------------------------------------------------
-def cpu_baseline(wl, n_sample: int, min_seconds: float = 10.0) -> dict:
-    import kpool_synth as ks
-    import oracle as O
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: numpy's BLAS thread count is not reported
-        threads = os.cpu_count() or 1
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the host's CPU count
+        return os.cpu_count() or 1
+
+
+def _oracle_inputs(wl, j: int, ape):
+    """Host inputs of decode query j (regenerated outside any timed region): pre-filled pooled keys, the key / gate
+    rows of a pool completing this step, the queries, and the latent rows the query attends (found by one untimed
+    selection pass) with a token -> row map, so the timed pass can gather through it."""
+    import kpool_synth as ks
+    import oracle as O
+    s, i = int(wl.q_seq[j]), int(wl.q_pos[j])
+    n_c, r, tau = O.pool_geometry(i, wl.P)
+    first_new = wl.new_from[s] // wl.P
+    pre = np.zeros((n_c, wl.D))
+    pre[:min(first_new, n_c)] = ks.host_pool_keys(wl, s, np.arange(min(first_new, n_c))).astype(np.float64)
+    comp = None
+    if n_c > first_new:                                       # pools completing this step
+        toks = np.arange(first_new * wl.P, n_c * wl.P)
+        comp = (ks.host_token_keys(wl, s, toks).reshape(-1, wl.P, wl.D).astype(np.float64),
+                ks.host_gates(wl, s, toks).reshape(-1, wl.P, wl.D).astype(np.float64), first_new)
+        pre[first_new:] = O.store_round(O.pool_compress(comp[0], comp[1], ape), wl.dtype)
+    qidx = ks.host_qidx(wl, s, i)[0].astype(np.float64)
+    w = ks.host_w(wl, s, i)[0].astype(np.float64)
+    q = ks.host_q(wl, s, i)[0].astype(np.float64)
+    sel0 = O.select_pools(O.indexer_scores(qidx, w, pre, n_c), i, wl.P, wl.k)
+    toks0 = O.attended_tokens(sel0, i, wl.P)
+    rows = ks.host_latent(wl, s, toks0).astype(np.float64)
+    tmap = np.full(i + 1, -1, dtype=np.int64)
+    tmap[toks0] = np.arange(len(toks0))
+    return (i, pre, comp, qidx, w, q, rows, tmap)
+
+
+def _oracle_pass(wl, prepared, ape, stage: dict) -> None:
+    """One pass of the whole layer per prepared query (pool, score, select, attend) in float64 numpy, adding each
+    stage's wall time to `stage`."""
+    import oracle as O
+    for (i, pre, comp, qidx, w, q, rows, tmap) in prepared:
+        n_c = (i + 1) // wl.P
+        t0 = time.perf_counter()
+        pooled = pre
+        if comp is not None:
+            pooled = pre.copy()
+            pooled[comp[2]:n_c] = O.store_round(O.pool_compress(comp[0], comp[1], ape), wl.dtype)
+        t1 = time.perf_counter()
+        s_ = O.indexer_scores(qidx, w, pooled, n_c)
+        t2 = time.perf_counter()
+        sel = O.select_pools(s_, i, wl.P, wl.k)
+        t3 = time.perf_counter()
+        toks = O.attended_tokens(sel, i, wl.P)
+        O.sparse_mla(q, rows[tmap[toks]], wl.scale, wl.V)
+        t4 = time.perf_counter()
+        for k, a, b in (("pool", t0, t1), ("score", t1, t2), ("select", t2, t3), ("attend", t3, t4)):
+            stage[k] = stage.get(k, 0.0) + (b - a)
+
+
+def _time_oracle(wl, queries, min_seconds: float) -> dict:
+    import kpool_synth as ks
     ape = ks.host_ape(wl).astype(np.float64)
-    prepared = []
-    for j in range(n_sample):                                   # host inputs, outside the timed region
-        s, i = int(wl.q_seq[j]), int(wl.q_pos[j])
-        n_c, r, tau = O.pool_geometry(i, wl.P)
-        pre = ks.host_pool_keys(wl, s, np.arange(n_c)).astype(np.float64)
-        comp = None
-        if wl.ctx[s] % wl.P == 0:                               # this step completes pool n_c - 1
-            toks = np.arange((n_c - 1) * wl.P, n_c * wl.P)
-            comp = (ks.host_token_keys(wl, s, toks)[None].astype(np.float64),
-                    ks.host_gates(wl, s, toks)[None].astype(np.float64))
-        qidx = ks.host_qidx(wl, s, i)[0].astype(np.float64)
-        w = ks.host_w(wl, s, i)[0].astype(np.float64)
-        q = ks.host_q(wl, s, i)[0].astype(np.float64)
-        # regenerate only the latent rows this query attends (found by an untimed selection pass); the timed
-        # pass below redoes the whole layer and gathers its rows through the token -> row map
-        sel0 = O.select_pools(O.indexer_scores(qidx, w, pre, n_c), i, wl.P, wl.k)
-        toks0 = O.attended_tokens(sel0, i, wl.P)
-        rows = ks.host_latent(wl, s, toks0).astype(np.float64)
-        tmap = np.full(i + 1, -1, dtype=np.int64)
-        tmap[toks0] = np.arange(len(toks0))
-        prepared.append((i, pre, comp, qidx, w, q, rows, tmap))
-    t0 = time.perf_counter()
-    reps = 0
+    prepared = [_oracle_inputs(wl, j, ape) for j in queries]
+    stage, reps, t0 = {}, 0, time.perf_counter()
     while True:                                                 # repeat the sample to >= min_seconds of work
-        for (i, pre, comp, qidx, w, q, rows, tmap) in prepared:
-            n_c = (i + 1) // wl.P
-            pooled = pre
-            if comp is not None:
-                pooled = pre.copy()
-                pooled[n_c - 1] = O.store_round(O.pool_compress(comp[0], comp[1], ape), wl.dtype)[0]
-            s_ = O.indexer_scores(qidx, w, pooled, n_c)
-            sel = O.select_pools(s_, i, wl.P, wl.k)
-            toks = O.attended_tokens(sel, i, wl.P)
-            O.sparse_mla(q, rows[tmap[toks]], wl.scale, wl.V)
+        _oracle_pass(wl, prepared, ape, stage)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
-    return {"value": round(reps * n_sample / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"{n_sample} of the 64 decode queries (sequences 0..{n_sample - 1}) x {reps} passes, the whole "
-                      f"layer per query (pool, score, select, attend) in float64 numpy; host input regeneration "
-                      f"not timed"}
+    n = reps * len(queries)
+    return {"tokens_per_s": round(n / dt, 3), "queries": n, "seconds": round(dt, 3),
+            "stage_ms_per_query": {k: round(v / n * 1e3, 3) for k, v in stage.items()}}
+
+
+def cpu_baseline(wl, n_sample: int, min_seconds: float = 10.0, extra: bool = True) -> dict:
+    """The oracle as it stands, timed on this machine's host cores: a bounded sample of the decode workload with
+    numpy's BLAS on all its threads (the reported baseline), then the tiny prefill (all 64 queries) and the
+    32K-context decode single-threaded."""
+    threads = _blas_threads()
+    main = _time_oracle(wl, list(range(n_sample)), min_seconds)
+    out = {"value": main["tokens_per_s"], "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "host_cpus": os.cpu_count(), "blas_threads": int(threads), "seconds": main["seconds"],
+           "stage_ms_per_query": main["stage_ms_per_query"],
+           "sample": f"{n_sample} of the 64 decode queries (sequences 0..{n_sample - 1}), repeated to "
+                     f"{main['queries']} queries, the whole layer per query (pool, score, select, attend) in float64 "
+                     f"numpy; host input regeneration not timed"}
+    if extra:
+        import kpool_synth as ks
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:
+            threadpool_limits = None
+        if threadpool_limits is not None:
+            W = ks.workloads()
+            with threadpool_limits(limits=1):
+                out["single_thread"] = {
+                    "tiny": dict(_time_oracle(W["tiny"], list(range(64)), 2.0), unit="queries/s"),
+                    "decode32k": dict(_time_oracle(W["decode32k"], [0], 3.0), unit="tokens/s"),
+                }
+    return out
 
 # the dense projections beside the path (kp_linear) at the layer's shapes: hidden 4096, q_lora 1536, 32 index heads
 # x 128, 64 MLA heads, kv_lora 512, qk_nope = v_head = 256
@@ -367,7 +476,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,128k,long1m,fp8,prefill,proj,copy")
+    ap.add_argument("--legs", default="decode,ceiling,32k,128k,long1m,fp8,prefill,proj,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=16)
     args = ap.parse_args()
@@ -392,53 +501,83 @@ def main():
     if "decode" in legs:
         print("[bench] decode leg: 64 sequences, contexts up to 128K", file=sys.stderr, flush=True)
         leg = Leg(wl, copies=2)
-        ms = leg.time_steps(args.steps, args.warmup)
+        t = leg.time_steps(args.steps, args.warmup)
+        ms = t["mean"]
         st = leg.time_stages(args.steps)
         by = decode_bytes(wl)
         tot = sum(by.values())
         res.update(value=round(wl.n_q / (ms * 1e-3), 1), ms_per_step=round(ms, 5))
+        res["ms_per_step_median"], res["ms_per_step_min"] = round(t["median"], 5), round(t["min"], 5)
         res["hbm_gbs"] = round(tot / (ms * 1e-3) / 1e9, 1)
         res["hbm_frac"] = round(res["hbm_gbs"] / HBM_PEAK_GBS, 4)
         res["stages_ms"] = {k: round(v, 5) for k, v in st.items()}
         res["stage_bytes"] = by
         res["roofline"] = roofline(st, by)
+        if "ceiling" in legs:
+            # what HBM delivers for the step's own access patterns, read-only, nothing else running: the
+            # attended tokens' value rows and the scanned pooled-key pages
+            print("[bench] ceiling leg: read-only gathers of the decode step's own rows", file=sys.stderr, flush=True)
+            ca, cs = leg.time_read_rows("attend"), leg.time_read_rows("score")
+            res["ceiling"] = {"attend_rows": ca, "score_pages": cs,
+                              "attend_stage_vs_ceiling": round(ca["ms"] / st["attend"], 4),
+                              "score_stage_vs_ceiling": round(cs["ms"] / st["score"], 4),
+                              "step_at_ceiling_ms": round(ca["ms"] + cs["ms"], 5),
+                              "step_frac_at_ceiling": round(tot / ((ca["ms"] + cs["ms"]) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                                            4)}
         leg.free()
     res["config"] = {"workload": "batch64-decode-128k: 64 sequences, context U[8192,131072] seed 3 (sum 4,151,643),"
                                  " paged 64-token pages in a seeded random order, full layer dims",
                      "global_batch": wl.n_q, "seq_len": int(max(wl.ctx)), "parallelism": "none (1 GPU)",
                      "index_heads": wl.Hi, "index_dim": wl.D, "pool": wl.P, "topk": wl.k, "mla_heads": wl.H,
                      "latent": wl.L}
-    if "128k" in legs:
-        print("[bench] 128k leg: one sequence at context 131072", file=sys.stderr, flush=True)
-        w1 = W["decode128k"]
-        leg = Leg(w1, copies=40)
-        ms = leg.time_steps(max(args.steps, 50), args.warmup)
+
+    def single(name, key, copies):
+        w1 = W[name]
+        leg = Leg(w1, copies=copies)
+        t = leg.time_steps(max(args.steps, 50), args.warmup)
+        ms = t["mean"]
         st = leg.time_stages(max(args.steps, 50))
         by = decode_bytes(w1)
         msg = leg.time_steps_graph(max(args.steps, 50))
-        res["decode128k"] = {"tokens_per_s": round(1 / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
-                             "hbm_gbs": round(sum(by.values()) / (ms * 1e-3) / 1e9, 1),
-                             "stages_ms": {k: round(v, 5) for k, v in st.items()},
-                             "graph": {"ms_per_step": round(msg, 5), "tokens_per_s": round(1 / (msg * 1e-3), 1),
-                                       "hbm_gbs": round(sum(by.values()) / (msg * 1e-3) / 1e9, 1)}}
+        gbs = sum(by.values()) / (ms * 1e-3) / 1e9
+        res[key] = {"tokens_per_s": round(1 / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+                    "ms_per_step_median": round(t["median"], 5), "ms_per_step_min": round(t["min"], 5),
+                    "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "stages_ms": {k: round(v, 5) for k, v in st.items()}, "bytes": int(sum(by.values())),
+                    "graph": {"ms_per_step": round(msg, 5), "tokens_per_s": round(1 / (msg * 1e-3), 1),
+                              "hbm_gbs": round(sum(by.values()) / (msg * 1e-3) / 1e9, 1)}}
         leg.free()
+    if "32k" in legs:
+        print("[bench] 32k leg: one sequence at context 32768", file=sys.stderr, flush=True)
+        single("decode32k", "decode32k", 40)
+    if "128k" in legs:
+        print("[bench] 128k leg: one sequence at context 131072", file=sys.stderr, flush=True)
+        single("decode128k", "decode128k", 40)
     if "long1m" in legs:
         print("[bench] long1m leg: 8 sequences at context 1048576", file=sys.stderr, flush=True)
         w5 = W["long1m"]
         leg = Leg(w5, copies=2)
-        ms = leg.time_steps(args.steps, args.warmup)
+        t = leg.time_steps(args.steps, args.warmup)
+        ms = t["mean"]
         st = leg.time_stages(args.steps)
         by = decode_bytes(w5)
         gbs = sum(by.values()) / (ms * 1e-3) / 1e9
         res["long1m"] = {"tokens_per_s": round(w5.n_q / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+                         "ms_per_step_median": round(t["median"], 5), "ms_per_step_min": round(t["min"], 5),
                          "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                          "stages_ms": {k: round(v, 5) for k, v in st.items()}, "stage_bytes": by}
+        if "ceiling" in legs:
+            ca, cs = leg.time_read_rows("attend"), leg.time_read_rows("score")
+            res["long1m"]["ceiling"] = {"attend_rows": ca, "score_pages": cs,
+                                        "step_frac_at_ceiling": round(sum(by.values()) / ((ca["ms"] + cs["ms"]) * 1e-3)
+                                                                      / 1e9 / HBM_PEAK_GBS, 4)}
         leg.free()
     if "fp8" in legs:
         print("[bench] fp8 leg: the 64-sequence decode over an fp8 (E4M3) latent cache", file=sys.stderr, flush=True)
         w8 = W["batch64_fp8"]
         leg = Leg(w8, copies=2)
-        ms = leg.time_steps(args.steps, args.warmup)
+        t = leg.time_steps(args.steps, args.warmup)
+        ms = t["mean"]
         st = leg.time_stages(args.steps)
         by = decode_bytes(w8)
         gbs = sum(by.values()) / (ms * 1e-3) / 1e9
@@ -451,7 +590,7 @@ def main():
         print("[bench] prefill leg: 4096 queries on 65536 tokens", file=sys.stderr, flush=True)
         wp = W["prefill64k"]
         leg = Leg(wp, copies=1)
-        ms = leg.time_steps(max(3, args.steps // 4), 2)
+        ms = leg.time_steps(max(3, args.steps // 4), 2)["mean"]
         st = leg.time_stages(max(3, args.steps // 4))
         fl = prefill_flops(wp)
         tf = fl / (st["score"] * 1e-3) / 1e12

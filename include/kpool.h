@@ -298,6 +298,21 @@ size_t kp_linear_group_workspace_size(int32_t n, const kp_linear_problem* proble
 kp_status kp_linear_group(int32_t n, const kp_linear_problem* problems, void* workspace, size_t ws_bytes,
                           void* stream);
 
+/*
+ * kp_read_rows -- measurement reference: reads rows and discards them.
+ *   Reads rows[i] (0 <= i < n_rows) of `base`, each row_bytes long at byte offset rows[i] * row_stride, the way the
+ *   attention stage gathers its value rows (whole 1 KiB units straight into LDS, in list order, in contiguous runs
+ *   per wave), and keeps nothing: no compute, no barrier, no output.  Timed over the attention's own row list (the
+ *   attended tokens' physical latent rows), it gives the read bandwidth HBM delivers for that gather pattern -- the
+ *   practical ceiling the attention kernel is measured against.  Not part of the layer.
+ *   base: device, 16-byte aligned; rows: device int32 [n_rows], each row inside the caller's buffer (not checked).
+ *   row_bytes: 1024 (a value row) or 4096 (a 64-token page of pooled keys); row_stride >= row_bytes, a multiple of
+ *   16; blocks_per_cu 1..8.
+ *   Errors: KP_ERR_INVALID_ARG, KP_ERR_LAUNCH.
+ */
+kp_status kp_read_rows(const void* base, int64_t row_stride, int32_t row_bytes, const int32_t* rows, int64_t n_rows,
+                       int32_t blocks_per_cu, void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  Owned by the library. */
 const char* kp_last_error(void);
 

@@ -25,7 +25,7 @@ ABI_VERSION = 5
 
 EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk_select",
             "sparse_mla_workspace_size", "sparse_mla_attn", "sparse_mla_attn_shared", "sparse_mla_attn_fp8",
-            "sparse_mla_attn_noalloc",
+            "sparse_mla_attn_noalloc", "kp_read_rows",
             "kp_linear", "kp_linear_workspace_size", "kp_linear_group", "kp_linear_group_workspace_size",
             "kp_last_error", "kp_abi_version")
 
@@ -90,6 +90,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_mla_attn_fp8.argtypes = [D, C, Q, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.sparse_mla_attn_shared.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sparse_mla_attn_noalloc.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp]
+    lib.kp_read_rows.argtypes = [vp, i64, i32, vp, i64, i32, vp]
     lib.kp_linear.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, ctypes.c_float,
                               vp, sz, vp]
     lib.kp_linear_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -99,7 +100,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kp_linear_group_workspace_size.argtypes = [i32, LP]
     lib.kp_linear_group_workspace_size.restype = sz
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_shared",
-              "sparse_mla_attn_fp8", "sparse_mla_attn_noalloc", "kp_linear", "kp_linear_group"):
+              "sparse_mla_attn_fp8", "sparse_mla_attn_noalloc", "kp_read_rows", "kp_linear", "kp_linear_group"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kp_last_error.restype = ctypes.c_char_p
     lib.kp_abi_version.restype = i32
@@ -325,6 +326,16 @@ def sparse_mla_attn_shared(dims: Dims, cache: Cache, queries: Queries, q, sel, n
                                                                    ctypes.byref(queries.c()), _ptr(q), _ptr(sel),
                                                                    _ptr(n_sel), _ptr(sel_row), _ptr(out), _ptr(lse),
                                                                    _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def read_rows(base, row_bytes: int, rows, blocks_per_cu: int = 2, stream=None) -> None:
+    """kp_read_rows: read the rows `rows` (int32 device tensor) of `base` (a device tensor whose first dimension
+    indexes rows; row stride = its stride(0) in bytes) and discard them -- the gather-bandwidth reference."""
+    fn = "kp_read_rows"
+    _want(fn, "rows", rows, _i32(), (rows.numel(),))
+    stride = base.stride(0) * base.element_size()
+    _check(fn, load().kp_read_rows(_ptr(base), stride, int(row_bytes), _ptr(rows), int(rows.numel()),
+                                   int(blocks_per_cu), _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 36 << 20    # KP_NOALLOC_SCRATCH_BYTES of include/kpool.h

@@ -408,6 +408,24 @@ static kp_linear_problem one_problem(int32_t batch, int32_t M, int32_t N, int32_
   return q;
 }
 
+kp_status kp_read_rows(const void* base, int64_t row_stride, int32_t row_bytes, const int32_t* rows, int64_t n_rows,
+                       int32_t blocks_per_cu, void* stream) {
+  const char* fn = "kp_read_rows";
+  KP_REQUIRE(n_rows >= 0, KP_ERR_INVALID_ARG, "%s: n_rows < 0", fn);
+  if (n_rows == 0) return KP_OK;
+  KP_REQUIRE(base && rows && aligned(base), KP_ERR_INVALID_ARG, "%s: NULL or misaligned base / rows", fn);
+  KP_REQUIRE(row_bytes == 1024 || row_bytes == 4096, KP_ERR_INVALID_ARG,
+             "%s: row_bytes must be 1024 (a value row) or 4096 (a page of pooled keys), got %d", fn, row_bytes);
+  KP_REQUIRE(row_stride >= row_bytes && row_stride % 16 == 0, KP_ERR_INVALID_ARG,
+             "%s: row_stride must be >= row_bytes and a multiple of 16", fn);
+  KP_REQUIRE(blocks_per_cu >= 1 && blocks_per_cu <= 8, KP_ERR_INVALID_ARG, "%s: blocks_per_cu in 1..8", fn);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus <= 0)
+    cus = 256;
+  return launch_read_rows(base, row_stride, row_bytes, rows, n_rows, cus * blocks_per_cu, (hipStream_t)stream);
+}
+
 size_t kp_linear_workspace_size(int32_t batch, int32_t M, int32_t N, int32_t K) {
   // only the shape matters: stand-in operands that pass validation
   static const char dummy[16] __attribute__((aligned(16))) = {0};

@@ -86,6 +86,9 @@ kp_status launch_attn(const AttnLaunch& a, hipStream_t s);
 // first call per device.
 kp_status attn_noalloc_scratch(void** ptr);
 
+kp_status launch_read_rows(const void* base, int64_t row_stride, int32_t row_bytes, const int32_t* rows,
+                           int64_t n_rows, int blocks, hipStream_t s);
+
 struct LinearLaunch {
   int batch, M, N, K, c_dtype;
   const void* A;

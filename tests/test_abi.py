@@ -21,7 +21,7 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_fp8",
-              "sparse_mla_attn_shared", "sparse_mla_attn_noalloc", "kp_linear", "kp_linear_workspace_size", "kp_linear_group",
+              "sparse_mla_attn_shared", "sparse_mla_attn_noalloc", "kp_read_rows", "kp_linear", "kp_linear_workspace_size", "kp_linear_group",
               "kp_linear_group_workspace_size",
               "dsa_topk_workspace_size", "sparse_mla_workspace_size", "kp_last_error", "kp_abi_version"):
         assert f in names

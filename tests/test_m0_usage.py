@@ -28,7 +28,8 @@ def _asm(src):
     return r.stdout
 
 
-@pytest.mark.parametrize("name", ["kp_attn.hip", "kp_score.hip", "kp_linear.hip", "kp_topk.hip", "kp_compress.hip"])
+@pytest.mark.parametrize("name", sorted(f for f in os.listdir(os.path.join(ROOT, "sparse_attention_kpool_amd", "csrc"))
+                                  if f.endswith(".hip")))
 def test_m0_holds_only_the_direct_load_address(name):
     try:
         from sparse_attention_kpool_amd import build as B
