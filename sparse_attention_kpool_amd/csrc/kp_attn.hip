@@ -742,22 +742,25 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
       for (int nt = 0; nt < HT; ++nt) bank[mt * HT + nt] = mfma16(av[mt], bq[nt], bank[mt * HT + nt]);
   };
 
-  // Iteration j: wait for this wave's loads of block j (those of blocks j + 1 and j + 2 stay in flight), publish
-  // it with the barrier -- after which every wave is past iteration j - 1, so buffer (j + 3) % 4, last read in
+  // Iteration j: wait for this wave's loads of block j (those of blocks j + 1 and j + 2, when they exist, stay in
+  // flight), publish it with the barrier -- after which every wave is past iteration j - 1, so buffer (j + 3) % 4, last read in
   // iteration j - 1 (by S(j - 1) and by the O waves' fragment reads), is free -- start block j + 3, then S(j) on S
   // waves; O waves read block j's C^T fragments and multiply block j - 1's (read in iteration j - 1).  Three blocks
-  // stay in flight from HBM per compute unit.  Loads are unconditional (a block past the end reads the zero row),
-  // so every iteration issues the same count and the wait is exact.  (The barrier's release fence waits for each
+  // stay in flight from HBM per compute unit.  (The barrier's release fence waits for each
   // wave's LDS reads, so no read of a buffer is still pending when its next block is started.)
   if constexpr (!FP8) {
+    // Blocks past the end are never loaded, so the last iterations wait for fewer blocks in flight (the wait
+    // counts stay exact: a wave's loads complete in issue order).
     load_block(0, block_rows(0));
-    load_block(1, block_rows(1));
-    load_block(2, block_rows(2));
+    if (nblk > 1) load_block(1, block_rows(1));
+    if (nblk > 2) load_block(2, block_rows(2));
     int rows_next = block_rows(3);
     auto publish = [&](int j) __attribute__((always_inline)) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::CHT));
+      if (j + 2 < nblk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::CHT));
+      else if (j + 1 < nblk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::CHT));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
-      load_block(j + 3, rows_next);
+      if (j + 3 < nblk) load_block(j + 3, rows_next);
       rows_next = block_rows(j + 4);
     };
     // One loop per role (the role is wave-uniform and both loops pass the same barriers), so the O waves' two

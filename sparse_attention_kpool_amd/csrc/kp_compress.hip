@@ -25,37 +25,8 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ key
   const int c = int(gid - i * D);
   if (i >= n_pools) return;
   const int64_t s = src ? src[i] : i;
-  const T* kr = keys + s * P * D + c;
-  // sum_j a_j k_j written as k_0 + sum_j a_j (k_j - k_0): the same value in exact arithmetic, and exactly k_0
-  // when the pool's keys are equal
-  const float k0 = Elem<T>::to_f32(kr[0]);
-  float den = 0.f, num = 0.f;
-  if (gates && ape) {
-    // softmax over the pool's P tokens of (gate + position term), this channel only
-    const T* gr = gates + s * P * D + c;
-    const T* ar = ape + c;
-    float m = -INFINITY;
-    for (int j = 0; j < P; ++j) m = fmaxf(m, Elem<T>::to_f32(gr[j * D]) + Elem<T>::to_f32(ar[j * D]));
-    for (int j = 0; j < P; ++j) {
-      const float e = __expf(Elem<T>::to_f32(gr[j * D]) + Elem<T>::to_f32(ar[j * D]) - m);
-      den += e;
-      num += e * (Elem<T>::to_f32(kr[j * D]) - k0);
-    }
-  } else {
-    // a NULL gates or ape contributes 0 to the logits (both NULL: every weight is exactly 1, the plain mean)
-    auto z = [&](int j) __attribute__((always_inline)) {
-      const float gz = gates ? Elem<T>::to_f32(gates[s * P * D + j * D + c]) : 0.f;
-      return gz + (ape ? Elem<T>::to_f32(ape[j * D + c]) : 0.f);
-    };
-    float m = -INFINITY;
-    for (int j = 0; j < P; ++j) m = fmaxf(m, z(j));
-    for (int j = 0; j < P; ++j) {
-      const float e = __expf(z(j) - m);
-      den += e;
-      num += e * (Elem<T>::to_f32(kr[j * D]) - k0);
-    }
-  }
-  const float v = k0 + num / den;
+  const float v = pool_channel<T>(keys + s * P * D + c, gates ? gates + s * P * D + c : nullptr, ape ? ape + c : nullptr,
+                                  P, D);
   const int64_t row = paged_row(bt, bt_stride, pool_seq[i], pool_id[i], log2_ppp);
   pooled[row * D + c] = Elem<T>::from_f32(v);
 }

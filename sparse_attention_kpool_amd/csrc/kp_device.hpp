@@ -85,6 +85,39 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// One channel of a pooled index key: z_j = gate_j + ape_j, a = softmax_j(z), pooled = sum_j a_j key_j, computed in
+// fp32 as key_0 + sum_j a_j (key_j - key_0) -- equal in exact arithmetic, and exactly key_0 when the pool's keys are
+// equal.  kr, gr, ar point at channel c of token 0 of the pool's keys, gates and ape (stride D between tokens); gr and
+// ar may be NULL (zero gate logits / zero position term; both NULL: the plain mean).  Every kernel that pools uses
+// this function, so a pooled key has one value wherever it is computed.
+template <class T>
+__device__ __forceinline__ float pool_channel(const T* __restrict__ kr, const T* __restrict__ gr,
+                                              const T* __restrict__ ar, int P, int D) {
+  const float k0 = Elem<T>::to_f32(kr[0]);
+  float den = 0.f, num = 0.f;
+  if (gr && ar) {  // straight-line loops for the learned pooling
+    float m = -INFINITY;
+    for (int j = 0; j < P; ++j) m = fmaxf(m, Elem<T>::to_f32(gr[j * D]) + Elem<T>::to_f32(ar[j * D]));
+    for (int j = 0; j < P; ++j) {
+      const float e = __expf(Elem<T>::to_f32(gr[j * D]) + Elem<T>::to_f32(ar[j * D]) - m);
+      den += e;
+      num += e * (Elem<T>::to_f32(kr[j * D]) - k0);
+    }
+  } else {
+    auto z = [&](int j) __attribute__((always_inline)) {
+      return (gr ? Elem<T>::to_f32(gr[j * D]) : 0.f) + (ar ? Elem<T>::to_f32(ar[j * D]) : 0.f);
+    };
+    float m = -INFINITY;
+    for (int j = 0; j < P; ++j) m = fmaxf(m, z(j));
+    for (int j = 0; j < P; ++j) {
+      const float e = __expf(z(j) - m);
+      den += e;
+      num += e * (Elem<T>::to_f32(kr[j * D]) - k0);
+    }
+  }
+  return k0 + num / den;
+}
+
 // Row index (in units of rows of `rows_per_page` per page) of logical row `r` of sequence row `seq`.
 __device__ __forceinline__ int64_t paged_row(const int32_t* __restrict__ bt, int bt_stride, int seq, int r,
                                              int log2_rows_per_page) {
