@@ -251,8 +251,10 @@ def measured_traffic(stage: str):
         total = 0.0
         for k in STAGE_KERNELS[stage]:
             e = rec["kernels"][k]
-            cur = hashlib.sha256(open(os.path.join(ROOT, e["source"]), "rb").read()).hexdigest()[:16]
-            if cur != e["sha256_16"]:
+            h = hashlib.sha256()
+            for src in e["sources"]:                      # the kernel's source file, then the shared device header
+                h.update(open(os.path.join(ROOT, src), "rb").read())
+            if h.hexdigest()[:16] != e["sha256_16"]:
                 return None
             total += e["read_bytes"] + e["write_bytes"]
         return int(total)
