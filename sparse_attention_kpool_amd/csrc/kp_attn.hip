@@ -14,7 +14,7 @@
 // The 8 waves form a two-stage pipeline over 32-slot blocks, one barrier per block:
 //   load   bf16 rows of 512 value columns (attn_dma_kernel): each wave brings four whole 1 KiB rows per block
 //          straight from global memory into LDS (one wave-wide 16-byte direct load per row, no register
-//          staging), two blocks ahead in a ring of four buffers whose rows are XOR-swizzled so that both
+//          staging), three blocks in flight in a ring of four buffers whose rows are XOR-swizzled so that both
 //          products read them without bank conflicts.  Other shapes (attn_kernel): every thread keeps 16-byte
 //          chunks of the rows in registers four blocks ahead and writes them to a 3-deep ring of padded LDS
 //          buffers.
@@ -29,8 +29,8 @@
 //          8g + s/4 and lane i receives channel i of those 4 tokens.
 // Each SIMD runs one S wave and one O wave, so the two products overlap on the matrix core.  S waves keep Q in
 // the same register bank in which O waves keep their accumulators.  Without register staging (attn_dma_kernel)
-// S waves keep twelve C-fragment reads in flight ahead of their MFMAs and O waves read a block's C^T and P
-// fragments before theirs, so LDS latency stays off the MFMA chains.
+// S waves keep twelve C-fragment reads in flight ahead of their MFMAs and O waves read a block's C^T fragments
+// one iteration before they multiply them, so LDS latency stays off the MFMA chains.
 // A query's selection is split over several blocks when the batch is small (split s takes every n_split-th
 // selected pool from the s-th on).  Splits write unnormalised partials (O, running max, running sum) that a
 // second kernel merges in split order, so results are deterministic.
@@ -461,11 +461,11 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(
 // ---------------------------------------------------------------------------------------------------------------
 // bf16 latent rows of V = 512 value columns: the same split, slots and two-role pipeline as attn_kernel, with the
 // value rows going straight from global memory into LDS (one wave-wide 16-byte direct load per 1 KiB row, no
-// register staging), two blocks ahead in a ring of four swizzled 32 KiB buffers.  The registers this frees let
-// the S waves keep twelve C-fragment reads in flight ahead of their MFMAs, and the O waves read all of a block's
-// C^T and P fragments before theirs.
+// register staging), three blocks in flight in a ring of four swizzled 32 KiB buffers.  The registers this frees
+// let the S waves keep twelve C-fragment reads in flight ahead of their MFMAs, and the O waves read a block's C^T
+// fragments one iteration before they multiply them.
 // ---------------------------------------------------------------------------------------------------------------
-constexpr int AD_NBUF = 4;        // LDS block buffers: S reads block j, O reads j - 1, j + 1 and j + 2 land
+constexpr int AD_NBUF = 4;        // LDS block buffers: blocks j .. j + 2 land or are read, j + 3 is refilled
 constexpr int AD_MAXPOOL = 2048 + 16;  // pools of one split held in the LDS pool table (k pools + 1)
 constexpr int AD_DIST = 12;       // S waves: C-fragment reads in flight ahead of the MFMAs
 
