@@ -131,11 +131,12 @@ class Leg:
         per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
         return {"mean": ev[0].elapsed_time(ev[steps]) / steps, "median": float(np.median(per)), "min": min(per)}
 
-    def time_steps_graph(self, steps: int) -> float:
-        """Mean ms per step with `steps` steps captured in one HIP graph and replayed: the GPU time of a step whose
-        kernels finish faster than Python can enqueue them (a single query)."""
+    def time_steps_graph(self, steps: int, warmup: int, replays: int = 5) -> dict:
+        """ms per step with `steps` steps captured in one HIP graph and replayed, as a serving loop replays its
+        captured decode step: `mean` from the first timed replay (exactly `steps` steps, after one untimed
+        replay), `median` and `min` of the per-step times of `replays` timed replays."""
         torch = self.torch
-        for i in range(3):
+        for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -145,12 +146,15 @@ class Leg:
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
+        per = []
+        for _ in range(replays):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / steps)
         del g
-        return e0.elapsed_time(e1) / steps
+        return {"mean": per[0], "median": float(np.median(per)), "min": min(per)}
 
     def time_stages(self, steps: int) -> dict:
         """Mean ms per stage, events recorded between the four calls on the launch stream."""
@@ -239,6 +243,12 @@ class Leg:
 
 STAGE_KERNELS = {"score": ["kp::score_decode_kernel<kp::bf16, 128>"],
                  "attend": ["kp::attn_dma_kernel<4, false>", "kp::attn_combine_kernel<kp::bf16, 8>"]}
+
+
+def eager_stats(t: dict, n_q: int) -> dict:
+    """The same steps launched one call at a time (no graph): ms per step (mean, median, min) and tokens/s."""
+    return {"ms_per_step": round(t["mean"], 5), "ms_per_step_median": round(t["median"], 5),
+            "ms_per_step_min": round(t["min"], 5), "tokens_per_s": round(n_q / (t["mean"] * 1e-3), 1)}
 
 
 def measured_traffic(stage: str):
@@ -503,13 +513,16 @@ def main():
     if "decode" in legs:
         print("[bench] decode leg: 64 sequences, contexts up to 128K", file=sys.stderr, flush=True)
         leg = Leg(wl, copies=2)
-        t = leg.time_steps(args.steps, args.warmup)
+        te = leg.time_steps(args.steps, args.warmup)
+        t = leg.time_steps_graph(args.steps, args.warmup)
         ms = t["mean"]
         st = leg.time_stages(args.steps)
         by = decode_bytes(wl)
         tot = sum(by.values())
         res.update(value=round(wl.n_q / (ms * 1e-3), 1), ms_per_step=round(ms, 5))
         res["ms_per_step_median"], res["ms_per_step_min"] = round(t["median"], 5), round(t["min"], 5)
+        res["launch"] = "the timed steps captured in one HIP graph, replayed"
+        res["eager"] = eager_stats(te, wl.n_q)
         res["hbm_gbs"] = round(tot / (ms * 1e-3) / 1e9, 1)
         res["hbm_frac"] = round(res["hbm_gbs"] / HBM_PEAK_GBS, 4)
         res["stages_ms"] = {k: round(v, 5) for k, v in st.items()}
@@ -536,18 +549,18 @@ def main():
     def single(name, key, copies):
         w1 = W[name]
         leg = Leg(w1, copies=copies)
-        t = leg.time_steps(max(args.steps, 50), args.warmup)
+        n = max(args.steps, 50)
+        te = leg.time_steps(n, args.warmup)
+        t = leg.time_steps_graph(n, args.warmup)
         ms = t["mean"]
-        st = leg.time_stages(max(args.steps, 50))
+        st = leg.time_stages(n)
         by = decode_bytes(w1)
-        msg = leg.time_steps_graph(max(args.steps, 50))
         gbs = sum(by.values()) / (ms * 1e-3) / 1e9
         res[key] = {"tokens_per_s": round(1 / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
                     "ms_per_step_median": round(t["median"], 5), "ms_per_step_min": round(t["min"], 5),
                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                     "stages_ms": {k: round(v, 5) for k, v in st.items()}, "bytes": int(sum(by.values())),
-                    "graph": {"ms_per_step": round(msg, 5), "tokens_per_s": round(1 / (msg * 1e-3), 1),
-                              "hbm_gbs": round(sum(by.values()) / (msg * 1e-3) / 1e9, 1)}}
+                    "eager": eager_stats(te, 1)}
         leg.free()
     if "32k" in legs:
         print("[bench] 32k leg: one sequence at context 32768", file=sys.stderr, flush=True)
@@ -559,7 +572,8 @@ def main():
         print("[bench] long1m leg: 8 sequences at context 1048576", file=sys.stderr, flush=True)
         w5 = W["long1m"]
         leg = Leg(w5, copies=2)
-        t = leg.time_steps(args.steps, args.warmup)
+        te = leg.time_steps(args.steps, args.warmup)
+        t = leg.time_steps_graph(args.steps, args.warmup)
         ms = t["mean"]
         st = leg.time_stages(args.steps)
         by = decode_bytes(w5)
@@ -567,7 +581,8 @@ def main():
         res["long1m"] = {"tokens_per_s": round(w5.n_q / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
                          "ms_per_step_median": round(t["median"], 5), "ms_per_step_min": round(t["min"], 5),
                          "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "stages_ms": {k: round(v, 5) for k, v in st.items()}, "stage_bytes": by}
+                         "stages_ms": {k: round(v, 5) for k, v in st.items()}, "stage_bytes": by,
+                         "eager": eager_stats(te, w5.n_q)}
         if "ceiling" in legs:
             ca, cs = leg.time_read_rows("attend"), leg.time_read_rows("score")
             res["long1m"]["ceiling"] = {"attend_rows": ca, "score_pages": cs,
@@ -578,7 +593,8 @@ def main():
         print("[bench] fp8 leg: the 64-sequence decode over an fp8 (E4M3) latent cache", file=sys.stderr, flush=True)
         w8 = W["batch64_fp8"]
         leg = Leg(w8, copies=2)
-        t = leg.time_steps(args.steps, args.warmup)
+        te = leg.time_steps(args.steps, args.warmup)
+        t = leg.time_steps_graph(args.steps, args.warmup)
         ms = t["mean"]
         st = leg.time_stages(args.steps)
         by = decode_bytes(w8)
@@ -586,7 +602,7 @@ def main():
         res["decode_fp8_latent"] = {"tokens_per_s": round(w8.n_q / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
                                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                                     "kv_scale": w8.kv_scale, "stages_ms": {k: round(v, 5) for k, v in st.items()},
-                                    "stage_bytes": by}
+                                    "stage_bytes": by, "eager": eager_stats(te, w8.n_q)}
         leg.free()
     if "prefill" in legs:
         print("[bench] prefill leg: 4096 queries on 65536 tokens", file=sys.stderr, flush=True)

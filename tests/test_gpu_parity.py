@@ -224,6 +224,54 @@ def test_paged_equals_contiguous_and_deterministic():
     _free()
 
 
+@pytest.mark.parametrize("case", ["small_decode_general", "two_step_mixed"])
+def test_decode_step_graph_replay(case):
+    """The layer step captured in a HIP graph (as a serving loop replays its decode step): every replay writes what
+    the eager step wrote, bit for bit -- pooled keys of the pools completing in-step, scores, selection, output and
+    lse -- with every output cleared by eager work and a synchronisation between the replays."""
+    from harness import SENTINEL
+    wl = SMALL[case]()
+    _say(f"[case graph_replay {case}] n_q={wl.n_q}")
+    run = DeviceRun(wl).run()
+    L, d = run.layer, run.inputs
+    ppp = wl.page_tokens // wl.P
+    done = None
+    if d.c_seq is not None:   # cache rows of the pools compressed in-step
+        pages = d.block_table[d.c_seq.long(), (d.c_pool // ppp).long()].long()
+        done = (pages, (d.c_pool % ppp).long())
+
+    def bits(t):
+        return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+    def outputs():
+        o = {"scores": L.scores, "sel": L.sel, "n_sel": L.n_sel, "out": run.out, "lse": run.lse}
+        if done is not None:
+            o["pooled"] = run.pooled[done[0], done[1]]
+        return {k: bits(v).clone() for k, v in o.items()}
+
+    ref = outputs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.step(run.cache, run.queries, run.q_idx, run.w, run.q, run.out, lse=run.lse, compress=run.compress)
+    for r in range(3):
+        bits(L.scores).fill_(SENTINEL[torch.float32])
+        L.sel.fill_(-7)
+        L.n_sel.fill_(-7)
+        bits(run.out).fill_(0x7FC1)
+        bits(run.lse).fill_(0x7FC0DEAD)
+        if done is not None:
+            run.pooled[done[0], done[1]] = 0
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = outputs()
+        for k in ref:
+            assert torch.equal(got[k], ref[k]), f"replay {r}: {k} differs from the eager step"
+        run.check_guards()
+    del g, run
+    _free()
+
+
 def test_workspace_reuse_across_query_counts():
     """One attention workspace serves calls with different query counts (so different split counts) in any
     order: results repeat bit for bit, and match a repeated batch within the attention tolerance."""
