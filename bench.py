@@ -188,7 +188,8 @@ class Leg:
         return {n: acc[n] / steps for n in names}
 
     def attended_rows(self):
-        """Physical latent rows of every token the last step attended (int32, in each query's selection order)."""
+        """Physical latent rows of every token the last step attended (int32, in each query's selection order).
+        Raises unless a step has run: the selection is checked on the host before it indexes the block table."""
         torch, wl = self.torch, self.wl
         P, pt = wl.P, wl.page_tokens
         bt = self.d.block_table.long()
@@ -196,7 +197,11 @@ class Leg:
         for j in range(wl.n_q):
             s, pos = int(wl.q_seq[j]), int(wl.q_pos[j])
             ns = int(self.layer.n_sel[j].item())
+            if not 0 <= ns <= wl.k:
+                raise RuntimeError("attended_rows: no step has written the selection")
             p = self.layer.sel[j, :ns].long()
+            if ns and (int(p.min().item()) < 0 or int(p.max().item()) > pos // P):
+                raise RuntimeError("attended_rows: no step has written the selection")
             tok = (p[:, None] * P + torch.arange(P, device="cuda")[None, :]).reshape(-1)
             tok = tok[tok <= pos]
             out.append(bt[s, tok // pt] * pt + tok % pt)

@@ -115,6 +115,62 @@ __device__ __forceinline__ void score_tiles(const typename Elem<T>::frag (&qa)[Q
 constexpr int SC_MAXCHUNK = 4096;    // decode: scores buffered in LDS per block (SC_MAXCHUNK / 4 per wave)
 constexpr int SC_DBLOCKS_PER_CU = 2;  // decode: persistent blocks of 4 waves per compute unit
 
+// The persistent decode grids split the TILE-pool tiles of all queries, taken query by query, into one contiguous
+// range per wave of about equal length, so rows of any length mix keep every wave streaming.  Wave gw of n_waves
+// gets `left` tiles starting at tile tc of query qc; false when its range is empty.  seq0 is q_seq of query `lane`
+// (lanes below n_q; queries past 64 read q_seq themselves).  With at most 64 queries, one wave scan (one query per
+// lane) gives both the total and the cursor; more queries take a second pass.
+template <int TILE>
+__device__ __forceinline__ bool decode_wave_range(const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
+                                                  int n_q, int P, int64_t ld, int64_t gw, int64_t n_waves, int lane,
+                                                  int64_t& left, int& qc, int& tc, int& seq0) {
+  auto tiles_of = [&](int q) __attribute__((always_inline)) {
+    return uint32_t((min(int64_t((q_pos[q] + 1) / P), ld) + TILE - 1) / TILE);  // ld bounds a row
+  };
+  int64_t total = 0;
+  uint32_t nt0 = 0, inc0 = 0;
+  seq0 = 0;
+  for (int q0 = 0; q0 < n_q; q0 += 64) {
+    const int q = q0 + lane;
+    const uint32_t nt = q < n_q ? tiles_of(q) : 0u;
+    if (q0 == 0) seq0 = q < n_q ? q_seq[q] : 0;
+    uint32_t sum;
+    const uint32_t inc = wave_scan_u32(nt, sum);
+    if (q0 == 0) {
+      nt0 = nt;
+      inc0 = inc;
+    }
+    total += sum;
+  }
+  const int64_t t_begin = gw * total / n_waves, t_end = (gw + 1) * total / n_waves;
+  left = t_end - t_begin;
+  qc = tc = 0;
+  if (t_begin >= t_end) return false;
+  if (n_q <= 64) {
+    const uint64_t m = __ballot(int64_t(inc0) > t_begin);
+    const int l = __builtin_ctzll(m);
+    qc = l;
+    tc = int(t_begin - int64_t(__builtin_amdgcn_readlane(int(inc0 - nt0), l)));
+  } else {
+    int64_t before = 0;
+    for (int q0 = 0; q0 < n_q; q0 += 64) {
+      const int q = q0 + lane;
+      const uint32_t nt = q < n_q ? tiles_of(q) : 0u;
+      uint32_t sum;
+      const uint32_t inc = wave_scan_u32(nt, sum);
+      if (before + sum > t_begin) {
+        const uint64_t m = __ballot(before + inc > t_begin);
+        const int l = __builtin_ctzll(m);
+        qc = q0 + l;
+        tc = int(t_begin - before - int64_t(__builtin_amdgcn_readlane(int(inc - nt), l)));
+        break;
+      }
+      before += sum;
+    }
+  }
+  return true;
+}
+
 // ---------------------------------------------------------------------------------------------------------------
 // decode: a persistent grid; the 32-pool tiles of all queries, taken query by query, are split into one contiguous
 // range per wave of about equal length, so rows of any length mix keep every wave streaming.  A wave covers its
@@ -136,59 +192,18 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
-  const int64_t n_waves = int64_t(gridDim.x) * 4;
-  const int64_t gw = int64_t(blockIdx.x) * 4 + wave;
   auto pools_of = [&](int q) __attribute__((always_inline)) {
     return int(min(int64_t((q_pos[q] + 1) / P), ld));  // ld bounds a row
   };
-
-  // total tiles, then the query holding this wave's first tile (64 queries per step, one per lane; with at most
-  // 64 queries one scan serves both, and the sequence ids come with it)
-  int64_t total = 0;
-  uint32_t nt0 = 0, inc0 = 0;
-  int seq0 = 0;
-  for (int q0 = 0; q0 < n_q; q0 += 64) {
-    const int q = q0 + lane;
-    const uint32_t nt = q < n_q ? uint32_t((pools_of(q) + 31) / 32) : 0u;
-    if (q0 == 0) seq0 = q < n_q ? q_seq[q] : 0;
-    uint32_t sum;
-    const uint32_t inc = wave_scan_u32(nt, sum);
-    if (q0 == 0) {
-      nt0 = nt;
-      inc0 = inc;
-    }
-    total += sum;
-  }
-  const int64_t t_begin = gw * total / n_waves, t_end = (gw + 1) * total / n_waves;
-  if (t_begin >= t_end) return;
-  int qc = 0, tc = 0;  // query and tile of the cursor
-  if (n_q <= 64) {
-    const uint64_t m = __ballot(int64_t(inc0) > t_begin);
-    const int l = __builtin_ctzll(m);
-    qc = l;
-    tc = int(t_begin - int64_t(__builtin_amdgcn_readlane(int(inc0 - nt0), l)));
-  } else {
-    int64_t before = 0;
-    for (int q0 = 0; q0 < n_q; q0 += 64) {
-      const int q = q0 + lane;
-      const uint32_t nt = q < n_q ? uint32_t((pools_of(q) + 31) / 32) : 0u;
-      uint32_t sum;
-      const uint32_t inc = wave_scan_u32(nt, sum);
-      if (before + sum > t_begin) {
-        const uint64_t m = __ballot(before + inc > t_begin);
-        const int l = __builtin_ctzll(m);
-        qc = q0 + l;
-        tc = int(t_begin - before - int64_t(__builtin_amdgcn_readlane(int(inc - nt), l)));
-        break;
-      }
-      before += sum;
-    }
-  }
+  int64_t left;
+  int qc, tc, seq0;  // query and tile of the cursor; q_seq of query `lane` (first 64 queries)
+  if (!decode_wave_range<32>(q_seq, q_pos, n_q, P, ld, int64_t(blockIdx.x) * 4 + wave, int64_t(gridDim.x) * 4,
+                             lane, left, qc, tc, seq0))
+    return;
 
   T* tile = tiles[wave];
   float* sb = sbuf[wave];
   const int ppp_mask = (1 << log2_ppp) - 1;
-  int64_t left = t_end - t_begin;
   while (left > 0 && qc < n_q) {
     const int n_c = pools_of(qc);
     const int nt = (n_c + 31) / 32;
@@ -559,11 +574,12 @@ kp_status launch_score(const ScoreLaunch& a, hipStream_t s) {
   // prefill shape when the caller promises runs of >= 8 queries of one sequence (a block takes 16)
   const bool prefill = a.group >= 8;
   if (!prefill) {
-    // persistent decode grid: SC_DBLOCKS_PER_CU blocks per compute unit, fewer when the tiles are few (at least
-    // about four tiles per wave, counted on the longest row)
+    // persistent decode grid: SC_DBLOCKS_PER_CU blocks per compute unit, fewer when the tiles are few (about one
+    // tile per wave, counted on the longest row: a small batch is latency-bound, and more waves in flight shorten
+    // it -- one 32K-context query runs 1.3 us faster than with four tiles per wave)
     const int64_t tiles_ub = int64_t(a.n_q) * ((ncmax + 31) / 32);
     int64_t blocks = int64_t(SC_DBLOCKS_PER_CU) * cu_count();
-    const int64_t few = (tiles_ub + 15) / 16;
+    const int64_t few = (tiles_ub + 3) / 4;
     if (few < blocks) blocks = few < 1 ? 1 : few;
     if (a.dtype == KP_DTYPE_BF16) {
       if (a.D == 128) launch_score_t<bf16, 128>(a, false, 0, 0, 0, int(blocks), s);
