@@ -250,6 +250,89 @@ STAGE_KERNELS = {"score": ["kp::score_decode_kernel<kp::bf16, 128>"],
                  "attend": ["kp::attn_dma_kernel<4, false>", "kp::attn_combine_kernel<kp::bf16, 8>"]}
 
 
+def mtp_leg(W, steps: int) -> dict:
+    """MTP verification attention: 32 sequences of the batch-64 decode workload, each with a target query at T-2 and
+    its draft at T-1 sharing the target's selection.  The same attention done two ways -- sparse_mla_attn_shared
+    (each query gathers its own rows) and sparse_mla_attn_mtp (one gather per pair) -- timed as graph replays of
+    `steps` calls over alternating cache copies, with the latent bytes each way gathers per query."""
+    import torch
+    import kpool_synth as ks
+    import sparse_attention_kpool_amd as K
+    base = W["batch64"]
+    ctx = [int(t) for t in base.ctx[:32]]
+    q_seq = np.repeat(np.arange(32, dtype=np.int32), 2)
+    q_pos = np.array([[t - 2, t - 1] for t in ctx], np.int32).reshape(-1)
+    wl = ks.scaled(base, name="mtp_verify", ctx=ctx, new_from=[t - 2 for t in ctx], q_seq=q_seq, q_pos=q_pos)
+    leg = Leg(wl, copies=2)
+    leg.step(0)
+    torch.cuda.synchronize()
+    n_q = wl.n_q
+    sel = leg.layer.sel[:n_q][0::2].contiguous()            # the targets' rows, one per pair
+    n_sel = leg.layer.n_sel[:n_q][0::2].contiguous()
+    sel_row = torch.arange(n_q, device="cuda", dtype=torch.int32) // 2
+    out = torch.empty((n_q, wl.H, wl.V), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((n_q, wl.H), dtype=torch.float32, device="cuda")
+    ws_s = torch.empty(max(K.sparse_mla_workspace_size(leg.dims, leg.queries) // 4, 4), dtype=torch.float32,
+                       device="cuda")
+    ws_m = torch.empty(max(K.sparse_mla_mtp_workspace_size(leg.dims, leg.queries) // 4, 4), dtype=torch.float32,
+                       device="cuda")
+
+    def shared(i):
+        K.sparse_mla_attn_shared(leg.dims, leg.caches[i % 2], leg.queries, leg.d.q, sel, n_sel, sel_row, out,
+                                 lse=lse, workspace=ws_s)
+
+    def mtp(i):
+        K.sparse_mla_attn_mtp(leg.dims, leg.caches[i % 2], leg.queries, leg.d.q, sel, n_sel, out, lse=lse,
+                              workspace=ws_m)
+
+    def graph_ms(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        per = []
+        for _ in range(5):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / steps)
+        del g
+        return float(np.median(per))
+
+    ms_s, ms_m = graph_ms(shared), graph_ms(mtp)
+    # tokens each query attends (its target's selected pools cut at its position, plus its own incomplete tail),
+    # and per pair the union the one-gather call reads
+    P = wl.P
+    sel_h, ns_h = sel.cpu().numpy(), n_sel.cpu().numpy()
+    per_query = 0
+    per_pair = 0
+    for r in range(len(ctx)):
+        sets = []
+        for i in (2 * r, 2 * r + 1):
+            pos = int(q_pos[i])
+            pools = set(int(x) for x in sel_h[r, :min(int(ns_h[r]), wl.k)])
+            if (pos + 1) % P:
+                pools.add(pos // P)
+            toks = {P * p + t for p in pools for t in range(P) if P * p + t <= pos}
+            sets.append(toks)
+            per_query += len(toks)
+        per_pair += len(sets[0] | sets[1])
+    row_b = wl.V * 2
+    leg.free()
+    return {"queries": n_q, "pairs": len(ctx), "shared_ms": round(ms_s, 5), "mtp_ms": round(ms_m, 5),
+            "speedup": round(ms_s / ms_m, 3),
+            "latent_mb_gathered": {"shared": round(per_query * row_b / 1e6, 2), "mtp": round(per_pair * row_b / 1e6, 2)},
+            "latent_kb_per_query": {"shared": round(per_query * row_b / n_q / 1e3, 1),
+                                    "mtp": round(per_pair * row_b / n_q / 1e3, 1)}}
+
+
 def eager_stats(t: dict, n_q: int) -> dict:
     """The same steps launched one call at a time (no graph): ms per step (mean, median, min) and tokens/s."""
     return {"ms_per_step": round(t["mean"], 5), "ms_per_step_median": round(t["median"], 5),
@@ -493,7 +576,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,ceiling,32k,128k,long1m,fp8,prefill,proj,copy")
+    ap.add_argument("--legs", default="decode,ceiling,32k,128k,long1m,fp8,mtp,prefill,proj,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=16)
     args = ap.parse_args()
@@ -594,6 +677,10 @@ def main():
                                         "step_frac_at_ceiling": round(sum(by.values()) / ((ca["ms"] + cs["ms"]) * 1e-3)
                                                                       / 1e9 / HBM_PEAK_GBS, 4)}
         leg.free()
+    if "mtp" in legs:
+        print("[bench] mtp leg: 32 targets at T-2 and their drafts at T-1, one selection per pair", file=sys.stderr,
+              flush=True)
+        res["mtp_verify"] = mtp_leg(W, args.steps)
     if "fp8" in legs:
         print("[bench] fp8 leg: the 64-sequence decode over an fp8 (E4M3) latent cache", file=sys.stderr, flush=True)
         w8 = W["batch64_fp8"]

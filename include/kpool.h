@@ -202,6 +202,31 @@ kp_status sparse_mla_attn_shared(const kp_dims* dims, const kp_cache* cache, con
                                  void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sparse_mla_attn_mtp -- MTP verification: a target and its draft over one gather of their shared selection.
+ *   [MAX glm5_next API page, index_share_for_mtp_iteration: the draft reuses its target's top-k selection;
+ *   index_kpool_always_select_tail]; [metrale glm5_next_load/loader.rs page: each sparse-attention layer's
+ *   workspace is sized for verify_k rows, the tokens one verification step carries].  Queries come in runs of two
+ *   consecutive entries -- query 2r
+ *   (a target) and query 2r + 1 (its draft; absent for the last run when n_q is odd) -- and both attend
+ *   selection row r of sel / n_sel (one row per run: ceil(n_q / 2) rows, as dsa_topk_select writes for the
+ *   targets).  Each query attends exactly what sparse_mla_attn_shared with sel_row[i] = i / 2 gives it: the row's
+ *   pools cut at its own position plus its own incomplete trailing pool when the row lacks it.
+ *   The difference is the gather: when the two queries of a run are of one sequence (the verification layout),
+ *   one block computes 32 heads of both queries over a single gathered copy of their rows, and the blocks of the
+ *   two head halves run side by side on one XCD, so each latent row is read from HBM about once per run instead
+ *   of once per query.  Runs of two sequences are still exact (each query's rows are listed separately).
+ *   Results equal sparse_mla_attn_shared's within rounding (the split of the work differs).
+ *   q, out, lse: [n_q, ...] as in sparse_mla_attn.  workspace: device, at least sparse_mla_mtp_workspace_size
+ *   bytes (split-KV partials; NULL when that is 0).
+ *   Limit: bf16 with v_dim 512 and heads <= 64 (else KP_ERR_UNSUPPORTED); 2 (topk + 1) <= 32 * min(8320 / P,
+ *   2064).  Other errors as in sparse_mla_attn.
+ */
+size_t sparse_mla_mtp_workspace_size(const kp_dims* dims, const kp_queries* queries);
+kp_status sparse_mla_attn_mtp(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
+                              const int32_t* sel, const int32_t* n_sel, void* out, float* lse, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/*
  * sparse_mla_attn_noalloc -- sparse_mla_attn with no workspace argument and no allocation.
  *   For callers that cannot allocate device memory or pass a workspace: code under HIP graph capture, tight
  *   serving loops, harnesses that forbid allocation.  Same formula, kernels, split count and results as

@@ -21,11 +21,11 @@ LIB_PATH = os.path.join(PKG, "libkpool.so")
 
 KP_OK, KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED, KP_ERR_WORKSPACE, KP_ERR_LAUNCH = 0, -1, -2, -3, -4
 KP_DTYPE_F32, KP_DTYPE_BF16 = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk_select",
             "sparse_mla_workspace_size", "sparse_mla_attn", "sparse_mla_attn_shared", "sparse_mla_attn_fp8",
-            "sparse_mla_attn_noalloc", "kp_read_rows",
+            "sparse_mla_attn_noalloc", "sparse_mla_mtp_workspace_size", "sparse_mla_attn_mtp", "kp_read_rows",
             "kp_linear", "kp_linear_workspace_size", "kp_linear_group", "kp_linear_group_workspace_size",
             "kp_last_error", "kp_abi_version")
 
@@ -90,6 +90,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_mla_attn_fp8.argtypes = [D, C, Q, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.sparse_mla_attn_shared.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sparse_mla_attn_noalloc.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp]
+    lib.sparse_mla_mtp_workspace_size.argtypes = [D, Q]
+    lib.sparse_mla_mtp_workspace_size.restype = sz
+    lib.sparse_mla_attn_mtp.argtypes = [D, C, Q, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kp_read_rows.argtypes = [vp, i64, i32, vp, i64, i32, vp]
     lib.kp_linear.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, ctypes.c_float,
                               vp, sz, vp]
@@ -100,7 +103,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kp_linear_group_workspace_size.argtypes = [i32, LP]
     lib.kp_linear_group_workspace_size.restype = sz
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_shared",
-              "sparse_mla_attn_fp8", "sparse_mla_attn_noalloc", "kp_read_rows", "kp_linear", "kp_linear_group"):
+              "sparse_mla_attn_fp8", "sparse_mla_attn_noalloc", "sparse_mla_attn_mtp", "kp_read_rows", "kp_linear",
+              "kp_linear_group"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kp_last_error.restype = ctypes.c_char_p
     lib.kp_abi_version.restype = i32
@@ -287,13 +291,13 @@ def sparse_mla_workspace_size(dims: Dims, queries: Queries) -> int:
 
 
 def _check_attn(fn: str, dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, out, lse, workspace,
-                fp8: bool = False, sel_row=None) -> None:
+                fp8: bool = False, sel_row=None, runs: bool = False) -> None:
     import torch
     n = _check_queries(fn, queries)
     st = _storage(dims)
     _want(fn, "cache.latent", cache.latent, (torch.uint8,) if fp8 else st, (None, dims.page_tokens, dims.latent_dim))
     _want(fn, "q", q, st, (n, dims.heads, dims.latent_dim), min_rows=True)
-    rows = n if sel_row is None else None
+    rows = (n + 1) // 2 if runs else n if sel_row is None else None
     _want(fn, "sel", sel, _i32(), (rows, dims.topk), min_rows=True)
     _want(fn, "n_sel", n_sel, _i32(), (sel.shape[0],), min_rows=True)
     if sel_row is not None:
@@ -326,6 +330,22 @@ def sparse_mla_attn_shared(dims: Dims, cache: Cache, queries: Queries, q, sel, n
                                                                    ctypes.byref(queries.c()), _ptr(q), _ptr(sel),
                                                                    _ptr(n_sel), _ptr(sel_row), _ptr(out), _ptr(lse),
                                                                    _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def sparse_mla_mtp_workspace_size(dims: Dims, queries: Queries) -> int:
+    return int(load().sparse_mla_mtp_workspace_size(ctypes.byref(dims.c()), ctypes.byref(queries.c())))
+
+
+def sparse_mla_attn_mtp(dims: Dims, cache: Cache, queries: Queries, q, sel, n_sel, out, lse=None, workspace=None,
+                        stream=None) -> None:
+    """MTP verification: queries 2r (target) and 2r + 1 (draft) attend selection row r (sel has ceil(n_q / 2) rows),
+    each as sparse_mla_attn_shared would with sel_row[i] = i // 2; one gather per run (see include/kpool.h)."""
+    _check_attn("sparse_mla_attn_mtp", dims, cache, queries, q, sel, n_sel, out, lse, workspace, runs=True)
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    _check("sparse_mla_attn_mtp", load().sparse_mla_attn_mtp(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+                                                             ctypes.byref(queries.c()), _ptr(q), _ptr(sel),
+                                                             _ptr(n_sel), _ptr(out), _ptr(lse), _ptr(workspace),
+                                                             ws_bytes, _stream(stream)))
 
 
 def read_rows(base, row_bytes: int, rows, blocks_per_cu: int = 2, stream=None) -> None:

@@ -90,7 +90,7 @@ using namespace kp;
 
 extern "C" {
 
-int32_t kp_abi_version(void) { return 5; }
+int32_t kp_abi_version(void) { return 6; }
 
 const char* kp_last_error(void) { return g_err; }
 
@@ -209,11 +209,17 @@ size_t sparse_mla_workspace_size(const kp_dims* dims, const kp_queries* queries)
   return attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)));
 }
 
-// Shared body of sparse_mla_attn and sparse_mla_attn_fp8 (fp8: latent rows of latent_dim E4M3 codes).
+size_t sparse_mla_mtp_workspace_size(const kp_dims* dims, const kp_queries* queries) {
+  if (!dims || !queries || queries->n_q <= 0 || dims->pool < 1 || dims->topk < 1 || dims->heads < 1) return 0;
+  return attn_workspace_mtp(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)));
+}
+
+// Shared body of the attention calls (fp8: latent rows of latent_dim E4M3 codes; mtp: runs of a target and its
+// draft attending selection row i / 2).
 static kp_status attn_call(const char* fn, bool fp8, float kv_scale, const kp_dims* dims, const kp_cache* cache,
                            const kp_queries* queries, const void* q, const int32_t* sel, const int32_t* n_sel,
                            const int32_t* sel_row, void* out, float* lse, void* workspace, size_t ws_bytes,
-                           void* stream) {
+                           void* stream, bool mtp = false) {
   kp_status st = check_dims(dims, fn);
   if (st != KP_OK) return st;
   st = check_queries(queries, fn);
@@ -232,6 +238,9 @@ static kp_status attn_call(const char* fn, bool fp8, float kv_scale, const kp_di
                "%s: v_dim %d with dtype %d is not built (bf16: 512, 64; f32: 64)", fn, dims->v_dim, dims->dtype);
   }
   KP_REQUIRE(dims->heads <= 64, KP_ERR_UNSUPPORTED, "%s: heads %d > 64", fn, dims->heads);
+  if (mtp)
+    KP_REQUIRE(dims->dtype == KP_DTYPE_BF16 && dims->v_dim == 512, KP_ERR_UNSUPPORTED,
+               "%s: built for bf16 with v_dim 512 (got dtype %d, v_dim %d)", fn, dims->dtype, dims->v_dim);
   const int64_t lat_es = fp8 ? 1 : int64_t(elem_size(dims));
   KP_REQUIRE((int64_t(dims->latent_dim) * lat_es) % 16 == 0, KP_ERR_INVALID_ARG,
              "%s: latent rows must be a multiple of 16 bytes (latent_dim %d)", fn, dims->latent_dim);
@@ -240,10 +249,12 @@ static kp_status attn_call(const char* fn, bool fp8, float kv_scale, const kp_di
                  (!sel_row || aligned(sel_row)),
              KP_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
   const size_t ws_need =
-      attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)));
+      mtp ? attn_workspace_mtp(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)))
+          : attn_workspace(dims->pool, dims->topk, dims->heads, dims->v_dim, queries->n_q, int(elem_size(dims)));
   KP_REQUIRE(ws_bytes >= ws_need && (ws_need == 0 || (workspace && aligned(workspace))), KP_ERR_WORKSPACE,
              "%s: workspace of %zu bytes < %zu required", fn, ws_bytes, ws_need);
   AttnLaunch a{};
+  a.mtp = mtp ? 1 : 0;
   a.dtype = dims->dtype;
   a.P = dims->pool;
   a.H = dims->heads;
@@ -285,6 +296,13 @@ kp_status sparse_mla_attn_shared(const kp_dims* dims, const kp_cache* cache, con
   KP_REQUIRE(sel_row || !queries || queries->n_q == 0, KP_ERR_INVALID_ARG, "sparse_mla_attn_shared: NULL sel_row");
   return attn_call("sparse_mla_attn_shared", false, 1.f, dims, cache, queries, q, sel, n_sel, sel_row, out, lse,
                    workspace, ws_bytes, stream);
+}
+
+kp_status sparse_mla_attn_mtp(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries, const void* q,
+                              const int32_t* sel, const int32_t* n_sel, void* out, float* lse, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  return attn_call("sparse_mla_attn_mtp", false, 1.f, dims, cache, queries, q, sel, n_sel, nullptr, out, lse,
+                   workspace, ws_bytes, stream, true);
 }
 
 kp_status sparse_mla_attn_noalloc(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries,

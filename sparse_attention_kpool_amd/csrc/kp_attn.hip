@@ -101,20 +101,19 @@ __device__ __align__(16) uint32_t attn_zero_row[256];
 // target's selection), its own trailing pool tau = pos / P when that pool is incomplete ((pos + 1) mod P != 0) and
 // the row lacks it.  The shared item is the target's top-k pick; the incomplete tail is not a pick but is always
 // visible, so a draft always sees its own pending tokens -- itself included.  Returns the entry count; entry
-// n_row, when present, is `extra`.  With `shared` set every thread of the block must call it (one barrier).
-__device__ __forceinline__ int attn_row_pools(const int32_t* __restrict__ row, int n_row, bool shared, int pos,
-                                              int log2P, int& extra) {
-  extra = -1;
-  if (!shared) return n_row;
+// n_row, when present, is `extra`.  With `shared` set every thread of the block must call it (one barrier), as
+// attn_own_tail (that tail pool, or -1 when the row holds it or it is complete).
+__device__ __forceinline__ int attn_own_tail(const int32_t* __restrict__ row, int n_row, int pos, int log2P) {
   const int tau = pos >> log2P;
   int has = 0;
   for (int j = threadIdx.x; j < n_row; j += blockDim.x) has |= row[j] == tau ? 1 : 0;
   has = __syncthreads_or(has);
-  if (has == 0 && ((pos + 1) & ((1 << log2P) - 1)) != 0) {
-    extra = tau;
-    return n_row + 1;
-  }
-  return n_row;
+  return (has == 0 && ((pos + 1) & ((1 << log2P) - 1)) != 0) ? tau : -1;
+}
+__device__ __forceinline__ int attn_row_pools(const int32_t* __restrict__ row, int n_row, bool shared, int pos,
+                                              int log2P, int& extra) {
+  extra = shared ? attn_own_tail(row, n_row, pos, log2P) : -1;
+  return n_row + (extra >= 0 ? 1 : 0);
 }
 
 // A-operand fragment of C^T (channels c0 .. c0+15 x tokens 8g .. 8g+7 of k-step s) from the row-major block.
@@ -474,14 +473,24 @@ constexpr int AD_DIST = 12;       // S waves: C-fragment reads in flight ahead o
 // converts every code to bf16 once -- exactly: E4M3 values are bf16 values -- and writes the same swizzled bf16
 // block the direct loads produce, two blocks ahead of the S phase, so the S and O phases are unchanged.  The cache
 // scale is folded into the softmax scale and applied to O on the way out.
-template <int HT, bool FP8>
+//
+// MTP (verification runs): queries come in runs of two consecutive entries -- a target and its draft -- that attend
+// selection row `run` (one row per run), each cut at its own position plus its own incomplete trailing pool when
+// the row lacks it (see attn_own_tail).  A block takes (run, split, head half hb): its 64 score / output rows are 32
+// heads (hb * 32 ..) of each of the two queries -- S waves 0, 1 the target's, 2, 3 the draft's -- over ONE list of
+// gathered rows: the row's pools and the queries' added tails, each row with one validity mask per query.  When
+// the two queries belong to different sequences the list is the two queries' pools one after the other (each row
+// attended by one query only).  The two head-half blocks of a (run, split) are launched 8 apart, so they run on
+// one XCD at about the same time and the second reads each row from that XCD's L2.
+template <int HT, bool FP8, bool MTP = false>
 __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
     const void* __restrict__ latent_v, int L, const int32_t* __restrict__ bt, int bt_stride, int log2_pt,
     const bf16* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, const int32_t* __restrict__ sel_row,
     int log2P, int k, int H, float scale_log2,
     int n_split, bf16* __restrict__ out, float* __restrict__ lse, bf16* __restrict__ part_o,
-    float* __restrict__ part_ml, float oscale) {
+    float* __restrict__ part_ml, float oscale, int n_q) {
+  static_assert(!MTP || (!FP8 && HT == 4), "MTP runs: bf16 latent rows, 64 score rows per block");
   using T = bf16;
   // S waves: C-fragment reads in flight ahead of the MFMAs (fewer with fp8: the staging registers take the rest)
   constexpr int DIST = FP8 ? 6 : AD_DIST;
@@ -501,41 +510,99 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
   __shared__ uint32_t resc_s[2];
   __shared__ float m_s[64];
   __shared__ float l_s[64];
-  __shared__ uint32_t vmask_s[AT_MAXSLOT / AT_NT];  // valid-slot mask of every block of the split
+  __shared__ uint32_t vmask_s[MTP ? 2 : 1][AT_MAXSLOT / AT_NT];  // valid-slot mask of every block, per query
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // the same value, known to be wave-uniform
   const int l16 = lane & 15, g = lane >> 4;
   const bool o_wave = wave >= 4;
   const int wl = wave & 3;  // index within the wave's role
-  const int qi = blockIdx.x / n_split;
-  const int srow = sel_row ? sel_row[qi] : qi;  // the selection row this query attends (shared by MTP drafts)
-  const int sp = blockIdx.x - qi * n_split;
+  const int P = 1 << log2P;
+  int qi, sp, hb = 0, srow;
+  if constexpr (MTP) {
+    // block b: unit u = run * n_split + split, head half hb; units go 8 to a group, a group's head halves 8 apart
+    const int nhb = (H + 31) >> 5;
+    const int per = 8 * nhb, b = int(blockIdx.x);
+    const int u = (b / per) * 8 + (b % per) % 8;
+    hb = (b % per) / 8;
+    if (u >= ((n_q + 1) >> 1) * n_split) return;  // launch padding: the whole block leaves before any barrier
+    srow = u / n_split;
+    sp = u - srow * n_split;
+    qi = 2 * srow;
+  } else {
+    qi = blockIdx.x / n_split;
+    sp = blockIdx.x - qi * n_split;
+    srow = sel_row ? sel_row[qi] : qi;  // the selection row this query attends (shared by MTP drafts)
+  }
   const int seq = q_seq[qi];
   const int pos = q_pos[qi];
-  const int P = 1 << log2P;
-  // split sp takes the selected pools sp, sp + n_split, sp + 2 n_split, ... (as attn_kernel)
+  // the run's draft (MTP), when present
+  const bool has_b = MTP && qi + 1 < n_q;
+  const int seq_b = has_b ? q_seq[qi + 1] : seq;
+  const int pos_b = has_b ? q_pos[qi + 1] : -1;
+  // split sp takes the entries sp, sp + n_split, sp + 2 n_split, ... of the pool list (as attn_kernel)
   // The first selection entry of each thread is loaded right away, with the selection count rather than after
   // it (an entry past the count is read but not used; every index stays inside the row of k entries).
-  const int32_t* qsel = sel + int64_t(srow) * k + sp;
+  const int32_t* rowp = sel + int64_t(srow) * k;
+  const int32_t* qsel = rowp + sp;
   const int kq = (k - sp + n_split - 1) / n_split;  // entries of the row this split strides over
   const int p_first = tid < kq ? qsel[int64_t(tid) * n_split] : -1;
   const int n_row = min(n_sel[srow], k);
-  int extra;  // a shared row's added tail pool (entry n_row), or -1
-  const int ns_pools = attn_row_pools(sel + int64_t(srow) * k, n_row, sel_row != nullptr, pos, log2P, extra);
+  // Pool list: the row's n_row pools and the added tails.  One query: entry n_row is `extra` when present.  MTP
+  // (tail_a, tail_b: each query's own added tail, or -1): one sequence -- the row, then tail_a, then tail_b unless
+  // it is the same pool (ex_b); two sequences -- the target's row and tail_a (n_a entries), then the draft's row
+  // and tail_b.
+  int extra = -1, tail_a = -1, tail_b = -1, ex_b = -1, n_a = 0, ns_pools;
+  bool one_seq = true;
+  if constexpr (MTP) {
+    tail_a = attn_own_tail(rowp, n_row, pos, log2P);
+    if (has_b) tail_b = attn_own_tail(rowp, n_row, pos_b, log2P);
+    one_seq = !has_b || seq_b == seq;
+    n_a = n_row + (tail_a >= 0 ? 1 : 0);
+    if (one_seq) {
+      ex_b = tail_b != tail_a ? tail_b : -1;
+      ns_pools = n_a + (ex_b >= 0 ? 1 : 0);
+    } else {
+      ns_pools = n_a + n_row + (tail_b >= 0 ? 1 : 0);
+    }
+  } else {
+    ns_pools = attn_row_pools(rowp, n_row, sel_row != nullptr, pos, log2P, extra);
+  }
   const int my_pools = ns_pools > sp ? (ns_pools - sp + n_split - 1) / n_split : 0;
   const int nsl = my_pools * P;  // slots of this split
 
-  if (nsl == 0) {  // an empty split (this query selected fewer tokens)
-    if (n_split > 1) {
-      for (int h = tid; h < H; h += AT_THREADS) {
-        part_ml[(int64_t(qi * n_split + sp) * H + h) * 2 + 0] = -INFINITY;
-        part_ml[(int64_t(qi * n_split + sp) * H + h) * 2 + 1] = 0.f;
-      }
+  // Output row r of the block (0 .. 63): query and head, and whether it exists.  One query: row r is head r.  MTP:
+  // rows 0 .. 31 are heads hb * 32 .. of the target, rows 32 .. 63 the same heads of the draft.
+  auto row_dest = [&](int r, int& qd, int& hd) __attribute__((always_inline)) -> bool {
+    if constexpr (MTP) {
+      qd = qi + (r >> 5);
+      hd = hb * 32 + (r & 31);
+      return hd < H && (r < 32 || has_b);
     } else {
-      for (int64_t e = tid; e < int64_t(H) * V; e += AT_THREADS) out[int64_t(qi) * H * V + e] = E::from_f32(0.f);
-      if (lse)
-        for (int h = tid; h < H; h += AT_THREADS) lse[int64_t(qi) * H + h] = -INFINITY;
+      qd = qi;
+      hd = r;
+      return r < H;
+    }
+  };
+  constexpr int NROW = MTP ? 64 : 16 * HT;  // output rows of the block (rows past H are never written)
+
+  if (nsl == 0) {  // an empty split (these queries selected fewer tokens)
+    for (int r = tid; r < NROW; r += AT_THREADS) {
+      int qd, hd;
+      if (!row_dest(r, qd, hd)) continue;
+      if (n_split > 1) {
+        part_ml[(int64_t(qd * n_split + sp) * H + hd) * 2 + 0] = -INFINITY;
+        part_ml[(int64_t(qd * n_split + sp) * H + hd) * 2 + 1] = 0.f;
+      } else if (lse) {
+        lse[int64_t(qd) * H + hd] = -INFINITY;
+      }
+    }
+    if (n_split == 1) {
+      for (int i = tid; i < NROW * (V / 8); i += AT_THREADS) {
+        int qd, hd;
+        if (!row_dest(i / (V / 8), qd, hd)) continue;
+        *reinterpret_cast<u32x4*>(out + (int64_t(qd) * H + hd) * V + (i % (V / 8)) * 8) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
     return;
   }
@@ -546,39 +613,78 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
   f32x4 bank[S::NB];
 #pragma unroll
   for (int b = 0; b < S::NB; ++b) bank[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool s_active = !o_wave && wl < HT;
+  // S wave wl: query s_q, heads s_h = 16 wl + l16 (MTP: waves 0, 1 the target's heads hb * 32 .., 2, 3 the draft's)
+  const int s_member = MTP ? (wl >> 1) : 0;
+  const int s_q = qi + s_member;
+  const int s_h = MTP ? hb * 32 + 16 * (wl & 1) + l16 : 16 * wl + l16;
+  const bool s_active = !o_wave && (MTP ? (s_member == 0 || has_b) : wl < HT);
   if (s_active) {
-    const int h = 16 * wl + l16;
-    if (h < H) {
-      const T* qp = q + (int64_t(qi) * H + h) * L + g * (V / 4);
+    if (s_h < H) {
+      const T* qp = q + (int64_t(s_q) * H + s_h) * L + g * (V / 4);
 #pragma unroll
       for (int s = 0; s < S::SK; ++s) bank[s] = __builtin_bit_cast(f32x4, E::frag_load(qp + s * S::KPL));
     }
   }
   // Pool table: cache row of every pool's first token and how many of its tokens the query sees (the tail pool is
   // cut at the query), one block-table lookup per pool; and the valid-slot mask of every block, OR-ed over the
-  // 32 / P consecutive lanes that hold the block's pools (no LDS round trip).
+  // 32 / P consecutive lanes that hold the block's pools (no LDS round trip).  MTP: a pool counts the tokens that
+  // either query sees (the rows the block loads), and each query has its own mask.
   {
     const int pt_mask = (1 << log2_pt) - 1;
     const int ppb = AT_NT >> log2P;  // pools per block (P <= 32)
     for (int j0 = 0; j0 < my_pools; j0 += AT_THREADS) {
       const int j = j0 + tid;
       const bool valid = j < my_pools;
-      const int gj = sp + j * n_split;  // entry of the row
-      const int p = gj >= n_row ? (valid ? extra : -1) : j0 == 0 ? p_first : qsel[int64_t(j) * n_split];
-      int nt = 0, row = 0;
+      const int gj = sp + j * n_split;  // entry of the pool list
+      int p = -1, eseq = seq;
+      bool att_a = true, att_b = false;  // which queries attend the entry
+      auto row_entry = [&](int e) __attribute__((always_inline)) {
+        return (j0 == 0 && e == gj) ? p_first : rowp[e];
+      };
+      if constexpr (MTP) {
+        if (valid) {
+          if (one_seq) {
+            if (gj < n_row) {
+              p = row_entry(gj);
+              att_b = has_b;
+            } else {
+              p = (gj == n_row && tail_a >= 0) ? tail_a : ex_b;
+              att_a = p == tail_a;
+              att_b = has_b && p == tail_b;
+            }
+          } else if (gj < n_a) {
+            p = gj < n_row ? row_entry(gj) : tail_a;
+          } else {
+            const int e2 = gj - n_a;
+            p = e2 < n_row ? rowp[e2] : tail_b;
+            eseq = seq_b;
+            att_a = false;
+            att_b = true;
+          }
+        }
+      } else {
+        p = gj >= n_row ? (valid ? extra : -1) : j0 == 0 ? p_first : qsel[int64_t(j) * n_split];
+      }
+      int nt = 0, nt_b = 0, row = 0;
       if (valid && p >= 0) {
         const int first = p << log2P;
-        nt = max(min(P, pos - first + 1), 0);
-        if (nt > 0) row = bt[int64_t(seq) * bt_stride + (first >> log2_pt)] * (pt_mask + 1) + (first & pt_mask);
+        if (att_a) nt = max(min(P, pos - first + 1), 0);
+        if (att_b) nt_b = max(min(P, pos_b - first + 1), 0);
+        if (max(nt, nt_b) > 0)
+          row = bt[int64_t(eseq) * bt_stride + (first >> log2_pt)] * (pt_mask + 1) + (first & pt_mask);
       }
       if (valid) {
         prow_s[j] = row;
-        pnt_s[j] = uint8_t(nt);
+        pnt_s[j] = uint8_t(max(nt, nt_b));
       }
       uint32_t bits = (nt >= 32 ? 0xffffffffu : (1u << nt) - 1u) << ((j & (ppb - 1)) << log2P);
       for (int o = 1; o < ppb; o <<= 1) bits |= uint32_t(__shfl_xor(int(bits), o));
-      if (valid && (j & (ppb - 1)) == 0) vmask_s[j / ppb] = bits;
+      if (valid && (j & (ppb - 1)) == 0) vmask_s[0][j / ppb] = bits;
+      if constexpr (MTP) {
+        uint32_t bb = (nt_b >= 32 ? 0xffffffffu : (1u << nt_b) - 1u) << ((j & (ppb - 1)) << log2P);
+        for (int o = 1; o < ppb; o <<= 1) bb |= uint32_t(__shfl_xor(int(bb), o));
+        if (valid && (j & (ppb - 1)) == 0) vmask_s[1][j / ppb] = bb;
+      }
     }
   }
 
@@ -634,8 +740,8 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
       if (f + DIST < 2 * S::SK) cf[f % DIST] = rd(f + DIST);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // lane holds head 16*wl + l16, slots 16t + 4g + i
-    const uint32_t vm = vmask_s[j];
+    // lane holds score row 16*wl + l16, slots 16t + 4g + i
+    const uint32_t vm = vmask_s[s_member][j];
     float x[2][4];
     float lmax = -INFINITY;
 #pragma unroll
@@ -884,31 +990,37 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
   if (o_wave) {
 #pragma unroll
     for (int nt = 0; nt < HT; ++nt) {
-      const int h = 16 * nt + l16;
-      if (h >= H) continue;
-      const float f = n_split == 1 ? oscale / l_s[h] : oscale;
+      const int r = 16 * nt + l16;
+      int qd, hd;
+      if (!row_dest(r, qd, hd)) continue;
+      // (a query that sees no token of this block's list -- possible for one query of an MTP run -- has l = 0)
+      const float f = n_split == 1 ? (l_s[r] > 0.f ? oscale / l_s[r] : 0.f) : oscale;
 #pragma unroll
       for (int mt = 0; mt < S::MT; ++mt) {
         const f32x4 o = bank[mt * HT + nt] * f;
-        *reinterpret_cast<uint2*>(stg + h * SROW + wl * S::VW + 16 * mt + 4 * g) =
+        *reinterpret_cast<uint2*>(stg + r * SROW + wl * S::VW + 16 * mt + 4 * g) =
             make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
       }
     }
   }
   __syncthreads();
-  T* dst = n_split == 1 ? out + int64_t(qi) * H * V : part_o + int64_t(qi * n_split + sp) * H * V;
-  for (int i = tid; i < H * (V / S::EPC); i += AT_THREADS) {
-    const int h = i / (V / S::EPC), c = i % (V / S::EPC);
-    *reinterpret_cast<u32x4*>(dst + int64_t(h) * V + c * S::EPC) =
-        *reinterpret_cast<const u32x4*>(stg + h * SROW + c * S::EPC);
+  for (int i = tid; i < NROW * (V / S::EPC); i += AT_THREADS) {
+    const int r = i / (V / S::EPC), c = i % (V / S::EPC);
+    int qd, hd;
+    if (!row_dest(r, qd, hd)) continue;
+    T* dst = n_split == 1 ? out + (int64_t(qd) * H + hd) * V : part_o + (int64_t(qd * n_split + sp) * H + hd) * V;
+    *reinterpret_cast<u32x4*>(dst + c * S::EPC) = *reinterpret_cast<const u32x4*>(stg + r * SROW + c * S::EPC);
   }
-  if (tid < H) {
-    if (n_split == 1) {
-      if (lse) lse[int64_t(qi) * H + tid] = (m_s[tid] + log2f(l_s[tid])) * LN2;
-    } else {
-      const int64_t base = int64_t(qi * n_split + sp) * H + tid;
-      part_ml[base * 2 + 0] = m_s[tid];
-      part_ml[base * 2 + 1] = l_s[tid];
+  if (tid < NROW) {
+    int qd, hd;
+    if (row_dest(tid, qd, hd)) {
+      if (n_split == 1) {
+        if (lse) lse[int64_t(qd) * H + hd] = l_s[tid] > 0.f ? (m_s[tid] + log2f(l_s[tid])) * LN2 : -INFINITY;
+      } else {
+        const int64_t base = int64_t(qd * n_split + sp) * H + hd;
+        part_ml[base * 2 + 0] = m_s[tid];
+        part_ml[base * 2 + 1] = l_s[tid];
+      }
     }
   }
 }
@@ -972,7 +1084,7 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __res
       acc += w * v;
     }
   }
-  const float inv = 1.f / wsum;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;  // a query that attends no token: zeros, lse -inf
   T* op = out + (int64_t(qi) * H + h) * V + c;
   if constexpr (sizeof(T) == 2) {
     *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
@@ -980,7 +1092,7 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __res
   } else {
     *reinterpret_cast<float4*>(op) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   }
-  if (lse && c == 0) lse[int64_t(qi) * H + h] = (M + log2f(wsum)) * LN2;
+  if (lse && c == 0) lse[int64_t(qi) * H + h] = wsum > 0.f ? (M + log2f(wsum)) * LN2 : -INFINITY;
 }
 
 int attn_splits(int P, int k, int n_q) {
@@ -994,6 +1106,25 @@ int attn_splits(int P, int k, int n_q) {
   const int64_t min_splits = (int64_t(k) + 1 + per_split - 1) / per_split;
   if (want < min_splits) want = min_splits;
   return want < 1 ? 1 : int(want);
+}
+
+int attn_splits_mtp(int P, int k, int n_q, int H) {
+  // about 256 blocks over the runs' head halves, at most 32 splits, and few enough list entries per split for the
+  // LDS tables: a run of two sequences lists both queries' pools, 2 (k + 1) entries
+  const int64_t units = int64_t((n_q + 1) / 2) * ((H + 31) / 32);
+  int64_t want = (256 + units - 1) / (units > 0 ? units : 1);
+  if (want > k) want = k;
+  if (want > 32) want = 32;
+  const int64_t per_split = AT_MAXSLOT / P < AD_MAXPOOL ? AT_MAXSLOT / P : AD_MAXPOOL;
+  const int64_t min_splits = (2 * (int64_t(k) + 1) + per_split - 1) / per_split;
+  if (want < min_splits) want = min_splits;
+  return want < 1 ? 1 : int(want);
+}
+
+size_t attn_workspace_mtp(int P, int k, int H, int V, int n_q, int esize) {
+  const int ns = attn_splits_mtp(P, k, n_q, H);
+  if (ns <= 1) return 0;
+  return size_t(n_q) * ns * H * (size_t(V) * esize + 2 * sizeof(float));
 }
 
 size_t attn_workspace(int P, int k, int H, int V, int n_q, int esize) {
@@ -1032,6 +1163,44 @@ kp_status attn_noalloc_scratch(void** ptr) {
   return KP_OK;
 }
 
+// Split merge of n_q queries' partials (ns splits each) into out / lse.
+template <class T>
+static kp_status launch_combine(const AttnLaunch& a, int ns, const T* part_o, const float* part_ml, hipStream_t s) {
+  const int hpb = CB_THREADS / (a.V / 4);
+  const int64_t cblocks = int64_t(a.n_q) * ((a.H + hpb - 1) / hpb);
+  if (ns <= 8)
+    attn_combine_kernel<T, 8><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H, a.V,
+                                                                                   (T*)a.out, a.lse);
+  else
+    attn_combine_kernel<T, CB_MAXSPLIT><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(
+        part_o, part_ml, ns, a.H, a.V, (T*)a.out, a.lse);
+  return check_launch("sparse_mla_attn (split merge)");
+}
+
+// MTP runs (sparse_mla_attn_mtp): bf16 rows of 512 value columns, 64 heads at most.  Blocks: every (run, split)
+// unit once per head half, the units 8 to a group and a group's head halves 8 blocks apart (one XCD).
+static kp_status launch_attn_mtp(const AttnLaunch& a, hipStream_t s) {
+  const int ns = attn_splits_mtp(a.P, a.k, a.n_q, a.H);
+  bf16* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (ns > 1) {
+    part_o = reinterpret_cast<bf16*>(a.ws);
+    part_ml = reinterpret_cast<float*>(part_o + size_t(a.n_q) * ns * a.H * a.V);
+  }
+  const int64_t units = int64_t((a.n_q + 1) / 2) * ns;
+  const int64_t blocks = (units + 7) / 8 * 8 * ((a.H + 31) / 32);
+  if (blocks > 0x7fffffff) {
+    set_error("sparse_mla_attn_mtp: too many queries for one launch");
+    return KP_ERR_INVALID_ARG;
+  }
+  attn_dma_kernel<4, false, true><<<dim3(unsigned(blocks)), dim3(AT_THREADS), 0, s>>>(
+      a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const bf16*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel, nullptr,
+      ilog2(a.P), a.k, a.H, a.scale * 1.4426950408889634f, ns, (bf16*)a.out, a.lse, part_o, part_ml, 1.f, a.n_q);
+  kp_status st = check_launch("sparse_mla_attn_mtp");
+  if (st != KP_OK || ns == 1) return st;
+  return launch_combine<bf16>(a, ns, part_o, part_ml, s);
+}
+
 template <class T, int V, int HT>
 static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
   const int ns = attn_splits(a.P, a.k, a.n_q);
@@ -1046,11 +1215,12 @@ static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
     if (a.latent_fp8)  // the cache scale multiplies every logit and the output
       attn_dma_kernel<HT, true><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
           a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel, a.sel_row,
-          ilog2(a.P), a.k, a.H, scale_log2 * a.kv_scale, ns, (T*)a.out, a.lse, part_o, part_ml, a.kv_scale);
+          ilog2(a.P), a.k, a.H, scale_log2 * a.kv_scale, ns, (T*)a.out, a.lse, part_o, part_ml, a.kv_scale,
+          a.n_q);
     else
       attn_dma_kernel<HT, false><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
           a.latent, a.L, a.bt, a.bt_stride, a.log2_pt, (const T*)a.q, a.q_seq, a.q_pos, a.sel, a.n_sel, a.sel_row,
-          ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml, 1.f);
+          ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml, 1.f, a.n_q);
   } else
 
     attn_kernel<T, V, HT><<<dim3(unsigned(int64_t(a.n_q) * ns)), dim3(AT_THREADS), 0, s>>>(
@@ -1059,19 +1229,23 @@ static kp_status launch_attn_t(const AttnLaunch& a, hipStream_t s) {
         ilog2(a.P), a.k, a.H, scale_log2, ns, (T*)a.out, a.lse, part_o, part_ml);
   kp_status st = check_launch("sparse_mla_attn");
   if (st != KP_OK || ns == 1) return st;
-  const int hpb = CB_THREADS / (a.V / 4);
-  const int64_t cblocks = int64_t(a.n_q) * ((a.H + hpb - 1) / hpb);
-  if (ns <= 8)
-    attn_combine_kernel<T, 8><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H, a.V,
-                                                                                   (T*)a.out, a.lse);
-  else
-    attn_combine_kernel<T, CB_MAXSPLIT><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(
-        part_o, part_ml, ns, a.H, a.V, (T*)a.out, a.lse);
-  return check_launch("sparse_mla_attn (split merge)");
+  return launch_combine<T>(a, ns, part_o, part_ml, s);
 }
 
 kp_status launch_attn(const AttnLaunch& a, hipStream_t s) {
   if (a.n_q == 0) return KP_OK;
+  if (a.mtp) {
+    if (!(a.dtype == KP_DTYPE_BF16 && a.V == 512 && !a.latent_fp8 && a.H <= 64)) {
+      set_error("sparse_mla_attn_mtp: built for bf16 with v_dim 512 and at most 64 heads");
+      return KP_ERR_UNSUPPORTED;
+    }
+    if (attn_splits_mtp(a.P, a.k, a.n_q, a.H) > CB_MAXSPLIT) {
+      set_error("sparse_mla_attn_mtp: topk %d pools of %d tokens needs more than %d splits per query", a.k, a.P,
+                CB_MAXSPLIT);
+      return KP_ERR_UNSUPPORTED;
+    }
+    return launch_attn_mtp(a, s);
+  }
   if (a.latent_fp8 && !(a.dtype == KP_DTYPE_BF16 && a.V == 512)) {
     set_error("sparse_mla_attn_fp8: built for bf16 queries with v_dim 512 only");
     return KP_ERR_UNSUPPORTED;

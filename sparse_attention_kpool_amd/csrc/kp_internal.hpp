@@ -73,6 +73,7 @@ struct AttnLaunch {
   const int32_t* sel;
   const int32_t* n_sel;
   const int32_t* sel_row;  // query i attends selection row sel_row[i] (NULL: row i)
+  int mtp;                 // runs of a target and its draft attending selection row i / 2 (sparse_mla_attn_mtp)
   void* out;
   float* lse;
   void* ws;
@@ -81,6 +82,9 @@ struct AttnLaunch {
 // Number of split-KV partitions per query for a call shape (a pure function of its arguments).
 int attn_splits(int P, int k, int n_q);
 size_t attn_workspace(int P, int k, int H, int V, int n_q, int esize);
+// The same for sparse_mla_attn_mtp's launch (n_q queries in runs of two).
+int attn_splits_mtp(int P, int k, int n_q, int H);
+size_t attn_workspace_mtp(int P, int k, int H, int V, int n_q, int esize);
 kp_status launch_attn(const AttnLaunch& a, hipStream_t s);
 // Device address of the current device's static split-KV scratch (KP_NOALLOC_SCRATCH_BYTES), looked up on the
 // first call per device.

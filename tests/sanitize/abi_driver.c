@@ -39,7 +39,7 @@ static void explained(const char* what) {
 }
 
 int main(void) {
-  CHECK(kp_abi_version() == 5, "abi version");
+  CHECK(kp_abi_version() == 6, "abi version");
   kp_dims d = dims();
   kp_cache c = cache();
   kp_queries q = queries(4, 100);
@@ -103,6 +103,14 @@ int main(void) {
           "shared null sel_row");
     CHECK(sparse_mla_attn_fp8(&d, &c, &q, FAKE, FAKE, FAKE, 0.0f, FAKE, NULL, FAKE, need, NULL) == KP_ERR_INVALID_ARG,
           "fp8 scale 0");
+    { size_t mneed = sparse_mla_mtp_workspace_size(&d, &q);
+      CHECK(mneed > 0, "mtp workspace size");
+      CHECK(sparse_mla_attn_mtp(&d, &c, &q, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, mneed - 16, NULL) == KP_ERR_WORKSPACE,
+            "mtp workspace short");
+      explained("mtp workspace message");
+      kp_dims b = d; b.v_dim = 64;
+      CHECK(sparse_mla_attn_mtp(&b, &c, &q, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, mneed, NULL) == KP_ERR_UNSUPPORTED,
+            "mtp v 64"); }
     { kp_dims b = d; b.topk = 65536; kp_queries q64 = queries(64, 100);
       CHECK(sparse_mla_attn_noalloc(&b, &c, &q64, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == KP_ERR_WORKSPACE,
             "noalloc beyond its scratch"); }

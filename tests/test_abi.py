@@ -21,7 +21,8 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_fp8",
-              "sparse_mla_attn_shared", "sparse_mla_attn_noalloc", "kp_read_rows", "kp_linear", "kp_linear_workspace_size", "kp_linear_group",
+              "sparse_mla_attn_shared", "sparse_mla_attn_noalloc", "sparse_mla_attn_mtp",
+              "sparse_mla_mtp_workspace_size", "kp_read_rows", "kp_linear", "kp_linear_workspace_size", "kp_linear_group",
               "kp_linear_group_workspace_size",
               "dsa_topk_workspace_size", "sparse_mla_workspace_size", "kp_last_error", "kp_abi_version"):
         assert f in names
@@ -136,6 +137,32 @@ def test_noalloc_limits():
     st = lib.sparse_mla_attn_noalloc(ctypes.byref(d), ctypes.byref(_cache()), ctypes.byref(_queries(n_q=4096)),
                                      FAKE, None, FAKE, FAKE, None, None)
     assert st == K.KP_ERR_INVALID_ARG
+
+
+def test_mtp_validation_and_workspace():
+    """sparse_mla_attn_mtp: built for bf16 with v_dim 512; its workspace follows its own split rule (about 256 blocks
+    over the runs' head halves, and at least two splits for a run that lists two queries' pools)."""
+    lib = K.load()
+    d = _dims()
+    ws = lambda n, dd=d: lib.sparse_mla_mtp_workspace_size(ctypes.byref(dd), ctypes.byref(_queries(n_q=n)))
+    per = 64 * (512 * 2 + 8)              # one query's partial per split: H x (V bf16 + (m, l) fp32)
+    assert ws(64) == 64 * 4 * per         # 32 runs x 2 head halves = 64 units: 4 splits
+    assert ws(8) == 8 * 32 * per          # 4 runs: 32 splits (the cap)
+    assert ws(4096) == 4096 * 2 * per     # many runs: still 2 splits, the two-sequence list needs them
+    assert ws(7) == 7 * 32 * per          # an odd count: 4 runs, the last a target alone
+    q = _queries(n_q=64)
+    st = lib.sparse_mla_attn_mtp(ctypes.byref(d), ctypes.byref(_cache()), ctypes.byref(q), FAKE, FAKE, FAKE, FAKE,
+                                 None, FAKE, ws(64) - 16, None)
+    assert st == K.KP_ERR_WORKSPACE and "sparse_mla_attn_mtp" in K.last_error()
+    for bad in (_dims(v_dim=64), _dims(dtype=K.KP_DTYPE_F32, v_dim=64)):
+        st = lib.sparse_mla_attn_mtp(ctypes.byref(bad), ctypes.byref(_cache()), ctypes.byref(q), FAKE, FAKE, FAKE,
+                                     FAKE, None, FAKE, 1 << 40, None)
+        assert st == K.KP_ERR_UNSUPPORTED
+    st = lib.sparse_mla_attn_mtp(ctypes.byref(d), ctypes.byref(_cache()), ctypes.byref(q), FAKE, None, FAKE, FAKE,
+                                 None, FAKE, 1 << 40, None)
+    assert st == K.KP_ERR_INVALID_ARG
+    assert lib.sparse_mla_attn_mtp(ctypes.byref(d), ctypes.byref(_cache()), ctypes.byref(_queries(n_q=0)), None,
+                                   None, None, None, None, None, 0, None) == K.KP_OK
 
 
 def test_workspace_sizes_follow_the_split_rule():

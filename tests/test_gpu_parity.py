@@ -351,6 +351,57 @@ def test_mtp_shared_selection():
     _free()
 
 
+def test_mtp_runs_one_gather():
+    """sparse_mla_attn_mtp: queries 2r (target) and 2r + 1 (draft) attend selection row r.  Runs of one sequence
+    (targets at T-2, drafts at T-1; the draft at 9000 starts a pool the target could not select), a run whose two
+    queries are of different sequences (each query's rows listed on their own), and an odd last run (a target
+    alone).  Every query matches the oracle over the tokens sparse_mla_attn_shared with sel_row[i] = i // 2 would
+    give it, and that call within the attention tolerance; nothing is written outside out / lse."""
+    import sparse_attention_kpool_amd as K
+    from harness import Guarded
+    ctx = [37, 1000, 4099, 9001, 20000, 3000, 512]
+    q_seq = [0, 0, 1, 1, 2, 2, 3, 3, 4, 5, 6]
+    q_pos = [35, 36, 998, 999, 4097, 4098, 8999, 9000, 19998, 2999, 511]
+    base = ks.workloads()["batch64"]
+    wl = ks.scaled(base, name="mtp_runs", ctx=ctx, new_from=[t - 2 for t in ctx],
+                   q_seq=np.array(q_seq, np.int32), q_pos=np.array(q_pos, np.int32), page_perm_seed=11)
+    n_q, n_runs = wl.n_q, (wl.n_q + 1) // 2
+    _say(f"[case mtp_runs] n_q={n_q} runs={n_runs}")
+    run = DeviceRun(wl).run()
+    targets = torch.arange(0, n_q, 2, device="cuda")
+    sel = run.layer.sel[:n_q][targets].contiguous()
+    n_sel = run.layer.n_sel[:n_q][targets].contiguous()
+    ws_n = K.sparse_mla_mtp_workspace_size(run.dims, run.queries)
+    ws = torch.empty(max(ws_n // 4, 4), dtype=torch.float32, device="cuda")
+    g_out = Guarded((n_q, wl.H, wl.V), torch.bfloat16, "cuda")
+    g_lse = Guarded((n_q, wl.H), torch.float32, "cuda")
+    K.sparse_mla_attn_mtp(run.dims, run.cache, run.queries, run.q, sel, n_sel, g_out.t, lse=g_lse.t, workspace=ws)
+    torch.cuda.synchronize()
+    assert g_out.intact() and g_lse.intact(), "sparse_mla_attn_mtp wrote outside out / lse"
+    out, lse = g_out.t, g_lse.t
+    # the same sets through sparse_mla_attn_shared
+    sel_row = torch.arange(n_q, device="cuda", dtype=torch.int32) // 2
+    out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+    K.sparse_mla_attn_shared(run.dims, run.cache, run.queries, run.q, sel, n_sel, sel_row, out2, lse=lse2,
+                             workspace=run.layer.ws_attn)
+    torch.cuda.synchronize()
+    tol_abs, tol_rel = attn_tolerance(wl.dtype)
+    for i in range(n_q):
+        s, p = q_seq[i], q_pos[i]
+        sel_t, ns = run.sel_row(2 * (i // 2))
+        toks = O.shared_attended_tokens(sel_t[:ns], p, wl.P)
+        ref_out, ref_lse = O.sparse_mla(ks.host_q(wl, s, p)[0], ks.host_latent(wl, s, toks), wl.scale, wl.V)
+        for name, o, l in (("mtp", out, lse), ("shared", out2, lse2)):
+            got = o[i].float().cpu().numpy()
+            assert np.abs(got - ref_out).max() <= tol_abs, f"{name} query {i}: max-abs"
+            assert rel_rms(got, ref_out) <= tol_rel, f"{name} query {i}: rel-RMS"
+            np.testing.assert_allclose(l[i].cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-3, err_msg=f"{name} q {i}")
+        assert p in set(toks.tolist()), f"query {i} must attend itself"
+    assert 9000 // wl.P not in set(run.sel_row(6)[0][:run.sel_row(6)[1]].tolist())
+    del run
+    _free()
+
+
 def test_compress_plain_mean():
     """Pooling without the learned weights (gates and ape NULL) against the oracle's plain mean: bit-exact on
     dyadic keys (every step exact in fp32), within one bf16 ulp on random bf16 keys; and NULL gates / ape write
