@@ -1027,11 +1027,12 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s per (query, head), with
 // M the max of m_s over non-empty splits, both sums taken in split order.  Each split's O is stored in the cache
-// dtype (rounded once, as the output is), its (m, l) in fp32.  128 threads per block, 4 channels per thread, V / 4
-// threads per head.  Every thread issues the loads of all its splits' partial O and (m, l) at once (PER >= the
-// split count registers of each; an empty split's O was never written, so its value is dropped by a select) and
-// computes its head's weights itself: no LDS, no barrier, one wait on memory.
-constexpr int CB_THREADS = 128;
+// dtype (rounded once, as the output is), its (m, l) in fp32.  Each thread merges 16 bytes of channels (8 bf16 or
+// 4 fp32) of one head, V / that many threads per head, 256 threads per block.  Every thread issues the loads of
+// all its splits' partial O and (m, l) at once (PER >= the split count registers of each; an empty split's O was
+// never written, so its value is dropped by a select) and computes its head's weights itself: no LDS, no barrier,
+// one wait on memory.
+constexpr int CB_THREADS = 256;
 constexpr int CB_MAXSPLIT = 32;  // attn_splits never returns more
 
 template <class T, int PER>
@@ -1040,26 +1041,25 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __res
                                                                   int H, int V, T* __restrict__ out,
                                                                   float* __restrict__ lse) {
   static_assert(PER <= CB_MAXSPLIT, "splits per thread");
-  // raw 4-channel partial: 4 bf16 in two dwords, or 4 floats
-  using Raw = typename std::conditional<sizeof(T) == 2, uint2, f32x4>::type;
-  const int tph = V / 4;                    // threads per head
+  constexpr int EPT = 16 / int(sizeof(T));  // channels per thread
+  const int tph = V / EPT;                  // threads per head
   const int hpb = CB_THREADS / tph;         // heads per block
   const int bpq = (H + hpb - 1) / hpb;      // blocks per query
   const int qi = blockIdx.x / bpq;
   const int tid = threadIdx.x;
   const int h = (blockIdx.x - qi * bpq) * hpb + tid / tph;
-  const int c = (tid % tph) * 4;
+  const int c = (tid % tph) * EPT;
   const int64_t mls = int64_t(H) * 2, pos_ = int64_t(H) * V;
   if (h >= H) return;
   const int64_t row = int64_t(qi) * n_split * H + h;  // split s: O at part_o + (row + s * H) * V, (m, l) likewise
   const T* po = part_o + row * V + c;
   const float* pm = part_ml + row * 2;
-  Raw o[PER];
+  u32x4 o[PER];
   float2 ml[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     if (u < n_split) {
-      o[u] = *reinterpret_cast<const Raw*>(po + u * pos_);
+      o[u] = *reinterpret_cast<const u32x4*>(po + u * pos_);
       ml[u] = *reinterpret_cast<const float2*>(pm + u * mls);
     }
   }
@@ -1068,30 +1068,37 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __res
   for (int u = 0; u < PER; ++u)
     if (u < n_split && ml[u].y > 0.f) M = fmaxf(M, ml[u].x);
   float wsum = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     if (u < n_split && ml[u].y > 0.f) {
       const float w = exp2f(ml[u].x - M);
       wsum += ml[u].y * w;
-      f32x4 v;
-      if constexpr (sizeof(T) == 2) {
-        v = f32x4{__uint_as_float(o[u].x << 16), __uint_as_float(o[u].x & 0xffff0000u),
-                  __uint_as_float(o[u].y << 16), __uint_as_float(o[u].y & 0xffff0000u)};
-      } else {
-        v = o[u];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        float v;
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t d = o[u][e / 2];
+          v = __uint_as_float((e & 1) ? (d & 0xffff0000u) : (d << 16));
+        } else {
+          v = __uint_as_float(o[u][e]);
+        }
+        acc[e] += w * v;
       }
-      acc += w * v;
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;  // a query that attends no token: zeros, lse -inf
-  T* op = out + (int64_t(qi) * H + h) * V + c;
+  u32x4 r;
   if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
-                                               pack_bf16x2(acc[2] * inv, acc[3] * inv));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
   } else {
-    *reinterpret_cast<float4*>(op) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = __float_as_uint(acc[e] * inv);
   }
+  *reinterpret_cast<u32x4*>(out + (int64_t(qi) * H + h) * V + c) = r;
   if (lse && c == 0) lse[int64_t(qi) * H + h] = wsum > 0.f ? (M + log2f(wsum)) * LN2 : -INFINITY;
 }
 
@@ -1166,7 +1173,7 @@ kp_status attn_noalloc_scratch(void** ptr) {
 // Split merge of n_q queries' partials (ns splits each) into out / lse.
 template <class T>
 static kp_status launch_combine(const AttnLaunch& a, int ns, const T* part_o, const float* part_ml, hipStream_t s) {
-  const int hpb = CB_THREADS / (a.V / 4);
+  const int hpb = CB_THREADS / (a.V / (16 / int(sizeof(T))));
   const int64_t cblocks = int64_t(a.n_q) * ((a.H + hpb - 1) / hpb);
   if (ns <= 8)
     attn_combine_kernel<T, 8><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H, a.V,
