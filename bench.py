@@ -246,7 +246,9 @@ class Leg:
         self.torch.cuda.empty_cache()
 
 
-STAGE_KERNELS = {"score": ["kp::score_decode_kernel<kp::bf16, 128>"],
+STAGE_KERNELS = {"compress": ["kp::compress_kernel<kp::bf16>"],
+                 "score": ["kp::score_decode_kernel<kp::bf16, 128>"],
+                 "topk": ["kp::topk_chunk_kernel<16>", "kp::topk_merge_kernel<16, true>"],
                  "attend": ["kp::attn_dma_kernel<4, false, false>", "kp::attn_combine_kernel<kp::bf16, 8>"]}
 
 
@@ -616,6 +618,11 @@ def main():
         res["stages_ms"] = {k: round(v, 5) for k, v in st.items()}
         res["stage_bytes"] = by
         res["roofline"] = roofline(st, by)
+        meas = [measured_traffic(k) for k in STAGE_KERNELS]
+        # the step's HBM bytes as the counters measured them (profiles/), over the same step time; None once any of
+        # the step's kernels changed since the counters were taken
+        res["hbm_gbs_measured"] = (round(sum(meas) / (ms * 1e-3) / 1e9, 1) if all(m is not None for m in meas)
+                                   else None)
         if "ceiling" in legs:
             # what HBM delivers for the step's own access patterns, read-only, nothing else running: the
             # attended tokens' value rows and the scanned pooled-key pages
@@ -707,6 +714,17 @@ def main():
         res["prefill_indexer"] = {"tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
                                   "ms": round(st["score"], 4), "flops": fl, "step_ms": round(ms, 4),
                                   "stages_ms": {k: round(v, 4) for k, v in st.items()}}
+        # the prefill attention: 2 H (V + V) flop per (query, attended token), tokens counted from the step's own
+        # selection (each selected pool cut at the query)
+        L = leg.layer
+        sel = L.sel[:wp.n_q].long()
+        pos = leg.d.q_pos.long()[:, None]
+        nt = torch.clamp(pos - wp.P * sel + 1, 0, wp.P) * (sel >= 0)
+        pairs = int(nt.sum().item())
+        afl = 2 * wp.H * 2 * wp.V * pairs
+        atf = afl / (st["attend"] * 1e-3) / 1e12
+        res["prefill_attention"] = {"tflops": round(atf, 2), "frac_of_bf16_peak": round(atf / BF16_PEAK_TFLOPS, 4),
+                                    "ms": round(st["attend"], 4), "flops": afl, "query_token_pairs": pairs}
         leg.free()
     if "proj" in legs:
         print("[bench] proj leg: the five projections at 64 tokens (decode) and 4096 tokens (prefill)",
@@ -730,6 +748,8 @@ def main():
         ms = e0.elapsed_time(e1) / reps
         res["copy"] = {"bytes_moved": 2 * 4 * n, "ms": round(ms, 4),
                        "gbs": round(2 * 4 * n / (ms * 1e-3) / 1e9, 1)}
+        if res.get("hbm_gbs"):   # the decode step against what a plain copy reaches on this machine
+            res["hbm_frac_of_copy"] = round(res["hbm_gbs"] / res["copy"]["gbs"], 4)
         del src, dst
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

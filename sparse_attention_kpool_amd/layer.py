@@ -17,7 +17,7 @@ import torch
 from . import (KP_DTYPE_BF16, KP_DTYPE_F32, Cache, Dims, Queries, absorb_product, dsa_indexer_score,
                dsa_topk_select, dsa_topk_workspace_size, indexer_products, kpool_compress, linear_group,
                linear_shapes_workspace_size, mla_unabsorb_o, sparse_mla_attn, sparse_mla_attn_fp8,
-               sparse_mla_workspace_size)
+               sparse_mla_attn_mtp, sparse_mla_mtp_workspace_size, sparse_mla_workspace_size)
 
 
 @dataclass
@@ -32,7 +32,9 @@ class CompressInput:
 
 
 class KPoolDSALayer:
-    def __init__(self, dims: Dims, device, max_q: int, max_pos: int):
+    """``mtp=True`` also sizes the workspace of ``verify_step`` (MTP verification: targets and their drafts)."""
+
+    def __init__(self, dims: Dims, device, max_q: int, max_pos: int, mtp: bool = False):
         self.dims = dims
         self.device = torch.device(device)
         n_pool_max = (max_pos + 1) // dims.pool
@@ -51,6 +53,13 @@ class KPoolDSALayer:
             need_attn = max(need_attn, sparse_mla_workspace_size(dims, qn))
         self.ws_topk = self._ws(need_topk)
         self.ws_attn = self._ws(need_attn)
+        self.ws_mtp = None
+        if mtp:
+            need_mtp = max(sparse_mla_mtp_workspace_size(dims, Queries(seq=probe.seq[:n], pos=probe.pos[:n],
+                                                                       max_pos=max_pos))
+                           for n in range(1, max_q + 1))
+            self.ws_mtp = self._ws(need_mtp)
+        self.mtp = mtp
         self.max_q, self.max_pos = max_q, max_pos
 
     def _ws(self, nbytes: int):
@@ -75,6 +84,26 @@ class KPoolDSALayer:
         else:
             sparse_mla_attn(self.dims, cache, queries, q, self.sel[:n_q], self.n_sel[:n_q], out, lse=lse,
                             workspace=self.ws_attn)
+
+    def verify_step(self, cache: Cache, queries: Queries, targets: Queries, q_idx, w, q, out, lse=None,
+                    compress: Optional[CompressInput] = None) -> None:
+        """MTP verification: ``queries`` holds runs of a target (entry 2r) and its draft (entry 2r + 1); ``targets``
+        holds the targets alone (entry r = queries' entry 2r), with their index queries ``q_idx`` and head weights
+        ``w``.  The targets are scored and selected; then every query attends its run's selection through
+        sparse_mla_attn_mtp (one gather per run).  ``q``, ``out``, ``lse`` are per query of ``queries``."""
+        if not self.mtp:
+            raise ValueError("verify_step needs a layer built with mtp=True")
+        n_q, n_t = int(queries.seq.numel()), int(targets.seq.numel())
+        if n_q > self.max_q or n_t != (n_q + 1) // 2 or max(queries.max_pos, targets.max_pos) > self.max_pos:
+            raise ValueError("call shape exceeds the layer's allocation, or targets are not one per run")
+        if compress is not None and compress.pool_seq.numel() > 0:
+            kpool_compress(self.dims, cache, compress.keys, compress.gates, compress.ape, compress.pool_seq,
+                           compress.pool_id, src=compress.src)
+        dsa_indexer_score(self.dims, cache, targets, q_idx, w, self.scores[:n_t])
+        dsa_topk_select(self.dims, targets, self.scores[:n_t], self.sel[:n_t], self.n_sel[:n_t],
+                        workspace=self.ws_topk)
+        sparse_mla_attn_mtp(self.dims, cache, queries, q, self.sel[:n_t], self.n_sel[:n_t], out, lse=lse,
+                            workspace=self.ws_mtp)
 
 
 @dataclass

@@ -398,7 +398,19 @@ def test_mtp_runs_one_gather():
             np.testing.assert_allclose(l[i].cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-3, err_msg=f"{name} q {i}")
         assert p in set(toks.tolist()), f"query {i} must attend itself"
     assert 9000 // wl.P not in set(run.sel_row(6)[0][:run.sel_row(6)[1]].tolist())
-    del run
+    # the layer's verification step (score and select the targets alone, then one gather per run) writes the same
+    # bits as the calls above
+    from sparse_attention_kpool_amd.layer import KPoolDSALayer
+    d = run.inputs
+    tq = K.Queries(seq=d.q_seq[0::2].contiguous(), pos=d.q_pos[0::2].contiguous(), max_pos=wl.max_pos(), group=1)
+    layer = KPoolDSALayer(run.dims, "cuda", max_q=n_q, max_pos=wl.max_pos(), mtp=True)
+    out3, lse3 = torch.empty_like(out), torch.empty_like(lse)
+    layer.verify_step(run.cache, run.queries, tq, run.q_idx[0::2].contiguous(), run.w[0::2].contiguous(), run.q,
+                      out3, lse=lse3)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.sel[:n_runs], sel) and torch.equal(layer.n_sel[:n_runs], n_sel)
+    assert torch.equal(out3, out) and torch.equal(lse3, lse), "verify_step differs from the direct calls"
+    del run, layer
     _free()
 
 
