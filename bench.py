@@ -4,7 +4,8 @@
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--legs decode,ceiling,32k,...]
 
 A step is one pass of the whole layer -- kpool_compress (pools completing this step) -> dsa_indexer_score ->
-dsa_topk_select -> sparse_mla_attn -- over one batch, enqueued on one stream through the C ABI.
+dsa_topk_select -> sparse_mla_attn -- over one batch, enqueued on one stream through the C ABI (a decode step
+pools and scores in one launch: dsa_compress_score).
 
 Legs (inputs are seeded synthetic data already resident in HBM when timing starts):
   decode   the headline: 64 sequences, contexts U[8192, 131072] (seed 3, up to 128K), paged 64-token pages,
@@ -63,7 +64,8 @@ def decode_bytes(wl) -> dict:
       topk      per query: the selection written, k*4
       attend    per query: the V-wide value columns of every attended token V*les*|S| (les = 1 for an fp8
                 latent cache, else es), the query's nope part H*V*es, the output H*V*es, the selection read k*4
-    Score rows and split-KV partials are intermediate traffic, not algorithmic."""
+    Score rows and split-KV partials are intermediate traffic, not algorithmic.  A decode step pools in its scoring
+    launch (dsa_compress_score), so its score stage moves the compress bytes too (see fused_stage_bytes)."""
     es = 2 if wl.dtype == "bf16" else 4
     les = 1 if wl.latent_fp8 else es
     P, D, Hi, k, H, V = wl.P, wl.D, wl.Hi, wl.k, wl.H, wl.V
@@ -75,6 +77,11 @@ def decode_bytes(wl) -> dict:
         out["topk"] += k * 4
         out["attend"] += V * les * attended(pos, P, k) + 2 * H * V * es + k * 4
     return out
+
+
+def fused_stage_bytes(by: dict) -> dict:
+    """decode_bytes by stage as a decode step launches them: pooling folded into the scoring launch."""
+    return {"score": by["score"] + by["compress"], "topk": by["topk"], "attend": by["attend"]}
 
 
 def prefill_flops(wl) -> int:
@@ -156,33 +163,44 @@ class Leg:
         del g
         return {"mean": per[0], "median": float(np.median(per)), "min": min(per)}
 
-    def time_stages(self, steps: int) -> dict:
-        """Mean ms per stage, events recorded between the four calls on the launch stream."""
+    def time_stages(self, steps: int, split_compress: bool = False) -> dict:
+        """Mean ms per stage, events recorded between the calls on the launch stream.  Stages as the layer step
+        launches them: `score` is the step's pooling and scoring (dsa_compress_score: one launch for a decode
+        batch); split_compress times kpool_compress on its own first (`compress`) and `score` without it.  The
+        steps are enqueued back to back with one synchronisation at the end, so the host runs ahead of the device
+        and no stage includes the device waiting for a launch."""
         torch, K, L = self.torch, self.K, self.layer
         n_q = self.wl.n_q
-        names = ["compress", "score", "topk", "attend"]
-        acc = dict.fromkeys(names, 0.0)
+        names = (["compress"] if split_compress else []) + ["score", "topk", "attend"]
+        c = self.compress
+        evs = []
+        torch.cuda.synchronize()
         for i in range(steps):
             cache = self.caches[i % len(self.caches)]
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
             ev[0].record()
-            c = self.compress
-            if c is not None:
-                K.kpool_compress(self.dims, cache, c.keys, c.gates, c.ape, c.pool_seq, c.pool_id, src=c.src)
-            ev[1].record()
-            K.dsa_indexer_score(self.dims, cache, self.queries, self.d.q_idx, self.d.w, L.scores[:n_q])
-            ev[2].record()
+            if split_compress:
+                if c is not None:
+                    K.kpool_compress(self.dims, cache, c.keys, c.gates, c.ape, c.pool_seq, c.pool_id, src=c.src)
+                ev[1].record()
+                K.dsa_indexer_score(self.dims, cache, self.queries, self.d.q_idx, self.d.w, L.scores[:n_q])
+            else:
+                L._compress_score(cache, c, self.queries, self.d.q_idx, self.d.w, L.scores[:n_q])
+            ev[len(names) - 2].record()
             K.dsa_topk_select(self.dims, self.queries, L.scores[:n_q], L.sel[:n_q], L.n_sel[:n_q],
                               workspace=L.ws_topk)
-            ev[3].record()
+            ev[len(names) - 1].record()
             if cache.latent.dtype == torch.uint8:
                 K.sparse_mla_attn_fp8(self.dims, cache, self.queries, self.d.q, L.sel[:n_q], L.n_sel[:n_q],
                                       cache.latent_scale, self.out, lse=self.lse, workspace=L.ws_attn)
             else:
                 K.sparse_mla_attn(self.dims, cache, self.queries, self.d.q, L.sel[:n_q], L.n_sel[:n_q], self.out,
                                   lse=self.lse, workspace=L.ws_attn)
-            ev[4].record()
-            torch.cuda.synchronize()
+            ev[len(names)].record()
+            evs.append(ev)
+        torch.cuda.synchronize()
+        acc = dict.fromkeys(names, 0.0)
+        for ev in evs:
             for j, n in enumerate(names):
                 acc[n] += ev[j].elapsed_time(ev[j + 1])
         return {n: acc[n] / steps for n in names}
@@ -246,8 +264,8 @@ class Leg:
         self.torch.cuda.empty_cache()
 
 
-STAGE_KERNELS = {"compress": ["kp::compress_kernel<kp::bf16>"],
-                 "score": ["kp::score_decode_kernel<kp::bf16, 128>"],
+# the batch-64 decode step's kernels by stage (the scorer pools the step's completed pools in the same launch)
+STAGE_KERNELS = {"score": ["kp::score_decode_kernel<kp::bf16, 128, true>"],
                  "topk": ["kp::topk_chunk_kernel<16>", "kp::topk_merge_kernel<16, true>"],
                  "attend": ["kp::attn_dma_kernel<4, false, false>", "kp::attn_combine_kernel<kp::bf16, 8>"]}
 
@@ -607,7 +625,7 @@ def main():
         t = leg.time_steps_graph(args.steps, args.warmup)
         ms = t["mean"]
         st = leg.time_stages(args.steps)
-        by = decode_bytes(wl)
+        by = fused_stage_bytes(decode_bytes(wl))
         tot = sum(by.values())
         res.update(value=round(wl.n_q / (ms * 1e-3), 1), ms_per_step=round(ms, 5))
         res["ms_per_step_median"], res["ms_per_step_min"] = round(t["median"], 5), round(t["min"], 5)
@@ -649,7 +667,7 @@ def main():
         t = leg.time_steps_graph(n, args.warmup)
         ms = t["mean"]
         st = leg.time_stages(n)
-        by = decode_bytes(w1)
+        by = fused_stage_bytes(decode_bytes(w1))
         gbs = sum(by.values()) / (ms * 1e-3) / 1e9
         res[key] = {"tokens_per_s": round(1 / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
                     "ms_per_step_median": round(t["median"], 5), "ms_per_step_min": round(t["min"], 5),
@@ -671,7 +689,7 @@ def main():
         t = leg.time_steps_graph(args.steps, args.warmup)
         ms = t["mean"]
         st = leg.time_stages(args.steps)
-        by = decode_bytes(w5)
+        by = fused_stage_bytes(decode_bytes(w5))
         gbs = sum(by.values()) / (ms * 1e-3) / 1e9
         res["long1m"] = {"tokens_per_s": round(w5.n_q / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
                          "ms_per_step_median": round(t["median"], 5), "ms_per_step_min": round(t["min"], 5),
@@ -696,7 +714,7 @@ def main():
         t = leg.time_steps_graph(args.steps, args.warmup)
         ms = t["mean"]
         st = leg.time_stages(args.steps)
-        by = decode_bytes(w8)
+        by = fused_stage_bytes(decode_bytes(w8))
         gbs = sum(by.values()) / (ms * 1e-3) / 1e9
         res["decode_fp8_latent"] = {"tokens_per_s": round(w8.n_q / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
                                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -708,7 +726,7 @@ def main():
         wp = W["prefill64k"]
         leg = Leg(wp, copies=1)
         ms = leg.time_steps(max(3, args.steps // 4), 2)["mean"]
-        st = leg.time_stages(max(3, args.steps // 4))
+        st = leg.time_stages(max(3, args.steps // 4), split_compress=True)
         fl = prefill_flops(wp)
         tf = fl / (st["score"] * 1e-3) / 1e12
         res["prefill_indexer"] = {"tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),

@@ -136,6 +136,25 @@ kp_status dsa_indexer_score(const kp_dims* dims, const kp_cache* cache, const kp
                             const void* q_idx, const float* w, float* scores, int64_t ld_scores, void* stream);
 
 /*
+ * dsa_compress_score -- kpool_compress followed by dsa_indexer_score, as one call.
+ *   [llama.cpp PR, "What I implemented new": a decode step pools the keys of the tokens that complete a pool, then
+ *   the indexer scores the pools]; [MAX glm5_next API page, per-request state: indexer tail rings, read here as
+ *   each sequence's pending rows of its incomplete pool].  The arguments are kpool_compress's (dims, cache,
+ *   n_pools .. pool_id) then dsa_indexer_score's (queries .. ld_scores), with the same meaning, layouts and checks.
+ *   The results are exactly those of the two calls in that order: the pooled rows written, and scores computed
+ *   over the cache with those rows in it.
+ *   A decode batch (queries->group < 8) with 1 .. 64 pools to pool takes ONE launch: the scorer pools those
+ *   entries itself (the rows are still written to the cache), saving the second launch and the wait between the
+ *   two kernels.  Anything else runs the two kernels in order.  In either case the rows of the listed pools must
+ *   not be read or written by other work in flight.
+ *   Errors: those of kpool_compress and dsa_indexer_score; nothing is launched on an error.
+ */
+kp_status dsa_compress_score(const kp_dims* dims, const kp_cache* cache, int32_t n_pools, const void* keys,
+                             const void* gates, const int32_t* src, const void* ape, const int32_t* pool_seq,
+                             const int32_t* pool_id, const kp_queries* queries, const void* q_idx, const float* w,
+                             float* scores, int64_t ld_scores, void* stream);
+
+/*
  * dsa_topk_select -- causal top-k pools of each query, the incomplete tail forced.
  *   [MAX glm5_next API page, index_kpool_always_select_tail: the incomplete trailing pool is always visible];
  *   [llama.cpp PR, "What I implemented new": always keeps the incomplete tail]; [GLM-5.3-Flash model card,

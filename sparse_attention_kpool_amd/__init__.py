@@ -21,9 +21,9 @@ LIB_PATH = os.path.join(PKG, "libkpool.so")
 
 KP_OK, KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED, KP_ERR_WORKSPACE, KP_ERR_LAUNCH = 0, -1, -2, -3, -4
 KP_DTYPE_F32, KP_DTYPE_BF16 = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
-EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk_select",
+EXPORTED = ("kpool_compress", "dsa_indexer_score", "dsa_compress_score", "dsa_topk_workspace_size", "dsa_topk_select",
             "sparse_mla_workspace_size", "sparse_mla_attn", "sparse_mla_attn_shared", "sparse_mla_attn_fp8",
             "sparse_mla_attn_noalloc", "sparse_mla_mtp_workspace_size", "sparse_mla_attn_mtp", "kp_read_rows",
             "kp_linear", "kp_linear_workspace_size", "kp_linear_group", "kp_linear_group_workspace_size",
@@ -81,6 +81,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     D, C, Q = ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.POINTER(_Queries)
     lib.kpool_compress.argtypes = [D, C, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.dsa_indexer_score.argtypes = [D, C, Q, vp, vp, vp, i64, vp]
+    lib.dsa_compress_score.argtypes = [D, C, i32, vp, vp, vp, vp, vp, vp, Q, vp, vp, vp, i64, vp]
     lib.dsa_topk_workspace_size.argtypes = [D, Q]
     lib.dsa_topk_workspace_size.restype = sz
     lib.dsa_topk_select.argtypes = [D, Q, vp, i64, vp, vp, vp, sz, vp]
@@ -102,7 +103,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kp_linear_group.argtypes = [i32, LP, vp, sz, vp]
     lib.kp_linear_group_workspace_size.argtypes = [i32, LP]
     lib.kp_linear_group_workspace_size.restype = sz
-    for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_shared",
+    for f in ("kpool_compress", "dsa_indexer_score", "dsa_compress_score", "dsa_topk_select", "sparse_mla_attn",
+              "sparse_mla_attn_shared",
               "sparse_mla_attn_fp8", "sparse_mla_attn_noalloc", "sparse_mla_attn_mtp", "kp_read_rows", "kp_linear",
               "kp_linear_group"):
         getattr(lib, f).restype = ctypes.c_int
@@ -228,10 +230,8 @@ def _check_queries(fn: str, queries: "Queries") -> int:
 # ----------------------------------------------------------------------------------------------------------
 # the four calls
 # ----------------------------------------------------------------------------------------------------------
-def kpool_compress(dims: Dims, cache: Cache, keys, gates, ape, pool_seq, pool_id, src=None, stream=None) -> None:
-    """Pooled keys of complete pools -> rows (pool_seq[i], pool_id[i]) of cache.pooled (see include/kpool.h)."""
-    import torch
-    fn = "kpool_compress"
+def _compress_args(fn, dims: Dims, cache: Cache, keys, gates, ape, pool_seq, pool_id, src) -> int:
+    """Checks kpool_compress's tensors; returns n_pools."""
     n = int(pool_seq.numel())
     st = _storage(dims)
     _want(fn, "pool_seq", pool_seq, _i32(), (n,))
@@ -247,6 +247,21 @@ def kpool_compress(dims: Dims, cache: Cache, keys, gates, ape, pool_seq, pool_id
             _want(fn, "src", src, _i32(), (n,))
         elif keys.shape[0] < n:
             raise ValueError(f"{fn}: keys holds {keys.shape[0]} pools, fewer than the {n} to compress")
+    return n
+
+
+def _score_args(fn, dims: Dims, cache: Cache, queries: Queries, q_idx, w, scores) -> None:
+    import torch
+    n = _check_queries(fn, queries)
+    _want(fn, "q_idx", q_idx, _storage(dims), (n, dims.idx_heads, dims.idx_dim), min_rows=True)
+    _want(fn, "w", w, (torch.float32,), (n, dims.idx_heads), min_rows=True)
+    _want(fn, "scores", scores, (torch.float32,), (n, None), rows_only=True, min_rows=True)
+    _want(fn, "cache.pooled", cache.pooled, _storage(dims), (None, dims.page_tokens // dims.pool, dims.idx_dim))
+
+
+def kpool_compress(dims: Dims, cache: Cache, keys, gates, ape, pool_seq, pool_id, src=None, stream=None) -> None:
+    """Pooled keys of complete pools -> rows (pool_seq[i], pool_id[i]) of cache.pooled (see include/kpool.h)."""
+    n = _compress_args("kpool_compress", dims, cache, keys, gates, ape, pool_seq, pool_id, src)
     _check("kpool_compress", load().kpool_compress(ctypes.byref(dims.c()), ctypes.byref(cache.c()), n,
                                                    _ptr(keys), _ptr(gates), _ptr(src), _ptr(ape), _ptr(pool_seq),
                                                    _ptr(pool_id), _stream(stream)))
@@ -254,16 +269,23 @@ def kpool_compress(dims: Dims, cache: Cache, keys, gates, ape, pool_seq, pool_id
 
 def dsa_indexer_score(dims: Dims, cache: Cache, queries: Queries, q_idx, w, scores, stream=None) -> None:
     """scores[q, p] for p < (pos[q] + 1) / P; scores is fp32 [n_q, ld]."""
-    import torch
-    fn = "dsa_indexer_score"
-    n = _check_queries(fn, queries)
-    _want(fn, "q_idx", q_idx, _storage(dims), (n, dims.idx_heads, dims.idx_dim), min_rows=True)
-    _want(fn, "w", w, (torch.float32,), (n, dims.idx_heads), min_rows=True)
-    _want(fn, "scores", scores, (torch.float32,), (n, None), rows_only=True, min_rows=True)
-    _want(fn, "cache.pooled", cache.pooled, _storage(dims), (None, dims.page_tokens // dims.pool, dims.idx_dim))
+    _score_args("dsa_indexer_score", dims, cache, queries, q_idx, w, scores)
     _check("dsa_indexer_score", load().dsa_indexer_score(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
                                                          ctypes.byref(queries.c()), _ptr(q_idx), _ptr(w),
                                                          _ptr(scores), int(scores.stride(0)), _stream(stream)))
+
+
+def dsa_compress_score(dims: Dims, cache: Cache, keys, gates, ape, pool_seq, pool_id, queries: Queries, q_idx, w,
+                       scores, src=None, stream=None) -> None:
+    """kpool_compress(...) then dsa_indexer_score(...) as one call: a decode batch with at most 64 pools to pool
+    takes one launch (see include/kpool.h)."""
+    fn = "dsa_compress_score"
+    n = _compress_args(fn, dims, cache, keys, gates, ape, pool_seq, pool_id, src)
+    _score_args(fn, dims, cache, queries, q_idx, w, scores)
+    _check(fn, load().dsa_compress_score(ctypes.byref(dims.c()), ctypes.byref(cache.c()), n, _ptr(keys),
+                                         _ptr(gates), _ptr(src), _ptr(ape), _ptr(pool_seq), _ptr(pool_id),
+                                         ctypes.byref(queries.c()), _ptr(q_idx), _ptr(w), _ptr(scores),
+                                         int(scores.stride(0)), _stream(stream)))
 
 
 def dsa_topk_workspace_size(dims: Dims, queries: Queries) -> int:

@@ -90,14 +90,15 @@ using namespace kp;
 
 extern "C" {
 
-int32_t kp_abi_version(void) { return 6; }
+int32_t kp_abi_version(void) { return 7; }
 
 const char* kp_last_error(void) { return g_err; }
 
-kp_status kpool_compress(const kp_dims* dims, const kp_cache* cache, int32_t n_pools, const void* keys,
-                         const void* gates, const int32_t* src, const void* ape, const int32_t* pool_seq,
-                         const int32_t* pool_id, void* stream) {
-  const char* fn = "kpool_compress";
+// Validation and launch record of kpool_compress (KP_OK with a.n_pools == 0: nothing to pool).
+static kp_status compress_prepare(const char* fn, const kp_dims* dims, const kp_cache* cache, int32_t n_pools,
+                                  const void* keys, const void* gates, const int32_t* src, const void* ape,
+                                  const int32_t* pool_seq, const int32_t* pool_id, CompressLaunch& a) {
+  a = CompressLaunch{};
   kp_status st = check_dims(dims, fn);
   if (st != KP_OK) return st;
   st = check_cache(cache, false, true, fn);
@@ -107,7 +108,6 @@ kp_status kpool_compress(const kp_dims* dims, const kp_cache* cache, int32_t n_p
   KP_REQUIRE(keys && pool_seq && pool_id, KP_ERR_INVALID_ARG, "%s: NULL input", fn);
   KP_REQUIRE(aligned(keys) && (!gates || aligned(gates)) && (!ape || aligned(ape)), KP_ERR_INVALID_ARG,
              "%s: misaligned input", fn);
-  CompressLaunch a{};
   a.dtype = dims->dtype;
   a.P = dims->pool;
   a.D = dims->idx_dim;
@@ -122,12 +122,13 @@ kp_status kpool_compress(const kp_dims* dims, const kp_cache* cache, int32_t n_p
   a.pool_id = pool_id;
   a.pooled = cache->pooled;
   a.bt = cache->block_table;
-  return launch_compress(a, (hipStream_t)stream);
+  return KP_OK;
 }
 
-kp_status dsa_indexer_score(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries,
-                            const void* q_idx, const float* w, float* scores, int64_t ld_scores, void* stream) {
-  const char* fn = "dsa_indexer_score";
+// Validation and launch record of dsa_indexer_score (KP_OK with a.n_q == 0: nothing to score).
+static kp_status score_prepare(const char* fn, const kp_dims* dims, const kp_cache* cache, const kp_queries* queries,
+                               const void* q_idx, const float* w, float* scores, int64_t ld_scores, ScoreLaunch& a) {
+  a = ScoreLaunch{};
   kp_status st = check_dims(dims, fn);
   if (st != KP_OK) return st;
   st = check_queries(queries, fn);
@@ -145,7 +146,6 @@ kp_status dsa_indexer_score(const kp_dims* dims, const kp_cache* cache, const kp
              (long long)ld_scores, (long long)need);
   KP_REQUIRE(ld_scores % 4 == 0, KP_ERR_INVALID_ARG, "%s: ld_scores %lld is not a multiple of 4", fn,
              (long long)ld_scores);
-  ScoreLaunch a{};
   a.dtype = dims->dtype;
   a.P = dims->pool;
   a.D = dims->idx_dim;
@@ -163,7 +163,41 @@ kp_status dsa_indexer_score(const kp_dims* dims, const kp_cache* cache, const kp
   a.q_pos = queries->pos;
   a.scores = scores;
   a.ld = ld_scores;
+  return KP_OK;
+}
+
+kp_status kpool_compress(const kp_dims* dims, const kp_cache* cache, int32_t n_pools, const void* keys,
+                         const void* gates, const int32_t* src, const void* ape, const int32_t* pool_seq,
+                         const int32_t* pool_id, void* stream) {
+  CompressLaunch a;
+  const kp_status st = compress_prepare("kpool_compress", dims, cache, n_pools, keys, gates, src, ape, pool_seq,
+                                        pool_id, a);
+  if (st != KP_OK || a.n_pools == 0) return st;
+  return launch_compress(a, (hipStream_t)stream);
+}
+
+kp_status dsa_indexer_score(const kp_dims* dims, const kp_cache* cache, const kp_queries* queries,
+                            const void* q_idx, const float* w, float* scores, int64_t ld_scores, void* stream) {
+  ScoreLaunch a;
+  const kp_status st = score_prepare("dsa_indexer_score", dims, cache, queries, q_idx, w, scores, ld_scores, a);
+  if (st != KP_OK || a.n_q == 0) return st;
   return launch_score(a, (hipStream_t)stream);
+}
+
+kp_status dsa_compress_score(const kp_dims* dims, const kp_cache* cache, int32_t n_pools, const void* keys,
+                             const void* gates, const int32_t* src, const void* ape, const int32_t* pool_seq,
+                             const int32_t* pool_id, const kp_queries* queries, const void* q_idx, const float* w,
+                             float* scores, int64_t ld_scores, void* stream) {
+  const char* fn = "dsa_compress_score";
+  CompressLaunch c;
+  kp_status st = compress_prepare(fn, dims, cache, n_pools, keys, gates, src, ape, pool_seq, pool_id, c);
+  if (st != KP_OK) return st;
+  ScoreLaunch a;
+  st = score_prepare(fn, dims, cache, queries, q_idx, w, scores, ld_scores, a);
+  if (st != KP_OK) return st;
+  if (a.n_q == 0) return c.n_pools ? launch_compress(c, (hipStream_t)stream) : KP_OK;
+  if (c.n_pools == 0) return launch_score(a, (hipStream_t)stream);
+  return launch_compress_score(c, a, (hipStream_t)stream);
 }
 
 size_t dsa_topk_workspace_size(const kp_dims* dims, const kp_queries* queries) {

@@ -93,6 +93,27 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
 template <class T>
 __device__ __forceinline__ float pool_channel(const T* __restrict__ kr, const T* __restrict__ gr,
                                               const T* __restrict__ ar, int P, int D) {
+  if (P == 4 && gr && ar) {
+    // the model's pool size: every load issued before the first is used (one memory round trip, not one per
+    // token), then the same operations in the same order as the loops below
+    float k[4], z[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      k[j] = Elem<T>::to_f32(kr[j * D]);
+      z[j] = Elem<T>::to_f32(gr[j * D]) + Elem<T>::to_f32(ar[j * D]);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, z[j]);
+    float den = 0.f, num = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = __expf(z[j] - m);
+      den += e;
+      num += e * (k[j] - k[0]);
+    }
+    return k[0] + num / den;
+  }
   const float k0 = Elem<T>::to_f32(kr[0]);
   float den = 0.f, num = 0.f;
   if (gr && ar) {  // straight-line loops for the learned pooling

@@ -46,6 +46,8 @@ struct ScoreLaunch {
   int64_t ld;
 };
 kp_status launch_score(const ScoreLaunch& a, hipStream_t s);
+// launch_compress(c) then launch_score(a), in one launch where the decode scorer can pool c's entries itself
+kp_status launch_compress_score(const CompressLaunch& c, const ScoreLaunch& a, hipStream_t s);
 
 struct TopkLaunch {
   int P, k, n_q, max_pos;

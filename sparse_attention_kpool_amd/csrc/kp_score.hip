@@ -114,6 +114,7 @@ __device__ __forceinline__ void score_tiles(const typename Elem<T>::frag (&qa)[Q
 
 constexpr int SC_MAXCHUNK = 4096;    // decode: scores buffered in LDS per block (SC_MAXCHUNK / 4 per wave)
 constexpr int SC_DBLOCKS_PER_CU = 2;  // decode: persistent blocks of 4 waves per compute unit
+constexpr int SC_MAXPEND = 64;        // decode: pools pooled in the scoring launch (one per lane)
 
 // The persistent decode grids split the TILE-pool tiles of all queries, taken query by query, into one contiguous
 // range per wave of about equal length, so rows of any length mix keep every wave streaming.  Wave gw of n_waves
@@ -171,18 +172,48 @@ __device__ __forceinline__ bool decode_wave_range(const int32_t* __restrict__ q_
   return true;
 }
 
+// Pools pooled in the same launch as the decode scoring (dsa_compress_score): entry e < n is pool pool_id[e] of
+// sequence pool_seq[e], pooled from key / gate rows src[e] (src NULL: row e), exactly as kpool_compress does.
+template <class T>
+struct PendPools {
+  const T* keys;
+  const T* gates;  // may be NULL
+  const T* ape;    // may be NULL
+  const int32_t* src;
+  const int32_t* pool_seq;
+  const int32_t* pool_id;
+  T* pooled;  // the pooled cache the entries are written to
+  int n;      // 0 .. SC_MAXPEND
+};
+
+// channel c of entry e's pooled key, rounded to the storage type: the value kpool_compress stores
+template <class T>
+__device__ __forceinline__ T pend_value(const PendPools<T>& pp, int64_t src_row, int c, int P, int D) {
+  return Elem<T>::from_f32(pool_channel<T>(pp.keys + src_row * P * D + c,
+                                           pp.gates ? pp.gates + src_row * P * D + c : nullptr,
+                                           pp.ape ? pp.ape + c : nullptr, P, D));
+}
+
 // ---------------------------------------------------------------------------------------------------------------
 // decode: a persistent grid; the 32-pool tiles of all queries, taken query by query, are split into one contiguous
 // range per wave of about equal length, so rows of any length mix keep every wave streaming.  A wave covers its
 // range as segments, one per query it touches (and at most 31 tiles and 63 pages each): per segment it loads the
 // query's fragments and page ids once, streams the tiles through its private LDS tile two ahead in registers, and
 // writes the segment's scores out.  No block-wide barrier: waves run independently.
+//
+// FUSE: the launch also pools the entries of `pend` (at most 64, one per lane).  Global wave w writes entries
+// w, w + waves, ... to the pooled cache.  A wave whose segment contains an entry's pool does not wait for that
+// write: it pools the entry itself (the same function of the same inputs, so the same bits) and puts the row into
+// its LDS tile over whatever the tile load read from the cache, before the tile is multiplied.  The first entry of
+// a segment is pooled in the segment's prologue, beside its other loads; further ones (several pools of one
+// sequence completing in one call) are pooled when their tile comes.
 // ---------------------------------------------------------------------------------------------------------------
-template <class T, int D>
+template <class T, int D, bool FUSE>
 __global__ __launch_bounds__(256) void score_decode_kernel(
-    const T* __restrict__ pooled, const int32_t* __restrict__ bt, int bt_stride, int log2_ppp,
+    const T* pooled, const int32_t* __restrict__ bt, int bt_stride, int log2_ppp,
     const T* __restrict__ q_idx, const float* __restrict__ w, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_pos, int n_q, int Hi, int P, float* __restrict__ scores, int64_t ld) {
+    const int32_t* __restrict__ q_pos, int n_q, int Hi, int P, float* __restrict__ scores, int64_t ld,
+    const PendPools<T> pend) {
   using S = ScoreShape<T, D>;
   using E = Elem<T>;
   using F = typename E::frag;
@@ -195,11 +226,52 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   auto pools_of = [&](int q) __attribute__((always_inline)) {
     return int(min(int64_t((q_pos[q] + 1) / P), ld));  // ld bounds a row
   };
+  // FUSE: lane e holds entry e (lanes past the list: sequence -1, which no query has)
+  constexpr int NPV = (D + 63) / 64;  // channels per lane of one pooled row
+  int pend_seq = -1, pend_id = 0, pend_src = 0;
+  const int gw = int(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(wave), nw = int(gridDim.x) * 4;
+  // pooled row of entry e (lane's channels lane + 64 i), and its cache row
+  auto pool_entry = [&](int e, T(&v)[NPV]) __attribute__((always_inline)) {
+    const int64_t sr = __builtin_amdgcn_readlane(pend_src, e);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i)
+      if (lane + 64 * i < D) v[i] = pend_value(pend, sr, lane + 64 * i, P, D);
+    return paged_row(bt, bt_stride, __builtin_amdgcn_readlane(pend_seq, e), __builtin_amdgcn_readlane(pend_id, e),
+                     log2_ppp);
+  };
+  auto store_entry = [&](int64_t row, const T(&v)[NPV]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NPV; ++i)
+      if (lane + 64 * i < D) pend.pooled[row * D + lane + 64 * i] = v[i];
+  };
+  // Wave gw writes entries gw, gw + nw, ...: the first one pooled in its first segment's prologue (its loads join
+  // that prologue's) and stored after its last segment, so the write costs the scoring no latency; any further
+  // ones (a grid of fewer waves than entries) at once.
+  T wv_e[NPV];
+  int64_t w_row = 0;
+  bool w_pooled = false;
+  const bool w_own = FUSE && gw < pend.n;
+  if constexpr (FUSE) {
+    if (lane < pend.n) {
+      pend_seq = pend.pool_seq[lane];
+      pend_id = pend.pool_id[lane];
+      pend_src = pend.src ? pend.src[lane] : lane;
+    }
+    for (int e = gw + nw; e < pend.n; e += nw) {
+      T v[NPV];
+      store_entry(pool_entry(e, v), v);
+    }
+  }
   int64_t left;
   int qc, tc, seq0;  // query and tile of the cursor; q_seq of query `lane` (first 64 queries)
   if (!decode_wave_range<32>(q_seq, q_pos, n_q, P, ld, int64_t(blockIdx.x) * 4 + wave, int64_t(gridDim.x) * 4,
-                             lane, left, qc, tc, seq0))
+                             lane, left, qc, tc, seq0)) {
+    if (w_own) {
+      w_row = pool_entry(gw, wv_e);
+      store_entry(w_row, wv_e);
+    }
     return;
+  }
 
   T* tile = tiles[wave];
   float* sb = sbuf[wave];
@@ -224,6 +296,25 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
       const int pg0 = w_begin >> log2_ppp;
       const int npg = ((w_end - 1) >> log2_ppp) - pg0 + 1;
       const int page_reg = lane < npg ? bt[int64_t(seq) * bt_stride + pg0 + lane] : 0;
+      // FUSE: the segment's first pending pool (pr: its offset from w_begin, -1 if none), pooled now; `more` holds
+      // any further entries that fall in the segment.  The wave's own entry to write is pooled in its first
+      // prologue.
+      T pv[NPV];
+      int pr = -1;
+      uint64_t more = 0;
+      if constexpr (FUSE) {
+        if (w_own && !w_pooled) {
+          w_row = pool_entry(gw, wv_e);
+          w_pooled = true;
+        }
+        const uint64_t mm = __ballot(pend_seq == seq && pend_id >= w_begin && pend_id < w_end);
+        if (mm) {
+          const int e = __builtin_ctzll(mm);
+          pr = __builtin_amdgcn_readlane(pend_id, e) - w_begin;
+          pool_entry(e, pv);
+          more = mm & (mm - 1);
+        }
+      }
       // The first tile needs the page ids anyway: wait for every prologue load here, so that only tile loads are
       // in flight in the loop and the compiler's wait counts there stay exact.
       __builtin_amdgcn_s_waitcnt(0);
@@ -259,6 +350,25 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
             const int c = i * 64 + lane;
             *reinterpret_cast<u32x4*>(tile + (c / S::CPR) * S::RS + (c % S::CPR) * S::EPC) = R[i];
           }
+          if constexpr (FUSE) {
+            // pending pools of this tile replace the rows just stored (LDS operations of a wave run in order)
+            const int r = pr - t * 32;
+            if (r >= 0 && r < 32) {
+#pragma unroll
+              for (int i = 0; i < NPV; ++i)
+                if (lane + 64 * i < D) tile[r * S::RS + lane + 64 * i] = pv[i];
+            }
+            for (uint64_t m = more; m; m &= m - 1) {
+              const int e = __builtin_ctzll(m);
+              const int rr = __builtin_amdgcn_readlane(pend_id, e) - w_begin - t * 32;
+              if (rr < 0 || rr >= 32) continue;
+              T v[NPV];
+              pool_entry(e, v);
+#pragma unroll
+              for (int i = 0; i < NPV; ++i)
+                if (lane + 64 * i < D) tile[rr * S::RS + lane + 64 * i] = v[i];
+            }
+          }
           load_tile(t + 2, R);
           F kb[S::STEPS];
           const T* kp = tile + n * S::RS + g * (D / 2);
@@ -287,6 +397,12 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
     if (tc >= nt) {
       ++qc;
       tc = 0;
+    }
+  }
+  if constexpr (FUSE) {
+    if (w_own) {
+      if (!w_pooled) w_row = pool_entry(gw, wv_e);
+      store_entry(w_row, wv_e);
     }
   }
 }
@@ -543,15 +659,22 @@ __global__ __launch_bounds__(SC_PTHREADS, 2) void score_prefill_kernel(
 
 template <class T, int D>
 static void launch_score_t(const ScoreLaunch& a, bool prefill, int chunk, int n_chunks, int n_groups,
-                           int decode_blocks, hipStream_t s) {
-  if (prefill)
+                           int decode_blocks, const CompressLaunch* c, hipStream_t s) {
+  if (prefill) {
     score_prefill_kernel<T, D><<<dim3(unsigned(int64_t(n_groups) * n_chunks)), dim3(SC_PTHREADS), 0, s>>>(
         (const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp, (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.n_q, a.Hi,
         a.P, a.scores, a.ld, chunk, n_chunks);
-  else
-    score_decode_kernel<T, D><<<dim3(unsigned(decode_blocks)), dim3(256), 0, s>>>(
+  } else if (c) {
+    const PendPools<T> pp{(const T*)c->keys, (const T*)c->gates, (const T*)c->ape, c->src, c->pool_seq,
+                          c->pool_id, (T*)c->pooled, c->n_pools};
+    score_decode_kernel<T, D, true><<<dim3(unsigned(decode_blocks)), dim3(256), 0, s>>>(
         (const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp, (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.n_q, a.Hi,
-        a.P, a.scores, a.ld);
+        a.P, a.scores, a.ld, pp);
+  } else {
+    score_decode_kernel<T, D, false><<<dim3(unsigned(decode_blocks)), dim3(256), 0, s>>>(
+        (const T*)a.pooled, a.bt, a.bt_stride, a.log2_ppp, (const T*)a.q_idx, a.w, a.q_seq, a.q_pos, a.n_q, a.Hi,
+        a.P, a.scores, a.ld, PendPools<T>{});
+  }
 }
 
 // compute units of the current device (looked up once per device)
@@ -567,12 +690,16 @@ static int cu_count() {
   return cached[dev];
 }
 
-kp_status launch_score(const ScoreLaunch& a, hipStream_t s) {
+// the decode kernel is the one that runs (the prefill kernel takes runs of >= 8 queries of one sequence)
+static bool score_decode_shape(const ScoreLaunch& a) { return a.group < 8; }
+
+// c: pools to pool in the same launch (decode kernel only; NULL for none)
+static kp_status launch_score_impl(const ScoreLaunch& a, const CompressLaunch* c, hipStream_t s) {
   const int64_t ncmax = (int64_t(a.max_pos) + 1) / a.P;
   if (a.n_q == 0 || ncmax == 0) return KP_OK;
   const int64_t ppp = int64_t(1) << a.log2_ppp;
   // prefill shape when the caller promises runs of >= 8 queries of one sequence (a block takes 16)
-  const bool prefill = a.group >= 8;
+  const bool prefill = !score_decode_shape(a);
   if (!prefill) {
     // persistent decode grid: SC_DBLOCKS_PER_CU blocks per compute unit, fewer when the tiles are few (about one
     // tile per wave, counted on the longest row: a small batch is latency-bound, and more waves in flight shorten
@@ -582,12 +709,12 @@ kp_status launch_score(const ScoreLaunch& a, hipStream_t s) {
     const int64_t few = (tiles_ub + 3) / 4;
     if (few < blocks) blocks = few < 1 ? 1 : few;
     if (a.dtype == KP_DTYPE_BF16) {
-      if (a.D == 128) launch_score_t<bf16, 128>(a, false, 0, 0, 0, int(blocks), s);
-      else launch_score_t<bf16, 32>(a, false, 0, 0, 0, int(blocks), s);
+      if (a.D == 128) launch_score_t<bf16, 128>(a, false, 0, 0, 0, int(blocks), c, s);
+      else launch_score_t<bf16, 32>(a, false, 0, 0, 0, int(blocks), c, s);
     } else {
-      launch_score_t<float, 32>(a, false, 0, 0, 0, int(blocks), s);
+      launch_score_t<float, 32>(a, false, 0, 0, 0, int(blocks), c, s);
     }
-    return check_launch("dsa_indexer_score");
+    return check_launch(c ? "dsa_compress_score" : "dsa_indexer_score");
   }
   const int64_t n_groups = (a.n_q + SC_QG - 1) / SC_QG;
   // pools per block: a multiple of 128 sized for about 1024 blocks, at most SC_PMAXCHUNK, and SC_MAXPG pages per
@@ -608,12 +735,26 @@ kp_status launch_score(const ScoreLaunch& a, hipStream_t s) {
     return KP_ERR_INVALID_ARG;
   }
   if (a.dtype == KP_DTYPE_BF16) {
-    if (a.D == 128) launch_score_t<bf16, 128>(a, true, int(chunk), int(n_chunks), int(n_groups), 0, s);
-    else launch_score_t<bf16, 32>(a, true, int(chunk), int(n_chunks), int(n_groups), 0, s);
+    if (a.D == 128) launch_score_t<bf16, 128>(a, true, int(chunk), int(n_chunks), int(n_groups), 0, nullptr, s);
+    else launch_score_t<bf16, 32>(a, true, int(chunk), int(n_chunks), int(n_groups), 0, nullptr, s);
   } else {
-    launch_score_t<float, 32>(a, true, int(chunk), int(n_chunks), int(n_groups), 0, s);
+    launch_score_t<float, 32>(a, true, int(chunk), int(n_chunks), int(n_groups), 0, nullptr, s);
   }
   return check_launch("dsa_indexer_score");
+}
+
+kp_status launch_score(const ScoreLaunch& a, hipStream_t s) { return launch_score_impl(a, nullptr, s); }
+
+// kpool_compress then dsa_indexer_score.  One launch when the decode kernel scores and the list has 1 ..
+// SC_MAXPEND entries (the decode step's case: at most one completing pool per sequence); otherwise the two
+// launches, in that order.
+kp_status launch_compress_score(const CompressLaunch& c, const ScoreLaunch& a, hipStream_t s) {
+  const bool scores = a.n_q > 0 && (int64_t(a.max_pos) + 1) / a.P > 0;
+  if (c.n_pools > 0 && c.n_pools <= SC_MAXPEND && scores && score_decode_shape(a))
+    return launch_score_impl(a, &c, s);
+  const kp_status st = launch_compress(c, s);
+  if (st != KP_OK) return st;
+  return launch_score(a, s);
 }
 
 }  // namespace kp

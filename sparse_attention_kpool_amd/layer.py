@@ -14,8 +14,9 @@ from typing import Optional
 
 import torch
 
-from . import (KP_DTYPE_BF16, KP_DTYPE_F32, Cache, Dims, Queries, absorb_product, dsa_indexer_score,
-               dsa_topk_select, dsa_topk_workspace_size, indexer_products, kpool_compress, linear_group,
+from . import (KP_DTYPE_BF16, KP_DTYPE_F32, Cache, Dims, Queries, absorb_product, dsa_compress_score,
+               dsa_indexer_score,
+               dsa_topk_select, dsa_topk_workspace_size, indexer_products, linear_group,
                linear_shapes_workspace_size, mla_unabsorb_o, sparse_mla_attn, sparse_mla_attn_fp8,
                sparse_mla_attn_mtp, sparse_mla_mtp_workspace_size, sparse_mla_workspace_size)
 
@@ -67,16 +68,22 @@ class KPoolDSALayer:
             return None
         return torch.empty(((nbytes + 15) // 16 * 4,), dtype=torch.float32, device=self.device)
 
+    def _compress_score(self, cache: Cache, compress: Optional[CompressInput], queries: Queries, q_idx, w,
+                        scores) -> None:
+        # the step's completed pools, then the scores (one launch for a decode batch: dsa_compress_score)
+        if compress is not None and compress.pool_seq.numel() > 0:
+            dsa_compress_score(self.dims, cache, compress.keys, compress.gates, compress.ape, compress.pool_seq,
+                               compress.pool_id, queries, q_idx, w, scores, src=compress.src)
+        else:
+            dsa_indexer_score(self.dims, cache, queries, q_idx, w, scores)
+
     def step(self, cache: Cache, queries: Queries, q_idx, w, q, out, lse=None,
              compress: Optional[CompressInput] = None) -> None:
         n_q = int(queries.seq.numel())
         if n_q > self.max_q or queries.max_pos > self.max_pos:
             raise ValueError("call shape exceeds the layer's allocation")
-        if compress is not None and compress.pool_seq.numel() > 0:
-            kpool_compress(self.dims, cache, compress.keys, compress.gates, compress.ape, compress.pool_seq,
-                           compress.pool_id, src=compress.src)
         scores = self.scores[:n_q]
-        dsa_indexer_score(self.dims, cache, queries, q_idx, w, scores)
+        self._compress_score(cache, compress, queries, q_idx, w, scores)
         dsa_topk_select(self.dims, queries, scores, self.sel[:n_q], self.n_sel[:n_q], workspace=self.ws_topk)
         if cache.latent.dtype == torch.uint8:   # an fp8 (E4M3) latent cache
             sparse_mla_attn_fp8(self.dims, cache, queries, q, self.sel[:n_q], self.n_sel[:n_q], cache.latent_scale,
@@ -96,10 +103,7 @@ class KPoolDSALayer:
         n_q, n_t = int(queries.seq.numel()), int(targets.seq.numel())
         if n_q > self.max_q or n_t != (n_q + 1) // 2 or max(queries.max_pos, targets.max_pos) > self.max_pos:
             raise ValueError("call shape exceeds the layer's allocation, or targets are not one per run")
-        if compress is not None and compress.pool_seq.numel() > 0:
-            kpool_compress(self.dims, cache, compress.keys, compress.gates, compress.ape, compress.pool_seq,
-                           compress.pool_id, src=compress.src)
-        dsa_indexer_score(self.dims, cache, targets, q_idx, w, self.scores[:n_t])
+        self._compress_score(cache, compress, targets, q_idx, w, self.scores[:n_t])
         dsa_topk_select(self.dims, targets, self.scores[:n_t], self.sel[:n_t], self.n_sel[:n_t],
                         workspace=self.ws_topk)
         sparse_mla_attn_mtp(self.dims, cache, queries, q, self.sel[:n_t], self.n_sel[:n_t], out, lse=lse,

@@ -39,7 +39,7 @@ static void explained(const char* what) {
 }
 
 int main(void) {
-  CHECK(kp_abi_version() == 6, "abi version");
+  CHECK(kp_abi_version() == 7, "abi version");
   kp_dims d = dims();
   kp_cache c = cache();
   kp_queries q = queries(4, 100);
@@ -70,6 +70,23 @@ int main(void) {
   { kp_queries b = queries(4, 100); b.seq = NULL;
     CHECK(dsa_indexer_score(&d, &c, &b, FAKE, FAKE, FAKE, 64, NULL) == KP_ERR_INVALID_ARG, "null seq"); }
   CHECK(dsa_indexer_score(&d, &c, NULL, FAKE, FAKE, FAKE, 64, NULL) == KP_ERR_INVALID_ARG, "null queries");
+
+  /* dsa_compress_score: both calls' checks, before anything is launched */
+  CHECK(dsa_compress_score(&d, &c, 2, NULL, FAKE, NULL, FAKE, FAKE, FAKE, &q, FAKE, FAKE, FAKE, 64, NULL) ==
+            KP_ERR_INVALID_ARG, "fused: null keys");
+  explained("fused: null keys message");
+  CHECK(dsa_compress_score(&d, &c, -1, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, &q, FAKE, FAKE, FAKE, 64, NULL) ==
+            KP_ERR_INVALID_ARG, "fused: n_pools < 0");
+  CHECK(dsa_compress_score(&d, &c, 2, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, &q, FAKE, FAKE, FAKE, 16, NULL) ==
+            KP_ERR_INVALID_ARG, "fused: ld too small");
+  { kp_dims b = d; b.idx_dim = 64;
+    CHECK(dsa_compress_score(&b, &c, 2, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, &q, FAKE, FAKE, FAKE, 64, NULL) ==
+              KP_ERR_UNSUPPORTED, "fused: idx_dim 64"); }
+  CHECK(dsa_compress_score(&d, &c, 2, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, 64, NULL) ==
+            KP_ERR_INVALID_ARG, "fused: null queries");
+  { kp_queries e = queries(0, 0);
+    CHECK(dsa_compress_score(&d, &c, 0, NULL, NULL, NULL, NULL, NULL, NULL, &e, NULL, NULL, NULL, 4, NULL) == KP_OK,
+          "fused: empty"); }
 
   /* dsa_topk_select */
   {

@@ -20,7 +20,8 @@ def _declared():
 
 def test_header_declares_the_four_calls():
     names = _declared()
-    for f in ("kpool_compress", "dsa_indexer_score", "dsa_topk_select", "sparse_mla_attn", "sparse_mla_attn_fp8",
+    for f in ("kpool_compress", "dsa_indexer_score", "dsa_compress_score", "dsa_topk_select", "sparse_mla_attn",
+              "sparse_mla_attn_fp8",
               "sparse_mla_attn_shared", "sparse_mla_attn_noalloc", "sparse_mla_attn_mtp",
               "sparse_mla_mtp_workspace_size", "kp_read_rows", "kp_linear", "kp_linear_workspace_size", "kp_linear_group",
               "kp_linear_group_workspace_size",
@@ -85,6 +86,23 @@ def test_score_rejects_small_ld_and_nulls_and_misalignment():
     assert _score(_dims(), qidx=FAKE + 8) == K.KP_ERR_INVALID_ARG
     assert "misaligned" in K.last_error()
     assert _score(_dims(), q=K._Queries(4, None, FAKE, 100, 1)) == K.KP_ERR_INVALID_ARG
+
+
+def test_compress_score_checks_both_calls_before_launching():
+    """dsa_compress_score applies kpool_compress's and dsa_indexer_score's checks (each failure is one of theirs,
+    found before anything is launched); with no pools and no queries it is a valid no-op."""
+    lib = K.load()
+    d, c, q = _dims(), _cache(), _queries()
+
+    def call(d=d, n_pools=2, keys=FAKE, q=q, ld=64):
+        return lib.dsa_compress_score(ctypes.byref(d), ctypes.byref(c), n_pools, keys, FAKE, None, FAKE, FAKE, FAKE,
+                                      None if q is None else ctypes.byref(q), FAKE, FAKE, FAKE, ld, None)
+    assert call(keys=None) == K.KP_ERR_INVALID_ARG and b"dsa_compress_score" in lib.kp_last_error()
+    assert call(n_pools=-1) == K.KP_ERR_INVALID_ARG
+    assert call(ld=16) == K.KP_ERR_INVALID_ARG and b"ld_scores" in lib.kp_last_error()
+    assert call(d=_dims(idx_dim=64)) == K.KP_ERR_UNSUPPORTED
+    assert call(q=None) == K.KP_ERR_INVALID_ARG
+    assert call(n_pools=0, keys=None, q=_queries(0, 0), ld=4) == K.KP_OK
 
 
 def test_empty_query_batches_are_valid_noops():

@@ -512,6 +512,67 @@ def test_compress_through_ring():
     _free()
 
 
+def _ints(x):
+    return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
+
+
+FUSED = {
+    # 4 sequences x 16 pools pooled in the call (64 entries, one launch): every segment holds many of them
+    "general_16_per_seq": lambda: (_small_decode("fused_general", ctx=(1000, 4099, 8192, 20001), key_per_token=True,
+                                                 new_from=[t - 64 for t in (1000, 4099, 8192, 20001)]), {}),
+    # 5 x 16 = 80 entries: more than one launch pools, so the two kernels run in order
+    "over_64": lambda: (_small_decode("fused_over64", ctx=(1000, 4099, 8192, 20001, 3000), key_per_token=True,
+                                      new_from=[t - 64 for t in (1000, 4099, 8192, 20001, 3000)]), {}),
+    # 25 queries per sequence at consecutive positions: an entry is visible to the later queries only; sequence 0
+    # has entries but no query; the first entry is listed twice
+    "partly_visible": lambda: (SMALL["many_queries"](), {"drop_seq0": True, "duplicate": True}),
+    # D = 32, one index head
+    "narrow": lambda: (SMALL["small_bf16_narrow"](), {}),
+    # fp32 storage, 64 tokens of one sequence scored as a decode batch (16 entries)
+    "f32_decode_shape": lambda: (SMALL["tiny_general"](), {}),
+}
+
+
+@pytest.mark.parametrize("plain", [False, True], ids=["learned", "plain_mean"])
+@pytest.mark.parametrize("case", list(FUSED))
+def test_compress_score_fused(case, plain):
+    """dsa_compress_score equals kpool_compress followed by dsa_indexer_score bit for bit: the whole pooled cache
+    and every visible score column, whether the decode scorer pools the entries itself (up to 64) or the two kernels
+    run (more).  Learned pooling and the plain mean (gates and ape NULL)."""
+    import sparse_attention_kpool_amd as K
+    wl, opt = FUSED[case]()
+    _say(f"[case fused {case} plain={plain}] n_q={wl.n_q} dtype={wl.dtype}")
+    runs = [DeviceRun(wl, group=1), DeviceRun(wl, group=1)]
+    c = runs[0].compress
+    n = int(c.pool_seq.numel())
+    src = torch.arange(n, dtype=torch.int32, device="cuda")
+    seq, pid = c.pool_seq, c.pool_id
+    if opt.get("duplicate"):
+        src, seq, pid = (torch.cat([x, x[:1]]) for x in (src, seq, pid))
+    keep = torch.ones(wl.n_q, dtype=torch.bool, device="cuda")
+    if opt.get("drop_seq0"):
+        keep = runs[0].queries.seq != 0
+    qs = K.Queries(seq=runs[0].queries.seq[keep].contiguous(), pos=runs[0].queries.pos[keep].contiguous(),
+                   max_pos=wl.max_pos(), group=1)
+    m = int(keep.sum().item())
+    gates, ape = (None, None) if plain else (c.gates, c.ape)
+    a, b = runs
+    K.kpool_compress(a.dims, a.cache, c.keys, gates, ape, seq, pid, src=src)
+    K.dsa_indexer_score(a.dims, a.cache, qs, a.q_idx[keep], a.w[keep], a.layer.scores[:m])
+    K.dsa_compress_score(b.dims, b.cache, c.keys, gates, ape, seq, pid, qs, b.q_idx[keep], b.w[keep],
+                         b.layer.scores[:m], src=src)
+    torch.cuda.synchronize()
+    assert torch.equal(_ints(a.pooled), _ints(b.pooled)), "pooled cache differs"
+    n_c = ((qs.pos.long() + 1) // wl.P).cpu().numpy()
+    for j in range(m):
+        assert torch.equal(_ints(a.layer.scores[j, :n_c[j]]), _ints(b.layer.scores[j, :n_c[j]])), f"scores of query {j}"
+    if m == wl.n_q:
+        for r in runs:
+            r.check_guards()
+    del runs, a, b
+    _free()
+
+
 def test_chunked_prefill_equals_one_shot():
     """A prefill of 500 queries run as chunks of 77, 128 and 200 queries (each chunk compressing the pools its
     tokens complete before it scores, as a chunked prefill does) gives the same scores and selections as one call
