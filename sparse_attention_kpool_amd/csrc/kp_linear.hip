@@ -20,6 +20,9 @@
 //          or N read row M-1 / N-1 (their results are never stored), so every wave issues the same loads every
 //          stage and the waits are exact counts.  No stage past the end of k is loaded (the last stages wait for
 //          every load instead): at 4096 tokens the absorb, 4 stages a tile, ran 162 -> 153 us with it.
+//   units  a block of an unsplit product with at least LN_REP_MIN tiles takes LN_REP tiles in turn, as one stream
+//          of stages: the next tile's first stage loads while this tile's last one is multiplied and its output
+//          leaves (4096-token un-absorb 133 -> 128 us; 4 tiles a block measured no better).
 //   math   wave (wn, wm) owns the BN/2 x BM/2 quarter of the tile: (BN/32) x (BM/32) MFMA tiles, BK/32 k-steps a
 //          stage.
 // Tiles are numbered in panels of 8 m-tiles (m-fastest inside a panel, then n), and each XCD takes a contiguous
@@ -38,6 +41,8 @@
 namespace kp {
 
 constexpr int LN_THREADS = 256;
+constexpr int LN_REP = 2;              // units per block of an unsplit product of many short tiles ...
+constexpr int64_t LN_REP_MIN = 2048;   // ... of at least this many tiles
 constexpr int LN_MAXGROUP = 8;  // products per grouped launch
 
 // A stage holds BK of k for every tile row: CPR = BK / 8 chunks of 16 bytes.  Chunk c of row r sits at position
@@ -59,7 +64,8 @@ struct LinearProb {
   int M, N, K, c_bf16, tiles_m, tiles_n, splits, nk_per;
   float alpha;
   int block0;   // first block of this product in the product grid (a multiple of 8)
-  int nblocks;  // its blocks (tiles x splits); the grid gives it nblocks rounded up to a multiple of 8
+  int nblocks;  // its units (tiles x splits), in 8 runs of (nblocks + 7) / 8, one run per XCD
+  int rep;      // units per block at most: the grid gives it 8 * ceil(run / rep) blocks
   int rblock0;  // first block of its split-K reduction in the reduce grid
 };
 struct LinearGroup {
@@ -125,55 +131,65 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const LinearGroup gr
   static_assert(BM * BN <= LN_NBUF * (BM + BN) * BK, "the output tile fits the stage ring");
 
   // Each product owns an 8-aligned range of 8 k blocks (blocks are dealt to the 8 XCDs round-robin, so every
-  // product spreads over all XCDs); inside it, slot j runs block (j mod 8) k + j / 8, so each XCD takes a
-  // contiguous run of the product's tiles (in panel order: shared operand tiles stay in that XCD's L2).  Slots
-  // past the product's blocks exit at once.
+  // product spreads over all XCDs); inside it, slot j runs units (tile, k-split) of run (j mod 8), the
+  // contiguous run of the product's units (in panel order) that this XCD takes: units j / 8, j / 8 + k,
+  // j / 8 + 2k, ... (rep of them at most), so the blocks of one XCD always work on neighbouring units and shared
+  // operand tiles stay in its L2.  Slots past the run's units exit at once.
   const LinearProb& P = grp.p[linear_find(grp, blockIdx.x, false)];
   const int j = blockIdx.x - P.block0, per = (P.nblocks + 7) >> 3;
-  int bid = (j & 7) * per + (j >> 3);
-  if (bid >= P.nblocks) return;
+  const int rep = P.rep, nq = (per + rep - 1) / rep;  // units per block at most; blocks per XCD run
+  const int x = j & 7, q = j >> 3;
+  const int run_len = min(per, P.nblocks - x * per);
+  if (q >= run_len) return;
+  const int n_units = min(rep, (run_len - q + nq - 1) / nq);
   const int M = P.M, N = P.N, K = P.K, splits = P.splits, nk_per = P.nk_per, tiles_m = P.tiles_m;
-  const int sp = bid % splits;  // k-split of this block
-  bid /= splits;
-  const int per_b = tiles_m * P.tiles_n;
-  const int b = bid / per_b;
-  const int t = bid - b * per_b;
-  int tm, tn;
-  linear_tile_at(t, tiles_m, P.tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const bf16* A = P.A + b * P.sa;
-  const bf16* W = P.W + b * P.sw;
   const int64_t lda = P.lda, ldw = P.ldw;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g = lane >> 4;
 
-  // per-lane source of each load instruction at k = 0: row RPI (wave * L + i) + lane / CPR of the tile, the
-  // chunk whose swizzled position is lane % CPR
-  const bf16* srcA[LA];
-  const bf16* srcW[LW];
+  // One unit: its batch entry, k-split, tile origin, stages [s0, s0 + nk) of the K / BK, and each load
+  // instruction's per-lane source at k = 0: row RPI (wave * L + i) + lane / CPR of the tile, the chunk whose
+  // swizzled position is lane % CPR
+  struct Unit {
+    int b, sp, m0, n0, s0, nk;
+    const bf16* srcA[LA];
+    const bf16* srcW[LW];
+  };
+  auto setup = [&](int i, Unit& U) __attribute__((always_inline)) {
+    int bid = x * per + q + i * nq;
+    U.sp = bid % splits;
+    bid /= splits;
+    const int per_b = tiles_m * P.tiles_n;
+    U.b = bid / per_b;
+    int tm, tn;
+    linear_tile_at(bid - U.b * per_b, tiles_m, P.tiles_n, tm, tn);
+    U.m0 = tm * BM;
+    U.n0 = tn * BN;
+    const bf16* A = P.A + U.b * P.sa;
+    const bf16* W = P.W + U.b * P.sw;
 #pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int r = RPI * (wave * LA + i) + lane / CPR;
-    srcA[i] = A + int64_t(min(m0 + r, M - 1)) * lda + 8 * ((lane % CPR) ^ ln_swz<CPR>(r));
-  }
+    for (int l = 0; l < LA; ++l) {
+      const int r = RPI * (wave * LA + l) + lane / CPR;
+      U.srcA[l] = A + int64_t(min(U.m0 + r, M - 1)) * lda + 8 * ((lane % CPR) ^ ln_swz<CPR>(r));
+    }
 #pragma unroll
-  for (int i = 0; i < LW; ++i) {
-    const int r = RPI * (wave * LW + i) + lane / CPR;
-    srcW[i] = W + int64_t(min(n0 + r, N - 1)) * ldw + 8 * ((lane % CPR) ^ ln_swz<CPR>(r));
-  }
-  // this block's stages: [s0, s0 + nk) of the K / BK
-  const int s0 = sp * nk_per;
-  const int nk = min(nk_per, K / BK - s0);
-  // stage s (below nk) into buffer s % NBUF: LA + LW loads per wave
-  auto issue = [&](int s) __attribute__((always_inline)) {
-    const int64_t k0 = int64_t(s0 + s) * BK;
-    const uint32_t ba = lds_off(sA[s % LN_NBUF]), bw = lds_off(sW[s % LN_NBUF]);
+    for (int l = 0; l < LW; ++l) {
+      const int r = RPI * (wave * LW + l) + lane / CPR;
+      U.srcW[l] = W + int64_t(min(U.n0 + r, N - 1)) * ldw + 8 * ((lane % CPR) ^ ln_swz<CPR>(r));
+    }
+    U.s0 = U.sp * nk_per;
+    U.nk = min(nk_per, K / BK - U.s0);
+  };
+  // stage s (below U.nk) of unit U into buffer buf: LA + LW loads per wave
+  auto issue = [&](const Unit& U, int s, int buf) __attribute__((always_inline)) {
+    const int64_t k0 = int64_t(U.s0 + s) * BK;
+    const uint32_t ba = lds_off(sA[buf]), bw = lds_off(sW[buf]);
 #pragma unroll
-    for (int i = 0; i < LA; ++i) lds_dma16(srcA[i] + k0, ba + uint32_t(1024 * (wave * LA + i)));
+    for (int l = 0; l < LA; ++l) lds_dma16(U.srcA[l] + k0, ba + uint32_t(1024 * (wave * LA + l)));
 #pragma unroll
-    for (int i = 0; i < LW; ++i) lds_dma16(srcW[i] + k0, bw + uint32_t(1024 * (wave * LW + i)));
+    for (int l = 0; l < LW; ++l) lds_dma16(U.srcW[l] + k0, bw + uint32_t(1024 * (wave * LW + l)));
   };
 
   // fragment rows of this wave: weight rows wn * BN/2 + 16 a + l16, activation rows wm * BM/2 + 16 c + l16; the
@@ -182,13 +198,8 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const LinearGroup gr
   const int wn = wave >> 1, wm = wave & 1;
   const int sw_l = ln_swz<CPR>(l16);
   f32x4 acc[TN][TM];
-#pragma unroll
-  for (int a = 0; a < TN; ++a)
-#pragma unroll
-    for (int c = 0; c < TM; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto multiply = [&](int s) __attribute__((always_inline)) {
-    const uint32_t ba = lds_off(sA[s % LN_NBUF]), bw = lds_off(sW[s % LN_NBUF]);
+  auto multiply = [&](int buf) __attribute__((always_inline)) {
+    const uint32_t ba = lds_off(sA[buf]), bw = lds_off(sW[buf]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint32_t cpos = 16 * ((4 * ks + g) ^ sw_l);
@@ -204,78 +215,103 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const LinearGroup gr
     }
   };
 
+  // The stages of the block's units form one stream: stage s of unit u is stream stage G = u nk + s, in buffer
+  // G % NBUF (a block takes several units only of an unsplit product whose nk >= NBUF, so every unit has the same
+  // nk and the next unit's first stages are loaded while this unit's last ones are multiplied and its output
+  // leaves).  The bf16 output is staged in the buffer of the unit's last stage, which no load in flight targets.
+  Unit cur, nxt;
+  setup(0, cur);
+  const int nk = cur.nk, total = n_units * nk;
 #pragma unroll
   for (int s = 0; s < LN_AHEAD; ++s)
-    if (s < nk) issue(s);
-  for (int s = 0; s < nk; ++s) {
-    // stages s .. min(s + AHEAD, nk) - 1 are in flight: wait for s (the last AHEAD - 1 stages wait for every
-    // load; with AHEAD <= 2 that is exact), publish it; after the barrier every wave is past multiply(s-1), so
-    // buffer (s+AHEAD) % NBUF = (s-1) % NBUF is free for stage s + AHEAD.  No stage past the end is loaded.
-    if (s + LN_AHEAD - 1 < nk)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((LN_AHEAD - 1) * (LA + LW)));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-    if (s + LN_AHEAD < nk) issue(s + LN_AHEAD);
-    multiply(s);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // no load may land in LDS after the block ends
-
-  if (splits > 1) {
-    // split K: store the fp32 partial tile in lane order, [tile][split][wave][n tile][m tile][lane]; the reduce
-    // kernel adds the splits in order and writes the output
-    f32x4* pt = P.part + (int64_t(bid) * splits + sp) * (4 * TN * TM * 64) + (wave * TN * TM) * 64 + lane;
+    if (s < nk) issue(cur, s, s);
+  for (int u = 0; u < n_units; ++u) {
+    const bool has_next = u + 1 < n_units;
+    if (has_next) setup(u + 1, nxt);
 #pragma unroll
     for (int a = 0; a < TN; ++a)
 #pragma unroll
-      for (int c = 0; c < TM; ++c) pt[(a * TM + c) * 64] = acc[a][c];
-    return;
-  }
+      for (int c = 0; c < TM; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nk; ++s) {
+      // stream stages G .. min(G + AHEAD, total) - 1 are in flight (and, after a unit's first stages, its
+      // predecessor's output stores, which are younger and only make the wait longer): wait for G -- the last
+      // AHEAD - 1 stages of the stream wait for every load; with AHEAD <= 2 that is exact -- and publish it.
+      // After the barrier every wave is past multiply(G-1) and past the previous unit's output staging, so
+      // buffer (G + AHEAD) % NBUF = (G - 1) % NBUF is free for stream stage G + AHEAD.
+      const int G = u * nk + s;
+      if (G + LN_AHEAD - 1 < total)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((LN_AHEAD - 1) * (LA + LW)));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();
+      if (s + LN_AHEAD < nk) issue(cur, s + LN_AHEAD, (G + LN_AHEAD) % LN_NBUF);
+      else if (has_next) issue(nxt, s + LN_AHEAD - nk, (G + LN_AHEAD) % LN_NBUF);
+      multiply(G % LN_NBUF);
+    }
+    const int last = (u * nk + nk - 1) % LN_NBUF;  // buffer of the unit's last stage
 
-  if (P.c_bf16 && P.ldc % 8 == 0 && P.sc % 8 == 0) {
-    // bf16 output through LDS: chunk ch (16 bytes) of tile row r sits at position ch ^ (r mod CH), which spreads the
-    // 16 rows of one fragment store over distinct bank groups (BN = 128; two rows per group at BN = 64); then the
-    // rows are copied out as whole 16-byte chunks
-    constexpr int CH = BN / 8;
-    __syncthreads();  // every wave is done with the stage buffers
+    if (splits > 1) {
+      // split K: store the fp32 partial tile in lane order, [tile][split][wave][n tile][m tile][lane]; the reduce
+      // kernel adds the splits in order and writes the output
+      const int64_t tile = (int64_t(x * per + q + u * nq)) / splits;
+      f32x4* pt = P.part + (tile * splits + cur.sp) * (4 * TN * TM * 64) + (wave * TN * TM) * 64 + lane;
 #pragma unroll
-    for (int a = 0; a < TN; ++a) {
-      const int cc = wn * (BN / 2) + 16 * a + 4 * g;
+      for (int a = 0; a < TN; ++a)
 #pragma unroll
-      for (int c = 0; c < TM; ++c) {
-        const int r = wm * (BM / 2) + 16 * c + l16;
-        const f32x4 v = acc[a][c] * P.alpha;
-        *reinterpret_cast<uint2*>(smem + r * BN + 8 * ((cc >> 3) ^ (r & (CH - 1))) + (cc & 7)) =
-            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        for (int c = 0; c < TM; ++c) pt[(a * TM + c) * 64] = acc[a][c];
+    } else if (P.c_bf16 && P.ldc % 8 == 0 && P.sc % 8 == 0) {
+      // bf16 output through LDS, in the last stage's buffer (rows 0 .. BM*BK/BN - 1 in its activation part, the
+      // rest in its weight part): chunk ch (16 bytes) of tile row r sits at position ch ^ (r mod CH), which
+      // spreads the 16 rows of one fragment store over distinct bank groups (BN = 128; two rows per group at
+      // BN = 64); then the rows are copied out as whole 16-byte chunks
+      constexpr int CH = BN / 8;
+      constexpr int RA = BM * BK / BN;  // output rows held in the activation part
+      static_assert((BM * BK) % BN == 0 && BM * BN <= (BM + BN) * BK, "the output tile fits one stage buffer");
+      auto srow = [&](int r) __attribute__((always_inline)) -> bf16* {
+        return r < RA ? sA[last] + r * BN : sW[last] + (r - RA) * BN;
+      };
+      __syncthreads();  // every wave is done with the last stage's buffer
+#pragma unroll
+      for (int a = 0; a < TN; ++a) {
+        const int cc = wn * (BN / 2) + 16 * a + 4 * g;
+#pragma unroll
+        for (int c = 0; c < TM; ++c) {
+          const int r = wm * (BM / 2) + 16 * c + l16;
+          const f32x4 v = acc[a][c] * P.alpha;
+          *reinterpret_cast<uint2*>(srow(r) + 8 * ((cc >> 3) ^ (r & (CH - 1))) + (cc & 7)) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+      }
+      __syncthreads();
+      bf16* Cb = static_cast<bf16*>(P.C) + int64_t(cur.b) * P.sc;
+      for (int i = threadIdx.x; i < BM * CH; i += LN_THREADS) {
+        const int r = i / CH, ch = i - r * CH;
+        const int m = cur.m0 + r, n = cur.n0 + 8 * ch;
+        if (m >= M || n >= N) continue;
+        const bf16* src = srow(r) + 8 * (ch ^ (r & (CH - 1)));
+        bf16* dst = Cb + int64_t(m) * P.ldc + n;
+        if (n + 8 <= N) {
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          for (int e = 0; e < N - n; ++e) dst[e] = src[e];
+        }
+      }
+    } else {
+      // lane holds D[n][m] for n = tile n + 4 g .. +3, m = tile m + l16
+#pragma unroll
+      for (int a = 0; a < TN; ++a) {
+        const int n = cur.n0 + wn * (BN / 2) + 16 * a + 4 * g;
+#pragma unroll
+        for (int c = 0; c < TM; ++c) {
+          const int m = cur.m0 + wm * (BM / 2) + 16 * c + l16;
+          if (m >= M || n >= N) continue;
+          linear_store4(P, int64_t(cur.b) * P.sc + int64_t(m) * P.ldc + n, n, acc[a][c] * P.alpha);
+        }
       }
     }
-    __syncthreads();
-    bf16* Cb = static_cast<bf16*>(P.C) + int64_t(b) * P.sc;
-    for (int i = threadIdx.x; i < BM * CH; i += LN_THREADS) {
-      const int r = i / CH, ch = i - r * CH;
-      const int m = m0 + r, n = n0 + 8 * ch;
-      if (m >= M || n >= N) continue;
-      const bf16* src = smem + r * BN + 8 * (ch ^ (r & (CH - 1)));
-      bf16* dst = Cb + int64_t(m) * P.ldc + n;
-      if (n + 8 <= N) {
-        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-      } else {
-        for (int e = 0; e < N - n; ++e) dst[e] = src[e];
-      }
-    }
-    return;
+    if (has_next) cur = nxt;
   }
-  // lane holds D[n][m] for n = tile n + 4 g .. +3, m = tile m + l16
-#pragma unroll
-  for (int a = 0; a < TN; ++a) {
-    const int n = n0 + wn * (BN / 2) + 16 * a + 4 * g;
-#pragma unroll
-    for (int c = 0; c < TM; ++c) {
-      const int m = m0 + wm * (BM / 2) + 16 * c + l16;
-      if (m >= M || n >= N) continue;
-      linear_store4(P, int64_t(b) * P.sc + int64_t(m) * P.ldc + n, n, acc[a][c] * P.alpha);
-    }
-  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may land in LDS after the block ends
 }
 
 // Split-K reduction: one thread per 4 outputs (one lane's f32x4 of one MFMA tile of one wave); the partials of the
@@ -405,7 +441,11 @@ static kp_status launch_group(const LinearLaunch* probs, int n, void* ws, size_t
     P.block0 = int(blocks);
     P.nblocks = int(tiles * sp);  // below 2^31: the grid check after the loop covers it
     P.rblock0 = int(rblocks);
-    blocks += (tiles * sp + 7) / 8 * 8;
+    // several units per block for an unsplit product of many short tiles (the next unit's first stages load
+    // while this one's output leaves); every unit then has the same K / BK >= NBUF stages
+    P.rep = (sp == 1 && a.K / BK >= NBUF && tiles >= LN_REP_MIN) ? LN_REP : 1;
+    const int64_t run = (tiles * sp + 7) / 8;
+    blocks += 8 * ((run + P.rep - 1) / P.rep);
     if (sp > 1) rblocks += tiles * (BM * BN / 4) / 256;  // one thread per f32x4 of the partial tiles
     if (blocks > 0x7fffffff || rblocks > 0x7fffffff) {
       set_error("kp_linear: %lld blocks exceed the grid", (long long)blocks);
