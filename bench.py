@@ -140,8 +140,9 @@ class Leg:
 
     def time_steps_graph(self, steps: int, warmup: int, replays: int = 5) -> dict:
         """ms per step with `steps` steps captured in one HIP graph and replayed, as a serving loop replays its
-        captured decode step: `mean` from the first timed replay (exactly `steps` steps, after one untimed
-        replay), `median` and `min` of the per-step times of `replays` timed replays."""
+        captured decode step: `mean` from the first timed replay (exactly `steps` steps, after three untimed
+        replays: the first replays after a capture run a few per cent slower), `median` and `min` of the per-step
+        times of `replays` timed replays."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
@@ -150,7 +151,8 @@ class Leg:
         with torch.cuda.graph(g):
             for i in range(steps):
                 self.step(i)
-        g.replay()
+        for _ in range(3):
+            g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         per = []
