@@ -129,6 +129,7 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const LinearGroup gr
   bf16 (*sA)[BM * BK] = reinterpret_cast<bf16 (*)[BM * BK]>(smem);
   bf16 (*sW)[BN * BK] = reinterpret_cast<bf16 (*)[BN * BK]>(smem + LN_NBUF * BM * BK);
   static_assert(BM * BN <= LN_NBUF * (BM + BN) * BK, "the output tile fits the stage ring");
+  constexpr bool LN_STAGE_ONE = BM * BN <= (BM + BN) * BK;  // the output tile fits one stage buffer
 
   // Each product owns an 8-aligned range of 8 k blocks (blocks are dealt to the 8 XCDs round-robin, so every
   // product spreads over all XCDs); inside it, slot j runs units (tile, k-split) of run (j mod 8), the
@@ -266,8 +267,10 @@ __global__ __launch_bounds__(LN_THREADS) void linear_kernel(const LinearGroup gr
       // BN = 64); then the rows are copied out as whole 16-byte chunks
       constexpr int CH = BN / 8;
       constexpr int RA = BM * BK / BN;  // output rows held in the activation part
-      static_assert((BM * BK) % BN == 0 && BM * BN <= (BM + BN) * BK, "the output tile fits one stage buffer");
+      static_assert((BM * BK) % BN == 0, "output rows do not straddle a stage buffer's parts");
       auto srow = [&](int r) __attribute__((always_inline)) -> bf16* {
+        // a tile too large for one stage buffer takes the whole ring (one unit per block: no load in flight)
+        if constexpr (!LN_STAGE_ONE) return smem + r * BN;
         return r < RA ? sA[last] + r * BN : sW[last] + (r - RA) * BN;
       };
       __syncthreads();  // every wave is done with the last stage's buffer
@@ -443,7 +446,7 @@ static kp_status launch_group(const LinearLaunch* probs, int n, void* ws, size_t
     P.rblock0 = int(rblocks);
     // several units per block for an unsplit product of many short tiles (the next unit's first stages load
     // while this one's output leaves); every unit then has the same K / BK >= NBUF stages
-    P.rep = (sp == 1 && a.K / BK >= NBUF && tiles >= LN_REP_MIN) ? LN_REP : 1;
+    P.rep = (sp == 1 && a.K / BK >= NBUF && tiles >= LN_REP_MIN && BM * BN <= (BM + BN) * BK) ? LN_REP : 1;
     const int64_t run = (tiles * sp + 7) / 8;
     blocks += 8 * ((run + P.rep - 1) / P.rep);
     if (sp > 1) rblocks += tiles * (BM * BN / 4) / 256;  // one thread per f32x4 of the partial tiles
