@@ -9,7 +9,8 @@
  *   sparse_mla_attn    nope-only absorbed MLA of each query over the tokens of its selected pools
  *
  * and, beside them, kp_linear: the dense projections that feed and follow the path (indexer query, head
- * weights and key | gate; the MLA query absorb and output un-absorb).
+ * weights and key | gate; the MLA query absorb and output un-absorb).  dsa_compress_score runs the first two
+ * calls as one (one launch for a decode batch).
  *
  * Sources (page title, section):
  *   [MAX "max.pipelines.architectures.glm5_next" API page]: fields index_kpool (tokens per scoring pool),
