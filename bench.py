@@ -269,7 +269,7 @@ class Leg:
 # the batch-64 decode step's kernels by stage (the scorer pools the step's completed pools in the same launch)
 STAGE_KERNELS = {"score": ["kp::score_decode_kernel<kp::bf16, 128, true>"],
                  "topk": ["kp::topk_chunk_kernel<16>", "kp::topk_merge_kernel<16, true>"],
-                 "attend": ["kp::attn_dma_kernel<4, false, false>", "kp::attn_combine_kernel<kp::bf16, 8>"]}
+                 "attend": ["kp::attn_dma_kernel<4, false, false>", "kp::attn_combine_kernel<kp::bf16, 8, 1>"]}
 
 
 def mtp_leg(W, steps: int) -> dict:

@@ -192,8 +192,8 @@ kp_status dsa_topk_select(const kp_dims* dims, const kp_queries* queries, const 
  *     When a query's selection is split over several blocks (batches too small to fill the GPU), each split's
  *     unnormalised partial output is stored in the storage dtype before the merge, so the output of such a
  *     query is rounded twice; the running max and sum stay fp32.
- *   Limit: a query's selection (plus the one pool sparse_mla_attn_shared may add) is split over at most 32
- *     blocks of at most min(8320 / P, 2064) pools, so topk + 1 <= 32 * min(8320 / P, 2064) (66048 pools at P = 4),
+ *   Limit: a query's selection (plus the one pool sparse_mla_attn_shared may add) is split over at most 64
+ *     blocks of at most min(8320 / P, 2064) pools, so topk + 1 <= 64 * min(8320 / P, 2064) (132096 pools at P = 4),
  *     else KP_ERR_UNSUPPORTED.  Only the first min(n_sel, topk) entries of a row are read.
  *   Errors: KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED (V, H, dtype, topk), KP_ERR_WORKSPACE.
  */

@@ -1033,32 +1033,37 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
 // never written, so its value is dropped by a select) and computes its head's weights itself: no LDS, no barrier,
 // one wait on memory.
 constexpr int CB_THREADS = 256;
-constexpr int CB_MAXSPLIT = 32;  // attn_splits never returns more
+constexpr int CB_MAXSPLIT = 64;  // attn_splits never returns more
 
-template <class T, int PER>
+// PER: splits per thread (registers for each); TPC: threads per 16-byte output chunk -- 2 above 32 splits, each
+// thread merging its own PER splits against the pair's common maximum, the pair's sums added across the two lanes
+// (adjacent lanes: one DPP exchange per value) and written by the first.
+template <class T, int PER, int TPC>
 __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml, int n_split,
                                                                   int H, int V, T* __restrict__ out,
                                                                   float* __restrict__ lse) {
-  static_assert(PER <= CB_MAXSPLIT, "splits per thread");
+  static_assert(PER * TPC <= CB_MAXSPLIT && (TPC == 1 || TPC == 2), "splits per thread");
   constexpr int EPT = 16 / int(sizeof(T));  // channels per thread
-  const int tph = V / EPT;                  // threads per head
+  const int tph = TPC * (V / EPT);          // threads per head
   const int hpb = CB_THREADS / tph;         // heads per block
   const int bpq = (H + hpb - 1) / hpb;      // blocks per query
   const int qi = blockIdx.x / bpq;
   const int tid = threadIdx.x;
   const int h = (blockIdx.x - qi * bpq) * hpb + tid / tph;
-  const int c = (tid % tph) * EPT;
+  const int c = ((tid % tph) / TPC) * EPT;
+  const int half = TPC == 2 ? (tid & 1) : 0;  // which PER splits this thread merges
   const int64_t mls = int64_t(H) * 2, pos_ = int64_t(H) * V;
-  if (h >= H) return;
+  if (h >= H) return;  // both lanes of a pair share h: pairs leave whole
   const int64_t row = int64_t(qi) * n_split * H + h;  // split s: O at part_o + (row + s * H) * V, (m, l) likewise
-  const T* po = part_o + row * V + c;
-  const float* pm = part_ml + row * 2;
+  const int s0 = half * PER, n_mine = min(PER, n_split - s0);
+  const T* po = part_o + (row + int64_t(s0) * H) * V + c;
+  const float* pm = part_ml + (row + int64_t(s0) * H) * 2;
   u32x4 o[PER];
   float2 ml[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    if (u < n_split) {
+    if (u < n_mine) {
       o[u] = *reinterpret_cast<const u32x4*>(po + u * pos_);
       ml[u] = *reinterpret_cast<const float2*>(pm + u * mls);
     }
@@ -1066,14 +1071,19 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __res
   float M = -INFINITY;
 #pragma unroll
   for (int u = 0; u < PER; ++u)
-    if (u < n_split && ml[u].y > 0.f) M = fmaxf(M, ml[u].x);
+    if (u < n_mine && ml[u].y > 0.f) M = fmaxf(M, ml[u].x);
+  // the other lane of the pair (quad_perm 1, 0, 3, 2)
+  auto other = [&](float v) __attribute__((always_inline)) {
+    return __uint_as_float(dpp_u32<0xB1>(0u, __float_as_uint(v)));
+  };
+  if constexpr (TPC == 2) M = fmaxf(M, other(M));
   float wsum = 0.f;
   float acc[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    if (u < n_split && ml[u].y > 0.f) {
+    if (u < n_mine && ml[u].y > 0.f) {
       const float w = exp2f(ml[u].x - M);
       wsum += ml[u].y * w;
 #pragma unroll
@@ -1089,6 +1099,12 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __res
       }
     }
   }
+  if constexpr (TPC == 2) {
+    wsum += other(wsum);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) acc[e] += other(acc[e]);
+    if (half) return;
+  }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;  // a query that attends no token: zeros, lse -inf
   u32x4 r;
   if constexpr (sizeof(T) == 2) {
@@ -1103,12 +1119,12 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __res
 }
 
 int attn_splits(int P, int k, int n_q) {
-  // about one block per CU (256), at most 32 splits, at least one pool per split, and few enough pools per
+  // about one block per CU (256), at most CB_MAXSPLIT splits, at least one pool per split, and few enough pools per
   // split (ceil((k + 1) / splits) <= AT_MAXSLOT / P, and <= AD_MAXPOOL) for the LDS slot and pool tables -- a
   // row shared by an MTP draft may carry the draft's own tail pool beyond its k entries
   int64_t want = (256 + int64_t(n_q) - 1) / (n_q > 0 ? n_q : 1);
   if (want > k) want = k;
-  if (want > 32) want = 32;
+  if (want > CB_MAXSPLIT) want = CB_MAXSPLIT;
   const int64_t per_split = AT_MAXSLOT / P < AD_MAXPOOL ? AT_MAXSLOT / P : AD_MAXPOOL;
   const int64_t min_splits = (int64_t(k) + 1 + per_split - 1) / per_split;
   if (want < min_splits) want = min_splits;
@@ -1173,14 +1189,18 @@ kp_status attn_noalloc_scratch(void** ptr) {
 // Split merge of n_q queries' partials (ns splits each) into out / lse.
 template <class T>
 static kp_status launch_combine(const AttnLaunch& a, int ns, const T* part_o, const float* part_ml, hipStream_t s) {
-  const int hpb = CB_THREADS / (a.V / (16 / int(sizeof(T))));
+  const int tpc = ns > 32 ? 2 : 1;  // threads per 16-byte output chunk
+  const int hpb = CB_THREADS / (tpc * (a.V / (16 / int(sizeof(T)))));
   const int64_t cblocks = int64_t(a.n_q) * ((a.H + hpb - 1) / hpb);
   if (ns <= 8)
-    attn_combine_kernel<T, 8><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H, a.V,
-                                                                                   (T*)a.out, a.lse);
+    attn_combine_kernel<T, 8, 1><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H,
+                                                                                      a.V, (T*)a.out, a.lse);
+  else if (ns <= 32)
+    attn_combine_kernel<T, 32, 1><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H,
+                                                                                       a.V, (T*)a.out, a.lse);
   else
-    attn_combine_kernel<T, CB_MAXSPLIT><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(
-        part_o, part_ml, ns, a.H, a.V, (T*)a.out, a.lse);
+    attn_combine_kernel<T, 32, 2><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H,
+                                                                                       a.V, (T*)a.out, a.lse);
   return check_launch("sparse_mla_attn (split merge)");
 }
 
