@@ -1027,36 +1027,36 @@ __global__ __launch_bounds__(AT_THREADS) void attn_dma_kernel(
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s per (query, head), with
 // M the max of m_s over non-empty splits, both sums taken in split order.  Each split's O is stored in the cache
-// dtype (rounded once, as the output is), its (m, l) in fp32.  Each thread merges 16 bytes of channels (8 bf16 or
-// 4 fp32) of one head, V / that many threads per head, 256 threads per block.  Every thread issues the loads of
-// all its splits' partial O and (m, l) at once (PER >= the split count registers of each; an empty split's O was
-// never written, so its value is dropped by a select) and computes its head's weights itself: no LDS, no barrier,
-// one wait on memory.
+// dtype (rounded once, as the output is), its (m, l) in fp32.  A group of TPC adjacent threads merges 16 bytes of
+// channels (8 bf16 or 4 fp32) of one head, each thread PER of its splits; 256 threads per block.  Every thread
+// issues the loads of all its splits' partial O and (m, l) at once (an empty split's O was never written, so its
+// value is dropped by a select) and computes its head's weights itself: no LDS, no barrier, one wait on memory.
 constexpr int CB_THREADS = 256;
 constexpr int CB_MAXSPLIT = 64;  // attn_splits never returns more
 
-// PER: splits per thread (registers for each); TPC: threads per 16-byte output chunk -- 2 above 32 splits, each
-// thread merging its own PER splits against the pair's common maximum, the pair's sums added across the two lanes
-// (adjacent lanes: one DPP exchange per value) and written by the first.
+// PER: splits per thread (registers for each); TPC: threads per 16-byte output chunk (1, 2, 4 or 8 adjacent lanes),
+// each merging its own PER splits against the group's common maximum, the group's sums added across its lanes
+// (one DPP exchange per value and lane bit) and written by the first lane.  More lanes per chunk spread a few
+// queries' many splits over more compute units: each holds fewer loads in flight.
 template <class T, int PER, int TPC>
 __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml, int n_split,
-                                                                  int H, int V, T* __restrict__ out,
+                                                                  int n_q, int H, int V, T* __restrict__ out,
                                                                   float* __restrict__ lse) {
-  static_assert(PER * TPC <= CB_MAXSPLIT && (TPC == 1 || TPC == 2), "splits per thread");
+  static_assert(PER * TPC <= CB_MAXSPLIT && (TPC == 1 || TPC == 2 || TPC == 4 || TPC == 8), "splits per thread");
   constexpr int EPT = 16 / int(sizeof(T));  // channels per thread
-  const int tph = TPC * (V / EPT);          // threads per head
-  const int hpb = CB_THREADS / tph;         // heads per block
-  const int bpq = (H + hpb - 1) / hpb;      // blocks per query
-  const int qi = blockIdx.x / bpq;
-  const int tid = threadIdx.x;
-  const int h = (blockIdx.x - qi * bpq) * hpb + tid / tph;
-  const int c = ((tid % tph) / TPC) * EPT;
-  const int half = TPC == 2 ? (tid & 1) : 0;  // which PER splits this thread merges
+  const int tph = TPC * (V / EPT);          // threads per head (a head may span blocks)
+  // thread t of the grid: query t / (H tph), head (t mod H tph) / tph, lane group (t mod tph) / TPC
+  const int64_t gt = int64_t(blockIdx.x) * CB_THREADS + threadIdx.x, per_q = int64_t(H) * tph;
+  const int qi = int(gt / per_q);
+  const int rem = int(gt - int64_t(qi) * per_q);
+  const int h = rem / tph;
+  const int c = ((rem % tph) / TPC) * EPT;
+  const int part = rem & (TPC - 1);  // which PER splits this thread merges (TPC divides tph)
   const int64_t mls = int64_t(H) * 2, pos_ = int64_t(H) * V;
-  if (h >= H) return;  // both lanes of a pair share h: pairs leave whole
+  if (qi >= n_q) return;  // past the last query (a group's lanes are adjacent: groups leave whole)
   const int64_t row = int64_t(qi) * n_split * H + h;  // split s: O at part_o + (row + s * H) * V, (m, l) likewise
-  const int s0 = half * PER, n_mine = min(PER, n_split - s0);
+  const int s0 = part * PER, n_mine = min(PER, n_split - s0);
   const T* po = part_o + (row + int64_t(s0) * H) * V + c;
   const float* pm = part_ml + (row + int64_t(s0) * H) * 2;
   u32x4 o[PER];
@@ -1072,11 +1072,17 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __res
 #pragma unroll
   for (int u = 0; u < PER; ++u)
     if (u < n_mine && ml[u].y > 0.f) M = fmaxf(M, ml[u].x);
-  // the other lane of the pair (quad_perm 1, 0, 3, 2)
-  auto other = [&](float v) __attribute__((always_inline)) {
-    return __uint_as_float(dpp_u32<0xB1>(0u, __float_as_uint(v)));
+  // the group's lanes: lane ^ 1 (quad_perm 1, 0, 3, 2), lane ^ 2 (quad_perm 2, 3, 0, 1), then the other quad of
+  // the 8 (row_half_mirror: each quad already holds its quad's value)
+  auto group = [&](float v, auto op) __attribute__((always_inline)) {
+    if constexpr (TPC >= 2) v = op(v, __uint_as_float(dpp_u32<0xB1>(0u, __float_as_uint(v))));
+    if constexpr (TPC >= 4) v = op(v, __uint_as_float(dpp_u32<0x4E>(0u, __float_as_uint(v))));
+    if constexpr (TPC >= 8) v = op(v, __uint_as_float(dpp_u32<0x141>(0u, __float_as_uint(v))));
+    return v;
   };
-  if constexpr (TPC == 2) M = fmaxf(M, other(M));
+  auto fmax2 = [](float a, float b) { return fmaxf(a, b); };
+  auto fadd2 = [](float a, float b) { return a + b; };
+  M = group(M, fmax2);
   float wsum = 0.f;
   float acc[EPT];
 #pragma unroll
@@ -1099,11 +1105,11 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine_kernel(const T* __res
       }
     }
   }
-  if constexpr (TPC == 2) {
-    wsum += other(wsum);
+  if constexpr (TPC > 1) {
+    wsum = group(wsum, fadd2);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) acc[e] += other(acc[e]);
-    if (half) return;
+    for (int e = 0; e < EPT; ++e) acc[e] = group(acc[e], fadd2);
+    if (part) return;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;  // a query that attends no token: zeros, lse -inf
   u32x4 r;
@@ -1189,18 +1195,17 @@ kp_status attn_noalloc_scratch(void** ptr) {
 // Split merge of n_q queries' partials (ns splits each) into out / lse.
 template <class T>
 static kp_status launch_combine(const AttnLaunch& a, int ns, const T* part_o, const float* part_ml, hipStream_t s) {
-  const int tpc = ns > 32 ? 2 : 1;  // threads per 16-byte output chunk
-  const int hpb = CB_THREADS / (tpc * (a.V / (16 / int(sizeof(T)))));
-  const int64_t cblocks = int64_t(a.n_q) * ((a.H + hpb - 1) / hpb);
-  if (ns <= 8)
-    attn_combine_kernel<T, 8, 1><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H,
-                                                                                      a.V, (T*)a.out, a.lse);
-  else if (ns <= 32)
-    attn_combine_kernel<T, 32, 1><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H,
-                                                                                       a.V, (T*)a.out, a.lse);
+  const int tpc = ns <= 8 ? 1 : ns <= 16 ? 2 : ns <= 32 ? 4 : 8;  // threads per 16-byte output chunk, 8 splits each
+  const int64_t threads = int64_t(a.n_q) * a.H * tpc * (a.V / (16 / int(sizeof(T))));
+  const dim3 grid(unsigned((threads + CB_THREADS - 1) / CB_THREADS)), block(CB_THREADS);
+  if (tpc == 1)
+    attn_combine_kernel<T, 8, 1><<<grid, block, 0, s>>>(part_o, part_ml, ns, a.n_q, a.H, a.V, (T*)a.out, a.lse);
+  else if (tpc == 2)
+    attn_combine_kernel<T, 8, 2><<<grid, block, 0, s>>>(part_o, part_ml, ns, a.n_q, a.H, a.V, (T*)a.out, a.lse);
+  else if (tpc == 4)
+    attn_combine_kernel<T, 8, 4><<<grid, block, 0, s>>>(part_o, part_ml, ns, a.n_q, a.H, a.V, (T*)a.out, a.lse);
   else
-    attn_combine_kernel<T, 32, 2><<<dim3(unsigned(cblocks)), dim3(CB_THREADS), 0, s>>>(part_o, part_ml, ns, a.H,
-                                                                                       a.V, (T*)a.out, a.lse);
+    attn_combine_kernel<T, 8, 8><<<grid, block, 0, s>>>(part_o, part_ml, ns, a.n_q, a.H, a.V, (T*)a.out, a.lse);
   return check_launch("sparse_mla_attn (split merge)");
 }
 
