@@ -310,6 +310,36 @@ def test_workspace_reuse_across_query_counts():
     _free()
 
 
+def test_split_merge_lane_groups():
+    """The split merge at every lane grouping: batches of 10, 15, 20 and 25 queries (5 queries repeated) take
+    26, 18, 13 and 11 splits, merged by groups of 4, 4, 2 and 2 lanes; every output row is within the attention
+    tolerance of the 5-query call (52 splits, groups of 8), which the oracle checks, and its lse likewise."""
+    import sparse_attention_kpool_amd as K
+    wl = _small_decode("merge_lanes")
+    _say("[case merge_lanes]")
+    run = DeviceRun(wl).run()
+    check_run(run, list(range(wl.n_q)))
+    n5 = wl.n_q
+    tol = attn_tolerance(wl.dtype)[0]
+    for rep in (2, 3, 4, 5):
+        idx = torch.arange(n5, device="cuda").repeat(rep)
+        qs = K.Queries(seq=run.queries.seq[idx].contiguous(), pos=run.queries.pos[idx].contiguous(),
+                       max_pos=run.queries.max_pos, group=1)
+        sel, nsel = run.layer.sel[:n5][idx].contiguous(), run.layer.n_sel[:n5][idx].contiguous()
+        out = torch.empty((n5 * rep, wl.H, wl.V), dtype=run.out.dtype, device="cuda")
+        lse = torch.empty((n5 * rep, wl.H), dtype=torch.float32, device="cuda")
+        ws = torch.empty((K.sparse_mla_workspace_size(run.dims, qs) + 15) // 16 * 4, dtype=torch.float32,
+                         device="cuda")
+        K.sparse_mla_attn(run.dims, run.cache, qs, run.q[idx].contiguous(), sel, nsel, out, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        err = (out.float() - run.out.float().repeat(rep, 1, 1)).abs().max().item()
+        assert err <= tol, f"{n5 * rep} queries: max abs {err} against the 5-query call"
+        lerr = (lse - run.lse.repeat(rep, 1)).abs().max().item()
+        assert lerr <= 1e-3, f"{n5 * rep} queries: lse differs by {lerr}"
+    del run
+    _free()
+
+
 def test_mtp_shared_selection():
     """MTP drafts reusing their targets' selections (sparse_mla_attn_shared): targets at T-2, drafts at T-1 of the
     same sequences.  A target reading its own row reproduces sparse_mla_attn bit for bit; a draft matches the oracle
