@@ -754,6 +754,21 @@ def test_full_prefill64k():
 
 
 @pytest.mark.slow
+def test_full_max_two_step_row():
+    """One sequence at 2,097,152 tokens, paged: a row of 524,288 pools, the longest the two-step selection takes
+    (16 chunks of 32,768 pools, merged as a tree of four groups of four), scored by the decode scorer and attended
+    in 64 splits; every stage against the oracle."""
+    T = 1 << 21
+    wl = ks.scaled(ks.workloads()["decode32k"], name="max_row", ctx=[T], new_from=[T - 1],
+                   q_seq=np.zeros(1, np.int32), q_pos=np.array([T - 1], np.int32), seed=6, page_perm_seed=66)
+    _say(f"[case max_row] B=1 T={T}")
+    run = DeviceRun(wl).run()
+    check_run(run, [0])
+    del run
+    _free()
+
+
+@pytest.mark.slow
 def test_full_long1m():
     wl = ks.workloads()["long1m"]
     _say("[case long1m] B=8 T=1048576")
