@@ -304,6 +304,9 @@ kp_status sparse_mla_attn_fp8(const kp_dims* dims, const kp_cache* cache, const 
  *                   -> C = q + h*L (ldc H*L): columns 0..V-1 of each query row; the rotary columns V..L-1 are
  *                   not written (keep them zero)
  *     un-absorb     batch H: A = out + h*V (lda H*V), W = W_UV[h] [dv, V] (stride dv*V) -> C = o + h*dv
+ *   The absorb and un-absorb shapes, (N, K) = (512, 256) or (256, 512), with batch >= 8, M >= 512 and rows
+ *     16-byte aligned (ldc, stride_c times the element size multiples of 16), run weight-stationary: one launch,
+ *     each batch entry's weight held on chip while its rows stream past; no workspace, same formula.
  *   Limits: K a multiple of 64; lda, ldw, stride_a, stride_w multiples of 8; ldc, stride_c multiples of 4;
  *   lda, ldw >= K; ldc >= N; every operand 16-byte aligned.  batch, M or N = 0 is a valid empty call.
  *   Errors: KP_ERR_INVALID_ARG (pointers, strides, alignment, c_dtype, alpha not finite), KP_ERR_UNSUPPORTED (K).
@@ -329,7 +332,8 @@ typedef struct {
 
 /*
  * kp_linear_group -- up to 8 independent kp_linear products in one launch (plus one launch that adds split-K
- *   partials, when any product splits): the products of one layer step that do not depend on each other (the
+ *   partials, when any product splits, and one launch of its own for each product that runs weight-stationary
+ *   under kp_linear's rule, issued first): the products of one layer step that do not depend on each other (the
  *   indexer's projections and the query absorb of a decode step) pay the launch cost once.  Each product follows
  *   kp_linear's formula and contract.  Its tile shape (chosen by the group's largest M) and its K split (chosen
  *   from the whole group's work) can differ from a kp_linear call of its own, and so can the rounding of its sums;

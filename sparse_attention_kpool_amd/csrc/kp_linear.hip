@@ -34,7 +34,8 @@
 //
 // Bound: the decode shapes (M = tokens of a step, tens) stream their weights once -- HBM.  The prefill shapes
 // (M = thousands) are MFMA-bound at 2 M N K flop, except the absorb and un-absorb, whose outputs and inputs
-// (268 + 134 MB at 4096 tokens) put their HBM time above their MFMA time.
+// (268 + 134 MB at 4096 tokens) put their HBM time above their MFMA time: at prefill sizes those two run in the
+// weight-stationary kernel further down instead of these tiles.
 #include "kp_device.hpp"
 #include "kp_internal.hpp"
 
@@ -466,7 +467,17 @@ static kp_status launch_group(const LinearLaunch* probs, int n, void* ws, size_t
   return check_launch("kp_linear");
 }
 
-size_t linear_group_workspace(const LinearLaunch* probs, int n) {
+static bool linear_ws_shape(const LinearLaunch& a, int& nt, int& ks, int& mt);
+
+size_t linear_group_workspace(const LinearLaunch* probs_in, int n_in) {
+  // the weight-stationary products never split; the rest are sized as the tiled launch will run them
+  LinearLaunch rest[LN_MAXGROUP];
+  int n = 0;
+  for (int i = 0; i < n_in && i < LN_MAXGROUP; ++i) {
+    int nt, ks, mt;
+    if (!linear_ws_shape(probs_in[i], nt, ks, mt)) rest[n++] = probs_in[i];
+  }
+  const LinearLaunch* probs = rest;
   int maxM = 0;
   for (int i = 0; i < n; ++i) maxM = max(maxM, probs[i].M);
   if (maxM == 0) return 0;
@@ -484,7 +495,237 @@ size_t linear_group_workspace(const LinearLaunch* probs, int n) {
   return total;
 }
 
-kp_status launch_linear_group(const LinearLaunch* probs, int n, void* ws, size_t ws_bytes, hipStream_t s) {
+// ---------------------------------------------------------------------------------------------------------------
+// Weight-stationary head products.  The absorb (N = 512, K = 256) and the un-absorb (N = 256, K = 512) of a
+// prefill chunk are batches over heads whose one entry's weight is only 256 KiB, while M is thousands of tokens.
+// Output-stationary tiles re-fetch a weight tile and an activation tile for every 128 x 128 outputs (128 KiB of
+// operands through L2 and LDS for 32 KiB of output at K = 256), which paced these two products well above their
+// HBM time.  Here one block of 8 waves owns one batch entry over a range of tokens: each wave holds its N / 8
+// output columns' weight rows in registers for the whole block (N K / 1024 VGPRs: 128 for both shapes), the
+// tokens stream through LDS in slabs of 16 MT rows (direct global->LDS loads, a ring of three, two slabs ahead,
+// rows XOR-swizzled as in the tiled kernel), and each slab's output leaves straight from the MFMA lanes (4
+// consecutive columns of one row a lane).  Per slab a block reads 16 MT K bf16 and writes 16 MT N outputs, which
+// is all the HBM traffic there is besides one read of the weight per block.
+//   math   D^T[n][m] = W . A^T on 16x16x32 bf16 MFMA: weight rows are the M operand (in registers), activation
+//          rows the N operand (one 16-byte LDS read per lane per m-tile and k-step, shared by the wave's NT
+//          n-tiles).
+//   stores raw buffer stores through a resource bounded at M rows, so rows past M (the last slab of a block) are
+//          dropped by the hardware and every lane issues the same stores: the waits below are exact counts.
+// Slots past the end: a block whose token range is empty exits; a slab index past the block's last one re-reads
+// the last slab (never multiplied), so each iteration issues the same loads.
+constexpr int LWS_WAVES = 8;
+constexpr int LWS_THREADS = 64 * LWS_WAVES;
+constexpr int LWS_NBUF = 3;
+
+template <int NT, int KS, int MT, bool OB>
+__global__ __launch_bounds__(LWS_THREADS) void linear_ws_kernel(const LinearProb P, int batch, int mblocks,
+                                                                int slabs_per_block) {
+  constexpr int K = 32 * KS, CPR = K / 8;  // 16-byte chunks per activation row
+  constexpr int MS = 16 * MT;              // tokens per slab
+  constexpr int SLAB = MS * K;             // bf16 per slab
+  constexpr int L = SLAB * 2 / (1024 * LWS_WAVES);  // direct-load instructions per wave per slab
+  constexpr int ESZ = OB ? 2 : 4;                   // output element bytes
+  constexpr int ROWB = 128 * NT * ESZ;              // bytes of one output row (N = 8 waves x 16 NT columns)
+  constexpr int CR = ROWB / 16;                     // 16-byte chunks per output row
+  constexpr int OUTB = MS * ROWB;                   // bytes of a slab's output
+  constexpr int S = OUTB / (1024 * LWS_WAVES);      // 1 KiB output stores per wave per slab
+  static_assert(L >= 1 && (SLAB * 2) % (1024 * LWS_WAVES) == 0, "a slab is a whole number of block-wide loads");
+  static_assert(S >= 1 && OUTB % (1024 * LWS_WAVES) == 0, "a slab's output is a whole number of block-wide stores");
+  static_assert(CPR >= 16 && CPR % 16 == 0 && CR >= 16 && CR % 16 == 0, "the row swizzles need 16 chunk positions");
+  __shared__ __align__(1024) bf16 ring[LWS_NBUF][SLAB];
+  __shared__ __align__(1024) char stage[OUTB];  // a slab's output rows, chunk c of row r at position c ^ (r mod 16)
+
+  // blocks are dealt to the 8 XCDs round-robin; XCD x takes the contiguous run [x per, (x + 1) per) of block
+  // slots, so the token ranges of one batch entry (which share its weight) run on one XCD
+  const int per = int(gridDim.x >> 3);
+  const int t = int(blockIdx.x & 7) * per + int(blockIdx.x >> 3);
+  const int b = t / mblocks, mb = t - b * mblocks;
+  const int M = P.M;
+  const int m_begin = mb * slabs_per_block * MS;
+  if (b >= batch || m_begin >= M) return;  // uniform over the block
+  const int nslab = min(slabs_per_block, (M - m_begin + MS - 1) / MS);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int l16 = lane & 15, g = lane >> 4;
+
+  // slab loads: wave instruction i fills LDS chunk positions 64 (wave L + i) + lane, i.e. row r, position p; the
+  // chunk stored there is c = p ^ (r mod 16) of that row
+  const bf16* A = P.A + int64_t(b) * P.sa;
+  int lrow[L], lcol[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int q = 64 * (wave * L + i) + lane;
+    lrow[i] = q / CPR;
+    lcol[i] = 8 * ((q % CPR) ^ (lrow[i] & 15));
+  }
+  auto issue = [&](int s, int buf) __attribute__((always_inline)) {
+    const int m0 = m_begin + min(s, nslab - 1) * MS;
+    const uint32_t base = lds_off(ring[buf]);
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      lds_dma16(A + int64_t(min(m0 + lrow[i], M - 1)) * P.lda + lcol[i], base + uint32_t(1024 * (wave * L + i)));
+  };
+  issue(0, 0);
+  issue(1, 1);
+
+  // this wave's weight rows n_w + 16 a + l16, k chunk 4 ks + g, for the whole block
+  const int n_w = wave * 16 * NT;
+  const bf16* W = P.W + int64_t(b) * P.sw;
+  bf16x8 wf[NT][KS];
+#pragma unroll
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      wf[a][ks] = *reinterpret_cast<const bf16x8*>(W + int64_t(n_w + 16 * a + l16) * P.ldw + 8 * (4 * ks + g));
+  // the weight is waited for here, once, and not inside the slab loop (this wait also covers slabs 0 and 1)
+#pragma unroll
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(wf[a][ks]));
+
+  // output rows of one batch entry through a buffer resource bounded at M rows
+  const uint64_t cb = reinterpret_cast<uint64_t>(static_cast<char*>(P.C) + int64_t(b) * P.sc * ESZ);
+  const uint64_t cb_u = (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(cb >> 32)))) << 32) |
+                        uint32_t(__builtin_amdgcn_readfirstlane(int(cb)));
+  const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(cb_u), 0, __builtin_amdgcn_readfirstlane(int(int64_t(M) * P.ldc * ESZ)), 0x00020000);
+  const float alpha = P.alpha;
+  const uint32_t st = lds_off(stage);
+
+  for (int s = 0; s < nslab; ++s) {
+    // issue order: slab loads (L a wave) then the slab's stores (S a wave) each iteration, after slabs 0 and 1
+    // up front; vector-memory operations complete in issue order, so slab s has landed once at most the ops
+    // issued after it are outstanding: slab 1 (s = 0); slab 2 and stores 0 (s = 1); stores s-2, slab s+1 and
+    // stores s-1 (s >= 2)
+    if (s == 0)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
+    else if (s == 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(L + S));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(L + 2 * S));
+    // slab s is visible to every wave; every wave is done with slab s - 1's buffer and its staged output
+    __syncthreads();
+    issue(s + 2, (s + 2) % LWS_NBUF);
+    const uint32_t base = lds_off(ring[s % LWS_NBUF]);
+    f32x4 acc[NT][MT];
+#pragma unroll
+    for (int a = 0; a < NT; ++a)
+#pragma unroll
+      for (int c = 0; c < MT; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // activation fragments one k-step ahead of the MFMAs that use them
+    bf16x8 fa[2][MT];
+    auto read_fa = [&](int ks, bf16x8(&f)[MT]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int c = 0; c < MT; ++c) f[c] = lds_load<bf16x8>(base + (16 * c + l16) * (2 * K) + 16 * ((4 * ks + g) ^ l16));
+    };
+    read_fa(0, fa[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) read_fa(ks + 1, fa[(ks + 1) & 1]);
+#pragma unroll
+      for (int a = 0; a < NT; ++a)
+#pragma unroll
+        for (int c = 0; c < MT; ++c) acc[a][c] = mfma16(wf[a][ks], fa[ks & 1][c], acc[a][c]);
+    }
+    // lane holds D^T[n][m] for n = n_w + 16 a + 4 g .. +3 and m = slab row 16 c + l16: staged, then the slab's
+    // rows leave as whole 1 KiB wave stores
+#pragma unroll
+    for (int a = 0; a < NT; ++a)
+#pragma unroll
+      for (int c = 0; c < MT; ++c) {
+        const f32x4 v = acc[a][c] * alpha;
+        const int r = 16 * c + l16, nb = (n_w + 16 * a + 4 * g) * ESZ;
+        const uint32_t at = st + uint32_t(r * ROWB + 16 * ((nb >> 4) ^ (r & 15)) + (nb & 15));
+        if constexpr (OB)
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(uintptr_t(at)) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        else
+          *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(uintptr_t(at)) = v;
+      }
+    __syncthreads();
+    const int m0 = m_begin + s * MS;
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const int q = 64 * (wave * S + i) + lane, r = q / CR, cl = q % CR;
+      const u32x4 v = lds_load<u32x4>(st + uint32_t(r * ROWB + 16 * (cl ^ (r & 15))));
+      __builtin_amdgcn_raw_buffer_store_b128(v, dst, int(int64_t(m0 + r) * P.ldc * ESZ + 16 * cl), 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may land in LDS after the block ends
+}
+
+// The shapes the weight-stationary kernel takes: the two head-product shapes with a prefill's token count, 16-byte
+// aligned operands, and row offsets that fit its 32-bit store offsets.
+static bool linear_ws_shape(const LinearLaunch& a, int& nt, int& ks, int& mt) {
+  if (a.N == 512 && a.K == 256) {
+    nt = 4, ks = 8, mt = 2;
+  } else if (a.N == 256 && a.K == 512) {
+    nt = 2, ks = 16, mt = 2;
+  } else {
+    return false;
+  }
+  const int esz = a.c_dtype == KP_DTYPE_BF16 ? 2 : 4;
+  const auto al = [](const void* p, int n) { return (reinterpret_cast<uintptr_t>(p) & uintptr_t(n - 1)) == 0; };
+  return a.batch >= 8 && a.M >= 512 && al(a.A, 16) && al(a.W, 16) && al(a.C, 16) && a.lda % 8 == 0 &&
+         a.sa % 8 == 0 && a.ldw % 8 == 0 && a.sw % 8 == 0 && (a.ldc * esz) % 16 == 0 && (a.sc * esz) % 16 == 0 &&
+         (int64_t(a.M) + 64) * a.ldc * esz < (int64_t(1) << 31);
+}
+
+static kp_status launch_linear_ws(const LinearLaunch& a, hipStream_t s) {
+  int nt = 0, ks = 0, mt = 0;
+  linear_ws_shape(a, nt, ks, mt);
+  const int ms = 16 * mt;
+  const int cus = device_cus();
+  // about one block per CU: the token ranges of a batch entry split its rows into whole slabs
+  const int mblocks = max(1, min((a.M + ms - 1) / ms, (cus + a.batch - 1) / a.batch));
+  const int slabs = ((a.M + ms - 1) / ms + mblocks - 1) / mblocks;
+  const int64_t blocks = (int64_t(a.batch) * mblocks + 7) / 8 * 8;
+  if (blocks > 0x7fffffff) {
+    set_error("kp_linear: %lld blocks exceed the grid", (long long)blocks);
+    return KP_ERR_INVALID_ARG;
+  }
+  LinearProb P{};
+  P.A = static_cast<const bf16*>(a.A);
+  P.W = static_cast<const bf16*>(a.W);
+  P.C = a.C;
+  P.lda = a.lda;
+  P.sa = a.sa;
+  P.ldw = a.ldw;
+  P.sw = a.sw;
+  P.ldc = a.ldc;
+  P.sc = a.sc;
+  P.M = a.M;
+  P.N = a.N;
+  P.K = a.K;
+  P.c_bf16 = a.c_dtype == KP_DTYPE_BF16;
+  P.alpha = a.alpha;
+  const dim3 grid{unsigned(blocks)}, blk{unsigned(LWS_THREADS)};
+  if (nt == 4 && P.c_bf16)
+    linear_ws_kernel<4, 8, 2, true><<<grid, blk, 0, s>>>(P, a.batch, mblocks, slabs);
+  else if (nt == 4)
+    linear_ws_kernel<4, 8, 2, false><<<grid, blk, 0, s>>>(P, a.batch, mblocks, slabs);
+  else if (P.c_bf16)
+    linear_ws_kernel<2, 16, 2, true><<<grid, blk, 0, s>>>(P, a.batch, mblocks, slabs);
+  else
+    linear_ws_kernel<2, 16, 2, false><<<grid, blk, 0, s>>>(P, a.batch, mblocks, slabs);
+  return check_launch("kp_linear");
+}
+
+kp_status launch_linear_group(const LinearLaunch* probs_in, int n_in, void* ws, size_t ws_bytes, hipStream_t s) {
+  // products of the weight-stationary shapes take a launch of their own; the rest share the tiled launch
+  LinearLaunch rest[LN_MAXGROUP];
+  int n = 0;
+  for (int i = 0; i < n_in; ++i) {
+    int nt, ks, mt;
+    if (linear_ws_shape(probs_in[i], nt, ks, mt)) {
+      const kp_status st = launch_linear_ws(probs_in[i], s);
+      if (st != KP_OK) return st;
+    } else {
+      rest[n++] = probs_in[i];
+    }
+  }
+  const LinearLaunch* probs = rest;
   int maxM = 0;
   for (int i = 0; i < n; ++i) maxM = max(maxM, probs[i].M);
   if (maxM == 0) return KP_OK;

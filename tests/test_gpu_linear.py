@@ -163,6 +163,53 @@ def test_mla_unabsorb_output(T, kind):
     _check(o.float().cpu().numpy(), ref, abs_sum, True, kind == "int", "unabsorb")
 
 
+@pytest.mark.parametrize("T,kind", [(512, "int"), (1000, "int"), (1000, "normal")])
+def test_absorb_weight_stationary(T, kind):
+    """The absorb at prefill token counts (the weight-stationary kernel: one block per head and token range, the
+    head's weight in registers, 32-token slabs; T = 1000 ends in a partial slab): every row of every head against
+    the oracle, and the rotary columns of q untouched."""
+    _say(f"mla_absorb_q (weight-stationary): T={T} kind={kind}")
+    q_nope = ks.host_matrix(SEED, f"ws{T}:q", (T, H, DN), kind)
+    w_uk = ks.host_matrix(SEED, f"ws{T}:w", (H, DN, V), kind, 1.0 if kind == "int" else 2.0 ** -4)
+    q = torch.full((T, H, L), 5.0, dtype=torch.bfloat16, device="cuda")
+    K.mla_absorb_q(_dev(q_nope), _dev(np.ascontiguousarray(np.transpose(w_uk, (0, 2, 1)))), q)
+    torch.cuda.synchronize()
+    got = q.float().cpu().numpy()
+    _check(got[:, :, :V], O.mla_absorb_q(q_nope, w_uk), O.mla_absorb_q(np.abs(q_nope), np.abs(w_uk)), True,
+           kind == "int", "absorb")
+    assert np.all(got[:, :, V:] == 5.0), "absorb wrote into the rotary columns"
+
+
+@pytest.mark.parametrize("T,kind,out", [(777, "int", torch.float32), (1000, "normal", torch.bfloat16),
+                                        (1000, "normal", torch.float32)])
+def test_unabsorb_weight_stationary(T, kind, out):
+    """The un-absorb at prefill token counts (weight-stationary kernel, bf16 and fp32 outputs): every output."""
+    _say(f"mla_unabsorb_o (weight-stationary): T={T} kind={kind} out={out}")
+    o_lat = ks.host_matrix(SEED, f"wsu{T}:o", (T, H, V), kind)
+    w_uv = ks.host_matrix(SEED, f"wsu{T}:w", (H, DV, V), kind, 1.0 if kind == "int" else 2.0 ** -4)
+    o = torch.full((T, H, DV), 7.0, dtype=out, device="cuda")
+    K.mla_unabsorb_o(_dev(o_lat), _dev(w_uv), o)
+    torch.cuda.synchronize()
+    _check(o.float().cpu().numpy(), O.mla_unabsorb_o(o_lat, w_uv), O.mla_unabsorb_o(np.abs(o_lat), np.abs(w_uv)),
+           out == torch.bfloat16, kind == "int", "unabsorb")
+
+
+def test_weight_stationary_batch8_alpha_and_padded_rows():
+    """A plain batch of 8 entries of each weight-stationary shape through kp_linear, with alpha and output rows
+    padded past N (the padding is never written), integer operands (exact)."""
+    for N_, K_, M in ((512, 256, 600), (256, 512, 513)):
+        _say(f"linear (weight-stationary): batch 8 M={M} N={N_} K={K_}")
+        a = ks.host_matrix(SEED, f"ws8:a{N_}", (8, M, K_), "int")
+        w = ks.host_matrix(SEED, f"ws8:w{N_}", (8, N_, K_), "int")
+        c_full = torch.full((8, M, N_ + 8), 3.0, dtype=torch.bfloat16, device="cuda")
+        K.linear(_dev(a), _dev(w), c_full[:, :, :N_], alpha=0.5)
+        torch.cuda.synchronize()
+        got = c_full[:, :, :N_].float().cpu().numpy()
+        ref = np.stack([0.5 * O.linear(a[i], w[i]) for i in range(8)])
+        np.testing.assert_array_equal(got, O.bf16_round(ref), err_msg=f"N={N_}")
+        assert torch.all(c_full[:, :, N_:] == 3.0).item(), "wrote past column N"
+
+
 def test_prefill_index_query_sampled_rows():
     """The 4096-token prefill chunk through the 128 x 128 tile path; 256 sampled rows, every column."""
     T = 4096
