@@ -23,7 +23,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // 16-byte staging registers.  A native vector type, not HIP's uint4 struct: copies of that struct-with-union
 // can keep whole staging arrays out of registers (in scratch).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 

@@ -513,6 +513,7 @@ size_t linear_group_workspace(const LinearLaunch* probs_in, int n_in) {
 //          dropped by the hardware and every lane issues the same stores: the waits below are exact counts.
 // Slots past the end: a block whose token range is empty exits; a slab index past the block's last one re-reads
 // the last slab (never multiplied), so each iteration issues the same loads.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // an 8-byte store's payload
 constexpr int LWS_WAVES = 8;
 constexpr int LWS_THREADS = 64 * LWS_WAVES;
 constexpr int LWS_NBUF = 3;
