@@ -364,8 +364,11 @@ static LinearTile linear_tile(int M) { return M <= 64 ? LinearTile{64, 64, 64} :
 
 // k-splits of a group's products, a pure function of the shapes.  The group's work is sum(tiles x stages); spread
 // over two blocks per CU it gives the stages each block slot runs on average (at least 4).  A product whose blocks
-// would run more than twice that is split down to about that many stages per block (the split-K reduction costs a
-// launch, so a product is split only where it would otherwise be the long pole).
+// would run more than twice that (decode tiles) or more than that (prefill tiles) is split down to about that many
+// stages per block (the split-K reduction costs a launch, so a product is split only where it would otherwise be
+// the long pole).  At 4096 tokens the head-weight, key and gate products (64 stages a block beside the index
+// query's 24) then split in two: the grouped indexer products 210 -> 192 us; the same rule at 64 tokens made the
+// decode group slower (20.7 -> 24.8 us), so decode tiles keep twice the average.
 static void linear_splits(const LinearTile& t, const LinearLaunch* probs, int n, int cus, int* sp) {
   int64_t work = 0;
   for (int i = 0; i < n; ++i) {
@@ -378,7 +381,7 @@ static void linear_splits(const LinearTile& t, const LinearLaunch* probs, int n,
   for (int i = 0; i < n; ++i) {
     const int nk = probs[i].K / t.BK;
     sp[i] = 1;
-    if (probs[i].batch <= 0 || probs[i].M <= 0 || probs[i].N <= 0 || nk <= 2 * load) continue;
+    if (probs[i].batch <= 0 || probs[i].M <= 0 || probs[i].N <= 0 || nk <= (t.BM >= 128 ? load : 2 * load)) continue;
     const int want = int((nk + load - 1) / load);
     const int s1 = max(1, min(want, nk / 4));  // at least 4 stages per split
     const int per = (nk + s1 - 1) / s1;
