@@ -246,6 +246,28 @@ def test_linear_workspace_sizes():
     assert n > 0 and n % (64 * 64 * 4) == 0
 
 
+def test_linear_prefill_split_rule_and_weight_stationary_products():
+    """At prefill sizes a product of 128 x 128 tiles splits K once its blocks would run more stages than the group's
+    average per block slot (the head-weight product beside the index query: 64 stages against an average of 52),
+    and the absorb / un-absorb shapes run weight-stationary: they take no workspace and do not count towards the
+    other products' split (a group with the absorb asks for exactly what the group without it asks for)."""
+    lib = K.load()
+    T = 4096
+
+    def prob(batch, M, N, K_, lda, sa, ldw, sw, ldc, sc, dt=K.KP_DTYPE_BF16):
+        return K._LinearProblem(batch, M, N, K_, FAKE, lda, sa, FAKE, ldw, sw, FAKE, ldc, sc, dt, 1.0)
+    index_query = prob(1, T, 4096, 1536, 1536, 0, 1536, 0, 4096, 0)
+    head_weights = prob(1, T, 32, 4096, 4096, 0, 4096, 0, 32, 0, K.KP_DTYPE_F32)
+    absorb = prob(64, T, 512, 256, 64 * 256, 256, 256, 512 * 256, 64 * 576, 576)
+    unabsorb = prob(64, T, 256, 512, 64 * 512, 512, 512, 256 * 512, 64 * 256, 256)
+    two = (K._LinearProblem * 2)(index_query, head_weights)
+    three = (K._LinearProblem * 3)(index_query, head_weights, absorb)
+    assert lib.kp_linear_group_workspace_size(2, two) > 0
+    assert lib.kp_linear_group_workspace_size(3, three) == lib.kp_linear_group_workspace_size(2, two)
+    assert K.linear_workspace_size(64, T, 512, 256) == 0 and K.linear_workspace_size(64, T, 256, 512) == 0
+    assert lib.kp_linear_group_workspace_size(1, (K._LinearProblem * 1)(unabsorb)) == 0
+
+
 def test_linear_group_validation():
     """kp_linear_group checks the product count, the list and every product before launching anything."""
     lib = K.load()
