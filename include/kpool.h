@@ -333,7 +333,7 @@ typedef struct {
 /*
  * kp_linear_group -- up to 8 independent kp_linear products in one launch (plus one launch that adds split-K
  *   partials, when any product splits, and one launch of its own for each product that runs weight-stationary
- *   under kp_linear's rule, issued first): the products of one layer step that do not depend on each other (the
+ *   under kp_linear's rule, issued after them): the products of one layer step that do not depend on each other (the
  *   indexer's projections and the query absorb of a decode step) pay the launch cost once.  Each product follows
  *   kp_linear's formula and contract.  Its tile shape (chosen by the group's largest M) and its K split (chosen
  *   from the whole group's work) can differ from a kp_linear call of its own, and so can the rounding of its sums;

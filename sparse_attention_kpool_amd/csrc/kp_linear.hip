@@ -744,25 +744,29 @@ static kp_status launch_linear_ws(const LinearLaunch& a, hipStream_t s) {
 }
 
 kp_status launch_linear_group(const LinearLaunch* probs_in, int n_in, void* ws, size_t ws_bytes, hipStream_t s) {
-  // products of the weight-stationary shapes take a launch of their own; the rest share the tiled launch
+  // products of the weight-stationary shapes take a launch of their own; the rest share the tiled launch, which
+  // goes first: its grid check is the last check that can fail, so an error leaves nothing enqueued (a
+  // weight-stationary grid, at most batch + one block per CU rounded to 8, always fits)
   LinearLaunch rest[LN_MAXGROUP];
-  int n = 0;
+  int n = 0, ws_idx[LN_MAXGROUP], n_ws = 0;
   for (int i = 0; i < n_in; ++i) {
     int nt, ks, mt;
-    if (linear_ws_shape(probs_in[i], nt, ks, mt)) {
-      const kp_status st = launch_linear_ws(probs_in[i], s);
-      if (st != KP_OK) return st;
-    } else {
-      rest[n++] = probs_in[i];
-    }
+    if (linear_ws_shape(probs_in[i], nt, ks, mt)) ws_idx[n_ws++] = i;
+    else rest[n++] = probs_in[i];
   }
-  const LinearLaunch* probs = rest;
   int maxM = 0;
-  for (int i = 0; i < n; ++i) maxM = max(maxM, probs[i].M);
-  if (maxM == 0) return KP_OK;
-  // one tile shape for the whole group, chosen by its largest row count
-  if (linear_tile(maxM).BM == 64) return launch_group<64, 64, 64, 3>(probs, n, ws, ws_bytes, s);
-  return launch_group<128, 128, 64, 2>(probs, n, ws, ws_bytes, s);
+  for (int i = 0; i < n; ++i) maxM = max(maxM, rest[i].M);
+  if (maxM > 0) {
+    // one tile shape for the whole group, chosen by its largest row count
+    const kp_status st = linear_tile(maxM).BM == 64 ? launch_group<64, 64, 64, 3>(rest, n, ws, ws_bytes, s)
+                                                    : launch_group<128, 128, 64, 2>(rest, n, ws, ws_bytes, s);
+    if (st != KP_OK) return st;
+  }
+  for (int i = 0; i < n_ws; ++i) {
+    const kp_status st = launch_linear_ws(probs_in[ws_idx[i]], s);
+    if (st != KP_OK) return st;
+  }
+  return KP_OK;
 }
 
 }  // namespace kp
